@@ -1,0 +1,257 @@
+// kvq_api.hip -- the C ABI of libkvq: argument validation, launch planning and
+// dispatch onto the caller's HIP stream.  Declarations and semantics are in
+// include/kvq.h.  Nothing here allocates device memory or synchronizes.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/kvq.h"
+#include "kvq_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return KVQ_OK;
+}
+
+int check_layout(const kvq_layout* L, kvq::Geom* g) {
+    if (L == nullptr) return fail(KVQ_ERR_INVALID_ARG, "layout is NULL");
+    if (L->n_kv_heads < 1 || L->head_dim < 1 || L->page_size < 1 || L->n_pages < 1)
+        return fail(KVQ_ERR_INVALID_ARG, "layout fields must be >= 1 (n_kv_heads=%d head_dim=%d page_size=%d n_pages=%d)",
+                    L->n_kv_heads, L->head_dim, L->page_size, L->n_pages);
+    if (L->head_dim != 64 && L->head_dim != 128 && L->head_dim != 256)
+        return fail(KVQ_ERR_UNSUPPORTED, "head_dim %d not built (64, 128, 256)", L->head_dim);
+    if (L->page_size % kvq::kChunk != 0 || L->page_size > 1024)
+        return fail(KVQ_ERR_UNSUPPORTED, "page_size %d must be a multiple of 32 in [32, 1024]", L->page_size);
+    *g = kvq::Geom{L->head_dim, L->page_size, L->n_kv_heads, L->n_pages};
+    const double total = (double)g->unit_bytes() * L->n_kv_heads * L->n_pages;
+    if (total > 9.0e18) return fail(KVQ_ERR_INVALID_ARG, "pool size overflows");
+    return KVQ_OK;
+}
+
+// Split heuristic: enough independent wavefronts to cover 256 CUs several
+// times over, with partials small next to the cache bytes.
+int auto_chunks_per_split(int kernel, int total_chunks, int n_kv, int n_q, int rows) {
+    long units = (long)total_chunks * n_kv;
+    if (kernel == 1) {
+        // one wave per (split, KV head, query); aim for ~4096 waves
+        long per = units * n_q / 4096;
+        return (int)(per < 1 ? 1 : per);
+    }
+    if (kernel == 2) {
+        // one wave per split of one KV head, all query rows at once; ~2048 waves
+        long per = units / 2048;
+        (void)rows;
+        return (int)(per < 1 ? 1 : per);
+    }
+    // LDS-tiled chunk kernel: splits only when there are few query tiles
+    long per = units / 1024;
+    return (int)(per < 1 ? 1 : per);
+}
+
+int make_plan(const kvq_layout* L, int n_heads, int ctx, int n_q, bool prefill,
+              const kvq_attn_opts* opts, kvq::AttnPlan* pl) {
+    const int group = n_heads / L->n_kv_heads;
+    const int rows = n_q * group;
+    int kernel = opts ? opts->kernel : 0;
+    if (kernel == 0) kernel = 1;
+    if (kernel < 1 || kernel > 3) return fail(KVQ_ERR_INVALID_ARG, "unknown kernel %d", kernel);
+    if (group > 16) return fail(KVQ_ERR_UNSUPPORTED, "group size %d > 16", group);
+    if (kernel == 2 && rows > 64) return fail(KVQ_ERR_UNSUPPORTED, "streaming MFMA kernel takes n_q*group <= 64 (got %d)", rows);
+    (void)prefill;
+    const int total_chunks = (ctx + kvq::kChunk - 1) / kvq::kChunk;
+    int cps = opts ? opts->chunks_per_split : 0;
+    if (cps < 0) return fail(KVQ_ERR_INVALID_ARG, "chunks_per_split %d < 0", cps);
+    if (cps == 0) cps = auto_chunks_per_split(kernel, total_chunks, L->n_kv_heads, n_q, rows);
+    if (cps > total_chunks) cps = total_chunks;
+    pl->kernel = kernel;
+    pl->chunks_per_split = cps;
+    pl->n_splits = (total_chunks + cps - 1) / cps;
+    pl->group = group;
+    pl->rows = rows;
+    return KVQ_OK;
+}
+
+int check_attn_shape(const kvq_layout* L, int32_t n_table, int32_t ctx, int32_t n_heads, int32_t n_q,
+                     bool prefill) {
+    if (n_heads < 1 || n_heads % L->n_kv_heads != 0)
+        return fail(KVQ_ERR_INVALID_ARG, "n_heads %d must be a positive multiple of n_kv_heads %d", n_heads, L->n_kv_heads);
+    if (n_q < 1) return fail(KVQ_ERR_INVALID_ARG, "n_q %d < 1", n_q);
+    if (!prefill && n_q > KVQ_MAX_NQ_DECODE)
+        return fail(KVQ_ERR_INVALID_ARG, "decode takes n_q <= %d (got %d); use kvq_prefill_attn", KVQ_MAX_NQ_DECODE, n_q);
+    if (ctx < n_q) return fail(KVQ_ERR_INVALID_ARG, "ctx_len %d < n_q %d", ctx, n_q);
+    if (n_table < 1) return fail(KVQ_ERR_INVALID_ARG, "n_table %d < 1", n_table);
+    if ((int64_t)ctx > (int64_t)n_table * L->page_size)
+        return fail(KVQ_ERR_CAPACITY, "ctx_len %d exceeds the page table (%d pages of %d)", ctx, n_table, L->page_size);
+    return KVQ_OK;
+}
+
+int workspace_impl(const kvq_layout* L, int32_t n_heads, int32_t ctx, int32_t n_q, bool prefill,
+                   const kvq_attn_opts* opts, size_t* bytes) {
+    kvq::Geom g;
+    int st = check_layout(L, &g);
+    if (st) return st;
+    if (bytes == nullptr) return fail(KVQ_ERR_INVALID_ARG, "bytes is NULL");
+    if (n_heads < 1 || n_heads % L->n_kv_heads != 0)
+        return fail(KVQ_ERR_INVALID_ARG, "n_heads %d must be a positive multiple of n_kv_heads %d", n_heads, L->n_kv_heads);
+    if (n_q < 1 || ctx < n_q) return fail(KVQ_ERR_INVALID_ARG, "need 1 <= n_q <= ctx_len (n_q=%d ctx_len=%d)", n_q, ctx);
+    kvq::AttnPlan pl;
+    st = make_plan(L, n_heads, ctx, n_q, prefill, opts, &pl);
+    if (st) return st;
+    *bytes = kvq::ws_bytes_for(pl, n_q, n_heads, L->head_dim);
+    return ok();
+}
+
+int attn_impl(const kvq_layout* L, const void* d_pool, const int32_t* d_page_table, int32_t n_table,
+              int32_t ctx, int32_t n_heads, int32_t n_q, const float* d_q, float scale,
+              float* d_out, float* d_lse, void* d_ws, size_t ws_bytes, bool prefill,
+              const kvq_attn_opts* opts, void* stream) {
+    kvq::Geom g;
+    int st = check_layout(L, &g);
+    if (st) return st;
+    if (d_pool == nullptr || d_page_table == nullptr || d_q == nullptr || d_out == nullptr)
+        return fail(KVQ_ERR_INVALID_ARG, "pool, page_table, q and out must be non-NULL");
+    st = check_attn_shape(L, n_table, ctx, n_heads, n_q, prefill);
+    if (st) return st;
+    kvq::AttnPlan pl;
+    st = make_plan(L, n_heads, ctx, n_q, prefill, opts, &pl);
+    if (st) return st;
+    const size_t need = kvq::ws_bytes_for(pl, n_q, n_heads, L->head_dim);
+    if (need > 0 && (d_ws == nullptr || ws_bytes < need))
+        return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, ws_bytes,
+                    d_ws == nullptr ? " (NULL)" : "");
+    if (((uintptr_t)d_pool & 255) != 0) return fail(KVQ_ERR_INVALID_ARG, "pool must be 256-byte aligned");
+    if (((uintptr_t)d_ws & 15) != 0) return fail(KVQ_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+
+    kvq::AttnArgs a;
+    a.g = g;
+    a.pool = static_cast<const uint8_t*>(d_pool);
+    a.page_table = d_page_table;
+    a.ctx = ctx;
+    a.n_heads = n_heads;
+    a.n_q = n_q;
+    a.q = d_q;
+    a.scale = scale;
+    a.out = d_out;
+    a.lse = d_lse;
+    const size_t rows = (size_t)n_q * n_heads;
+    const size_t ml = (rows * pl.n_splits * sizeof(float) + 255) / 256 * 256;
+    uint8_t* ws = static_cast<uint8_t*>(d_ws);
+    a.ws_m = reinterpret_cast<float*>(ws);
+    a.ws_l = reinterpret_cast<float*>(ws + ml);
+    a.ws_acc = reinterpret_cast<float*>(ws + 2 * ml);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    switch (pl.kernel) {
+        case 1: e = kvq::launch_attn_valu(a, pl, s); break;
+        case 2: e = kvq::launch_attn_mfma_stream(a, pl, s); break;
+        case 3: e = kvq::launch_attn_mfma_tiled(a, pl, s); break;
+    }
+    if (e == hipSuccess && !(pl.kernel == 3 && need == 0)) e = kvq::launch_merge(a, pl, s);
+    if (e != hipSuccess) return fail(KVQ_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvq_version(void) { return 10000; }
+
+const char* kvq_status_str(int status) {
+    switch (status) {
+        case KVQ_OK: return "KVQ_OK";
+        case KVQ_ERR_INVALID_ARG: return "KVQ_ERR_INVALID_ARG";
+        case KVQ_ERR_UNSUPPORTED: return "KVQ_ERR_UNSUPPORTED";
+        case KVQ_ERR_WORKSPACE: return "KVQ_ERR_WORKSPACE";
+        case KVQ_ERR_CAPACITY: return "KVQ_ERR_CAPACITY";
+        case KVQ_ERR_HIP: return "KVQ_ERR_HIP";
+        default: return "KVQ_ERR_UNKNOWN";
+    }
+}
+
+const char* kvq_last_error(void) { return g_err; }
+
+int kvq_unit_bytes(const kvq_layout* layout, size_t* bytes) {
+    kvq::Geom g;
+    int st = check_layout(layout, &g);
+    if (st) return st;
+    if (bytes == nullptr) return fail(KVQ_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = (size_t)g.unit_bytes();
+    return ok();
+}
+
+int kvq_pool_bytes(const kvq_layout* layout, size_t* bytes) {
+    kvq::Geom g;
+    int st = check_layout(layout, &g);
+    if (st) return st;
+    if (bytes == nullptr) return fail(KVQ_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = (size_t)g.unit_bytes() * layout->n_kv_heads * layout->n_pages;
+    return ok();
+}
+
+int kvq_append(const kvq_layout* layout, void* d_pool, const int32_t* d_page_table, int32_t n_table,
+               int32_t pos0, int32_t n_new, const float* d_k, const float* d_v, void* stream) {
+    kvq::Geom g;
+    int st = check_layout(layout, &g);
+    if (st) return st;
+    if (n_new < 0 || pos0 < 0) return fail(KVQ_ERR_INVALID_ARG, "pos0 %d and n_new %d must be >= 0", pos0, n_new);
+    if (d_pool == nullptr || d_page_table == nullptr || d_k == nullptr || d_v == nullptr)
+        return fail(KVQ_ERR_INVALID_ARG, "pool, page_table, k and v must be non-NULL");
+    if (n_table < 1) return fail(KVQ_ERR_INVALID_ARG, "n_table %d < 1", n_table);
+    if ((int64_t)pos0 + n_new > (int64_t)n_table * layout->page_size)
+        return fail(KVQ_ERR_CAPACITY, "positions up to %lld exceed the page table (%d pages of %d)",
+                    (long long)pos0 + n_new, n_table, layout->page_size);
+    if ((int64_t)pos0 + n_new > INT32_MAX) return fail(KVQ_ERR_CAPACITY, "positions overflow int32");
+    if (((uintptr_t)d_pool & 255) != 0) return fail(KVQ_ERR_INVALID_ARG, "pool must be 256-byte aligned");
+    if (n_new == 0) return ok();
+    hipError_t e = kvq::launch_append(g, static_cast<uint8_t*>(d_pool), d_page_table, pos0, n_new, d_k, d_v,
+                                      static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(KVQ_ERR_HIP, "append launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int kvq_workspace_bytes(const kvq_layout* layout, int32_t n_heads, int32_t ctx_len, int32_t n_q,
+                        int32_t prefill, size_t* bytes) {
+    return workspace_impl(layout, n_heads, ctx_len, n_q, prefill != 0, nullptr, bytes);
+}
+
+int kvq_workspace_bytes_ex(const kvq_layout* layout, int32_t n_heads, int32_t ctx_len, int32_t n_q,
+                           const kvq_attn_opts* opts, size_t* bytes) {
+    return workspace_impl(layout, n_heads, ctx_len, n_q, n_q > KVQ_MAX_NQ_DECODE, opts, bytes);
+}
+
+int kvq_decode_attn(const kvq_layout* layout, const void* d_pool, const int32_t* d_page_table, int32_t n_table,
+                    int32_t ctx_len, int32_t n_heads, int32_t n_q, const float* d_q, float scale,
+                    float* d_out, float* d_lse, void* d_ws, size_t ws_bytes, void* stream) {
+    return attn_impl(layout, d_pool, d_page_table, n_table, ctx_len, n_heads, n_q, d_q, scale, d_out, d_lse,
+                     d_ws, ws_bytes, false, nullptr, stream);
+}
+
+int kvq_prefill_attn(const kvq_layout* layout, const void* d_pool, const int32_t* d_page_table, int32_t n_table,
+                     int32_t ctx_len, int32_t n_heads, int32_t n_q, const float* d_q, float scale,
+                     float* d_out, float* d_lse, void* d_ws, size_t ws_bytes, void* stream) {
+    return attn_impl(layout, d_pool, d_page_table, n_table, ctx_len, n_heads, n_q, d_q, scale, d_out, d_lse,
+                     d_ws, ws_bytes, true, nullptr, stream);
+}
+
+int kvq_attn_ex(const kvq_layout* layout, const void* d_pool, const int32_t* d_page_table, int32_t n_table,
+                int32_t ctx_len, int32_t n_heads, int32_t n_q, const float* d_q, float scale,
+                float* d_out, float* d_lse, void* d_ws, size_t ws_bytes, const kvq_attn_opts* opts,
+                void* stream) {
+    return attn_impl(layout, d_pool, d_page_table, n_table, ctx_len, n_heads, n_q, d_q, scale, d_out, d_lse,
+                     d_ws, ws_bytes, n_q > KVQ_MAX_NQ_DECODE, opts, stream);
+}
+
+}  // extern "C"

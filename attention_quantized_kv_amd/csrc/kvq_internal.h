@@ -1,0 +1,101 @@
+// kvq_internal.h -- page-pool layout, launch plans and kernel entry points of
+// libkvq (gfx950).  Internal to the library; the public ABI is include/kvq.h.
+//
+// Layout of one unit (one page of one KV head; P = page_size, D = head_dim):
+//   K codes  [P*D]        int8, 16-token tiles, each tile D/64 wave-loads of
+//                         1 KiB; lane (g, n) of load p holds token n's dims
+//                         64p+8g..+7 and 64p+32+8g..+7 (the MFMA B operand of
+//                         two consecutive 32-value blocks)
+//   K scales [P][D/32]    fp16 bits
+//   V codes  [P*D/2]      4-bit, 32-token chunks, each chunk D/64 wave-loads of
+//                         1 KiB; lane (g, n) of load u holds, in dword w, dim
+//                         16(4u+w)+n of the 8 tokens 8g..8g+7 of the chunk
+//                         (the MFMA B operand of the P*V product)
+//   V scales [P][D/32]    fp16 bits
+// Every wave-level load of the streaming kernels is therefore one contiguous,
+// 16-byte-per-lane, 1 KiB request.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+constexpr int kBlock = 32;       // values per quantization block
+constexpr int kTile = 16;        // tokens per K tile (MFMA N/M = 16)
+constexpr int kChunk = 32;       // tokens per V chunk (MFMA K = 32)
+
+struct Geom {
+    int D;          // head_dim
+    int P;          // page_size
+    int n_kv;       // KV heads
+    int n_pages;    // physical pages
+    __host__ __device__ int nb() const { return D / kBlock; }
+    __host__ __device__ int64_t k_codes_off() const { return 0; }
+    __host__ __device__ int64_t k_scales_off() const { return (int64_t)P * D; }
+    __host__ __device__ int64_t v_codes_off() const { return (int64_t)P * D + (int64_t)P * nb() * 2; }
+    __host__ __device__ int64_t v_scales_off() const { return v_codes_off() + (int64_t)P * D / 2; }
+    __host__ __device__ int64_t unit_bytes() const { return v_scales_off() + (int64_t)P * nb() * 2; }
+    __host__ __device__ int64_t unit_index(int page, int kvh) const { return (int64_t)page * n_kv + kvh; }
+};
+
+// Byte offset (within a unit) of K code (slot s, dim d).
+__host__ __device__ inline int64_t k_code_pos(const Geom& g, int s, int d) {
+    int t = s / kTile, n = s % kTile;
+    int p = d / 64, r = d % 64, half = r / 32, w = r % 32, grp = w / 8, e = w % 8;
+    return (int64_t)t * kTile * g.D + ((int64_t)(p * 64 + grp * 16 + n) * 16) + half * 8 + e;
+}
+
+// Byte offset (within a unit) of the byte holding V code (slot s, dim d), and
+// the nibble (0 = low) inside it.  Slots 2k and 2k+1 share a byte.
+__host__ __device__ inline int64_t v_code_pos(const Geom& g, int s, int d, int* nibble) {
+    int c = s / kChunk, jj = s % kChunk, grp = jj / 8, i = jj % 8;
+    int tau = d / 16, n = d % 16, u = tau / 4, w = tau % 4;
+    *nibble = i & 1;
+    return g.v_codes_off() + (int64_t)c * kChunk * g.D / 2 +
+           (int64_t)(u * 64 + grp * 16 + n) * 16 + w * 4 + i / 2;
+}
+
+// Launch plan for attention: which kernel and how the keys are split.
+struct AttnPlan {
+    int kernel;            // 1 VALU, 2 MFMA streaming, 3 MFMA LDS-tiled
+    int chunks_per_split;  // 32-token chunks per merged partial
+    int n_splits;          // partials per query row
+    int group;             // q heads per KV head
+    int rows;              // n_q * group: query rows per KV head
+};
+
+struct AttnArgs {
+    Geom g;
+    const uint8_t* pool;
+    const int32_t* page_table;
+    int ctx;
+    int n_heads;
+    int n_q;
+    const float* q;
+    float scale;
+    float* out;
+    float* lse;
+    float* ws_acc;   // [n_q*n_heads][n_splits][D]
+    float* ws_m;     // [n_q*n_heads][n_splits]   log2-domain running max
+    float* ws_l;     // [n_q*n_heads][n_splits]   sum of exp2(s - m)
+};
+
+// Workspace bytes for a plan.
+inline size_t ws_bytes_for(const AttnPlan& pl, int n_q, int n_heads, int D) {
+    if (pl.n_splits <= 1 && pl.kernel == 3) return 0;
+    size_t rows = (size_t)n_q * n_heads;
+    size_t acc = rows * pl.n_splits * D * sizeof(float);
+    size_t ml = rows * pl.n_splits * sizeof(float);
+    return acc + 2 * ((ml + 255) / 256 * 256);
+}
+
+// Kernel launchers (each returns the hipError_t of its launch).
+hipError_t launch_append(const Geom& g, uint8_t* pool, const int32_t* page_table, int pos0,
+                         int n_new, const float* k, const float* v, hipStream_t stream);
+hipError_t launch_attn_valu(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream);
+hipError_t launch_attn_mfma_stream(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream);
+hipError_t launch_attn_mfma_tiled(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream);
+hipError_t launch_merge(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream);
+
+}  // namespace kvq

@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Benchmark of quantized-KV attention (K Q8_0, V Q4_0, 256-token pages) on one
+MI355X.
+
+Default workload: a 16-layer stack of full-attention layers, 24 query heads /
+4 KV heads x head_dim 256, 262,144 cached tokens per layer (436,207,616 bytes
+of quantized KV per layer, 6.98 GB for the stack).  One step = for every
+layer, kvq_append of the new token's K/V row (position 262,143) followed by
+kvq_decode_attn of one query over all 262,144 tokens (split over pages, merged
+by online log-sum-exp).  Each layer has its own pool, so consecutive layers
+never share cache lines and every step streams the whole 6.98 GB from HBM.
+
+Prints one JSON line: effective KV GB/s (algorithmic bytes / time), us per
+layer, the roofline of the decode kernel measured with HIP events on the
+launch stream, and the CPU oracle timed on a bounded sample of the same
+workload.  Inputs are seeded synthetic N(0,1) fp32 drawn on the device.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+
+def kv_bytes_per_token_layer(n_kv: int, D: int) -> int:
+    """Algorithmic bytes one token of one layer occupies: per 32-value block a
+    34-byte Q8_0 K block and an 18-byte Q4_0 V block."""
+    return n_kv * (D // 32) * (34 + 18)
+
+
+def device_normal(shape, seed, device):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+
+
+class Layer:
+    def __init__(self, w, layer, device, fill_chunk=16384):
+        import torch
+        import attention_quantized_kv_amd as kvq
+        self.kvq = kvq
+        self.w = w
+        self.L = kvq.Layout(w.n_kv, w.head_dim, w.page_size, w.n_pages)
+        self.pool = torch.empty(kvq.kvq_pool_bytes(self.L), dtype=torch.uint8, device=device)
+        perm = torch.randperm(w.n_pages, generator=torch.Generator().manual_seed(1000 + layer))
+        self.pt = perm.to(torch.int32).to(device)
+        base = (w.wid * 1000 + layer) * 1_000_003
+        for r in range(0, w.cached, fill_chunk):
+            n = min(fill_chunk, w.cached - r)
+            k = device_normal((n, w.n_kv, w.head_dim), base + 2 * r + 1, device)
+            v = device_normal((n, w.n_kv, w.head_dim), base + 2 * r + 2, device)
+            kvq.kvq_append(self.L, self.pool, self.pt, r, k, v)
+        self.k_new = device_normal((w.n_new, w.n_kv, w.head_dim), base + 7, device)
+        self.v_new = device_normal((w.n_new, w.n_kv, w.head_dim), base + 8, device)
+        self.q = device_normal((w.n_q, w.n_heads, w.head_dim), base + 9, device)
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty((w.n_q, w.n_heads), dtype=torch.float32, device=device)
+
+    def append(self):
+        self.kvq.kvq_append(self.L, self.pool, self.pt, self.w.cached, self.k_new, self.v_new)
+
+    def attend(self, ws, kernel, prefill):
+        kvq = self.kvq
+        if kernel:
+            kvq.kvq_attn_ex(self.L, self.pool, self.pt, self.w.ctx, self.q, self.w.scale, self.out, self.lse,
+                            ws, kernel=kernel)
+        elif prefill:
+            kvq.kvq_prefill_attn(self.L, self.pool, self.pt, self.w.ctx, self.q, self.w.scale, self.out,
+                                 self.lse, ws)
+        else:
+            kvq.kvq_decode_attn(self.L, self.pool, self.pt, self.w.ctx, self.q, self.w.scale, self.out,
+                                self.lse, ws)
+
+
+def attention_flops(w) -> float:
+    """Algorithmic flops of one layer's attention: 2 flops per multiply-add,
+    q.k and p.v over every visible key of every query row."""
+    pairs = sum(w.ctx - w.n_q + 1 + i for i in range(w.n_q))
+    return 4.0 * pairs * w.n_heads * w.head_dim
+
+
+def cpu_baseline(w, min_seconds: float, max_reps: int = 8):
+    """The oracle, as it stands, on one layer of the same workload (host numpy
+    inputs), repeated until min_seconds of CPU work."""
+    import oracle
+    import synth
+    k, v = synth.layer_kv(w, 0)
+    cache = oracle.QuantCache.from_float(k, v)
+    del k, v
+    q = synth.layer_q(w, 0)
+    if w.n_q <= 8:
+        rows = [(i, h) for i in range(w.n_q) for h in range(w.n_heads)]
+        desc = f"one {w.ctx}-token layer, all {len(rows)} query rows"
+        bytes_per_rep = w.ctx * kv_bytes_per_token_layer(w.n_kv, w.head_dim)
+    else:
+        rng = __import__("numpy").random.default_rng(0)
+        sel = sorted({0, 255, 256, w.n_q - 1, *rng.integers(0, w.n_q, 12).tolist()})
+        rows = [(i, h) for i in sel for h in range(w.n_heads)]
+        desc = f"{len(sel)} of {w.n_q} query rows x {w.n_heads} heads at full context"
+        bytes_per_rep = None
+    reps, t_total, threads = 0, 0.0, oracle.max_threads()
+    while reps < max_reps and (t_total < min_seconds or reps == 0):
+        t0 = time.perf_counter()
+        oracle.attention(q, cache, w.scale, rows=rows)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    if bytes_per_rep is not None:
+        value = reps * bytes_per_rep / t_total / 1e9
+        unit = "GB/s"
+    else:
+        flops = 4.0 * sum(w.ctx - w.n_q + 1 + i for i, _ in rows) * w.head_dim
+        value = reps * flops / t_total / 1e12
+        unit = "TFLOP/s"
+    return {"value": value, "unit": unit, "cores": threads, "kind": "oracle",
+            "sample": f"{desc}, {reps} repetition(s), {t_total:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="decode262k",
+                    choices=["tiny", "decode65k", "decode262k", "verify131k", "prefill262k"])
+    ap.add_argument("--layers", type=int, default=None, help="layers in the stack (default: the workload's)")
+    ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA streaming, 3 MFMA tiled")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
+              "the single-GPU value is the measurement.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import attention_quantized_kv_amd as kvq
+
+    w = synth.WORKLOADS[args.workload]
+    n_layers = args.layers or w.layers
+    prefill = w.n_q > kvq.KVQ_MAX_NQ_DECODE
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    t0 = time.time()
+    layers = [Layer(w, i, dev) for i in range(n_layers)]
+    ws_n = kvq.kvq_workspace_bytes_ex(layers[0].L, w.n_heads, w.ctx, w.n_q, args.kernel, 0) if args.kernel \
+        else kvq.kvq_workspace_bytes(layers[0].L, w.n_heads, w.ctx, w.n_q, prefill)
+    ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    print(f"[bench] {w.name}: {n_layers} layers filled in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+
+    def step(ev=None):
+        for i, lay in enumerate(layers):
+            lay.append()
+            if ev is not None:
+                ev[i][0].record()
+            lay.attend(ws, args.kernel, prefill)
+            if ev is not None:
+                ev[i][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_layers)]
+           for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(args.steps):
+        step(evs[s])
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    attn_ms = [e[0].elapsed_time(e[1]) for st in evs for e in st]
+    avg_attn_us = 1000.0 * sum(attn_ms) / len(attn_ms)
+
+    ms_per_step = total_ms / args.steps
+    bytes_layer = w.ctx * kv_bytes_per_token_layer(w.n_kv, w.head_dim)
+    us_per_layer = 1000.0 * ms_per_step / n_layers
+    flops_layer = attention_flops(w)
+    rec = {
+        "data": "synthetic",
+        "dtype": "f16 MFMA / f32" if args.kernel in (0, 2, 3) else "f32",
+        "config": {"workload": w.name, "layers": n_layers, "n_heads": w.n_heads, "n_kv_heads": w.n_kv,
+                   "head_dim": w.head_dim, "ctx": w.ctx, "n_q": w.n_q, "page_size": w.page_size,
+                   "kv_format": "K Q8_0 + V Q4_0", "kernel": args.kernel or "auto"},
+    }
+    if not prefill:
+        value = n_layers * bytes_layer * args.steps / (total_ms / 1e3) / 1e9
+        achieved = bytes_layer / (avg_attn_us / 1e6) / 1e9
+        rec.update({
+            "metric": "quantized-KV decode attention: effective KV GB/s (% HBM peak), us/layer @262k",
+            "value": round(value, 2), "unit": "GB/s",
+        })
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "kvq_decode_attn (split + merge launches)", "bytes_per_launch": bytes_layer,
+                "avg_launch_us": round(avg_attn_us, 3)}
+        extra = {"us_per_layer": round(us_per_layer, 3), "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+                 "ctx_tokens_per_s": round(w.ctx / (us_per_layer / 1e6), 1),
+                 "kv_bytes_per_layer": bytes_layer}
+    else:
+        value = flops_layer * n_layers * args.steps / (total_ms / 1e3) / 1e12
+        achieved = flops_layer / (avg_attn_us / 1e6) / 1e12
+        rec.update({"metric": "quantized-KV chunked prefill attention: TFLOP/s (MFMA utilisation)",
+                    "value": round(value, 2), "unit": "TFLOP/s"})
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "kvq_prefill_attn", "flops_per_launch": flops_layer,
+                "avg_launch_us": round(avg_attn_us, 3)}
+        extra = {"us_per_layer": round(us_per_layer, 3), "flops_per_layer": flops_layer}
+
+    rec.update({"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+                "higher_is_better": True, "scaling": "weak", "vs_baseline": None})
+    rec["roofline"] = roof
+    rec.update(extra)
+    del layers
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,200 @@
+/*
+ * kvq.h -- C ABI of libkvq: attention over a block-quantized, paged KV cache
+ * on one AMD Instinct MI355X (gfx950).
+ *
+ * K is stored as Q8_0 and V as Q4_0: blocks of 32 consecutive values of one
+ * (token, KV head) row, each block with one fp16 scale
+ *   ("Qwen 27B (IQ4_XS, Q8/Q4 KV) on a 16GB RX 9070 XT at 262k context, via
+ *    adaptive KV streaming", first paragraph;
+ *    "Adaptive KV streaming lands on ROCm: Qwen3.8-27B at full 262k context on
+ *    a 16 GB RX 9070 XT", "What shipped";
+ *    "OSCAR2 KV Cache benchmark", compression-ratio table: Q8_0 = 136 bytes
+ *    per 128 values).
+ * The cache lives in fixed-size pages of tokens reached through a page table;
+ * decode attention is computed split over pages and the per-split results are
+ * merged with an online log-sum-exp ("Qwen 27B ... RX 9070 XT", second and
+ * third paragraphs: per-page online-LSE accumulation for chunked prefill, and
+ * paged decode attention extended to the speculative verify batch).
+ *
+ * Conventions for every call:
+ *  - Pointers named d_* are device pointers (HIP, same device as the stream);
+ *    the library never dereferences them on the host and never copies them.
+ *  - The caller owns every buffer.  The library allocates nothing, keeps no
+ *    state between calls and may be called from several host threads.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *    and is asynchronous; a returned KVQ_OK means "validated and enqueued".
+ *  - Every condition that can be checked on the host is checked before any
+ *    launch; on failure nothing is enqueued, a negative kvq_status is
+ *    returned and kvq_last_error() describes it (thread-local).
+ *  - Page-table entries outside [0, n_pages) are never dereferenced: append
+ *    skips such rows, attention writes NaN for rows that would read them.
+ *  - Inputs must be finite; behaviour for NaN/Inf inputs is unspecified.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_BLOCK 32          /* values per quantization block */
+#define KVQ_MAX_NQ_DECODE 8   /* largest n_q accepted by kvq_decode_attn */
+
+typedef enum {
+    KVQ_OK = 0,
+    KVQ_ERR_INVALID_ARG = -1,   /* null pointer, negative size, inconsistent shapes */
+    KVQ_ERR_UNSUPPORTED = -2,   /* head_dim / page_size / group size outside the built set */
+    KVQ_ERR_WORKSPACE = -3,     /* workspace missing or smaller than kvq_workspace_bytes() */
+    KVQ_ERR_CAPACITY = -4,      /* positions beyond what the page table covers */
+    KVQ_ERR_HIP = -5            /* the HIP runtime reported an error at launch */
+} kvq_status;
+
+/*
+ * Shape of one layer's page pool.
+ *   n_kv_heads  KV heads of the layer, >= 1
+ *   head_dim    D, one of 64, 128, 256
+ *   page_size   tokens per page, a multiple of 32 in [32, 1024]
+ *   n_pages     physical pages in the pool, >= 1
+ */
+typedef struct {
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    int32_t page_size;
+    int32_t n_pages;
+} kvq_layout;
+
+/*
+ * Pool memory.  The pool is one device allocation of kvq_pool_bytes() bytes,
+ * 256-byte aligned, made of n_pages * n_kv_heads units; unit (page p, KV head
+ * g) starts at (p * n_kv_heads + g) * kvq_unit_bytes().  A unit holds the
+ * page_size tokens of one KV head (P = page_size, D = head_dim, nb = D/32):
+ *
+ *   [0, P*D)                 K codes, int8 two's complement, tile order:
+ *                            16-token tiles t; inside a tile, 16-byte pieces
+ *                            (p, lane) with p < D/64 and lane = g*16 + n
+ *                            (g < 4, n < 16) hold token 16t+n, bytes 0..7 =
+ *                            dims 64p+8g+(0..7) (block 2p), bytes 8..15 =
+ *                            dims 64p+32+8g+(0..7) (block 2p+1).
+ *   [P*D, P*D + 2*P*nb)      K scales, fp16 bits, [token][block].
+ *   next P*D/2 bytes         V codes, 4 bits each, chunk order: 32-token
+ *                            chunks c; inside a chunk, 16-byte pieces
+ *                            (u, lane) with u < D/64, lane = g*16 + n; dword
+ *                            w < 4 of a piece holds dim 16(4u+w)+n of tokens
+ *                            32c+8g+i (i < 8) in bits 4i..4i+3.
+ *   next 2*P*nb bytes        V scales, fp16 bits, [token][block].
+ *
+ * A value is scale * code for K and scale * (code - 8) for V.  The unit is
+ * 26*P*D/16 bytes: 416 bytes per token at D = 256, matching Q8_0 (34 B) +
+ * Q4_0 (18 B) per 32-value block ("Adaptive KV streaming lands on ROCm ...",
+ * "Why it matters": 26,624 bytes per token over 16 layers).
+ */
+int kvq_unit_bytes(const kvq_layout *layout, size_t *bytes);
+int kvq_pool_bytes(const kvq_layout *layout, size_t *bytes);
+
+/*
+ * kvq_append -- quantize n_new new K/V rows into the pool.
+ *
+ * Row r (0 <= r < n_new) is token position pos0 + r; it goes to physical page
+ * d_page_table[(pos0 + r) / page_size], slot (pos0 + r) % page_size.
+ *   d_k, d_v      fp32 [n_new][n_kv_heads][head_dim], device
+ *   d_page_table  int32 [n_table], device; logical page -> physical page
+ *   n_table       entries in the page table; (pos0 + n_new) <= n_table * page_size
+ * Per block of 32 values (IEEE fp32 arithmetic, bit-reproducible):
+ *   K (Q8_0): d = max|x| / 127; code = round-half-away-from-zero(x * (1/d))
+ *             (0 when d = 0); scale = fp16(d), nearest-even.
+ *   V (Q4_0): m = the first value of largest magnitude (+0 if all are zero);
+ *             d = m / -8; code = min(15, floor(x * (1/d) + 8.5)) with the
+ *             product and the sum rounded separately (code 8 when d = 0);
+ *             scale = fp16(d).
+ * Other slots of the touched pages are left as they were.  Rows that share a
+ * pool byte are written by one thread; calls on one stream are ordered, and
+ * calls on different streams must not touch the same page concurrently.
+ * Errors: INVALID_ARG (null pointers, n_new < 0, pos0 < 0), UNSUPPORTED,
+ * CAPACITY, HIP.  n_new == 0 is a no-op.
+ */
+int kvq_append(const kvq_layout *layout, void *d_pool,
+               const int32_t *d_page_table, int32_t n_table,
+               int32_t pos0, int32_t n_new,
+               const float *d_k, const float *d_v, void *stream);
+
+/*
+ * Attention.  Keys are the token positions [0, ctx_len).  Query i (0 <= i <
+ * n_q) sits at position ctx_len - n_q + i and attends to every key at a
+ * position <= its own (its own key included, so append first).  Query head h
+ * uses KV head h / (n_heads / n_kv_heads) ("Context window and KV cache", GQA
+ * section: several query heads share one KV head).  Attention reads the
+ * quantized values:
+ *   s_j = scale * sum_d q[d] * Khat_j[d],  o = sum_j softmax(s)_j * Vhat_j,
+ *   lse = log(sum_j exp(s_j))              (natural log)
+ * i.e. exact softmax attention ("Context window and KV cache", flash-attention
+ * lever) over the dequantized cache.
+ *   d_q    fp32 [n_q][n_heads][head_dim]
+ *   d_out  fp32 [n_q][n_heads][head_dim]
+ *   d_lse  fp32 [n_q][n_heads], may be NULL
+ *   d_ws   workspace of at least kvq_workspace_bytes() bytes (NULL if that is 0)
+ * The result does not depend on how the cache is split internally beyond
+ * fp32 rounding.  Errors: INVALID_ARG (nulls, n_q < 1, ctx_len < n_q,
+ * n_heads % n_kv_heads != 0), UNSUPPORTED (n_heads / n_kv_heads > 16 or
+ * n_q * group > 64 for decode), CAPACITY (ctx_len > n_table * page_size),
+ * WORKSPACE, HIP.
+ */
+
+/* Workspace bytes kvq_decode_attn / kvq_prefill_attn need for this shape. */
+int kvq_workspace_bytes(const kvq_layout *layout, int32_t n_heads, int32_t ctx_len,
+                        int32_t n_q, int32_t prefill, size_t *bytes);
+
+/* kvq_decode_attn -- one decode query (n_q = 1) or a speculative verify batch
+ * (2 <= n_q <= KVQ_MAX_NQ_DECODE): split over pages, merged by online LSE. */
+int kvq_decode_attn(const kvq_layout *layout, const void *d_pool,
+                    const int32_t *d_page_table, int32_t n_table,
+                    int32_t ctx_len, int32_t n_heads, int32_t n_q,
+                    const float *d_q, float scale,
+                    float *d_out, float *d_lse,
+                    void *d_ws, size_t ws_bytes, void *stream);
+
+/* kvq_prefill_attn -- a causal chunk of n_q >= 1 queries (chunked prefill). */
+int kvq_prefill_attn(const kvq_layout *layout, const void *d_pool,
+                     const int32_t *d_page_table, int32_t n_table,
+                     int32_t ctx_len, int32_t n_heads, int32_t n_q,
+                     const float *d_q, float scale,
+                     float *d_out, float *d_lse,
+                     void *d_ws, size_t ws_bytes, void *stream);
+
+/*
+ * Explicit kernel and split choice, for tests and tuning.  Same semantics and
+ * errors as kvq_decode_attn / kvq_prefill_attn.
+ *   kernel: 0 = automatic, 1 = portable VALU kernel (any supported shape),
+ *           2 = MFMA streaming kernel (n_q * group <= 64),
+ *           3 = MFMA LDS-tiled chunk kernel
+ *   chunks_per_split: 32-token chunks per merged partial; 0 = automatic.
+ */
+typedef struct {
+    int32_t kernel;
+    int32_t chunks_per_split;
+} kvq_attn_opts;
+
+int kvq_workspace_bytes_ex(const kvq_layout *layout, int32_t n_heads, int32_t ctx_len,
+                           int32_t n_q, const kvq_attn_opts *opts, size_t *bytes);
+
+int kvq_attn_ex(const kvq_layout *layout, const void *d_pool,
+                const int32_t *d_page_table, int32_t n_table,
+                int32_t ctx_len, int32_t n_heads, int32_t n_q,
+                const float *d_q, float scale,
+                float *d_out, float *d_lse,
+                void *d_ws, size_t ws_bytes, const kvq_attn_opts *opts, void *stream);
+
+/* Status name, and the detail of the last failure on this thread. */
+const char *kvq_status_str(int status);
+const char *kvq_last_error(void);
+
+/* Library version, as MAJOR*10000 + MINOR*100 + PATCH. */
+int kvq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,112 @@
+"""CPU: the C-ABI library loads, exports every symbol include/kvq.h declares,
+and rejects bad arguments with the documented status before touching the GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_quantized_kv_amd as kvq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x100000)     # a non-NULL, 256-aligned address never dereferenced
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 11
+    lib = kvq.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(kvq.EXPORTS)
+
+
+def test_sizes():
+    L = kvq.Layout(4, 256, 256, 1024)
+    assert kvq.kvq_unit_bytes(L) == 256 * 416                 # 416 B/token/KV head at D = 256
+    assert kvq.kvq_pool_bytes(L) == 436_207_616               # one 262,144-token layer
+    assert kvq.kvq_unit_bytes(kvq.Layout(1, 64, 32, 1)) == 32 * 64 * 26 // 16
+    assert kvq.kvq_workspace_bytes(L, 24, 262144, 1) > 0
+    assert kvq.kvq_version() >= 10000
+
+
+def _status(fn, *args):
+    st = fn(*args)
+    return st, kvq.lib().kvq_last_error().decode()
+
+
+@pytest.mark.parametrize("fields,status", [
+    ((0, 256, 256, 1), kvq.KVQ_ERR_INVALID_ARG),
+    ((4, 0, 256, 1), kvq.KVQ_ERR_INVALID_ARG),
+    ((4, 96, 256, 1), kvq.KVQ_ERR_UNSUPPORTED),
+    ((4, 32, 256, 1), kvq.KVQ_ERR_UNSUPPORTED),
+    ((4, 256, 48, 1), kvq.KVQ_ERR_UNSUPPORTED),
+    ((4, 256, 2048, 1), kvq.KVQ_ERR_UNSUPPORTED),
+    ((4, 256, 256, 0), kvq.KVQ_ERR_INVALID_ARG),
+])
+def test_layout_validation(fields, status):
+    L = kvq.Layout(*fields)
+    out = ctypes.c_size_t(0)
+    st, msg = _status(kvq.lib().kvq_pool_bytes, ctypes.byref(L), ctypes.byref(out))
+    assert st == status and msg
+
+
+def test_append_validation():
+    lib = kvq.lib()
+    L = kvq.Layout(4, 256, 256, 4)
+    args = lambda pool=FAKE, pt=FAKE, nt=4, pos0=0, n=1, k=FAKE, v=FAKE: (
+        ctypes.byref(L), pool, pt, nt, pos0, n, k, v, None)
+    assert _status(lib.kvq_append, *args(pool=None))[0] == kvq.KVQ_ERR_INVALID_ARG
+    assert _status(lib.kvq_append, *args(k=None))[0] == kvq.KVQ_ERR_INVALID_ARG
+    assert _status(lib.kvq_append, *args(n=-1))[0] == kvq.KVQ_ERR_INVALID_ARG
+    assert _status(lib.kvq_append, *args(pos0=-3))[0] == kvq.KVQ_ERR_INVALID_ARG
+    assert _status(lib.kvq_append, *args(pos0=1000, n=25))[0] == kvq.KVQ_ERR_CAPACITY
+    assert _status(lib.kvq_append, *args(nt=0))[0] == kvq.KVQ_ERR_INVALID_ARG
+    assert _status(lib.kvq_append, *args(pool=ctypes.c_void_p(0x100010)))[0] == kvq.KVQ_ERR_INVALID_ARG
+    assert _status(lib.kvq_append, *args(n=0))[0] == kvq.KVQ_OK          # no-op, no launch
+
+
+def test_attention_validation():
+    lib = kvq.lib()
+    L = kvq.Layout(4, 256, 256, 8)
+
+    def call(fn=lib.kvq_decode_attn, pool=FAKE, pt=FAKE, nt=8, ctx=1000, nh=24, nq=1, q=FAKE,
+             out=FAKE, ws=FAKE, wsb=1 << 30):
+        return _status(fn, ctypes.byref(L), pool, pt, nt, ctx, nh, nq, q, ctypes.c_float(0.0625), out,
+                       None, ws, wsb, None)
+
+    assert call(pool=None)[0] == kvq.KVQ_ERR_INVALID_ARG
+    assert call(q=None)[0] == kvq.KVQ_ERR_INVALID_ARG
+    assert call(out=None)[0] == kvq.KVQ_ERR_INVALID_ARG
+    assert call(nh=25)[0] == kvq.KVQ_ERR_INVALID_ARG                   # not a multiple of 4
+    assert call(nh=68)[0] == kvq.KVQ_ERR_UNSUPPORTED                   # group 17 > 16
+    assert call(nq=0)[0] == kvq.KVQ_ERR_INVALID_ARG
+    assert call(nq=9)[0] == kvq.KVQ_ERR_INVALID_ARG                    # decode takes n_q <= 8
+    assert call(ctx=3, nq=4)[0] == kvq.KVQ_ERR_INVALID_ARG
+    assert call(ctx=2049)[0] == kvq.KVQ_ERR_CAPACITY                   # 8 pages of 256
+    assert call(ws=None)[0] == kvq.KVQ_ERR_WORKSPACE
+    assert call(wsb=16)[0] == kvq.KVQ_ERR_WORKSPACE
+    st, msg = call(wsb=16)
+    assert "workspace" in msg
+    # prefill accepts long chunks; its workspace errors are the same
+    assert call(fn=lib.kvq_prefill_attn, nq=9, ws=None)[0] == kvq.KVQ_ERR_WORKSPACE
+
+
+def test_status_strings():
+    lib = kvq.lib()
+    for st, name in [(0, "KVQ_OK"), (-1, "KVQ_ERR_INVALID_ARG"), (-2, "KVQ_ERR_UNSUPPORTED"),
+                     (-3, "KVQ_ERR_WORKSPACE"), (-4, "KVQ_ERR_CAPACITY"), (-5, "KVQ_ERR_HIP")]:
+        assert lib.kvq_status_str(st).decode() == name
+
+
+def test_binding_raises():
+    with pytest.raises(kvq.KvqError) as e:
+        kvq.kvq_pool_bytes(kvq.Layout(4, 100, 256, 1))
+    assert e.value.status == kvq.KVQ_ERR_UNSUPPORTED
