@@ -64,11 +64,10 @@ int make_plan(const kvq_layout* L, int n_heads, int ctx, int n_q, bool prefill,
     const int group = n_heads / L->n_kv_heads;
     const int rows = n_q * group;
     int kernel = opts ? opts->kernel : 0;
-    if (kernel == 0) kernel = 1;
+    if (kernel == 0) kernel = (!prefill && rows <= 64) ? 2 : 1;
     if (kernel < 1 || kernel > 3) return fail(KVQ_ERR_INVALID_ARG, "unknown kernel %d", kernel);
     if (group > 16) return fail(KVQ_ERR_UNSUPPORTED, "group size %d > 16", group);
     if (kernel == 2 && rows > 64) return fail(KVQ_ERR_UNSUPPORTED, "streaming MFMA kernel takes n_q*group <= 64 (got %d)", rows);
-    (void)prefill;
     const int total_chunks = (ctx + kvq::kChunk - 1) / kvq::kChunk;
     int cps = opts ? opts->chunks_per_split : 0;
     if (cps < 0) return fail(KVQ_ERR_INVALID_ARG, "chunks_per_split %d < 0", cps);
@@ -76,7 +75,9 @@ int make_plan(const kvq_layout* L, int n_heads, int ctx, int n_q, bool prefill,
     if (cps > total_chunks) cps = total_chunks;
     pl->kernel = kernel;
     pl->chunks_per_split = cps;
-    pl->n_splits = (total_chunks + cps - 1) / cps;
+    // the streaming MFMA kernel folds 4 waves (4 * cps chunks) into one partial
+    const int per_partial = kernel == 2 ? 4 * cps : cps;
+    pl->n_splits = (total_chunks + per_partial - 1) / per_partial;
     pl->group = group;
     pl->rows = rows;
     return KVQ_OK;

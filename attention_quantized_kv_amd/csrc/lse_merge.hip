@@ -9,8 +9,9 @@
 // over pages ("Qwen 27B (IQ4_XS, Q8/Q4 KV) on a 16GB RX 9070 XT at 262k
 // context, via adaptive KV streaming", second paragraph).
 //
-// One workgroup per query row, one thread per output dimension; every thread
-// walks the row's partials in the same order, so the weights are identical.
+// One workgroup per (row, 64 output dims): its 4 wavefronts each fold every
+// 4th split with a running maximum (so the loads of different splits are
+// independent), then wave 0 folds the 4 wave results in a fixed order.
 // Splits with no visible key (l = 0) are skipped; a NaN partial (a page-table
 // entry outside the pool) propagates to the output.
 #include "kvq_internal.h"
@@ -18,38 +19,53 @@
 namespace kvq {
 namespace {
 
-template <int D>
-__global__ __launch_bounds__(D) void merge_kernel(AttnArgs a, int n_splits) {
+__global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int n_splits, int D) {
+    __shared__ float sm[4], sl[4], so[4][64];
     const int row = blockIdx.x;
-    const int d = threadIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int d = blockIdx.y * 64 + lane;
     const float* m = a.ws_m + (size_t)row * n_splits;
     const float* l = a.ws_l + (size_t)row * n_splits;
-    const float* acc = a.ws_acc + (size_t)row * n_splits * D;
+    const float* acc = a.ws_acc + (size_t)row * n_splits * D + d;
 
-    float M = -INFINITY;
-    for (int s = 0; s < n_splits; ++s) M = fmaxf(M, m[s]);
-    float L = 0.0f, o = 0.0f;
-    for (int s = 0; s < n_splits; ++s) {
+    float M = -INFINITY, L = 0.0f, o = 0.0f;
+    for (int s = wave; s < n_splits; s += 4) {
         const float ls = l[s];
         if (ls == 0.0f) continue;
-        const float w = exp2f(m[s] - M);
+        const float ms = m[s];
+        if (ms > M) {
+            const float f = exp2f(M - ms);
+            L *= f;
+            o *= f;
+            M = ms;
+        }
+        const float w = exp2f(ms - M);
         L = fmaf(ls, w, L);
-        o = fmaf(acc[(size_t)s * D + d], w, o);
+        o = fmaf(acc[(size_t)s * D], w, o);
     }
-    a.out[(size_t)row * D + d] = o / L;
-    if (a.lse != nullptr && d == 0) a.lse[row] = (M + log2f(L)) * 0.69314718055994531f;
+    if (lane == 0) { sm[wave] = M; sl[wave] = L; }
+    so[wave][lane] = o;
+    __syncthreads();
+    if (wave != 0) return;
+    float Mt = -INFINITY;
+    for (int w = 0; w < 4; ++w) Mt = fmaxf(Mt, sm[w]);
+    float Lt = 0.0f, ot = 0.0f;
+    for (int w = 0; w < 4; ++w) {
+        if (sl[w] == 0.0f) continue;
+        const float f = exp2f(sm[w] - Mt);
+        Lt = fmaf(sl[w], f, Lt);
+        ot = fmaf(so[w][lane], f, ot);
+    }
+    a.out[(size_t)row * D + d] = ot / Lt;
+    if (a.lse != nullptr && blockIdx.y == 0 && lane == 0) a.lse[row] = (Mt + log2f(Lt)) * 0.69314718055994531f;
 }
 
 }  // namespace
 
 hipError_t launch_merge(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) {
-    dim3 grid(a.n_q * a.n_heads);
-    switch (a.g.D) {
-        case 64:  hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(64), 0, stream, a, pl.n_splits); break;
-        case 128: hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(128), 0, stream, a, pl.n_splits); break;
-        case 256: hipLaunchKernelGGL(merge_kernel<256>, grid, dim3(256), 0, stream, a, pl.n_splits); break;
-        default: return hipErrorInvalidValue;
-    }
+    dim3 grid(a.n_q * a.n_heads, a.g.D / 64);
+    hipLaunchKernelGGL(merge_kernel, grid, dim3(256), 0, stream, a, pl.n_splits, a.g.D);
     return hipGetLastError();
 }
 

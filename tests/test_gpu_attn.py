@@ -82,7 +82,7 @@ def _rand_case(seed, ctx, n_kv, D, P=256, perm=True, mag=1.0):
     return Case(k, v, P=P, n_pages=n_pages, perm_seed=seed if perm else None), rng
 
 
-@pytest.fixture(scope="module", params=["valu"])
+@pytest.fixture(scope="module", params=["valu", "mfma_stream"])
 def kernel(request):
     return KERNELS[request.param]
 
@@ -178,6 +178,12 @@ def test_large_magnitudes(kernel):
 def test_prefill_chunk(kernel):
     c, rng = _rand_case(41, 1200, 2, 128, P=64)
     q = rng.standard_normal((200, 12, 128)).astype(np.float32)
+    if kernel == KERNELS["mfma_stream"]:
+        import attention_quantized_kv_amd as kvq
+        with pytest.raises(kvq.KvqError) as e:      # 1200 rows per KV head > 64
+            c.run(q, 1 / math.sqrt(128), kernel=kernel, prefill=True)
+        assert e.value.status == kvq.KVQ_ERR_UNSUPPORTED
+        return
     out, lse = c.run(q, 1 / math.sqrt(128), kernel=kernel, prefill=True)
     ref, ref_lse = c.ref(q, 1 / math.sqrt(128))
     tu.assert_close(out, ref, lse, ref_lse, "prefill")
