@@ -8,29 +8,32 @@
 // third paragraph: paged decode attention, extended to the verify batch;
 // second paragraph: online log-sum-exp across pages).
 //
-// Work split.  A workgroup (4 wavefronts) owns one KV head and a contiguous
-// run of 4*cps 32-token chunks; each wave streams cps of them.  All query
+// Work split.  A workgroup of W wavefronts owns one KV head and a contiguous
+// run of W*cps 32-token chunks; each wave streams cps of them.  All query
 // rows that use this KV head -- the G heads of the group ("Context window and
 // KV cache", GQA section) times n_q queries -- are served from one read of
 // every K/V byte, so the cache is read once per KV head.
 //
-// Per 32-token chunk and wave (D = head_dim, NB = D/32 blocks):
-//  * loads: two 16-token K tiles (D/64 x 16 B per lane each), their K scales,
-//    the V chunk (D/64 x 16 B per lane) and its V scales; every instruction
-//    is one contiguous 1 KiB request thanks to the pool layout, and chunk c+1
-//    is in flight while chunk c is computed;
+// Data path per 32-token chunk and wave (D = head_dim, NB = D/32 blocks):
+//  * global -> LDS directly (global_load_lds_dwordx4) into the wave's own
+//    landing zone: two 16-token K tiles, their K scales, the V chunk and its
+//    V scales.  Each instruction moves one contiguous 1 KiB (16 bytes per
+//    lane) thanks to the pool layout, and data in flight costs no VGPRs.
+//    K of chunk c+1 is requested as soon as chunk c's K has been read out of
+//    LDS (after its QK step), V of chunk c+1 as soon as chunk c's V has been
+//    read (after its PV step), so each load has about a chunk of work to hide
+//    behind, plus the other wave on the SIMD.
 //  * S = Q K^T on v_mfma_f32_16x16x32_f16: K = 32 is exactly one quant block,
 //    so the int8 codes go in unscaled (exact in fp16) and the block's fp16
 //    scale multiplies the fp32 result.  q is split into fp16 hi + lo parts
-//    (two MFMAs into one accumulator), so every product is exact in fp32;
+//    (two MFMAs into one accumulator), so every product is exact in fp32.
 //  * softmax: row max over the 16 tokens of a tile with DPP row rotations,
-//    running max m, exp2 in the log2 domain (q carries scale*log2 e), the
-//    accumulator is rescaled only when some row's max grows;
+//    log2 domain (q carries scale*log2 e), lazy rescaling (below).
 //  * P goes through a per-wave LDS buffer from the S layout (lane = token) to
 //    the MFMA A layout (lane = row), is multiplied by the V scale of its
 //    (token, block) in fp32 and rounded once to fp16; O += P' Vcodes on MFMA
-//    with the 4-bit codes converted exactly to fp16 (c - 8).
-// At the end the 4 waves are combined in LDS in a fixed order (deterministic)
+//    with the 4-bit codes converted exactly to fp16.
+// At the end the W waves are combined in LDS in a fixed order (deterministic)
 // and one partial per workgroup is written.
 #include <hip/hip_fp16.h>
 
@@ -43,28 +46,43 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
 
-constexpr int kWaves = 4;
 constexpr int kPStride = 36;   // floats per row of the P transpose buffer (32 + padding)
 constexpr float kLog2e = 1.4426950408889634f;
+// Lazy rescaling: a row's reference maximum m moves only when a chunk's
+// maximum exceeds it by more than kTau (log2 units).  Weights are formed as
+// 2^(s - m - kTau) <= 1 and the V codes carry the compensating 2^kTau
+// exactly, so fp16 operands never overflow; the row sum is scaled by 2^kTau
+// at the end.
+constexpr float kTau = 4.0f;
 
-template <int D>
+template <int D, int RT>
 struct Cfg {
     static constexpr int NB = D / kBlock;       // quant blocks per row
-    static constexpr int KL = D / 64;           // 16-byte loads per lane: K tile, V chunk
+    static constexpr int KL = D / 64;           // 1 KiB loads: per K tile, per V chunk
     static constexpr int NT = D / 16;           // 16-wide output tiles
-    static constexpr int KSW = NB / 2;          // K-scale dwords per token
-    static constexpr int VSD = 16 * NB;         // V-scale dwords per chunk (32 tokens)
-    static constexpr int VSW = (VSD + 63) / 64; // V-scale dwords per lane
+    static constexpr int W = RT == 1 ? 8 : 4;   // waves per workgroup (kThreadsFor / 64)
+    // per-wave landing zone and P buffer (bytes)
+    static constexpr int LAND_K = 2 * KL * 1024;
+    static constexpr int LAND_KS = 1024;        // 32 x NB fp16, padded to one full-wave DMA
+    static constexpr int LAND_V = KL * 1024;
+    static constexpr int LAND_VS = 1024;        // NB x 32 fp16, padded likewise
+    static constexpr int PBUF = RT * 16 * kPStride * 4;
+    static constexpr int WAVE_BYTES = LAND_K + LAND_KS + LAND_V + LAND_VS + PBUF;
+    static constexpr int Q_BYTES = RT * NB * 2 * 64 * 16;
+    static constexpr int COMB_BYTES = (W / 2) * RT * 16 * D * 4;
+    static constexpr int MAIN_BYTES = Q_BYTES + W * WAVE_BYTES > COMB_BYTES ? Q_BYTES + W * WAVE_BYTES : COMB_BYTES;
+    static constexpr int ML_BYTES = W * RT * 16 * 2 * 4;
+    static constexpr int LDS_BYTES = MAIN_BYTES + ML_BYTES;
+    // vector-memory instructions per request
+    static constexpr int K_ISSUES = 2 * KL + 1;
+    static constexpr int V_ISSUES = KL + 1;
 };
 
-template <int D>
-struct ChunkRegs {
-    u32x4 k[2][Cfg<D>::KL];
-    uint32_t ks[2][Cfg<D>::KSW];
-    u32x4 v[Cfg<D>::KL];
-    uint32_t vs[Cfg<D>::VSW];
-};
+template <int RT>
+constexpr int kThreadsFor = (RT == 1 ? 8 : 4) * 64;   // workgroup size (must match Cfg::W)
 
 template <int CTRL>
 __device__ inline float dpp(float x) {
@@ -88,11 +106,23 @@ __device__ inline float row16_sum(float x) {
     return x;
 }
 
-// Keeps the scheduler from hoisting later blocks' LDS reads and conversions
-// above this point (which would raise register pressure past the budget).
+// Keeps the scheduler from moving work across a block boundary (which would
+// lengthen live ranges past the register budget).
 #define SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 
+// Waits for this wave's outstanding LDS reads; also a compiler memory fence.
 __device__ inline void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Waits until at most N vector-memory requests of this wave are outstanding
+// (direct-to-LDS loads count); also a compiler memory fence, since the
+// compiler cannot see that later LDS reads depend on those loads.
+template <int N>
+__device__ inline void vm_wait() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
+
+// 16 bytes per lane, global -> LDS: lane i's bytes land at lds + 16 i.
+__device__ inline void dma16(const void* g, void* lds) {
+    __builtin_amdgcn_global_load_lds((glb_void*)g, (lds_void*)lds, 16, 0, 0);
+}
 
 // 2^x on the hardware exp unit (results below the normal range flush to 0,
 // which only drops weights far below the row maximum).
@@ -106,108 +136,106 @@ __device__ inline half2v as_h2(uint32_t x) { return __builtin_bit_cast(half2v, x
 __device__ inline half8 k_codes_to_half(uint32_t x0, uint32_t x1) {
     x0 ^= 0x80808080u;
     x1 ^= 0x80808080u;
-    const half2v off = {(_Float16)1152.0f, (_Float16)1152.0f};
     const u32x4 w = {__builtin_amdgcn_perm(0x64646464u, x0, 0x04010400u),
                      __builtin_amdgcn_perm(0x64646464u, x0, 0x04030402u),
                      __builtin_amdgcn_perm(0x64646464u, x1, 0x04010400u),
                      __builtin_amdgcn_perm(0x64646464u, x1, 0x04030402u)};
-    half8 h = __builtin_bit_cast(half8, w);
-    return h - half8{off.x, off.x, off.x, off.x, off.x, off.x, off.x, off.x};
+    const _Float16 off = 1152.0f;
+    return __builtin_bit_cast(half8, w) - half8{off, off, off, off, off, off, off, off};
 }
 
-// 8 four-bit codes (nibble i = token i of the lane's group) -> fp16 (c - 8),
-// exactly, in the order (t0, t4, t1, t5, t2, t6, t3, t7).  Nibbles at bits
-// 0-3 of a half become 1024 + n; at bits 4-7, 1024 + 16n.
-__device__ inline half8 v_codes_to_half(uint32_t x) {
-    const uint32_t magic = 0x64006400u;
+// 8 four-bit codes (nibble i = token i of the lane's group) -> fp16
+// (c - 8) * 2^kTau, exactly, in the order (t0, t4, t1, t5, t2, t6, t3, t7).
+// Nibbles at bits 0-3 of a half become 1024 + n, at bits 4-7 1024 + 16n;
+// one FMA per half then gives (n - 8) * 16 (a small integer, exact).  The
+// magic exponent lives in a register so that mask-and-insert is one
+// v_and_or_b32 (gfx9 VOP3 takes no literal).
+__device__ inline half8 v_codes_to_half(uint32_t x, uint32_t magic) {
     const uint32_t y = x >> 8;
     const u32x4 w = {(x & 0x000F000Fu) | magic, (x & 0x00F000F0u) | magic,
                      (y & 0x000F000Fu) | magic, (y & 0x00F000F0u) | magic};
     const half8 h = __builtin_bit_cast(half8, w);
-    const _Float16 one = 1.0f, sixteenth = 0.0625f, o0 = -1032.0f, o1 = -72.0f;
-    const half8 mul = {one, one, sixteenth, sixteenth, one, one, sixteenth, sixteenth};
-    const half8 add = {o0, o0, o1, o1, o0, o0, o1, o1};
+    const _Float16 m0 = 16.0f, m1 = 1.0f, a0 = -16512.0f, a1 = -1152.0f;
+    const half8 mul = {m0, m0, m1, m1, m0, m0, m1, m1};
+    const half8 add = {a0, a0, a1, a1, a0, a0, a1, a1};
     return h * mul + add;
 }
 
-__device__ inline float half_lo(uint32_t w) { return (float)__builtin_bit_cast(half2v, w).x; }
-__device__ inline float half_hi(uint32_t w) { return (float)__builtin_bit_cast(half2v, w).y; }
+// Per-wave LDS landing zone of one chunk.
+struct Land {
+    uint8_t* k;     // [2 tiles][KL][1 KiB]
+    uint8_t* ks;    // [32 tokens][NB] fp16 (then repeats)
+    uint8_t* v;     // [KL][1 KiB]
+    uint8_t* vs;    // [NB][32 tokens] fp16 (then repeats)
+};
 
-template <int D>
-__device__ inline void load_chunk(ChunkRegs<D>& r, const uint8_t* unit, const Geom& g, int slot0, int lane) {
-    using C = Cfg<D>;
-    const uint8_t* kbase = unit + (int64_t)(slot0 / kTile) * kTile * D + lane * 16;
+template <int D, int RT>
+__device__ inline void issue_k(const Land& L, const uint8_t* unit, const Geom& g, int slot0, int lane) {
+    using C = Cfg<D, RT>;
+    const uint8_t* src = unit + (int64_t)(slot0 / kTile) * kTile * D + lane * 16;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int p = 0; p < C::KL; ++p)
-            r.k[tt][p] = *reinterpret_cast<const u32x4*>(kbase + tt * kTile * D + p * 1024);
-    const uint32_t* ks = reinterpret_cast<const uint32_t*>(unit + g.k_scales_off());
+        for (int p = 0; p < C::KL; ++p) dma16(src + tt * kTile * D + p * 1024, L.k + (tt * C::KL + p) * 1024);
+    // 32 tokens x NB scales = 4*NB pieces of 16 bytes.  Every lane takes part
+    // (lanes past 4*NB repeat a piece): a DMA under a lane-dependent branch
+    // can get its LDS base merged with a neighbouring DMA's by the compiler.
+    dma16(unit + g.k_scales_off() + (int64_t)slot0 * C::NB * 2 + (lane % (4 * C::NB)) * 16, L.ks);
+}
+
+template <int D, int RT>
+__device__ inline void issue_v(const Land& L, const uint8_t* unit, const Geom& g, int slot0, int lane) {
+    using C = Cfg<D, RT>;
+    const uint8_t* src = unit + g.v_codes_off() + (int64_t)(slot0 / kChunk) * kChunk * D / 2 + lane * 16;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-        const int tok = slot0 + tt * kTile + (lane & 15);
-#pragma unroll
-        for (int w = 0; w < C::KSW; ++w) r.ks[tt][w] = ks[tok * C::KSW + w];
-    }
-    const uint8_t* vbase = unit + g.v_codes_off() + (int64_t)(slot0 / kChunk) * kChunk * D / 2 + lane * 16;
-#pragma unroll
-    for (int u = 0; u < C::KL; ++u) r.v[u] = *reinterpret_cast<const u32x4*>(vbase + u * 1024);
-    const uint32_t* vs = reinterpret_cast<const uint32_t*>(unit + g.v_scales_off()) + slot0 * C::NB / 2;
-#pragma unroll
-    for (int w = 0; w < C::VSW; ++w) {
-        const int i = lane + 64 * w;
-        r.vs[w] = i < C::VSD ? vs[i] : 0u;
-    }
+    for (int u = 0; u < C::KL; ++u) dma16(src + u * 1024, L.v + u * 1024);
+    dma16(unit + g.v_scales_off() + (int64_t)(slot0 / kChunk) * C::NB * kChunk * 2 + (lane % (4 * C::NB)) * 16,
+          L.vs);
 }
 
 template <int D, int RT>
 struct WaveState {
-    floatx4 o[RT][Cfg<D>::NT];   // unnormalized output, MFMA C layout
-    float m[RT][4];              // running max of each of the lane's 4 rows per tile
-    float l[RT][4];              // this lane's share of the row sums
+    floatx4 o[RT][Cfg<D, RT>::NT];   // unnormalized output, MFMA C layout
+    float m[RT][4];                  // reference max of each of the lane's 4 rows per tile
+    float l[RT][4];                  // this lane's share of the row sums
 };
 
-// Phase 1 of a 32-token chunk: S = (q_hi + q_lo) K^T for both 16-token tiles,
-// plus staging of the chunk's V scales.  MASK: some key of the chunk lies
-// beyond the last key of some row (causal edge, or positions past ctx_len).
+// S = (q_hi + q_lo) K^T for the chunk's two 16-token tiles.  MASK: some key
+// of the chunk lies beyond the last key of some row (causal edge, or
+// positions past ctx_len).
 template <int D, int RT, bool MASK>
-__device__ inline void qk_phase(floatx4 (&s)[RT][2], const ChunkRegs<D>& r, const half8* __restrict__ qlds,
-                                uint32_t* __restrict__ vslds, int lane, int j0, int first_last, int group,
-                                int rows) {
-    using C = Cfg<D>;
+__device__ inline void qk_step(floatx4 (&s)[RT][2], const Land& L, const half8* __restrict__ qlds, int lane,
+                               int j0, int first_last, int group, int rows) {
+    using C = Cfg<D, RT>;
     const int g4 = lane >> 4;
     const int n16 = lane & 15;
-    // stage this chunk's V scales block-major ([block][32 tokens] halves) for
-    // the P' products below: dword i of the chunk holds blocks 2w, 2w+1 of
-    // token i / (NB/2)
-    {
-        uint16_t* vsh = reinterpret_cast<uint16_t*>(vslds);
+    // K scales of the lane's token in each tile (NB halves)
+    uint32_t ksw[2][C::NB / 2];
 #pragma unroll
-        for (int w = 0; w < C::VSW; ++w) {
-            const int i = lane + 64 * w;
-            if (i < C::VSD) {
-                const int tok = i / (C::NB / 2), blk = 2 * (i % (C::NB / 2));
-                vsh[blk * kChunk + tok] = (uint16_t)(r.vs[w] & 0xFFFFu);
-                vsh[(blk + 1) * kChunk + tok] = (uint16_t)(r.vs[w] >> 16);
-            }
-        }
+    for (int tt = 0; tt < 2; ++tt) {
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(L.ks + (tt * kTile + n16) * C::NB * 2);
+#pragma unroll
+        for (int w = 0; w < C::NB / 2; ++w) ksw[tt][w] = src[w];
     }
-
-    // ---- S = (q_hi + q_lo) K^T, one 32-value block per MFMA K step
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) s[rt][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    u32x4 kr[2];
 #pragma unroll
     for (int b = 0; b < C::NB; ++b) {
+        if ((b & 1) == 0) {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+                kr[tt] = *reinterpret_cast<const u32x4*>(L.k + (tt * C::KL + b / 2) * 1024 + lane * 16);
+        }
         half8 kb[2];
         float ksc[2];
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-            const u32x4 kr = r.k[tt][b / 2];
-            kb[tt] = (b & 1) ? k_codes_to_half(kr.z, kr.w) : k_codes_to_half(kr.x, kr.y);
-            const uint32_t sw = r.ks[tt][b / 2];
-            ksc[tt] = (b & 1) ? half_hi(sw) : half_lo(sw);
+            kb[tt] = (b & 1) ? k_codes_to_half(kr[tt].z, kr[tt].w) : k_codes_to_half(kr[tt].x, kr[tt].y);
+            const half2v sw = as_h2(ksw[tt][b / 2]);
+            ksc[tt] = (b & 1) ? (float)sw.y : (float)sw.x;
         }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -222,8 +250,7 @@ __device__ inline void qk_phase(floatx4 (&s)[RT][2], const ChunkRegs<D>& r, cons
         }
         SCHED_FENCE();
     }
-
-    // ---- causal / tail mask: key j visible to row r iff j <= first_last + r / group
+    // causal / tail mask: key j visible to row r iff j <= first_last + r / group
     if (MASK) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
@@ -236,33 +263,30 @@ __device__ inline void qk_phase(floatx4 (&s)[RT][2], const ChunkRegs<D>& r, cons
                     if (j0 + tt * kTile + n16 > last) s[rt][tt][jj] = -INFINITY;
             }
     }
-
 }
 
-// Phase 2: online softmax over the chunk's scores, then O += (P * vscale) V.
-template <int D, int RT, bool MASK>
-__device__ inline void pv_phase(WaveState<D, RT>& st, floatx4 (&s)[RT][2], const u32x4 (&v)[Cfg<D>::KL],
-                                float* __restrict__ plds, const uint32_t* __restrict__ vslds, int lane) {
-    using C = Cfg<D>;
+// Online softmax over the chunk's scores; writes P to the wave's LDS buffer.
+template <int D, int RT>
+__device__ inline void softmax_step(WaveState<D, RT>& st, floatx4 (&s)[RT][2], float* __restrict__ plds, int lane) {
+    using C = Cfg<D, RT>;
     const int g4 = lane >> 4;
     const int n16 = lane & 15;
-    // ---- online softmax (log2 domain)
     float mnew[RT][4];
     bool grow = false;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-            const float mx = row16_max(fmaxf(s[rt][0][jj], s[rt][1][jj]));
-            mnew[rt][jj] = fmaxf(st.m[rt][jj], mx);
-            grow |= mnew[rt][jj] > st.m[rt][jj];
+            mnew[rt][jj] = row16_max(fmaxf(s[rt][0][jj], s[rt][1][jj]));
+            grow |= mnew[rt][jj] > st.m[rt][jj] + kTau;
         }
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                const float alpha = mnew[rt][jj] > st.m[rt][jj] ? fast_exp2(st.m[rt][jj] - mnew[rt][jj]) : 1.0f;
+                if (!(mnew[rt][jj] > st.m[rt][jj])) continue;
+                const float alpha = fast_exp2(st.m[rt][jj] - mnew[rt][jj]);
                 st.l[rt][jj] *= alpha;
 #pragma unroll
                 for (int nt = 0; nt < C::NT; ++nt) st.o[rt][nt][jj] *= alpha;
@@ -273,7 +297,7 @@ __device__ inline void pv_phase(WaveState<D, RT>& st, floatx4 (&s)[RT][2], const
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-            const float mref = st.m[rt][jj] == -INFINITY ? 0.0f : st.m[rt][jj];
+            const float mref = (st.m[rt][jj] == -INFINITY ? 0.0f : st.m[rt][jj]) + kTau;
             const float p0 = fast_exp2(s[rt][0][jj] - mref);
             const float p1 = fast_exp2(s[rt][1][jj] - mref);
             st.l[rt][jj] += p0 + p1;
@@ -282,8 +306,16 @@ __device__ inline void pv_phase(WaveState<D, RT>& st, floatx4 (&s)[RT][2], const
             prow[kTile + n16] = p1;
         }
     lds_fence();
+}
 
-    // ---- O += (P * vscale) Vcodes
+// O += (P * vscale) Vcodes for the chunk.
+template <int D, int RT, bool MASK>
+__device__ inline void pv_step(WaveState<D, RT>& st, const Land& L, const float* __restrict__ plds, int lane) {
+    using C = Cfg<D, RT>;
+    const int g4 = lane >> 4;
+    const int n16 = lane & 15;
+    uint32_t magic = 0x64006400u;
+    asm volatile("" : "+v"(magic));          // keep the constant in a VGPR
     float pf[RT][8];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -291,18 +323,20 @@ __device__ inline void pv_phase(WaveState<D, RT>& st, floatx4 (&s)[RT][2], const
 #pragma unroll
         for (int i = 0; i < 8; ++i) pf[rt][i] = prow[i];
     }
+    u32x4 vr;
 #pragma unroll
     for (int b = 0; b < C::NB; ++b) {
+        if ((b & 1) == 0) vr = *reinterpret_cast<const u32x4*>(L.v + (b / 2) * 1024 + lane * 16);
         // V scales of the lane's 8 tokens (8*g4 .. 8*g4+7) for block b
-        const u32x4 sw = reinterpret_cast<const u32x4*>(vslds)[(b * kChunk + 8 * g4) / 8];
-        const float sc[8] = {half_lo(sw.x), half_hi(sw.x), half_lo(sw.y), half_hi(sw.y),
-                             half_lo(sw.z), half_hi(sw.z), half_lo(sw.w), half_hi(sw.w)};
+        const half8 sc = *reinterpret_cast<const half8*>(L.vs + (b * kChunk + 8 * g4) * 2);
+        // P' = p * vscale: one fused fp32 multiply rounded once to fp16
         half8 a[RT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                float x0 = pf[rt][k] * sc[k], x1 = pf[rt][k + 4] * sc[k + 4];
+                float x0 = fmaf(pf[rt][k], (float)sc[k], 0.0f);
+                float x1 = fmaf(pf[rt][k + 4], (float)sc[k + 4], 0.0f);
                 if (MASK) {             // masked keys may hold unwritten scales
                     x0 = pf[rt][k] == 0.0f ? 0.0f : x0;
                     x1 = pf[rt][k + 4] == 0.0f ? 0.0f : x1;
@@ -313,7 +347,7 @@ __device__ inline void pv_phase(WaveState<D, RT>& st, floatx4 (&s)[RT][2], const
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int nt = 2 * b + h;
-            const half8 bv = v_codes_to_half(v[nt / 4][nt % 4]);
+            const half8 bv = v_codes_to_half(vr[nt % 4], magic);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
                 st.o[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[rt], bv, st.o[rt][nt], 0, 0, 0);
@@ -323,9 +357,10 @@ __device__ inline void pv_phase(WaveState<D, RT>& st, floatx4 (&s)[RT][2], const
 }
 
 template <int D, int RT>
-__global__ __launch_bounds__(256, 1) void attn_mfma_stream_kernel(AttnArgs a, int cps, int n_splits,
-                                                                                 int group, int rows) {
-    using C = Cfg<D>;
+__global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_stream_kernel(AttnArgs a, int cps, int n_splits,
+                                                                               int group, int rows) {
+    using C = Cfg<D, RT>;
+    constexpr int W = C::W;
     extern __shared__ __align__(16) uint8_t smem[];
     const Geom& g = a.g;
     const int lane = threadIdx.x & 63;
@@ -335,21 +370,35 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_stream_kernel(AttnArgs a, in
     const int total_chunks = (a.ctx + kChunk - 1) / kChunk;
     const int first_last = a.ctx - a.n_q;             // last key of query 0
 
-    // LDS carve-up: [Q hi/lo | P per wave | V scales per wave], reused for the
-    // final combine; [m, l per wave and row] kept apart.
-    const int q_bytes = RT * C::NB * 2 * 64 * 16;
-    const int p_bytes = kWaves * RT * 16 * kPStride * 4;
-    const int vs_bytes = kWaves * C::VSD * 4;
-    const int comb_bytes = 2 * RT * 16 * D * 4;
-    const int main_bytes = max(q_bytes + p_bytes + vs_bytes, comb_bytes);
+    // LDS: [Q hi/lo | per wave: landing zone + P buffer] (reused by the final
+    // combine) | [m, l per wave and row]
     half8* qlds = reinterpret_cast<half8*>(smem);
-    float* plds = reinterpret_cast<float*>(smem + q_bytes) + wave * RT * 16 * kPStride;
-    uint32_t* vslds = reinterpret_cast<uint32_t*>(smem + q_bytes + p_bytes) + wave * C::VSD;
-    float* mls = reinterpret_cast<float*>(smem + main_bytes);     // [wave][RT*16][2]
+    uint8_t* wbase = smem + C::Q_BYTES + wave * C::WAVE_BYTES;
+    const Land land = {wbase, wbase + C::LAND_K, wbase + C::LAND_K + C::LAND_KS,
+                       wbase + C::LAND_K + C::LAND_KS + C::LAND_V};
+    float* plds = reinterpret_cast<float*>(wbase + C::LAND_K + C::LAND_KS + C::LAND_V + C::LAND_VS);
+    float* mls = reinterpret_cast<float*>(smem + C::MAIN_BYTES);     // [wave][RT*16][2]
+
+    // ---- this wave's chunks; start their first loads before staging q
+    const int c0 = split * W * cps + wave * cps;
+    const int c1 = min(c0 + cps, total_chunks);
+    auto unit_of = [&](int c, bool& ok) -> const uint8_t* {
+        const int phys = a.page_table[(c * kChunk) / g.P];
+        ok = phys >= 0 && phys < g.n_pages;
+        return a.pool + g.unit_index(ok ? phys : 0, kvh) * g.unit_bytes();
+    };
+    bool ok_cur = false;
+    if (c0 < c1) {
+        const uint8_t* u0 = unit_of(c0, ok_cur);
+        if (ok_cur) {
+            issue_k<D, RT>(land, u0, g, (c0 * kChunk) % g.P, lane);
+            issue_v<D, RT>(land, u0, g, (c0 * kChunk) % g.P, lane);
+        }
+    }
 
     // ---- stage q rows as fp16 hi/lo in the MFMA A layout, pre-scaled by scale*log2(e)
     const float qscale = a.scale * kLog2e;
-    for (int e = threadIdx.x; e < RT * C::NB * 64; e += 256) {
+    for (int e = threadIdx.x; e < RT * C::NB * 64; e += W * 64) {
         const int l = e & 63, rb = e >> 6, b = rb % C::NB, rt = rb / C::NB;
         const int row = 16 * rt + (l & 15);
         half8 hi, lo;
@@ -380,60 +429,39 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_stream_kernel(AttnArgs a, in
         for (int nt = 0; nt < C::NT; ++nt) st.o[rt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // ---- stream this wave's chunks, chunk c+1 in flight while c is computed
-    const int c0 = split * kWaves * cps + wave * cps;
-    const int c1 = min(c0 + cps, total_chunks);
-    bool bad = false;
-    auto unit_of = [&](int c, bool& ok) -> const uint8_t* {
-        const int phys = a.page_table[(c * kChunk) / g.P];
-        ok = phys >= 0 && phys < g.n_pages;
-        return a.pool + g.unit_index(ok ? phys : 0, kvh) * g.unit_bytes();
-    };
-    // Chunk c's K registers die after its QK phase, so chunk c+1's loads are
-    // issued there: they fly during chunk c's softmax and P*V work.
-    auto phase1 = [&](floatx4 (&s)[RT][2], const ChunkRegs<D>& r, int c) {
+    // ---- stream: K(c+1) is requested after QK(c), V(c+1) after PV(c).  A
+    // page-table entry outside the pool stops the wave (nothing is loaded
+    // from it) and turns its partial into NaN.
+    bool bad = c0 < c1 && !ok_cur;
+    for (int c = c0; c < c1 && !bad; ++c) {
         const int j0 = c * kChunk;
-        if (j0 + kChunk - 1 > first_last)
-            qk_phase<D, RT, true>(s, r, qlds, vslds, lane, j0, first_last, group, rows);
-        else
-            qk_phase<D, RT, false>(s, r, qlds, vslds, lane, j0, first_last, group, rows);
-    };
-    auto phase2 = [&](floatx4 (&s)[RT][2], const ChunkRegs<D>& r, int c) {
-        if (c * kChunk + kChunk - 1 > first_last)
-            pv_phase<D, RT, true>(st, s, r.v, plds, vslds, lane);
-        else
-            pv_phase<D, RT, false>(st, s, r.v, plds, vslds, lane);
-    };
-    if (c0 < c1) {
-        ChunkRegs<D> ra, rb;
+        const bool mask = j0 + kChunk - 1 > first_last;
+        bool ok_next = false;
+        const uint8_t* u_next = c + 1 < c1 ? unit_of(c + 1, ok_next) : nullptr;
+        const int slot_next = ((c + 1) * kChunk) % g.P;
         floatx4 s[RT][2];
-        bool oka, okb = true;
-        const uint8_t* ua = unit_of(c0, oka);
-        if (oka) load_chunk<D>(ra, ua, g, (c0 * kChunk) % g.P, lane);
-        for (int c = c0; c < c1; c += 2) {
-            if (oka) phase1(s, ra, c);
-            if (c + 1 < c1) {
-                const uint8_t* ub = unit_of(c + 1, okb);
-                if (okb) load_chunk<D>(rb, ub, g, ((c + 1) * kChunk) % g.P, lane);
-            }
-            if (oka) phase2(s, ra, c); else bad = true;
-            if (c + 1 >= c1) break;
-            if (okb) phase1(s, rb, c + 1);
-            if (c + 2 < c1) {
-                ua = unit_of(c + 2, oka);
-                if (oka) load_chunk<D>(ra, ua, g, ((c + 2) * kChunk) % g.P, lane);
-            }
-            if (okb) phase2(s, rb, c + 1); else bad = true;
-        }
+        vm_wait<C::V_ISSUES>();                 // K(c) landed (V(c) may still fly)
+        if (mask) qk_step<D, RT, true>(s, land, qlds, lane, j0, first_last, group, rows);
+        else qk_step<D, RT, false>(s, land, qlds, lane, j0, first_last, group, rows);
+        lds_fence();                            // K(c) read out: the zone is free
+        if (ok_next) issue_k<D, RT>(land, u_next, g, slot_next, lane);
+        softmax_step<D, RT>(st, s, plds, lane);
+        if (ok_next) vm_wait<C::K_ISSUES>(); else vm_wait<0>();   // V(c) landed
+        if (mask) pv_step<D, RT, true>(st, land, plds, lane);
+        else pv_step<D, RT, false>(st, land, plds, lane);
+        lds_fence();                            // V(c) read out
+        if (ok_next) issue_v<D, RT>(land, u_next, g, slot_next, lane);
+        if (c + 1 < c1 && !ok_next) bad = true;
     }
+    vm_wait<0>();
 
-    // ---- finish the row sums, combine the 4 waves in a fixed order
+    // ---- finish the row sums, combine the W waves in a fixed order
     const int g4 = lane >> 4, n16 = lane & 15;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-            st.l[rt][jj] = row16_sum(st.l[rt][jj]);
+            st.l[rt][jj] = row16_sum(st.l[rt][jj]) * 16.0f;        // weights carried 2^-kTau
             if (bad) { st.m[rt][jj] = NAN; st.l[rt][jj] = NAN; }
             if (n16 == 0) {
                 const int row = 16 * rt + 4 * g4 + jj;
@@ -441,7 +469,7 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_stream_kernel(AttnArgs a, in
                 mls[(wave * RT * 16 + row) * 2 + 1] = st.l[rt][jj];
             }
         }
-    __syncthreads();
+    __syncthreads();                       // every wave is done with its landing zone
     float M[RT][4], Ltot[RT][4];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
@@ -450,10 +478,10 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_stream_kernel(AttnArgs a, in
             const int row = 16 * rt + 4 * g4 + jj;
             float mm = -INFINITY;
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, mls[(w * RT * 16 + row) * 2]);
+            for (int w = 0; w < W; ++w) mm = fmaxf(mm, mls[(w * RT * 16 + row) * 2]);
             float lt = 0.0f;
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
+            for (int w = 0; w < W; ++w) {
                 const float mw = mls[(w * RT * 16 + row) * 2], lw = mls[(w * RT * 16 + row) * 2 + 1];
                 lt += lw == 0.0f ? 0.0f : lw * exp2f(mw - mm);
             }
@@ -463,7 +491,7 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_stream_kernel(AttnArgs a, in
 #pragma unroll
             for (int nt = 0; nt < C::NT; ++nt) st.o[rt][nt][jj] *= f;
         }
-    float* ob = reinterpret_cast<float*>(smem);          // [2][RT*16][D]
+    float* ob = reinterpret_cast<float*>(smem);          // [W/2][RT*16][D]
     auto put = [&](int slot) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
@@ -482,15 +510,15 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_stream_kernel(AttnArgs a, in
                 for (int jj = 0; jj < 4; ++jj)
                     st.o[rt][nt][jj] += ob[((size_t)slot * RT * 16 + 16 * rt + 4 * g4 + jj) * D + 16 * nt + n16];
     };
-    __syncthreads();                       // every wave is done with Q / P / V-scale LDS
-    if (wave >= 2) put(wave - 2);
-    __syncthreads();
-    if (wave < 2) add(wave);
-    __syncthreads();
-    if (wave == 1) put(0);
-    __syncthreads();
+    // tree: waves [h, 2h) hand their sums to waves [0, h), h = W/2 .. 1
+#pragma unroll
+    for (int h = W / 2; h >= 1; h /= 2) {
+        if (wave >= h && wave < 2 * h) put(wave - h);
+        __syncthreads();
+        if (wave < h) add(wave);
+        __syncthreads();
+    }
     if (wave != 0) return;
-    add(0);
 
     // ---- write the partial of each row this workgroup serves
 #pragma unroll
@@ -512,28 +540,22 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_stream_kernel(AttnArgs a, in
 
 template <int D, int RT>
 hipError_t launch_dr(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) {
-    using C = Cfg<D>;
-    const int q_bytes = RT * C::NB * 2 * 64 * 16;
-    const int p_bytes = kWaves * RT * 16 * kPStride * 4;
-    const int vs_bytes = kWaves * C::VSD * 4;
-    const int comb_bytes = 2 * RT * 16 * D * 4;
-    const int main_bytes = q_bytes + p_bytes + vs_bytes > comb_bytes ? q_bytes + p_bytes + vs_bytes : comb_bytes;
-    const int lds = main_bytes + kWaves * RT * 16 * 2 * 4;
+    using C = Cfg<D, RT>;
     auto kern = attn_mfma_stream_kernel<D, RT>;
-    if (lds > 64 * 1024) {
+    if (C::LDS_BYTES > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
         if (e != hipSuccess) return e;
     }
     dim3 grid(pl.n_splits * a.g.n_kv);
-    hipLaunchKernelGGL(kern, grid, dim3(256), lds, stream, a, pl.chunks_per_split, pl.n_splits, pl.group, pl.rows);
+    hipLaunchKernelGGL(kern, grid, dim3(C::W * 64), C::LDS_BYTES, stream, a, pl.chunks_per_split, pl.n_splits,
+                       pl.group, pl.rows);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) {
-    const int rt = (pl.rows + 15) / 16;
-    switch (rt) {
+    switch ((pl.rows + 15) / 16) {
         case 1: return launch_dr<D, 1>(a, pl, stream);
         case 2: return launch_dr<D, 2>(a, pl, stream);
         case 3: return launch_dr<D, 3>(a, pl, stream);
@@ -543,6 +565,8 @@ hipError_t launch_d(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) {
 }
 
 }  // namespace
+
+int mfma_stream_waves(int rows) { return rows <= 16 ? 8 : 4; }
 
 hipError_t launch_attn_mfma_stream(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) {
     switch (a.g.D) {

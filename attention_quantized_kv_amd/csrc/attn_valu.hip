@@ -69,7 +69,7 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a, int cps, int 
         for (int e = 0; e < DPL; ++e) {
             const int d = lane * DPL + e;
             const float ks = f16_val(unit + g.k_scales_off() + (slot * nb + d / kBlock) * 2);
-            const float vs = f16_val(unit + g.v_scales_off() + (slot * nb + d / kBlock) * 2);
+            const float vs = f16_val(unit + g.v_scales_off() + v_scale_idx(g, slot, d / kBlock) * 2);
             kh[e] = ks * (float)(int8_t)unit[k_code_pos(g, slot, d)];
             int nib;
             const uint8_t byte = unit[v_code_pos(g, slot, d, &nib)];

@@ -75,8 +75,8 @@ int make_plan(const kvq_layout* L, int n_heads, int ctx, int n_q, bool prefill,
     if (cps > total_chunks) cps = total_chunks;
     pl->kernel = kernel;
     pl->chunks_per_split = cps;
-    // the streaming MFMA kernel folds 4 waves (4 * cps chunks) into one partial
-    const int per_partial = kernel == 2 ? 4 * cps : cps;
+    // the streaming MFMA kernel folds the waves of a workgroup into one partial
+    const int per_partial = kernel == 2 ? kvq::mfma_stream_waves(rows) * cps : cps;
     pl->n_splits = (total_chunks + per_partial - 1) / per_partial;
     pl->group = group;
     pl->rows = rows;

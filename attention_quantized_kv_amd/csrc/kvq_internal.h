@@ -11,7 +11,7 @@
 //                         1 KiB; lane (g, n) of load u holds, in dword w, dim
 //                         16(4u+w)+n of the 8 tokens 8g..8g+7 of the chunk
 //                         (the MFMA B operand of the P*V product)
-//   V scales [P][D/32]    fp16 bits
+//   V scales [P/32][D/32][32]  fp16 bits, block-major inside each 32-token chunk
 // Every wave-level load of the streaming kernels is therefore one contiguous,
 // 16-byte-per-lane, 1 KiB request.
 #pragma once
@@ -56,6 +56,11 @@ __host__ __device__ inline int64_t v_code_pos(const Geom& g, int s, int d, int* 
            (int64_t)(u * 64 + grp * 16 + n) * 16 + w * 4 + i / 2;
 }
 
+// Index (in fp16 elements, within the V-scale array) of V scale (slot s, block b).
+__host__ __device__ inline int v_scale_idx(const Geom& g, int s, int b) {
+    return ((s / kChunk) * g.nb() + b) * kChunk + s % kChunk;
+}
+
 // Launch plan for attention: which kernel and how the keys are split.
 struct AttnPlan {
     int kernel;            // 1 VALU, 2 MFMA streaming, 3 MFMA LDS-tiled
@@ -97,5 +102,7 @@ hipError_t launch_attn_valu(const AttnArgs& a, const AttnPlan& pl, hipStream_t s
 hipError_t launch_attn_mfma_stream(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream);
 hipError_t launch_attn_mfma_tiled(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream);
 hipError_t launch_merge(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream);
+// Waves per workgroup of the streaming MFMA kernel for a given row count.
+int mfma_stream_waves(int rows);
 
 }  // namespace kvq

@@ -10,8 +10,8 @@
 // context, via adaptive KV streaming", second paragraph).
 //
 // One workgroup per (row, 64 output dims): its 4 wavefronts each fold every
-// 4th split with a running maximum (so the loads of different splits are
-// independent), then wave 0 folds the 4 wave results in a fixed order.
+// 4th split with a running maximum, loading 8 splits at a time so their loads
+// overlap, then wave 0 folds the 4 wave results in a fixed order.
 // Splits with no visible key (l = 0) are skipped; a NaN partial (a page-table
 // entry outside the pool) propagates to the output.
 #include "kvq_internal.h"
@@ -29,20 +29,37 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a, int n_splits, in
     const float* l = a.ws_l + (size_t)row * n_splits;
     const float* acc = a.ws_acc + (size_t)row * n_splits * D + d;
 
+    // batches of 8 splits: all 24 loads of a batch are independent, so they
+    // are in flight together; the batch is then folded in order
     float M = -INFINITY, L = 0.0f, o = 0.0f;
-    for (int s = wave; s < n_splits; s += 4) {
-        const float ls = l[s];
-        if (ls == 0.0f) continue;
-        const float ms = m[s];
-        if (ms > M) {
-            const float f = exp2f(M - ms);
+    constexpr int kBatch = 8;
+    for (int s0 = wave; s0 < n_splits; s0 += 4 * kBatch) {
+        float ms[kBatch], ls[kBatch], xs[kBatch];
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            const int s = s0 + 4 * k;
+            const bool in = s < n_splits;
+            ms[k] = in ? m[s] : -INFINITY;
+            ls[k] = in ? l[s] : 0.0f;
+            xs[k] = in ? acc[(size_t)s * D] : 0.0f;
+        }
+        float bm = M;
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k)
+            if (ls[k] != 0.0f) bm = fmaxf(bm, ms[k]);
+        if (bm > M) {
+            const float f = exp2f(M - bm);
             L *= f;
             o *= f;
-            M = ms;
+            M = bm;
         }
-        const float w = exp2f(ms - M);
-        L = fmaf(ls, w, L);
-        o = fmaf(acc[(size_t)s * D], w, o);
+#pragma unroll
+        for (int k = 0; k < kBatch; ++k) {
+            if (ls[k] == 0.0f) continue;
+            const float w = exp2f(ms[k] - M);
+            L = fmaf(ls[k], w, L);
+            o = fmaf(xs[k], w, o);
+        }
     }
     if (lane == 0) { sm[wave] = M; sl[wave] = L; }
     so[wave][lane] = o;

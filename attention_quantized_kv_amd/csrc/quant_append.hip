@@ -108,7 +108,7 @@ __global__ __launch_bounds__(D) void append_kernel(Geom g, uint8_t* __restrict__
         const float idv = dv != 0.0f ? __fdiv_rn(1.0f, dv) : 0.0f;
         const float t = mul_rounded(xv, idv) + 8.5f;
         vcode[r] = min(15, __float2int_rz(t));
-        if ((d & (kBlock - 1)) == 0) v_scales[slot * nb + d / kBlock] = f16_bits(dv);
+        if ((d & (kBlock - 1)) == 0) v_scales[v_scale_idx(g, slot, d / kBlock)] = f16_bits(dv);
     }
 
     int nib;

@@ -84,7 +84,8 @@ typedef struct {
  *                            (u, lane) with u < D/64, lane = g*16 + n; dword
  *                            w < 4 of a piece holds dim 16(4u+w)+n of tokens
  *                            32c+8g+i (i < 8) in bits 4i..4i+3.
- *   next 2*P*nb bytes        V scales, fp16 bits, [token][block].
+ *   next 2*P*nb bytes        V scales, fp16 bits, [chunk][block][32 tokens]
+ *                            (block-major inside each 32-token chunk).
  *
  * A value is scale * code for K and scale * (code - 8) for V.  The unit is
  * 26*P*D/16 bytes: 416 bytes per token at D = 256, matching Q8_0 (34 B) +

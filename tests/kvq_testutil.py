@@ -54,7 +54,8 @@ def decode_unit(unit: np.ndarray, D: int, P: int):
     o += 2 * P * nb
     vraw = unit[o:o + P * D // 2]
     o += P * D // 2
-    vs = unit[o:o + 2 * P * nb].view(np.uint16).reshape(P, nb)
+    # V scales are block-major inside each 32-token chunk: [chunk][block][32]
+    vs = unit[o:o + 2 * P * nb].view(np.uint16).reshape(P // 32, nb, 32).transpose(0, 2, 1).reshape(P, nb)
     # K: [tile][p][g][n][half][e] -> token 16t+n, dim 64p+32half+8g+e
     k6 = kraw.reshape(P // 16, D // 64, 4, 16, 2, 8)
     kc = k6.transpose(0, 3, 1, 4, 2, 5).reshape(P, D)
