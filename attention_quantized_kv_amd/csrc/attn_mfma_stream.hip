@@ -8,8 +8,8 @@
 // third paragraph: paged decode attention, extended to the verify batch;
 // second paragraph: online log-sum-exp across pages).
 //
-// Work split.  A workgroup of W wavefronts owns one KV head and a contiguous
-// run of W*cps 32-token chunks; each wave streams cps of them.  All query
+// Work split.  A workgroup of W wavefronts belongs to one KV head; the
+// head's chunks are dealt round-robin to its waves (about cps each).  All query
 // rows that use this KV head -- the G heads of the group ("Context window and
 // KV cache", GQA section) times n_q queries -- are served from one read of
 // every K/V byte, so the cache is read once per KV head.
@@ -80,6 +80,17 @@ struct Cfg {
     static constexpr int K_ISSUES = 2 * KL + 1;
     static constexpr int V_ISSUES = KL + 1;
 };
+
+// MFMA row placement.  Row tile rt holds MFMA rows 0..15; lane group g4 of the
+// S / O layouts owns rows 4*g4 .. 4*g4+3.  With at most 8 query rows (JJ = 2)
+// the rows go to MFMA rows {0,1, 4,5, 8,9, 12,13}, so each lane holds 2 real
+// rows and the softmax work per lane halves; otherwise (JJ = 4) row i sits at
+// MFMA row i.  Returns the query row at MFMA row prow of tile rt, or -1.
+template <int JJ>
+__device__ inline int logical_row(int rt, int prow) {
+    if (JJ == 4) return 16 * rt + prow;
+    return (prow & 3) < 2 ? 8 * rt + 2 * (prow >> 2) + (prow & 3) : -1;
+}
 
 template <int RT>
 constexpr int kThreadsFor = (RT == 1 ? 8 : 4) * 64;   // workgroup size (must match Cfg::W)
@@ -203,9 +214,10 @@ struct WaveState {
 // S = (q_hi + q_lo) K^T for the chunk's two 16-token tiles.  MASK: some key
 // of the chunk lies beyond the last key of some row (causal edge, or
 // positions past ctx_len).
-template <int D, int RT, bool MASK>
-__device__ inline void qk_step(floatx4 (&s)[RT][2], const Land& L, const half8* __restrict__ qlds, int lane,
-                               int j0, int first_last, int group, int rows) {
+template <int D, int RT, int JJ, bool MASK>
+__device__ inline void qk_step(floatx4 (&s)[RT][2], const Land& L, const half8* __restrict__ qlds,
+                               const half8 (&qreg)[Cfg<D, RT>::NB][2], int lane, int j0, int first_last, int group,
+                               int rows) {
     using C = Cfg<D, RT>;
     const int g4 = lane >> 4;
     const int n16 = lane & 15;
@@ -239,8 +251,9 @@ __device__ inline void qk_step(floatx4 (&s)[RT][2], const Land& L, const half8* 
         }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            const half8 qh = qlds[((rt * C::NB + b) * 2 + 0) * 64 + lane];
-            const half8 ql = qlds[((rt * C::NB + b) * 2 + 1) * 64 + lane];
+            // one row tile: q lives in registers; more: read it from LDS
+            const half8 qh = RT == 1 ? qreg[b][0] : qlds[((rt * C::NB + b) * 2 + 0) * 64 + lane];
+            const half8 ql = RT == 1 ? qreg[b][1] : qlds[((rt * C::NB + b) * 2 + 1) * 64 + lane];
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
                 floatx4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh, kb[tt], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
@@ -255,9 +268,9 @@ __device__ inline void qk_step(floatx4 (&s)[RT][2], const Land& L, const half8* 
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int row = 16 * rt + 4 * g4 + jj;
-                const int last = row < rows ? first_last + row / group : -1;
+            for (int jj = 0; jj < JJ; ++jj) {
+                const int row = logical_row<JJ>(rt, 4 * g4 + jj);
+                const int last = row >= 0 && row < rows ? first_last + row / group : -1;
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt)
                     if (j0 + tt * kTile + n16 > last) s[rt][tt][jj] = -INFINITY;
@@ -266,7 +279,7 @@ __device__ inline void qk_step(floatx4 (&s)[RT][2], const Land& L, const half8* 
 }
 
 // Online softmax over the chunk's scores; writes P to the wave's LDS buffer.
-template <int D, int RT>
+template <int D, int RT, int JJ>
 __device__ inline void softmax_step(WaveState<D, RT>& st, floatx4 (&s)[RT][2], float* __restrict__ plds, int lane) {
     using C = Cfg<D, RT>;
     const int g4 = lane >> 4;
@@ -276,7 +289,7 @@ __device__ inline void softmax_step(WaveState<D, RT>& st, floatx4 (&s)[RT][2], f
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
+        for (int jj = 0; jj < JJ; ++jj) {
             mnew[rt][jj] = row16_max(fmaxf(s[rt][0][jj], s[rt][1][jj]));
             grow |= mnew[rt][jj] > st.m[rt][jj] + kTau;
         }
@@ -284,7 +297,7 @@ __device__ inline void softmax_step(WaveState<D, RT>& st, floatx4 (&s)[RT][2], f
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
+            for (int jj = 0; jj < JJ; ++jj) {
                 if (!(mnew[rt][jj] > st.m[rt][jj])) continue;
                 const float alpha = fast_exp2(st.m[rt][jj] - mnew[rt][jj]);
                 st.l[rt][jj] *= alpha;
@@ -296,7 +309,7 @@ __device__ inline void softmax_step(WaveState<D, RT>& st, floatx4 (&s)[RT][2], f
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
+        for (int jj = 0; jj < JJ; ++jj) {
             const float mref = (st.m[rt][jj] == -INFINITY ? 0.0f : st.m[rt][jj]) + kTau;
             const float p0 = fast_exp2(s[rt][0][jj] - mref);
             const float p1 = fast_exp2(s[rt][1][jj] - mref);
@@ -356,9 +369,9 @@ __device__ inline void pv_step(WaveState<D, RT>& st, const Land& L, const float*
     }
 }
 
-template <int D, int RT>
+template <int D, int RT, int JJ>
 __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_stream_kernel(AttnArgs a, int cps, int n_splits,
-                                                                               int group, int rows) {
+                                                                           int group, int rows) {
     using C = Cfg<D, RT>;
     constexpr int W = C::W;
     extern __shared__ __align__(16) uint8_t smem[];
@@ -379,9 +392,15 @@ __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_stream_kernel(AttnA
     float* plds = reinterpret_cast<float*>(wbase + C::LAND_K + C::LAND_KS + C::LAND_V + C::LAND_VS);
     float* mls = reinterpret_cast<float*>(smem + C::MAIN_BYTES);     // [wave][RT*16][2]
 
-    // ---- this wave's chunks; start their first loads before staging q
-    const int c0 = split * W * cps + wave * cps;
-    const int c1 = min(c0 + cps, total_chunks);
+    // ---- this wave's chunks: wave g of the KV head takes chunks g, g + N,
+    // g + 2N, ... (N waves per head), so all waves sweep the context together
+    // and the addresses in flight at any time stay close (better DRAM and
+    // translation locality than one contiguous run per wave).  Start the
+    // first loads before staging q.
+    const int stride = n_splits * W;
+    const int c0 = split * W + wave;
+    const int c1 = total_chunks;
+    (void)cps;
     auto unit_of = [&](int c, bool& ok) -> const uint8_t* {
         const int phys = a.page_table[(c * kChunk) / g.P];
         ok = phys >= 0 && phys < g.n_pages;
@@ -400,9 +419,9 @@ __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_stream_kernel(AttnA
     const float qscale = a.scale * kLog2e;
     for (int e = threadIdx.x; e < RT * C::NB * 64; e += W * 64) {
         const int l = e & 63, rb = e >> 6, b = rb % C::NB, rt = rb / C::NB;
-        const int row = 16 * rt + (l & 15);
+        const int row = logical_row<JJ>(rt, l & 15);
         half8 hi, lo;
-        if (row < rows) {
+        if (row >= 0 && row < rows) {
             const int qi = row / group, h = kvh * group + row % group;
             const float* src = a.q + ((size_t)qi * a.n_heads + h) * D + b * kBlock + 8 * (l >> 4);
 #pragma unroll
@@ -420,6 +439,15 @@ __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_stream_kernel(AttnA
     }
     __syncthreads();
 
+    half8 qreg[C::NB][2];
+    if (RT == 1) {
+#pragma unroll
+        for (int b = 0; b < C::NB; ++b) {
+            qreg[b][0] = qlds[(b * 2 + 0) * 64 + lane];
+            qreg[b][1] = qlds[(b * 2 + 1) * 64 + lane];
+        }
+    }
+
     WaveState<D, RT> st;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -433,25 +461,25 @@ __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_stream_kernel(AttnA
     // page-table entry outside the pool stops the wave (nothing is loaded
     // from it) and turns its partial into NaN.
     bool bad = c0 < c1 && !ok_cur;
-    for (int c = c0; c < c1 && !bad; ++c) {
+    for (int c = c0; c < c1 && !bad; c += stride) {
         const int j0 = c * kChunk;
         const bool mask = j0 + kChunk - 1 > first_last;
         bool ok_next = false;
-        const uint8_t* u_next = c + 1 < c1 ? unit_of(c + 1, ok_next) : nullptr;
-        const int slot_next = ((c + 1) * kChunk) % g.P;
+        const uint8_t* u_next = c + stride < c1 ? unit_of(c + stride, ok_next) : nullptr;
+        const int slot_next = ((c + stride) * kChunk) % g.P;
         floatx4 s[RT][2];
         vm_wait<C::V_ISSUES>();                 // K(c) landed (V(c) may still fly)
-        if (mask) qk_step<D, RT, true>(s, land, qlds, lane, j0, first_last, group, rows);
-        else qk_step<D, RT, false>(s, land, qlds, lane, j0, first_last, group, rows);
+        if (mask) qk_step<D, RT, JJ, true>(s, land, qlds, qreg, lane, j0, first_last, group, rows);
+        else qk_step<D, RT, JJ, false>(s, land, qlds, qreg, lane, j0, first_last, group, rows);
         lds_fence();                            // K(c) read out: the zone is free
         if (ok_next) issue_k<D, RT>(land, u_next, g, slot_next, lane);
-        softmax_step<D, RT>(st, s, plds, lane);
+        softmax_step<D, RT, JJ>(st, s, plds, lane);
         if (ok_next) vm_wait<C::K_ISSUES>(); else vm_wait<0>();   // V(c) landed
         if (mask) pv_step<D, RT, true>(st, land, plds, lane);
         else pv_step<D, RT, false>(st, land, plds, lane);
         lds_fence();                            // V(c) read out
         if (ok_next) issue_v<D, RT>(land, u_next, g, slot_next, lane);
-        if (c + 1 < c1 && !ok_next) bad = true;
+        if (c + stride < c1 && !ok_next) bad = true;
     }
     vm_wait<0>();
 
@@ -460,7 +488,7 @@ __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_stream_kernel(AttnA
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
+        for (int jj = 0; jj < JJ; ++jj) {
             st.l[rt][jj] = row16_sum(st.l[rt][jj]) * 16.0f;        // weights carried 2^-kTau
             if (bad) { st.m[rt][jj] = NAN; st.l[rt][jj] = NAN; }
             if (n16 == 0) {
@@ -474,7 +502,7 @@ __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_stream_kernel(AttnA
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
+        for (int jj = 0; jj < JJ; ++jj) {
             const int row = 16 * rt + 4 * g4 + jj;
             float mm = -INFINITY;
 #pragma unroll
@@ -498,7 +526,7 @@ __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_stream_kernel(AttnA
 #pragma unroll
             for (int nt = 0; nt < C::NT; ++nt)
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
+                for (int jj = 0; jj < JJ; ++jj)
                     ob[((size_t)slot * RT * 16 + 16 * rt + 4 * g4 + jj) * D + 16 * nt + n16] = st.o[rt][nt][jj];
     };
     auto add = [&](int slot) {
@@ -507,7 +535,7 @@ __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_stream_kernel(AttnA
 #pragma unroll
             for (int nt = 0; nt < C::NT; ++nt)
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
+                for (int jj = 0; jj < JJ; ++jj)
                     st.o[rt][nt][jj] += ob[((size_t)slot * RT * 16 + 16 * rt + 4 * g4 + jj) * D + 16 * nt + n16];
     };
     // tree: waves [h, 2h) hand their sums to waves [0, h), h = W/2 .. 1
@@ -524,9 +552,9 @@ __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_stream_kernel(AttnA
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int row = 16 * rt + 4 * g4 + jj;
-            if (row >= rows) continue;
+        for (int jj = 0; jj < JJ; ++jj) {
+            const int row = logical_row<JJ>(rt, 4 * g4 + jj);
+            if (row < 0 || row >= rows) continue;
             const int qi = row / group, h = kvh * group + row % group;
             const size_t ps = ((size_t)qi * a.n_heads + h) * n_splits + split;
             if (n16 == 0) {
@@ -538,10 +566,10 @@ __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_stream_kernel(AttnA
         }
 }
 
-template <int D, int RT>
+template <int D, int RT, int JJ>
 hipError_t launch_dr(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) {
     using C = Cfg<D, RT>;
-    auto kern = attn_mfma_stream_kernel<D, RT>;
+    auto kern = attn_mfma_stream_kernel<D, RT, JJ>;
     if (C::LDS_BYTES > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
@@ -555,11 +583,12 @@ hipError_t launch_dr(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) 
 
 template <int D>
 hipError_t launch_d(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) {
+    if (pl.rows <= 8) return launch_dr<D, 1, 2>(a, pl, stream);
     switch ((pl.rows + 15) / 16) {
-        case 1: return launch_dr<D, 1>(a, pl, stream);
-        case 2: return launch_dr<D, 2>(a, pl, stream);
-        case 3: return launch_dr<D, 3>(a, pl, stream);
-        case 4: return launch_dr<D, 4>(a, pl, stream);
+        case 1: return launch_dr<D, 1, 4>(a, pl, stream);
+        case 2: return launch_dr<D, 2, 4>(a, pl, stream);
+        case 3: return launch_dr<D, 3, 4>(a, pl, stream);
+        case 4: return launch_dr<D, 4, 4>(a, pl, stream);
         default: return hipErrorInvalidValue;
     }
 }

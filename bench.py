@@ -46,14 +46,17 @@ def device_normal(shape, seed, device):
 
 
 class Layer:
-    def __init__(self, w, layer, device, fill_chunk=16384):
+    def __init__(self, w, layer, device, shuffle_pages=False, fill_chunk=16384):
         import torch
         import attention_quantized_kv_amd as kvq
         self.kvq = kvq
         self.w = w
         self.L = kvq.Layout(w.n_kv, w.head_dim, w.page_size, w.n_pages)
         self.pool = torch.empty(kvq.kvq_pool_bytes(self.L), dtype=torch.uint8, device=device)
-        perm = torch.randperm(w.n_pages, generator=torch.Generator().manual_seed(1000 + layer))
+        if shuffle_pages:
+            perm = torch.randperm(w.n_pages, generator=torch.Generator().manual_seed(1000 + layer))
+        else:          # one sequence filled in order: logical page i is physical page i
+            perm = torch.arange(w.n_pages)
         self.pt = perm.to(torch.int32).to(device)
         base = (w.wid * 1000 + layer) * 1_000_003
         for r in range(0, w.cached, fill_chunk):
@@ -137,6 +140,10 @@ def main():
     ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA streaming, 3 MFMA tiled")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--shuffle-pages", action="store_true",
+                    help="random page table (pages scattered over the pool) instead of in-order pages")
+    ap.add_argument("--copy-gib", type=float, default=0.0,
+                    help="only copy a buffer of this many GiB --steps times (calibrates HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -148,6 +155,21 @@ def main():
     import synth
     import attention_quantized_kv_amd as kvq
 
+    if args.copy_gib > 0:
+        n = int(args.copy_gib * (1 << 30))
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / args.steps
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "steps": args.steps,
+                          "GB_per_s_read_plus_write": round(2 * n / dt / 1e9, 1)}), flush=True)
+        return
+
     w = synth.WORKLOADS[args.workload]
     n_layers = args.layers or w.layers
     prefill = w.n_q > kvq.KVQ_MAX_NQ_DECODE
@@ -155,7 +177,7 @@ def main():
     torch.cuda.set_device(dev)
 
     t0 = time.time()
-    layers = [Layer(w, i, dev) for i in range(n_layers)]
+    layers = [Layer(w, i, dev, shuffle_pages=args.shuffle_pages) for i in range(n_layers)]
     ws_n = kvq.kvq_workspace_bytes_ex(layers[0].L, w.n_heads, w.ctx, w.n_q, args.kernel, 0) if args.kernel \
         else kvq.kvq_workspace_bytes(layers[0].L, w.n_heads, w.ctx, w.n_q, prefill)
     ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device=dev)
@@ -197,7 +219,8 @@ def main():
         "dtype": "f16 MFMA / f32" if args.kernel in (0, 2, 3) else "f32",
         "config": {"workload": w.name, "layers": n_layers, "n_heads": w.n_heads, "n_kv_heads": w.n_kv,
                    "head_dim": w.head_dim, "ctx": w.ctx, "n_q": w.n_q, "page_size": w.page_size,
-                   "kv_format": "K Q8_0 + V Q4_0", "kernel": args.kernel or "auto"},
+                   "kv_format": "K Q8_0 + V Q4_0", "kernel": args.kernel or "auto",
+                   "page_table": "shuffled" if args.shuffle_pages else "in order"},
     }
     if not prefill:
         value = n_layers * bytes_layer * args.steps / (total_ms / 1e3) / 1e9
