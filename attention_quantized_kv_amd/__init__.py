@@ -13,7 +13,7 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libkvq.so")
+LIB_PATH = os.environ.get("KVQ_LIB") or os.path.join(HERE, "libkvq.so")
 
 KVQ_OK = 0
 KVQ_ERR_INVALID_ARG = -1

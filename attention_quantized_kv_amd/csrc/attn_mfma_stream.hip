@@ -401,14 +401,22 @@ __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_stream_kernel(AttnA
     const int c0 = split * W + wave;
     const int c1 = total_chunks;
     (void)cps;
-    auto unit_of = [&](int c, bool& ok) -> const uint8_t* {
-        const int phys = a.page_table[(c * kChunk) / g.P];
+    // Page-table entries: lane k of `ents` holds the entry of the wave's
+    // chunk number kb + k (batches of 64, one gather load per batch), and the
+    // loop picks them out with readlane -- no memory access, hence no wait,
+    // between the K/V requests in flight.
+    auto load_ents = [&](int kb) -> int {
+        const int ck = c0 + (kb + lane) * stride;
+        return ck < c1 ? a.page_table[(ck * kChunk) / g.P] : -1;
+    };
+    auto unit_at = [&](int phys, bool& ok) -> const uint8_t* {
         ok = phys >= 0 && phys < g.n_pages;
         return a.pool + g.unit_index(ok ? phys : 0, kvh) * g.unit_bytes();
     };
+    int ents = load_ents(0);
     bool ok_cur = false;
     if (c0 < c1) {
-        const uint8_t* u0 = unit_of(c0, ok_cur);
+        const uint8_t* u0 = unit_at(__builtin_amdgcn_readlane(ents, 0), ok_cur);
         if (ok_cur) {
             issue_k<D, RT>(land, u0, g, (c0 * kChunk) % g.P, lane);
             issue_v<D, RT>(land, u0, g, (c0 * kChunk) % g.P, lane);
@@ -461,11 +469,16 @@ __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_stream_kernel(AttnA
     // page-table entry outside the pool stops the wave (nothing is loaded
     // from it) and turns its partial into NaN.
     bool bad = c0 < c1 && !ok_cur;
-    for (int c = c0; c < c1 && !bad; c += stride) {
+    for (int c = c0, k = 0; c < c1 && !bad; c += stride, ++k) {
         const int j0 = c * kChunk;
         const bool mask = j0 + kChunk - 1 > first_last;
+        const bool has_next = c + stride < c1;
+        if (has_next && ((k + 1) & 63) == 0) {  // every 64 chunks
+            ents = load_ents(k + 1);
+            asm volatile("" : "+v"(ents));      // consume it here, so the loop's other path has nothing to wait for
+        }
         bool ok_next = false;
-        const uint8_t* u_next = c + stride < c1 ? unit_of(c + stride, ok_next) : nullptr;
+        const uint8_t* u_next = has_next ? unit_at(__builtin_amdgcn_readlane(ents, (k + 1) & 63), ok_next) : nullptr;
         const int slot_next = ((c + stride) * kChunk) % g.P;
         floatx4 s[RT][2];
         vm_wait<C::V_ISSUES>();                 // K(c) landed (V(c) may still fly)

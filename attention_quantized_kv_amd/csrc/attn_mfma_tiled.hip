@@ -1,5 +1,468 @@
-// attn_mfma_tiled.hip -- placeholder until the LDS-tiled MFMA kernel lands.
+// attn_mfma_tiled.hip -- chunked prefill attention over the Q8_0-K / Q4_0-V
+// cache on gfx950 matrix cores ("Qwen 27B (IQ4_XS, Q8/Q4 KV) on a 16GB RX 9070
+// XT at 262k context, via adaptive KV streaming", second paragraph: chunked
+// prefill over streamed pages with online log-sum-exp accumulation; "Context
+// window and KV cache", GQA section: the q heads of a group share one KV head).
+//
+// Work split.  A workgroup owns 128 query rows of one KV head (row = query i
+// times the G heads of the group, query-major) and one contiguous run of
+// 32-token chunks; each of its 8 wavefronts owns 16 of the rows.  Splits of the
+// key range are merged afterwards by lse_merge.hip (with a single split the
+// kernel writes the normalised output itself).
+//
+// Per 32-token chunk, shared by the whole workgroup (double-buffered in LDS):
+//  * every thread loads at most one 16-byte piece of K codes, one 8-byte half
+//    piece of V nibbles (+ the 8 V scales of its tokens) and one 16-byte piece
+//    of K scales into registers one chunk ahead, and after the current chunk's
+//    math converts them: K codes exactly to fp16 (int8 -> fp16 is exact, the
+//    scale stays apart), V to (c - 8) * scale as an exact fp16 hi + lo pair,
+//    laid out as the MFMA operand fragments the waves read with one 16-byte
+//    LDS load;
+//  * S^T = K Q^T on v_mfma_f32_16x16x32_f16, one K = 32 step per quant block:
+//    the block's scale multiplies the fp32 result per key (fma_mix), and q is
+//    split into fp16 hi + lo parts (two MFMAs), so every score is the exact
+//    dot product up to fp32 accumulation.  With keys on the MFMA M axis each
+//    lane owns one query row: the row max needs only two cross-row lane swaps
+//    and P comes out already in the B-operand layout of O^T = V^T P^T;
+//  * online softmax in the log2 domain (q carries scale * log2 e) with lazy
+//    rescaling: the reference max moves only when a chunk beats it by more
+//    than kTau, so weights stay <= 2^kTau and fp16 P cannot overflow;
+//  * O^T += V^T P^T with P and V each split into fp16 hi + lo (three MFMAs per
+//    tile; lo*lo is below 2^-22).  Rounding either factor to one fp16 leaves
+//    errors of 2^-12 of |v| per weight, which the output tolerance does not
+//    absorb when a few large values nearly cancel.
+#include <hip/hip_fp16.h>
+
+#include <type_traits>
+
 #include "kvq_internal.h"
+
 namespace kvq {
-hipError_t launch_attn_mfma_tiled(const AttnArgs&, const AttnPlan&, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kRowsPerWg = kWaves * 16;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kTau = 4.0f;
+
+template <int D>
+struct TCfg {
+    static constexpr int NB = D / kBlock;       // quant blocks per row
+    static constexpr int NT = D / 16;           // 16-wide output dim tiles
+    static constexpr int KL = D / 64;           // 1 KiB pieces per K tile / V chunk
+    static constexpr int K_FRAG = 2 * NB * 64 * 16;   // [tile][block][lane] x 16 B
+    static constexpr int KS = 2 * NB * 16 * 2;        // [tile][block][16 keys] fp16
+    static constexpr int V_FRAG = NT * 64 * 16;       // [dim tile][lane] x 16 B, hi then lo parts
+    static constexpr int STAGE = K_FRAG + KS + 2 * V_FRAG;
+    static constexpr int LDS = 2 * STAGE;
+    static constexpr int K_ITEMS = 128 * KL;    // 16-byte K-code pieces per chunk
+    static constexpr int V_ITEMS = 128 * KL;    // 8-byte V-nibble half pieces per chunk
+    static constexpr int KS_ITEMS = 4 * NB;     // 16-byte K-scale pieces per chunk
+    static_assert(K_ITEMS <= kThreads && V_ITEMS <= kThreads, "one item per thread");
+};
+
+// 8 int8 codes -> 8 fp16 values, exactly (bias by 128, put each byte under
+// the fp16 exponent of 1024, subtract 1152).
+__device__ inline half8 k_codes_to_half(uint32_t x0, uint32_t x1) {
+    x0 ^= 0x80808080u;
+    x1 ^= 0x80808080u;
+    const u32x4 w = {__builtin_amdgcn_perm(0x64646464u, x0, 0x04010400u),
+                     __builtin_amdgcn_perm(0x64646464u, x0, 0x04030402u),
+                     __builtin_amdgcn_perm(0x64646464u, x1, 0x04010400u),
+                     __builtin_amdgcn_perm(0x64646464u, x1, 0x04030402u)};
+    const _Float16 off = 1152.0f;
+    return __builtin_bit_cast(half8, w) - half8{off, off, off, off, off, off, off, off};
+}
+
+// Byte M of x holds the codes of two consecutive tokens (low nibble first).
+// Sets hi + lo = ((c_lo - 8) * s.x, (c_hi - 8) * s.y) exactly: the low
+// nibble lands under the exponent of 1024 in the low half, the high nibble
+// (times 16) in the high half, an exact FMA recovers c - 8; the product has at
+// most 15 significant bits, so hi = fp16(product) and the FMA residual
+// lo = product - hi are both exact.
+template <int M>
+__device__ inline void v_pair(uint32_t x, half2v s, uint32_t magic, half2v& hi, half2v& lo) {
+    const uint32_t t = __builtin_amdgcn_perm(x, x, 0x01010101u * M);
+    const half2v h = __builtin_bit_cast(half2v, (t & 0x00F0000Fu) | magic);
+    const half2v mul = {(_Float16)1.0f, (_Float16)0.0625f};
+    const half2v add = {(_Float16)-1032.0f, (_Float16)-72.0f};
+    const half2v c = h * mul + add;
+    hi = c * s;
+    lo = __builtin_elementwise_fma(c, s, -hi);
+}
+
+// Lanes l, l^16, l^32, l^48 hold one query row.  v_permlane16_swap a, b
+// swaps a's odd 16-lane rows with b's even rows; with a = b = x that leaves
+// (x0 x0 x2 x2) in a and (x1 x1 x3 x3) in b, and v_permlane32_swap does the
+// same for the 32-lane halves.  Written as inline asm: the compiler's
+// optimiser folds the builtin's second result into its first.
+__device__ inline void swap16(float x, float& r0, float& r1) {
+    r0 = x;
+    r1 = x;
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(r0), "+v"(r1));
+}
+__device__ inline void swap32(float x, float& r0, float& r1) {
+    r0 = x;
+    r1 = x;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(r0), "+v"(r1));
+}
+
+// max / sum over the four lanes of a query row
+__device__ inline float xmax4(float x) {
+    float a, b;
+    swap16(x, a, b);
+    swap32(fmaxf(a, b), a, b);
+    return fmaxf(a, b);
+}
+
+__device__ inline float xsum4(float x) {
+    float a, b;
+    swap16(x, a, b);
+    swap32(a + b, a, b);
+    return a + b;
+}
+
+#define SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// Raw bytes of one chunk held by one thread between its load and its conversion.
+struct Raw {
+    u32x4 k;      // 16 K codes
+    u32x2 v;      // 16 V nibbles: two dims x 8 tokens
+    u32x4 vs;     // 8 V scales (fp16) of those tokens
+    u32x4 ks;     // 8 K scales (fp16)
+};
+
+template <int D>
+__device__ inline void load_raw(Raw& r, const uint8_t* unit, const Geom& g, int slot0, int t) {
+    using C = TCfg<D>;
+    if (t < C::K_ITEMS) {
+        const int tt = t / (64 * C::KL), p = (t / 64) % C::KL, L = t % 64;
+        r.k = *reinterpret_cast<const u32x4*>(unit + (int64_t)(slot0 / kTile + tt) * kTile * D + p * 1024 + L * 16);
+    }
+    if (t < C::V_ITEMS) {
+        const int u = t / 128, lp = (t % 128) / 2, hf = t & 1;
+        const int64_t cbase = (int64_t)(slot0 / kChunk);
+        r.v = *reinterpret_cast<const u32x2*>(unit + g.v_codes_off() + cbase * kChunk * D / 2 + u * 1024 + lp * 16 +
+                                              hf * 8);
+        const int b = 2 * u + hf, grp = lp / 16;
+        r.vs = *reinterpret_cast<const u32x4*>(unit + g.v_scales_off() + ((cbase * C::NB + b) * kChunk + 8 * grp) * 2);
+    }
+    if (t < C::KS_ITEMS)
+        r.ks = *reinterpret_cast<const u32x4*>(unit + g.k_scales_off() + (int64_t)slot0 * C::NB * 2 + t * 16);
+}
+
+// Converts a thread's raw bytes into the stage's operand fragments.
+// kvalid: tokens of the chunk that exist (< ctx); V of the others is zeroed so
+// that a masked key (weight 0) cannot meet an unwritten, non-finite scale.
+template <int D>
+__device__ inline void store_stage(const Raw& r, uint8_t* stage, int t, int kvalid) {
+    using C = TCfg<D>;
+    uint8_t* kf = stage;
+    _Float16* ksl = reinterpret_cast<_Float16*>(stage + C::K_FRAG);
+    uint8_t* vf = stage + C::K_FRAG + C::KS;
+    if (t < C::K_ITEMS) {
+        const int tt = t / (64 * C::KL), p = (t / 64) % C::KL, L = t % 64;
+        *reinterpret_cast<half8*>(kf + ((tt * C::NB + 2 * p) * 64 + L) * 16) = k_codes_to_half(r.k.x, r.k.y);
+        *reinterpret_cast<half8*>(kf + ((tt * C::NB + 2 * p + 1) * 64 + L) * 16) = k_codes_to_half(r.k.z, r.k.w);
+    }
+    if (t < C::V_ITEMS) {
+        const int u = t / 128, lp = (t % 128) / 2, hf = t & 1;
+        const int n = lp % 16, grp = lp / 16;
+        uint32_t magic = 0x64006400u;
+        asm volatile("" : "+v"(magic));
+        const half8 s8 = __builtin_bit_cast(half8, r.vs);
+        const half2v s01 = {s8[0], s8[1]}, s23 = {s8[2], s8[3]}, s45 = {s8[4], s8[5]}, s67 = {s8[6], s8[7]};
+        // tokens 8grp+0..3 go to lane group 2(grp%2), 8grp+4..7 to the next
+        // one, at fragment halves 4(grp/2)..+3 (the key order of the P
+        // fragment: group G holds keys 4G..4G+3 and 16+4G..16+4G+3)
+        const int laneA = 16 * (2 * (grp % 2)) + n, laneB = laneA + 16, j0 = 4 * (grp / 2);
+        const bool clip = 8 * grp + 7 >= kvalid;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const uint32_t x = e == 0 ? r.v.x : r.v.y;
+            const int nt = 4 * u + 2 * hf + e;
+            half2v h0, h1, h2, h3, l0, l1, l2, l3;
+            v_pair<0>(x, s01, magic, h0, l0);
+            v_pair<1>(x, s23, magic, h1, l1);
+            v_pair<2>(x, s45, magic, h2, l2);
+            v_pair<3>(x, s67, magic, h3, l3);
+            half4 ah = {h0[0], h0[1], h1[0], h1[1]}, bh = {h2[0], h2[1], h3[0], h3[1]};
+            half4 al = {l0[0], l0[1], l1[0], l1[1]}, bl = {l2[0], l2[1], l3[0], l3[1]};
+            if (clip) {
+                const _Float16 z = (_Float16)0.0f;
+                const int k0 = 8 * grp;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (k0 + i >= kvalid) { ah[i] = z; al[i] = z; }
+                    if (k0 + 4 + i >= kvalid) { bh[i] = z; bl[i] = z; }
+                }
+            }
+            uint8_t* pa = vf + (nt * 64 + laneA) * 16 + j0 * 2;
+            uint8_t* pb = vf + (nt * 64 + laneB) * 16 + j0 * 2;
+            *reinterpret_cast<half4*>(pa) = ah;
+            *reinterpret_cast<half4*>(pb) = bh;
+            *reinterpret_cast<half4*>(pa + C::V_FRAG) = al;
+            *reinterpret_cast<half4*>(pb + C::V_FRAG) = bl;
+        }
+    }
+    if (t < C::KS_ITEMS) {
+        const half8 h = __builtin_bit_cast(half8, r.ks);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int e = 8 * t + i, j = e / C::NB, b = e % C::NB;
+            ksl[((j / kTile) * C::NB + b) * kTile + j % kTile] = h[i];
+        }
+    }
+}
+
+template <int D>
+struct Row {
+    floatx4 o[TCfg<D>::NT];   // O^T: this lane's row, dims 16 nt + 4 (lane / 16) + i
+    float m;                  // reference max (log2 domain), equal on the row's 4 lanes
+    float l;                  // this lane's share of the row sum
+};
+
+// One chunk: S^T = K Q^T, online softmax, O^T += V^T P^T.  MASK: some key of
+// the chunk lies beyond some row's last visible key.
+template <int D, bool MASK>
+__device__ inline void chunk_step(Row<D>& st, const uint8_t* __restrict__ stage, const half8 (&qh)[TCfg<D>::NB],
+                                  const half8 (&ql)[TCfg<D>::NB], int lane, int j0, int last) {
+    using C = TCfg<D>;
+    const uint8_t* kf = stage;
+    const _Float16* ksl = reinterpret_cast<const _Float16*>(stage + C::K_FRAG);
+    const uint8_t* vf = stage + C::K_FRAG + C::KS;
+    const int grp = lane >> 4;
+    floatx4 s[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int b = 0; b < C::NB; ++b) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const half8 ka = *reinterpret_cast<const half8*>(kf + ((tt * C::NB + b) * 64 + lane) * 16);
+            const half4 ks = *reinterpret_cast<const half4*>(ksl + (tt * C::NB + b) * kTile + 4 * grp);
+            floatx4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qh[b], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, ql[b], c, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s[tt][i] = fmaf(c[i], (float)ks[i], s[tt][i]);
+        }
+        SCHED_FENCE();
+    }
+    if (MASK) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (j0 + tt * kTile + 4 * grp + i > last) s[tt][i] = -INFINITY;
+    }
+    // online softmax (this lane: one row, 8 keys)
+    float cm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    cm = xmax4(cm);
+    const bool grow = cm > st.m + kTau;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        if (cm > st.m) {
+            const float alpha = __builtin_amdgcn_exp2f(st.m - cm);
+            st.l *= alpha;
+#pragma unroll
+            for (int nt = 0; nt < C::NT; ++nt) st.o[nt] *= alpha;
+            st.m = cm;
+        }
+    }
+    const float mref = st.m == -INFINITY ? 0.0f : st.m;
+    // P = ph + pl to about 2^-22 relative (weights are <= 2^kTau)
+    half8 ph, pl;
+    float lsum = 0.0f;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float p = __builtin_amdgcn_exp2f(s[tt][i] - mref);
+            lsum += p;
+            const _Float16 h = (_Float16)p;
+            ph[4 * tt + i] = h;
+            pl[4 * tt + i] = (_Float16)(p - (float)h);
+        }
+    st.l += lsum;
+    // O^T += V^T P^T with both factors split: hi*hi + hi*lo + lo*hi
+#pragma unroll
+    for (int nt = 0; nt < C::NT; ++nt) {
+        const half8 vh = *reinterpret_cast<const half8*>(vf + (nt * 64 + lane) * 16);
+        const half8 vl = *reinterpret_cast<const half8*>(vf + C::V_FRAG + (nt * 64 + lane) * 16);
+        floatx4 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh, ph, st.o[nt], 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh, pl, acc, 0, 0, 0);
+        st.o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vl, ph, acc, 0, 0, 0);
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_mfma_tiled_kernel(AttnArgs a, int cps, int n_splits, int group,
+                                                                   int rows, int row_tiles) {
+    using C = TCfg<D>;
+    extern __shared__ __align__(16) uint8_t smem[];
+    const Geom& g = a.g;
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+
+    // XCD-aware order: consecutive workgroup ids go to different XCDs, so the
+    // ids an XCD receives are remapped to consecutive work items -- the row
+    // tiles of one (KV head, split) -- which then share that XCD's L2.
+    const int nwg = gridDim.x;
+    int w = blockIdx.x;
+    if (nwg % 8 == 0) w = (w % 8) * (nwg / 8) + w / 8;
+    const int rtile = w % row_tiles;
+    const int split = (w / row_tiles) % n_splits;
+    const int kvh = w / (row_tiles * n_splits);
+
+    const int total_chunks = (a.ctx + kChunk - 1) / kChunk;
+    const int first_last = a.ctx - a.n_q;              // last key of query 0
+    const int r0 = rtile * kRowsPerWg;
+    const int rmax = min(r0 + kRowsPerWg, rows) - 1;
+    const int c_begin = split * cps;
+    const int c_end = min(min(total_chunks, c_begin + cps), (first_last + rmax / group) / kChunk + 1);
+    const int min_last = first_last + r0 / group;      // chunks ending at or below it need no mask
+
+    // this lane's query row
+    const int row = r0 + wave * 16 + (lane & 15);
+    const bool row_ok = row < rows;
+    const int qi = row_ok ? row / group : 0;
+    const int h = kvh * group + (row_ok ? row % group : 0);
+    const int last = row_ok ? first_last + qi : -1;
+
+    // Page-table entries: lane k of `ents` holds the entry of page pb + k
+    // (batches of 64 pages, one gather load per batch); the loop picks them
+    // out with readlane, so no memory access sits between the loads in flight.
+    int pb = (c_begin * kChunk) / g.P;
+    const int pend = c_end > c_begin ? ((c_end - 1) * kChunk) / g.P + 1 : pb;
+    auto load_ents = [&](int base) -> int { return base + lane < pend ? a.page_table[base + lane] : -1; };
+    int ents = load_ents(pb);
+    auto unit_of = [&](int c, bool& ok) -> const uint8_t* {
+        const int page = (c * kChunk) / g.P;
+        if (page - pb >= 64) {                 // next batch of entries
+            pb += 64;
+            ents = load_ents(pb);
+            asm volatile("" : "+v"(ents));
+        }
+        const int phys = __builtin_amdgcn_readlane(ents, page - pb);
+        ok = phys >= 0 && phys < g.n_pages;
+        return a.pool + g.unit_index(ok ? phys : 0, kvh) * g.unit_bytes();
+    };
+
+    Raw raw;
+    bool bad = false;
+    if (c_begin < c_end) {
+        bool ok;
+        const uint8_t* u = unit_of(c_begin, ok);
+        bad |= !ok;
+        load_raw<D>(raw, u, g, (c_begin * kChunk) % g.P, t);
+    }
+
+    // q of this lane's row as fp16 hi + lo, pre-scaled by scale * log2(e), in
+    // the B-operand layout (row = lane % 16, dims 8 (lane / 16) .. +7 per block)
+    half8 qh[C::NB], ql[C::NB];
+    {
+        const float qscale = a.scale * kLog2e;
+        const float* src = a.q + ((size_t)qi * a.n_heads + h) * D + 8 * (lane >> 4);
+#pragma unroll
+        for (int b = 0; b < C::NB; ++b)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float v = src[b * kBlock + i];          // in bounds: rows past the end read row 0
+                const float x = row_ok ? v * qscale : 0.0f;
+                qh[b][i] = (_Float16)x;
+                ql[b][i] = (_Float16)(x - (float)qh[b][i]);
+            }
+    }
+
+    Row<D> st;
+    st.m = -INFINITY;
+    st.l = 0.0f;
+#pragma unroll
+    for (int nt = 0; nt < C::NT; ++nt) st.o[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    if (c_begin < c_end) {
+        store_stage<D>(raw, smem + (c_begin & 1) * C::STAGE, t, a.ctx - c_begin * kChunk);
+        __syncthreads();
+    }
+    // chunks ending at or before min_last need no mask: run them in a loop of
+    // their own, then the masked tail
+    const int c_mask = max(c_begin, min(c_end, (min_last + 1) / kChunk));
+    auto step = [&](int c, auto masked) {
+        const bool more = c + 1 < c_end;
+        if (more) {
+            bool ok;
+            const uint8_t* u = unit_of(c + 1, ok);
+            bad |= !ok;
+            load_raw<D>(raw, u, g, ((c + 1) * kChunk) % g.P, t);
+        }
+        SCHED_FENCE();
+        chunk_step<D, decltype(masked)::value>(st, smem + (c & 1) * C::STAGE, qh, ql, lane, c * kChunk, last);
+        SCHED_FENCE();
+        if (more) store_stage<D>(raw, smem + ((c + 1) & 1) * C::STAGE, t, a.ctx - (c + 1) * kChunk);
+        __syncthreads();
+    };
+    for (int c = c_begin; c < c_mask; ++c) step(c, std::false_type{});
+    for (int c = c_mask; c < c_end; ++c) step(c, std::true_type{});
+
+    // row sum over the row's 4 lanes; every lane then holds (m, L) of its row
+    float L = xsum4(st.l);
+    float M = st.m;
+    if (bad) { M = NAN; L = NAN; }
+    if (!row_ok) return;
+    const int grp = lane >> 4;
+    const size_t orow = (size_t)qi * a.n_heads + h;
+    if (n_splits == 1) {
+        const float inv = 1.0f / L;
+        float* dst = a.out + orow * D + 4 * grp;
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt) *reinterpret_cast<floatx4*>(dst + 16 * nt) = st.o[nt] * inv;
+        if (a.lse != nullptr && grp == 0) a.lse[orow] = (M + log2f(L)) * 0.69314718055994531f;
+    } else {
+        const size_t ps = orow * n_splits + split;
+        if (grp == 0) {
+            a.ws_m[ps] = M;
+            a.ws_l[ps] = L;
+        }
+        float* dst = a.ws_acc + ps * D + 4 * grp;
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt) *reinterpret_cast<floatx4*>(dst + 16 * nt) = st.o[nt];
+    }
+}
+
+template <int D>
+hipError_t launch_d(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) {
+    using C = TCfg<D>;
+    auto kern = attn_mfma_tiled_kernel<D>;
+    if (C::LDS > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+        if (e != hipSuccess) return e;
+    }
+    const int row_tiles = (pl.rows + kRowsPerWg - 1) / kRowsPerWg;
+    dim3 grid(row_tiles * pl.n_splits * a.g.n_kv);
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), C::LDS, stream, a, pl.chunks_per_split, pl.n_splits, pl.group,
+                       pl.rows, row_tiles);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int mfma_tiled_rows_per_wg() { return kRowsPerWg; }
+
+hipError_t launch_attn_mfma_tiled(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) {
+    switch (a.g.D) {
+        case 64: return launch_d<64>(a, pl, stream);
+        case 128: return launch_d<128>(a, pl, stream);
+        case 256: return launch_d<256>(a, pl, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace kvq

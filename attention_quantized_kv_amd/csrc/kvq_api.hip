@@ -54,9 +54,17 @@ int auto_chunks_per_split(int kernel, int total_chunks, int n_kv, int n_q, int r
         (void)rows;
         return (int)(per < 1 ? 1 : per);
     }
-    // LDS-tiled chunk kernel: splits only when there are few query tiles
-    long per = units / 1024;
-    return (int)(per < 1 ? 1 : per);
+    // LDS-tiled chunk kernel: a workgroup per (row tile, KV head, split);
+    // split the keys until about three workgroups per CU exist, keeping at
+    // least 16 chunks per split
+    (void)units;
+    const int rpw = kvq::mfma_tiled_rows_per_wg();
+    const long tiles = (long)((rows + rpw - 1) / rpw) * n_kv;
+    long splits = (768 + tiles - 1) / tiles;
+    long max_splits = total_chunks / 16;
+    if (max_splits < 1) max_splits = 1;
+    if (splits > max_splits) splits = max_splits;
+    return (int)((total_chunks + splits - 1) / splits);
 }
 
 int make_plan(const kvq_layout* L, int n_heads, int ctx, int n_q, bool prefill,
@@ -64,7 +72,7 @@ int make_plan(const kvq_layout* L, int n_heads, int ctx, int n_q, bool prefill,
     const int group = n_heads / L->n_kv_heads;
     const int rows = n_q * group;
     int kernel = opts ? opts->kernel : 0;
-    if (kernel == 0) kernel = (!prefill && rows <= 64) ? 2 : 1;
+    if (kernel == 0) kernel = (!prefill && rows <= 64) ? 2 : 3;
     if (kernel < 1 || kernel > 3) return fail(KVQ_ERR_INVALID_ARG, "unknown kernel %d", kernel);
     if (group > 16) return fail(KVQ_ERR_UNSUPPORTED, "group size %d > 16", group);
     if (kernel == 2 && rows > 64) return fail(KVQ_ERR_UNSUPPORTED, "streaming MFMA kernel takes n_q*group <= 64 (got %d)", rows);

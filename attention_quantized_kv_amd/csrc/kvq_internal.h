@@ -104,5 +104,7 @@ hipError_t launch_attn_mfma_tiled(const AttnArgs& a, const AttnPlan& pl, hipStre
 hipError_t launch_merge(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream);
 // Waves per workgroup of the streaming MFMA kernel for a given row count.
 int mfma_stream_waves(int rows);
+// Query rows per workgroup of the LDS-tiled MFMA kernel.
+int mfma_tiled_rows_per_wg();
 
 }  // namespace kvq

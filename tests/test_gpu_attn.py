@@ -82,7 +82,7 @@ def _rand_case(seed, ctx, n_kv, D, P=256, perm=True, mag=1.0):
     return Case(k, v, P=P, n_pages=n_pages, perm_seed=seed if perm else None), rng
 
 
-@pytest.fixture(scope="module", params=["valu", "mfma_stream"])
+@pytest.fixture(scope="module", params=["valu", "mfma_stream", "mfma_tiled"])
 def kernel(request):
     return KERNELS[request.param]
 
