@@ -49,7 +49,10 @@ class Layout(ctypes.Structure):
 
 
 class AttnOpts(ctypes.Structure):
-    _fields_ = [("kernel", ctypes.c_int32), ("chunks_per_split", ctypes.c_int32)]
+    """kvq_attn_opts: kernel, chunks_per_split, and two optional hipEvent_t
+    handles recorded around the attention kernel (not the split merge)."""
+    _fields_ = [("kernel", ctypes.c_int32), ("chunks_per_split", ctypes.c_int32),
+                ("kernel_begin_event", ctypes.c_void_p), ("kernel_end_event", ctypes.c_void_p)]
 
 
 _lib = None
@@ -221,11 +224,17 @@ def kvq_prefill_attn(layout: Layout, pool, page_table, ctx_len: int, q, scale: f
 
 
 def kvq_attn_ex(layout: Layout, pool, page_table, ctx_len: int, q, scale: float, out, lse=None,
-                ws=None, kernel: int = 0, chunks_per_split: int = 0, stream=None, n_table=None):
-    """Attention with an explicit kernel and split size (tests, tuning)."""
+                ws=None, kernel: int = 0, chunks_per_split: int = 0, stream=None, n_table=None,
+                events=None):
+    """Attention with an explicit kernel and split size (tests, tuning).
+    events: optional (begin, end) torch.cuda.Event pair recorded around the
+    attention kernel itself."""
     n_q, n_heads, ws_bytes = _attn_args(pool, page_table, q, out, lse, ws)
     nt = _n_table(page_table) if n_table is None else n_table
     opts = AttnOpts(kernel, chunks_per_split)
+    if events is not None:
+        opts.kernel_begin_event = events[0].cuda_event
+        opts.kernel_end_event = events[1].cuda_event
     _check(lib().kvq_attn_ex(ctypes.byref(layout), _ptr(pool), _ptr(page_table), nt, int(ctx_len),
                              n_heads, n_q, _ptr(q), float(scale), _ptr(out), _ptr(lse), _ptr(ws),
                              ws_bytes, ctypes.byref(opts), _stream(stream)), "kvq_attn_ex")

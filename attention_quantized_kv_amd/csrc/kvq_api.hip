@@ -162,11 +162,16 @@ int attn_impl(const kvq_layout* L, const void* d_pool, const int32_t* d_page_tab
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
+    if (opts != nullptr && opts->kernel_begin_event != nullptr)
+        e = hipEventRecord(static_cast<hipEvent_t>(opts->kernel_begin_event), s);
+    if (e != hipSuccess) return fail(KVQ_ERR_HIP, "hipEventRecord failed: %s", hipGetErrorString(e));
     switch (pl.kernel) {
         case 1: e = kvq::launch_attn_valu(a, pl, s); break;
         case 2: e = kvq::launch_attn_mfma_stream(a, pl, s); break;
         case 3: e = kvq::launch_attn_mfma_tiled(a, pl, s); break;
     }
+    if (e == hipSuccess && opts != nullptr && opts->kernel_end_event != nullptr)
+        e = hipEventRecord(static_cast<hipEvent_t>(opts->kernel_end_event), s);
     if (e == hipSuccess && !(pl.kernel == 3 && need == 0)) e = kvq::launch_merge(a, pl, s);
     if (e != hipSuccess) return fail(KVQ_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return ok();

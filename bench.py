@@ -73,17 +73,47 @@ class Layer:
     def append(self):
         self.kvq.kvq_append(self.L, self.pool, self.pt, self.w.cached, self.k_new, self.v_new)
 
-    def attend(self, ws, kernel, prefill):
-        kvq = self.kvq
-        if kernel:
-            kvq.kvq_attn_ex(self.L, self.pool, self.pt, self.w.ctx, self.q, self.w.scale, self.out, self.lse,
-                            ws, kernel=kernel)
-        elif prefill:
-            kvq.kvq_prefill_attn(self.L, self.pool, self.pt, self.w.ctx, self.q, self.w.scale, self.out,
-                                 self.lse, ws)
-        else:
-            kvq.kvq_decode_attn(self.L, self.pool, self.pt, self.w.ctx, self.q, self.w.scale, self.out,
-                                self.lse, ws)
+    def attend(self, ws, kernel, events=None):
+        """kvq_attn_ex with the automatic plan (kernel 0: the same choice as
+        kvq_decode_attn / kvq_prefill_attn) or a forced kernel; `events`
+        (begin, end) are recorded by the library around the attention kernel
+        itself, excluding the split merge."""
+        self.kvq.kvq_attn_ex(self.L, self.pool, self.pt, self.w.ctx, self.q, self.w.scale, self.out, self.lse,
+                             ws, kernel=kernel, events=events)
+
+
+KERNEL_SOURCES = {"attn_mfma_stream": "attn_mfma_stream.hip", "attn_mfma_tiled": "attn_mfma_tiled.hip",
+                  "attn_valu": "attn_valu.hip"}
+
+
+def kernel_name(w, kernel: int) -> str:
+    """Name of the attention kernel the plan picks (mirrors the library's
+    automatic choice: streaming MFMA for decode / verify with at most 64 query
+    rows per KV head, the LDS-tiled MFMA kernel otherwise)."""
+    rows = w.n_q * (w.n_heads // w.n_kv)
+    if kernel == 0:
+        kernel = 2 if (w.n_q <= 8 and rows <= 64) else 3
+    return {1: "attn_valu", 2: "attn_mfma_stream", 3: "attn_mfma_tiled"}[kernel]
+
+
+def measured_traffic(workload: str, kname: str):
+    """HBM bytes per launch of `kname` on `workload` from the committed
+    rocprofv3 counter summary (profiles/hbm_traffic.txt: FETCH_SIZE and
+    WRITE_SIZE scaled by the factors a plain copy of known size gives), or
+    None when there is no entry or the kernel source has changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+    src = os.path.join(ROOT, "attention_quantized_kv_amd", "csrc", KERNEL_SOURCES[kname])
+    if not os.path.exists(path) or not os.path.exists(src):
+        return None
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    for line in open(path):
+        f = line.split()
+        if len(f) >= 8 and not line.startswith("#") and f[0] == workload and f[1] == kname:
+            if f[2] != digest:
+                return None
+            return float(f[7])
+    return None
 
 
 def attention_flops(w) -> float:
@@ -187,11 +217,7 @@ def main():
     def step(ev=None):
         for i, lay in enumerate(layers):
             lay.append()
-            if ev is not None:
-                ev[i][0].record()
-            lay.attend(ws, args.kernel, prefill)
-            if ev is not None:
-                ev[i][1].record()
+            lay.attend(ws, args.kernel, None if ev is None else ev[i])
 
     for _ in range(args.warmup):
         step()
@@ -208,7 +234,9 @@ def main():
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
     attn_ms = [e[0].elapsed_time(e[1]) for st in evs for e in st]
-    avg_attn_us = 1000.0 * sum(attn_ms) / len(attn_ms)
+    avg_attn_us = 1000.0 * sum(attn_ms) / len(attn_ms)       # the attention kernel alone
+    kname = kernel_name(w, args.kernel)
+    traffic = measured_traffic(w.name, kname)
 
     ms_per_step = total_ms / args.steps
     bytes_layer = w.ctx * kv_bytes_per_token_layer(w.n_kv, w.head_dim)
@@ -230,8 +258,8 @@ def main():
             "value": round(value, 2), "unit": "GB/s",
         })
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "kvq_decode_attn (split + merge launches)", "bytes_per_launch": bytes_layer,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": kname, "bytes_per_launch": bytes_layer,
                 "avg_launch_us": round(avg_attn_us, 3)}
         extra = {"us_per_layer": round(us_per_layer, 3), "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
                  "ctx_tokens_per_s": round(w.ctx / (us_per_layer / 1e6), 1),
@@ -242,8 +270,8 @@ def main():
         rec.update({"metric": "quantized-KV chunked prefill attention: TFLOP/s (MFMA utilisation)",
                     "value": round(value, 2), "unit": "TFLOP/s"})
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_F16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
-                "kernel": "kvq_prefill_attn", "flops_per_launch": flops_layer,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": traffic,
+                "kernel": kname, "flops_per_launch": flops_layer,
                 "avg_launch_us": round(avg_attn_us, 3)}
         extra = {"us_per_layer": round(us_per_layer, 3), "flops_per_layer": flops_layer}
 

@@ -171,10 +171,16 @@ int kvq_prefill_attn(const kvq_layout *layout, const void *d_pool,
  *           2 = MFMA streaming kernel (n_q * group <= 64),
  *           3 = MFMA LDS-tiled chunk kernel
  *   chunks_per_split: 32-token chunks per merged partial; 0 = automatic.
+ *   kernel_begin_event, kernel_end_event: optional hipEvent_t handles (or
+ *           NULL), recorded on `stream` immediately before and after the
+ *           attention kernel itself (not the split merge), so a caller can time
+ *           that kernel alone.  Owned by the caller.
  */
 typedef struct {
     int32_t kernel;
     int32_t chunks_per_split;
+    void *kernel_begin_event;
+    void *kernel_end_event;
 } kvq_attn_opts;
 
 int kvq_workspace_bytes_ex(const kvq_layout *layout, int32_t n_heads, int32_t ctx_len,
