@@ -227,14 +227,16 @@ def kvq_attn_ex(layout: Layout, pool, page_table, ctx_len: int, q, scale: float,
                 ws=None, kernel: int = 0, chunks_per_split: int = 0, stream=None, n_table=None,
                 events=None):
     """Attention with an explicit kernel and split size (tests, tuning).
-    events: optional (begin, end) torch.cuda.Event pair recorded around the
-    attention kernel itself."""
+    events: optional (begin, end) pair of raw hipEvent_t handles (ints) that
+    the library records around the attention kernel itself."""
     n_q, n_heads, ws_bytes = _attn_args(pool, page_table, q, out, lse, ws)
     nt = _n_table(page_table) if n_table is None else n_table
     opts = AttnOpts(kernel, chunks_per_split)
     if events is not None:
-        opts.kernel_begin_event = events[0].cuda_event
-        opts.kernel_end_event = events[1].cuda_event
+        if not events[0] or not events[1]:
+            raise ValueError("events must be two created hipEvent_t handles")
+        opts.kernel_begin_event = events[0]
+        opts.kernel_end_event = events[1]
     _check(lib().kvq_attn_ex(ctypes.byref(layout), _ptr(pool), _ptr(page_table), nt, int(ctx_len),
                              n_heads, n_q, _ptr(q), float(scale), _ptr(out), _ptr(lse), _ptr(ws),
                              ws_bytes, ctypes.byref(opts), _stream(stream)), "kvq_attn_ex")

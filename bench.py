@@ -38,6 +38,35 @@ def kv_bytes_per_token_layer(n_kv: int, D: int) -> int:
     return n_kv * (D // 32) * (34 + 18)
 
 
+class HipEvents:
+    """Raw hipEvent_t handles (the library records them on the launch stream
+    around the attention kernel; torch's Event objects cannot be handed over,
+    since torch creates their handle only on its own first record)."""
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+
+    def create(self):
+        ev = self.ct.c_void_p()
+        rc = self.hip.hipEventCreate(self.ct.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return ev.value
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def destroy(self, ev):
+        self.hip.hipEventDestroy(self.ct.c_void_p(ev))
+
+
 def device_normal(shape, seed, device):
     import torch
     g = torch.Generator(device=device)
@@ -223,8 +252,8 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_layers)]
-           for _ in range(args.steps)]
+    hip_ev = HipEvents()
+    evs = [[[hip_ev.create() for _ in range(2)] for _ in range(n_layers)] for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
@@ -233,7 +262,11 @@ def main():
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
-    attn_ms = [e[0].elapsed_time(e[1]) for st in evs for e in st]
+    attn_ms = [hip_ev.elapsed_ms(e[0], e[1]) for st in evs for e in st]
+    for st in evs:
+        for e in st:
+            hip_ev.destroy(e[0])
+            hip_ev.destroy(e[1])
     avg_attn_us = 1000.0 * sum(attn_ms) / len(attn_ms)       # the attention kernel alone
     kname = kernel_name(w, args.kernel)
     traffic = measured_traffic(w.name, kname)
