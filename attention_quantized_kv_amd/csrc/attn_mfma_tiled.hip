@@ -10,11 +10,15 @@
 // key range are merged afterwards by lse_merge.hip (with a single split the
 // kernel writes the normalised output itself).
 //
-// Per 32-token chunk, shared by the whole workgroup (double-buffered in LDS):
-//  * every thread loads at most one 16-byte piece of K codes, one 8-byte half
-//    piece of V nibbles (+ the 8 V scales of its tokens) and one 16-byte piece
-//    of K scales into registers one chunk ahead, and after the current chunk's
-//    math converts them: K codes exactly to fp16 (int8 -> fp16 is exact, the
+// Per 32-token chunk, shared by the whole workgroup:
+//  * the raw chunk arrives by direct-to-LDS loads (one contiguous 1 KiB wave
+//    request each) in a ring of kRing slots, requested kRing chunks ahead so
+//    that the loads of two chunks are in flight behind the math, at no VGPR
+//    cost;
+//  * every thread then converts at most one 16-byte piece of K codes, one
+//    8-byte half piece of V nibbles (with the 8 V scales of its tokens) and
+//    one 16-byte piece of K scales into one of two LDS stages (the math of
+//    the chunk before reads the other): K codes exactly to fp16 (int8 -> fp16 is exact, the
 //    scale stays apart), V to (c - 8) * scale as an exact fp16 hi + lo pair,
 //    laid out as the MFMA operand fragments the waves read with one 16-byte
 //    LDS load;
@@ -46,12 +50,15 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRowsPerWg = kWaves * 16;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kTau = 4.0f;
+constexpr int kRing = 4;         // raw chunks in flight per workgroup (direct-to-LDS ring); a power of 2
 
 template <int D>
 struct TCfg {
@@ -62,12 +69,22 @@ struct TCfg {
     static constexpr int KS = 2 * NB * 16 * 2;        // [tile][block][16 keys] fp16
     static constexpr int V_FRAG = NT * 64 * 16;       // [dim tile][lane] x 16 B, hi then lo parts
     static constexpr int STAGE = K_FRAG + KS + 2 * V_FRAG;
-    static constexpr int LDS = 2 * STAGE;
+    // raw chunk as it arrives by direct-to-LDS loads, one 1 KiB wave request
+    // each: [K tiles 2KL][K scales 1][V pieces KL][V scales 1]
+    static constexpr int N_DMA = 3 * KL + 2;
+    static constexpr int ND = (N_DMA + kWaves - 1) / kWaves;    // requests per wave and chunk
+    static constexpr int SLOT = N_DMA * 1024;
+    static constexpr int OFF_KS = 2 * KL * 1024, OFF_V = OFF_KS + 1024, OFF_VS = OFF_V + KL * 1024;
+    static constexpr int LDS = 2 * STAGE + kRing * SLOT;
     static constexpr int K_ITEMS = 128 * KL;    // 16-byte K-code pieces per chunk
-    static constexpr int V_ITEMS = 128 * KL;    // 8-byte V-nibble half pieces per chunk
     static constexpr int KS_ITEMS = 4 * NB;     // 16-byte K-scale pieces per chunk
-    static_assert(K_ITEMS <= kThreads && V_ITEMS <= kThreads, "one item per thread");
+    static_assert(K_ITEMS <= kThreads, "one K piece per thread");
 };
+
+// Reinterprets 32 bits as two fp16 values.  Takes the bits by value: hipcc's
+// __builtin_bit_cast applied directly to a vector element (v.y, v[1]) reads
+// element 0 instead.
+__device__ inline half2v as_h2(uint32_t x) { return __builtin_bit_cast(half2v, x); }
 
 // 8 int8 codes -> 8 fp16 values, exactly (bias by 128, put each byte under
 // the fp16 exponent of 1024, subtract 1152).
@@ -132,93 +149,135 @@ __device__ inline float xsum4(float x) {
 
 #define SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-// Raw bytes of one chunk held by one thread between its load and its conversion.
-struct Raw {
-    u32x4 k;      // 16 K codes
-    u32x2 v;      // 16 V nibbles: two dims x 8 tokens
-    u32x4 vs;     // 8 V scales (fp16) of those tokens
-    u32x4 ks;     // 8 K scales (fp16)
-};
-
-template <int D>
-__device__ inline void load_raw(Raw& r, const uint8_t* unit, const Geom& g, int slot0, int t) {
-    using C = TCfg<D>;
-    if (t < C::K_ITEMS) {
-        const int tt = t / (64 * C::KL), p = (t / 64) % C::KL, L = t % 64;
-        r.k = *reinterpret_cast<const u32x4*>(unit + (int64_t)(slot0 / kTile + tt) * kTile * D + p * 1024 + L * 16);
-    }
-    if (t < C::V_ITEMS) {
-        const int u = t / 128, lp = (t % 128) / 2, hf = t & 1;
-        const int64_t cbase = (int64_t)(slot0 / kChunk);
-        r.v = *reinterpret_cast<const u32x2*>(unit + g.v_codes_off() + cbase * kChunk * D / 2 + u * 1024 + lp * 16 +
-                                              hf * 8);
-        const int b = 2 * u + hf, grp = lp / 16;
-        r.vs = *reinterpret_cast<const u32x4*>(unit + g.v_scales_off() + ((cbase * C::NB + b) * kChunk + 8 * grp) * 2);
-    }
-    if (t < C::KS_ITEMS)
-        r.ks = *reinterpret_cast<const u32x4*>(unit + g.k_scales_off() + (int64_t)slot0 * C::NB * 2 + t * 16);
+// 16 bytes per lane, global -> LDS: lane i's bytes land at lds + 16 i.
+__device__ inline void dma16(const void* g, void* lds) {
+    __builtin_amdgcn_global_load_lds((glb_void*)g, (lds_void*)lds, 16, 0, 0);
 }
 
-// Converts a thread's raw bytes into the stage's operand fragments.
+// Waits until at most N vector-memory requests of this wave are outstanding
+// (direct-to-LDS loads count); also a compiler memory fence.
+template <int N>
+__device__ inline void vm_wait() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
+
+// Workgroup barrier for LDS data: waits for this wave's own LDS accesses,
+// then s_barrier.  Unlike __syncthreads() it carries no release fence, which
+// would also wait for every direct-to-LDS load still in flight (the ring's
+// later chunks); each wave waits for the loads that must have landed with an
+// explicit vm_wait before it.  The empty asm statements keep the compiler
+// from moving memory accesses across the barrier.
+__device__ inline void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// The raw chunk's N_DMA wave requests are dealt to the waves (wave w takes
+// requests w, w + 8, ...); waves left over repeat an earlier request, so
+// every wave issues exactly ND of them and the wait counts are the same for
+// all.  Every request runs on the full wave (a direct-to-LDS load under a
+// lane-dependent branch can get its LDS base merged with another one's): the
+// scale pieces, 4*NB of 16 bytes, are repeated across the remaining lanes.
+// A request's source is unit + off + mul * slot0, with off and mul fixed per
+// wave (computed once), slot0 = the chunk's first slot in its page.
+template <int D>
+struct Requests {
+    int64_t off[TCfg<D>::ND];
+    int mul[TCfg<D>::ND];
+    int dst[TCfg<D>::ND];
+
+    __device__ Requests(const Geom& g, int wave, int lane) {
+        using C = TCfg<D>;
+#pragma unroll
+        for (int j = 0; j < C::ND; ++j) {
+            int item = j * kWaves + wave;
+            if (item >= C::N_DMA) item -= C::N_DMA;
+            dst[j] = item * 1024;
+            if (item < 2 * C::KL) {                     // K codes: tile tt, piece p
+                const int tt = item / C::KL, pc = item % C::KL;
+                off[j] = (int64_t)tt * kTile * D + pc * 1024 + lane * 16;
+                mul[j] = D;                             // (slot0 / 16) * 16 * D
+            } else if (item == 2 * C::KL) {             // K scales [token][block]
+                off[j] = g.k_scales_off() + (lane % (4 * C::NB)) * 16;
+                mul[j] = C::NB * 2;
+            } else if (item < 3 * C::KL + 1) {          // V codes: piece u
+                off[j] = g.v_codes_off() + (item - 2 * C::KL - 1) * 1024 + lane * 16;
+                mul[j] = D / 2;                         // (slot0 / 32) * 32 * D / 2
+            } else {                                    // V scales [block][32]
+                off[j] = g.v_scales_off() + (lane % (4 * C::NB)) * 16;
+                mul[j] = C::NB * 2;                     // (slot0 / 32) * NB * 32 * 2
+            }
+        }
+    }
+
+    __device__ inline void issue(uint8_t* slot, const uint8_t* unit, int slot0) const {
+#pragma unroll
+        for (int j = 0; j < TCfg<D>::ND; ++j) dma16(unit + off[j] + (int64_t)mul[j] * slot0, slot + dst[j]);
+    }
+};
+
+// Converts one raw chunk (ring slot) into a stage's operand fragments.
+//  K: thread t < 128*KL takes K piece (tile, p), lane L: 16 codes -> the fp16
+//     fragments of blocks 2p and 2p+1 at lane L (the raw layout already is
+//     the fragment layout, so this is a straight per-lane conversion).
+//  V: V fragment (dim tile nt, lane fl = 16 G + n) holds dim 16 nt + n of the
+//     keys {4G..4G+3, 16+4G..16+4G+3} (the key order of the P fragment), as
+//     hi and lo fp16 parts; those keys are nibbles 4(G%2)..+3 of two raw
+//     dwords.  Threads take whole fragments, 64 consecutive threads one dim
+//     tile, so the 16-byte stores are conflict-free.
+//  K scales: thread t < 4*NB spreads 8 of them to [tile][block][16 keys].
 // kvalid: tokens of the chunk that exist (< ctx); V of the others is zeroed so
 // that a masked key (weight 0) cannot meet an unwritten, non-finite scale.
 template <int D>
-__device__ inline void store_stage(const Raw& r, uint8_t* stage, int t, int kvalid) {
+__device__ inline void convert_chunk(const uint8_t* slot, uint8_t* stage, int t, int kvalid) {
     using C = TCfg<D>;
     uint8_t* kf = stage;
     _Float16* ksl = reinterpret_cast<_Float16*>(stage + C::K_FRAG);
     uint8_t* vf = stage + C::K_FRAG + C::KS;
     if (t < C::K_ITEMS) {
-        const int tt = t / (64 * C::KL), p = (t / 64) % C::KL, L = t % 64;
-        *reinterpret_cast<half8*>(kf + ((tt * C::NB + 2 * p) * 64 + L) * 16) = k_codes_to_half(r.k.x, r.k.y);
-        *reinterpret_cast<half8*>(kf + ((tt * C::NB + 2 * p + 1) * 64 + L) * 16) = k_codes_to_half(r.k.z, r.k.w);
+        const int tt = t / (64 * C::KL), pc = (t / 64) % C::KL, L = t % 64;
+        const u32x4 k = *reinterpret_cast<const u32x4*>(slot + (tt * C::KL + pc) * 1024 + L * 16);
+        *reinterpret_cast<half8*>(kf + ((tt * C::NB + 2 * pc) * 64 + L) * 16) = k_codes_to_half(k.x, k.y);
+        *reinterpret_cast<half8*>(kf + ((tt * C::NB + 2 * pc + 1) * 64 + L) * 16) = k_codes_to_half(k.z, k.w);
     }
-    if (t < C::V_ITEMS) {
-        const int u = t / 128, lp = (t % 128) / 2, hf = t & 1;
-        const int n = lp % 16, grp = lp / 16;
-        uint32_t magic = 0x64006400u;
-        asm volatile("" : "+v"(magic));
-        const half8 s8 = __builtin_bit_cast(half8, r.vs);
-        const half2v s01 = {s8[0], s8[1]}, s23 = {s8[2], s8[3]}, s45 = {s8[4], s8[5]}, s67 = {s8[6], s8[7]};
-        // tokens 8grp+0..3 go to lane group 2(grp%2), 8grp+4..7 to the next
-        // one, at fragment halves 4(grp/2)..+3 (the key order of the P
-        // fragment: group G holds keys 4G..4G+3 and 16+4G..16+4G+3)
-        const int laneA = 16 * (2 * (grp % 2)) + n, laneB = laneA + 16, j0 = 4 * (grp / 2);
-        const bool clip = 8 * grp + 7 >= kvalid;
+    uint32_t magic = 0x64006400u;
+    asm volatile("" : "+v"(magic));
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const uint32_t x = e == 0 ? r.v.x : r.v.y;
-            const int nt = 4 * u + 2 * hf + e;
-            half2v h0, h1, h2, h3, l0, l1, l2, l3;
-            v_pair<0>(x, s01, magic, h0, l0);
-            v_pair<1>(x, s23, magic, h1, l1);
-            v_pair<2>(x, s45, magic, h2, l2);
-            v_pair<3>(x, s67, magic, h3, l3);
-            half4 ah = {h0[0], h0[1], h1[0], h1[1]}, bh = {h2[0], h2[1], h3[0], h3[1]};
-            half4 al = {l0[0], l0[1], l1[0], l1[1]}, bl = {l2[0], l2[1], l3[0], l3[1]};
-            if (clip) {
-                const _Float16 z = (_Float16)0.0f;
-                const int k0 = 8 * grp;
+    for (int it = 0; it < (C::NT * 64 + kThreads - 1) / kThreads; ++it) {
+        const int item = it * kThreads + t;
+        if (C::NT * 64 % kThreads != 0 && item >= C::NT * 64) break;
+        const int nt = item / 64, fl = item % 64, G = fl / 16, n = fl % 16;
+        const int u = nt / 4, w = nt % 4, b = nt / 2;
+        const uint8_t* vraw = slot + C::OFF_V + u * 1024 + n * 16 + w * 4;
+        const uint32_t x1 = *reinterpret_cast<const uint32_t*>(vraw + (G / 2) * 256);         // tokens 8(G/2)..
+        const uint32_t x2 = *reinterpret_cast<const uint32_t*>(vraw + (2 + G / 2) * 256);     // tokens 16+8(G/2)..
+        const u32x2 s1 = *reinterpret_cast<const u32x2*>(slot + C::OFF_VS + (b * kChunk + 4 * G) * 2);
+        const u32x2 s2 = *reinterpret_cast<const u32x2*>(slot + C::OFF_VS + (b * kChunk + 16 + 4 * G) * 2);
+        const int sh = 16 * (G % 2);
+        const uint32_t y1 = x1 >> sh, y2 = x2 >> sh;    // keys 4G..4G+3 / 16+4G.. in the low 16 bits
+        half2v h0, h1, h2, h3, l0, l1, l2, l3;
+        v_pair<0>(y1, as_h2(s1.x), magic, h0, l0);
+        v_pair<1>(y1, as_h2(s1.y), magic, h1, l1);
+        v_pair<0>(y2, as_h2(s2.x), magic, h2, l2);
+        v_pair<1>(y2, as_h2(s2.y), magic, h3, l3);
+        half8 hi = {h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+        half8 lo = {l0[0], l0[1], l1[0], l1[1], l2[0], l2[1], l3[0], l3[1]};
+        if (kvalid < kChunk) {
+            const _Float16 z = (_Float16)0.0f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if (k0 + i >= kvalid) { ah[i] = z; al[i] = z; }
-                    if (k0 + 4 + i >= kvalid) { bh[i] = z; bl[i] = z; }
-                }
+            for (int i = 0; i < 4; ++i) {
+                if (4 * G + i >= kvalid) { hi[i] = z; lo[i] = z; }
+                if (16 + 4 * G + i >= kvalid) { hi[4 + i] = z; lo[4 + i] = z; }
             }
-            uint8_t* pa = vf + (nt * 64 + laneA) * 16 + j0 * 2;
-            uint8_t* pb = vf + (nt * 64 + laneB) * 16 + j0 * 2;
-            *reinterpret_cast<half4*>(pa) = ah;
-            *reinterpret_cast<half4*>(pb) = bh;
-            *reinterpret_cast<half4*>(pa + C::V_FRAG) = al;
-            *reinterpret_cast<half4*>(pb + C::V_FRAG) = bl;
         }
+        *reinterpret_cast<half8*>(vf + (nt * 64 + fl) * 16) = hi;
+        *reinterpret_cast<half8*>(vf + C::V_FRAG + (nt * 64 + fl) * 16) = lo;
     }
     if (t < C::KS_ITEMS) {
-        const half8 h = __builtin_bit_cast(half8, r.ks);
+        const half8 h = *reinterpret_cast<const half8*>(slot + C::OFF_KS + t * 16);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int e = 8 * t + i, j = e / C::NB, b = e % C::NB;
-            ksl[((j / kTile) * C::NB + b) * kTile + j % kTile] = h[i];
+            const int e = 8 * t + i, j = e / C::NB, bb = e % C::NB;
+            ksl[((j / kTile) * C::NB + bb) * kTile + j % kTile] = h[i];
         }
     }
 }
@@ -329,7 +388,9 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_tiled_kernel(AttnArgs a, i
     const int c_end = min(min(total_chunks, c_begin + cps), (first_last + rmax / group) / kChunk + 1);
     const int min_last = first_last + r0 / group;      // chunks ending at or below it need no mask
 
-    // this lane's query row
+    // this lane's query row; a wave whose 16 rows all lie past the end (few
+    // rows, e.g. a verify batch) skips the math but still stages chunks
+    const bool wave_active = r0 + wave * 16 < rows;
     const int row = r0 + wave * 16 + (lane & 15);
     const bool row_ok = row < rows;
     const int qi = row_ok ? row / group : 0;
@@ -343,8 +404,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_tiled_kernel(AttnArgs a, i
     const int pend = c_end > c_begin ? ((c_end - 1) * kChunk) / g.P + 1 : pb;
     auto load_ents = [&](int base) -> int { return base + lane < pend ? a.page_table[base + lane] : -1; };
     int ents = load_ents(pb);
-    auto unit_of = [&](int c, bool& ok) -> const uint8_t* {
-        const int page = (c * kChunk) / g.P;
+    auto unit_of = [&](int page, bool& ok) -> const uint8_t* {
         if (page - pb >= 64) {                 // next batch of entries
             pb += 64;
             ents = load_ents(pb);
@@ -355,14 +415,23 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_tiled_kernel(AttnArgs a, i
         return a.pool + g.unit_index(ok ? phys : 0, kvh) * g.unit_bytes();
     };
 
-    Raw raw;
     bool bad = false;
-    if (c_begin < c_end) {
+    uint8_t* ring = smem + 2 * C::STAGE;
+    const Requests<D> req(g, wave, lane);
+    // position of the next chunk to request, advanced one chunk at a time
+    int iss_c = c_begin, iss_page = (c_begin * kChunk) / g.P, iss_slot = (c_begin * kChunk) % g.P;
+    auto issue_next = [&]() {
         bool ok;
-        const uint8_t* u = unit_of(c_begin, ok);
+        const uint8_t* u = unit_of(iss_page, ok);
         bad |= !ok;
-        load_raw<D>(raw, u, g, (c_begin * kChunk) % g.P, t);
-    }
+        req.issue(ring + (iss_c & (kRing - 1)) * C::SLOT, u, iss_slot);
+        ++iss_c;
+        iss_slot += kChunk;
+        if (iss_slot == g.P) { iss_slot = 0; ++iss_page; }
+    };
+    // raw chunks c_begin .. c_begin + kRing - 1 in flight before q is staged
+    for (int i = 0; i < kRing; ++i)
+        if (c_begin + i < c_end) issue_next();
 
     // q of this lane's row as fp16 hi + lo, pre-scaled by scale * log2(e), in
     // the B-operand layout (row = lane % 16, dims 8 (lane / 16) .. +7 per block)
@@ -387,27 +456,32 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_tiled_kernel(AttnArgs a, i
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt) st.o[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+    auto convert = [&](int c) {
+        convert_chunk<D>(ring + (c & (kRing - 1)) * C::SLOT, smem + (c & 1) * C::STAGE, t, a.ctx - c * kChunk);
+    };
     if (c_begin < c_end) {
-        store_stage<D>(raw, smem + (c_begin & 1) * C::STAGE, t, a.ctx - c_begin * kChunk);
-        __syncthreads();
+        vm_wait<0>();
+        lds_barrier();                         // chunks c_begin, c_begin + 1 have landed
+        convert(c_begin);
+        lds_barrier();
     }
+    // Per chunk c: convert c + 1 (landed before the last barrier) into the
+    // other stage, request c + kRing into the slot c just left, run the math
+    // on c, wait for this wave's requests of c + 2, barrier.
+    auto step = [&](int c, auto masked) {
+        if (c + 1 < c_end) convert(c + 1);
+        const bool more = c + kRing < c_end;
+        if (more) issue_next();
+        SCHED_FENCE();
+        if (wave_active)
+            chunk_step<D, decltype(masked)::value>(st, smem + (c & 1) * C::STAGE, qh, ql, lane, c * kChunk, last);
+        SCHED_FENCE();
+        if (more) vm_wait<(kRing - 2) * C::ND>(); else vm_wait<0>();
+        lds_barrier();
+    };
     // chunks ending at or before min_last need no mask: run them in a loop of
     // their own, then the masked tail
     const int c_mask = max(c_begin, min(c_end, (min_last + 1) / kChunk));
-    auto step = [&](int c, auto masked) {
-        const bool more = c + 1 < c_end;
-        if (more) {
-            bool ok;
-            const uint8_t* u = unit_of(c + 1, ok);
-            bad |= !ok;
-            load_raw<D>(raw, u, g, ((c + 1) * kChunk) % g.P, t);
-        }
-        SCHED_FENCE();
-        chunk_step<D, decltype(masked)::value>(st, smem + (c & 1) * C::STAGE, qh, ql, lane, c * kChunk, last);
-        SCHED_FENCE();
-        if (more) store_stage<D>(raw, smem + ((c + 1) & 1) * C::STAGE, t, a.ctx - (c + 1) * kChunk);
-        __syncthreads();
-    };
     for (int c = c_begin; c < c_mask; ++c) step(c, std::false_type{});
     for (int c = c_mask; c < c_end; ++c) step(c, std::true_type{});
 
