@@ -6,22 +6,22 @@
 //
 // Work split.  A workgroup owns 128 query rows of one KV head (row = query i
 // times the G heads of the group, query-major) and one contiguous run of
-// 32-token chunks; each of its 8 wavefronts owns 16 of the rows.  Splits of the
-// key range are merged afterwards by lse_merge.hip (with a single split the
-// kernel writes the normalised output itself).
+// 32-token chunks; each of its 128 / (16 RT) wavefronts owns RT tiles of 16
+// rows (RT = 1 is built: 8 waves, two per SIMD).  Every K/V fragment a wave
+// reads from LDS serves all its RT row tiles.
+// Splits of the key range are merged afterwards by lse_merge.hip (with a
+// single split the kernel writes the normalised output itself).
 //
 // Per 32-token chunk, shared by the whole workgroup:
 //  * the raw chunk arrives by direct-to-LDS loads (one contiguous 1 KiB wave
 //    request each) in a ring of kRing slots, requested kRing chunks ahead so
 //    that the loads of two chunks are in flight behind the math, at no VGPR
 //    cost;
-//  * every thread then converts at most one 16-byte piece of K codes, one
-//    8-byte half piece of V nibbles (with the 8 V scales of its tokens) and
-//    one 16-byte piece of K scales into one of two LDS stages (the math of
-//    the chunk before reads the other): K codes exactly to fp16 (int8 -> fp16 is exact, the
-//    scale stays apart), V to (c - 8) * scale as an exact fp16 hi + lo pair,
-//    laid out as the MFMA operand fragments the waves read with one 16-byte
-//    LDS load;
+//  * the threads then convert it into one of two LDS stages (the math of the
+//    chunk before reads the other): K codes exactly to fp16 (int8 -> fp16 is
+//    exact, the scale stays apart), V to (c - 8) * scale as an exact fp16
+//    hi + lo pair, laid out as the MFMA operand fragments the waves read with
+//    one 16-byte LDS load;
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_f16, one K = 32 step per quant block:
 //    the block's scale multiplies the fp32 result per key (fma_mix), and q is
 //    split into fp16 hi + lo parts (two MFMAs), so every score is the exact
@@ -53,15 +53,18 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * 64;
-constexpr int kRowsPerWg = kWaves * 16;
+constexpr int kRowsPerWg = 128;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kTau = 4.0f;
 constexpr int kRing = 4;         // raw chunks in flight per workgroup (direct-to-LDS ring); a power of 2
 
-template <int D>
+template <int RT>
+constexpr int kThreadsFor = kRowsPerWg / (16 * RT) * 64;
+
+template <int D, int RT>
 struct TCfg {
+    static constexpr int W = kRowsPerWg / (16 * RT);   // waves per workgroup
+    static constexpr int THREADS = W * 64;
     static constexpr int NB = D / kBlock;       // quant blocks per row
     static constexpr int NT = D / 16;           // 16-wide output dim tiles
     static constexpr int KL = D / 64;           // 1 KiB pieces per K tile / V chunk
@@ -72,13 +75,14 @@ struct TCfg {
     // raw chunk as it arrives by direct-to-LDS loads, one 1 KiB wave request
     // each: [K tiles 2KL][K scales 1][V pieces KL][V scales 1]
     static constexpr int N_DMA = 3 * KL + 2;
-    static constexpr int ND = (N_DMA + kWaves - 1) / kWaves;    // requests per wave and chunk
+    static constexpr int ND = (N_DMA + W - 1) / W;    // requests per wave and chunk
     static constexpr int SLOT = N_DMA * 1024;
     static constexpr int OFF_KS = 2 * KL * 1024, OFF_V = OFF_KS + 1024, OFF_VS = OFF_V + KL * 1024;
     static constexpr int LDS = 2 * STAGE + kRing * SLOT;
     static constexpr int K_ITEMS = 128 * KL;    // 16-byte K-code pieces per chunk
     static constexpr int KS_ITEMS = 4 * NB;     // 16-byte K-scale pieces per chunk
-    static_assert(K_ITEMS <= kThreads, "one K piece per thread");
+    static_assert(KS_ITEMS <= THREADS, "one K-scale piece per thread");
+    static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
 // Reinterprets 32 bits as two fp16 values.  Takes the bits by value: hipcc's
@@ -172,25 +176,25 @@ __device__ inline void lds_barrier() {
 }
 
 // The raw chunk's N_DMA wave requests are dealt to the waves (wave w takes
-// requests w, w + 8, ...); waves left over repeat an earlier request, so
+// requests w, w + W, ...); waves left over repeat an earlier request, so
 // every wave issues exactly ND of them and the wait counts are the same for
 // all.  Every request runs on the full wave (a direct-to-LDS load under a
 // lane-dependent branch can get its LDS base merged with another one's): the
 // scale pieces, 4*NB of 16 bytes, are repeated across the remaining lanes.
 // A request's source is unit + off + mul * slot0, with off and mul fixed per
 // wave (computed once), slot0 = the chunk's first slot in its page.
-template <int D>
+template <int D, int RT>
 struct Requests {
-    int64_t off[TCfg<D>::ND];
-    int mul[TCfg<D>::ND];
-    int dst[TCfg<D>::ND];
+    using C = TCfg<D, RT>;
+    int64_t off[C::ND];
+    int mul[C::ND];
+    int dst[C::ND];
 
     __device__ Requests(const Geom& g, int wave, int lane) {
-        using C = TCfg<D>;
 #pragma unroll
         for (int j = 0; j < C::ND; ++j) {
-            int item = j * kWaves + wave;
-            if (item >= C::N_DMA) item -= C::N_DMA;
+            int item = j * C::W + wave;
+            while (item >= C::N_DMA) item -= C::N_DMA;
             dst[j] = item * 1024;
             if (item < 2 * C::KL) {                     // K codes: tile tt, piece p
                 const int tt = item / C::KL, pc = item % C::KL;
@@ -211,30 +215,32 @@ struct Requests {
 
     __device__ inline void issue(uint8_t* slot, const uint8_t* unit, int slot0) const {
 #pragma unroll
-        for (int j = 0; j < TCfg<D>::ND; ++j) dma16(unit + off[j] + (int64_t)mul[j] * slot0, slot + dst[j]);
+        for (int j = 0; j < C::ND; ++j) dma16(unit + off[j] + (int64_t)mul[j] * slot0, slot + dst[j]);
     }
 };
 
 // Converts one raw chunk (ring slot) into a stage's operand fragments.
-//  K: thread t < 128*KL takes K piece (tile, p), lane L: 16 codes -> the fp16
-//     fragments of blocks 2p and 2p+1 at lane L (the raw layout already is
-//     the fragment layout, so this is a straight per-lane conversion).
+//  K: K piece (tile, p), lane L: 16 codes -> the fp16 fragments of blocks 2p
+//     and 2p+1 at lane L (the raw layout already is the fragment layout).
 //  V: V fragment (dim tile nt, lane fl = 16 G + n) holds dim 16 nt + n of the
 //     keys {4G..4G+3, 16+4G..16+4G+3} (the key order of the P fragment), as
 //     hi and lo fp16 parts; those keys are nibbles 4(G%2)..+3 of two raw
-//     dwords.  Threads take whole fragments, 64 consecutive threads one dim
-//     tile, so the 16-byte stores are conflict-free.
+//     dwords.  Consecutive threads take consecutive fragments of a dim tile,
+//     so the 16-byte stores are conflict-free.
 //  K scales: thread t < 4*NB spreads 8 of them to [tile][block][16 keys].
 // kvalid: tokens of the chunk that exist (< ctx); V of the others is zeroed so
 // that a masked key (weight 0) cannot meet an unwritten, non-finite scale.
-template <int D>
+template <int D, int RT>
 __device__ inline void convert_chunk(const uint8_t* slot, uint8_t* stage, int t, int kvalid) {
-    using C = TCfg<D>;
+    using C = TCfg<D, RT>;
     uint8_t* kf = stage;
     _Float16* ksl = reinterpret_cast<_Float16*>(stage + C::K_FRAG);
     uint8_t* vf = stage + C::K_FRAG + C::KS;
-    if (t < C::K_ITEMS) {
-        const int tt = t / (64 * C::KL), pc = (t / 64) % C::KL, L = t % 64;
+#pragma unroll
+    for (int it = 0; it < (C::K_ITEMS + C::THREADS - 1) / C::THREADS; ++it) {
+        const int item = it * C::THREADS + t;
+        if (C::K_ITEMS % C::THREADS != 0 && item >= C::K_ITEMS) break;
+        const int tt = item / (64 * C::KL), pc = (item / 64) % C::KL, L = item % 64;
         const u32x4 k = *reinterpret_cast<const u32x4*>(slot + (tt * C::KL + pc) * 1024 + L * 16);
         *reinterpret_cast<half8*>(kf + ((tt * C::NB + 2 * pc) * 64 + L) * 16) = k_codes_to_half(k.x, k.y);
         *reinterpret_cast<half8*>(kf + ((tt * C::NB + 2 * pc + 1) * 64 + L) * 16) = k_codes_to_half(k.z, k.w);
@@ -242,9 +248,9 @@ __device__ inline void convert_chunk(const uint8_t* slot, uint8_t* stage, int t,
     uint32_t magic = 0x64006400u;
     asm volatile("" : "+v"(magic));
 #pragma unroll
-    for (int it = 0; it < (C::NT * 64 + kThreads - 1) / kThreads; ++it) {
-        const int item = it * kThreads + t;
-        if (C::NT * 64 % kThreads != 0 && item >= C::NT * 64) break;
+    for (int it = 0; it < (C::NT * 64 + C::THREADS - 1) / C::THREADS; ++it) {
+        const int item = it * C::THREADS + t;
+        if (C::NT * 64 % C::THREADS != 0 && item >= C::NT * 64) break;
         const int nt = item / 64, fl = item % 64, G = fl / 16, n = fl % 16;
         const int u = nt / 4, w = nt % 4, b = nt / 2;
         const uint8_t* vraw = slot + C::OFF_V + u * 1024 + n * 16 + w * 4;
@@ -282,88 +288,150 @@ __device__ inline void convert_chunk(const uint8_t* slot, uint8_t* stage, int t,
     }
 }
 
-template <int D>
-struct Row {
-    floatx4 o[TCfg<D>::NT];   // O^T: this lane's row, dims 16 nt + 4 (lane / 16) + i
-    float m;                  // reference max (log2 domain), equal on the row's 4 lanes
-    float l;                  // this lane's share of the row sum
+template <int D, int RT>
+struct Rows {
+    floatx4 o[RT][TCfg<D, RT>::NT];   // O^T: row tile rt, this lane's row, dims 16 nt + 4 (lane / 16) + i
+    float m[RT];                      // reference max (log2 domain), equal on the row's 4 lanes
+    float l[RT];                      // this lane's share of the row sum
 };
 
-// One chunk: S^T = K Q^T, online softmax, O^T += V^T P^T.  MASK: some key of
-// the chunk lies beyond some row's last visible key.
-template <int D, bool MASK>
-__device__ inline void chunk_step(Row<D>& st, const uint8_t* __restrict__ stage, const half8 (&qh)[TCfg<D>::NB],
-                                  const half8 (&ql)[TCfg<D>::NB], int lane, int j0, int last) {
-    using C = TCfg<D>;
+// One chunk: S^T = K Q^T, online softmax, O^T += V^T P^T for the wave's RT
+// row tiles.  MASK: some key of the chunk lies beyond some row's last key.
+template <int D, int RT, bool MASK>
+__device__ inline void chunk_step(Rows<D, RT>& st, const uint8_t* __restrict__ stage,
+                                  const half8 (&qh)[RT][TCfg<D, RT>::NB], const half8 (&ql)[RT][TCfg<D, RT>::NB],
+                                  int lane, int j0, const int (&last)[RT]) {
+    using C = TCfg<D, RT>;
     const uint8_t* kf = stage;
     const _Float16* ksl = reinterpret_cast<const _Float16*>(stage + C::K_FRAG);
     const uint8_t* vf = stage + C::K_FRAG + C::KS;
     const int grp = lane >> 4;
-    floatx4 s[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+    floatx4 s[RT][2];
 #pragma unroll
-    for (int b = 0; b < C::NB; ++b) {
+    for (int rt = 0; rt < RT; ++rt) s[rt][0] = s[rt][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // Block b+1's fragments are read while block b's products run; hi and lo
+    // products of the tiles alternate so that no MFMA waits on the one issued
+    // right before it.  Each K fragment serves all RT row tiles.
+    half8 ka[2], kn[2];
+    half4 ks[2], ksn[2];
+    auto load_block = [&](int b, half8 (&k)[2], half4 (&sc)[2]) {
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-            const half8 ka = *reinterpret_cast<const half8*>(kf + ((tt * C::NB + b) * 64 + lane) * 16);
-            const half4 ks = *reinterpret_cast<const half4*>(ksl + (tt * C::NB + b) * kTile + 4 * grp);
-            floatx4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qh[b], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-            c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, ql[b], c, 0, 0, 0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) s[tt][i] = fmaf(c[i], (float)ks[i], s[tt][i]);
+            k[tt] = *reinterpret_cast<const half8*>(kf + ((tt * C::NB + b) * 64 + lane) * 16);
+            sc[tt] = *reinterpret_cast<const half4*>(ksl + (tt * C::NB + b) * kTile + 4 * grp);
         }
-        SCHED_FENCE();
+    };
+    load_block(0, ka, ks);
+#pragma unroll
+    for (int b = 0; b < C::NB; ++b) {
+        if (b + 1 < C::NB) load_block(b + 1, kn, ksn);
+        floatx4 c[RT][2];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+                c[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[tt], qh[rt][b], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+                c[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[tt], ql[rt][b], c[rt][tt], 0, 0, 0);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s[rt][tt][i] = fmaf(c[rt][tt][i], (float)ks[tt][i], s[rt][tt][i]);
+        if (b + 1 < C::NB) {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) { ka[tt] = kn[tt]; ks[tt] = ksn[tt]; }
+        }
+        SCHED_FENCE();      // one block of lookahead, no more (register budget)
     }
     if (MASK) {
 #pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (j0 + tt * kTile + 4 * grp + i > last[rt]) s[rt][tt][i] = -INFINITY;
+    }
+    // online softmax (per row tile, this lane: one row, 8 keys)
+    half8 ph[RT], pl[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        float cm = fmaxf(fmaxf(fmaxf(s[rt][0][0], s[rt][0][1]), fmaxf(s[rt][0][2], s[rt][0][3])),
+                         fmaxf(fmaxf(s[rt][1][0], s[rt][1][1]), fmaxf(s[rt][1][2], s[rt][1][3])));
+        cm = xmax4(cm);
+        const bool grow = cm > st.m[rt] + kTau;
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            if (cm > st.m[rt]) {
+                const float alpha = __builtin_amdgcn_exp2f(st.m[rt] - cm);
+                st.l[rt] *= alpha;
+#pragma unroll
+                for (int nt = 0; nt < C::NT; ++nt) st.o[rt][nt] *= alpha;
+                st.m[rt] = cm;
+            }
+        }
+        const float mref = st.m[rt] == -INFINITY ? 0.0f : st.m[rt];
+        // P = ph + pl to about 2^-22 relative (weights are <= 2^kTau)
+        float lsum = 0.0f;
+#pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (j0 + tt * kTile + 4 * grp + i > last) s[tt][i] = -INFINITY;
+            for (int i = 0; i < 4; ++i) {
+                const float p = __builtin_amdgcn_exp2f(s[rt][tt][i] - mref);
+                lsum += p;
+                const _Float16 h = (_Float16)p;
+                ph[rt][4 * tt + i] = h;
+                pl[rt][4 * tt + i] = (_Float16)(p - (float)h);
+            }
+        st.l[rt] += lsum;
     }
-    // online softmax (this lane: one row, 8 keys)
-    float cm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-    cm = xmax4(cm);
-    const bool grow = cm > st.m + kTau;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-        if (cm > st.m) {
-            const float alpha = __builtin_amdgcn_exp2f(st.m - cm);
-            st.l *= alpha;
+    // O^T += V^T P^T with both factors split: hi*hi + hi*lo + lo*hi, four
+    // output tiles at a time so that dependent products are 4 RT apart; each
+    // V fragment serves all RT row tiles
+    constexpr int NG = 4;
+    half8 vh[NG], vl[NG], vhn[NG], vln[NG];
+    auto load_group = [&](int n0, half8 (&h)[NG], half8 (&l)[NG]) {
 #pragma unroll
-            for (int nt = 0; nt < C::NT; ++nt) st.o[nt] *= alpha;
-            st.m = cm;
+        for (int i = 0; i < NG; ++i) {
+            h[i] = *reinterpret_cast<const half8*>(vf + ((n0 + i) * 64 + lane) * 16);
+            l[i] = *reinterpret_cast<const half8*>(vf + C::V_FRAG + ((n0 + i) * 64 + lane) * 16);
         }
-    }
-    const float mref = st.m == -INFINITY ? 0.0f : st.m;
-    // P = ph + pl to about 2^-22 relative (weights are <= 2^kTau)
-    half8 ph, pl;
-    float lsum = 0.0f;
+    };
+    load_group(0, vh, vl);
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int n0 = 0; n0 < C::NT; n0 += NG) {
+        if (n0 + NG < C::NT) load_group(n0 + NG, vhn, vln);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float p = __builtin_amdgcn_exp2f(s[tt][i] - mref);
-            lsum += p;
-            const _Float16 h = (_Float16)p;
-            ph[4 * tt + i] = h;
-            pl[4 * tt + i] = (_Float16)(p - (float)h);
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int i = 0; i < NG; ++i)
+                st.o[rt][n0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh[i], ph[rt], st.o[rt][n0 + i], 0, 0, 0);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int i = 0; i < NG; ++i)
+                st.o[rt][n0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh[i], pl[rt], st.o[rt][n0 + i], 0, 0, 0);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int i = 0; i < NG; ++i)
+                st.o[rt][n0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vl[i], ph[rt], st.o[rt][n0 + i], 0, 0, 0);
+        if (n0 + NG < C::NT) {
+#pragma unroll
+            for (int i = 0; i < NG; ++i) { vh[i] = vhn[i]; vl[i] = vln[i]; }
         }
-    st.l += lsum;
-    // O^T += V^T P^T with both factors split: hi*hi + hi*lo + lo*hi
-#pragma unroll
-    for (int nt = 0; nt < C::NT; ++nt) {
-        const half8 vh = *reinterpret_cast<const half8*>(vf + (nt * 64 + lane) * 16);
-        const half8 vl = *reinterpret_cast<const half8*>(vf + C::V_FRAG + (nt * 64 + lane) * 16);
-        floatx4 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh, ph, st.o[nt], 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh, pl, acc, 0, 0, 0);
-        st.o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vl, ph, acc, 0, 0, 0);
+        SCHED_FENCE();      // one group of lookahead
     }
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void attn_mfma_tiled_kernel(AttnArgs a, int cps, int n_splits, int group,
-                                                                   int rows, int row_tiles) {
-    using C = TCfg<D>;
+template <int D, int RT>
+__global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_tiled_kernel(AttnArgs a, int cps, int n_splits,
+                                                                          int group, int rows, int row_tiles) {
+    using C = TCfg<D, RT>;
     extern __shared__ __align__(16) uint8_t smem[];
     const Geom& g = a.g;
     const int t = threadIdx.x;
@@ -388,14 +456,21 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_tiled_kernel(AttnArgs a, i
     const int c_end = min(min(total_chunks, c_begin + cps), (first_last + rmax / group) / kChunk + 1);
     const int min_last = first_last + r0 / group;      // chunks ending at or below it need no mask
 
-    // this lane's query row; a wave whose 16 rows all lie past the end (few
-    // rows, e.g. a verify batch) skips the math but still stages chunks
-    const bool wave_active = r0 + wave * 16 < rows;
-    const int row = r0 + wave * 16 + (lane & 15);
-    const bool row_ok = row < rows;
-    const int qi = row_ok ? row / group : 0;
-    const int h = kvh * group + (row_ok ? row % group : 0);
-    const int last = row_ok ? first_last + qi : -1;
+    // this lane's query rows (one per row tile); a wave whose rows all lie
+    // past the end (few rows, e.g. a verify batch) skips the math but still
+    // stages chunks
+    const int wrow0 = r0 + wave * 16 * RT;
+    const bool wave_active = wrow0 < rows;
+    int qi[RT], hh[RT], last[RT];
+    bool row_ok[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int row = wrow0 + 16 * rt + (lane & 15);
+        row_ok[rt] = row < rows;
+        qi[rt] = row_ok[rt] ? row / group : 0;
+        hh[rt] = kvh * group + (row_ok[rt] ? row % group : 0);
+        last[rt] = row_ok[rt] ? first_last + qi[rt] : -1;
+    }
 
     // Page-table entries: lane k of `ents` holds the entry of page pb + k
     // (batches of 64 pages, one gather load per batch); the loop picks them
@@ -417,7 +492,7 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_tiled_kernel(AttnArgs a, i
 
     bool bad = false;
     uint8_t* ring = smem + 2 * C::STAGE;
-    const Requests<D> req(g, wave, lane);
+    const Requests<D, RT> req(g, wave, lane);
     // position of the next chunk to request, advanced one chunk at a time
     int iss_c = c_begin, iss_page = (c_begin * kChunk) / g.P, iss_slot = (c_begin * kChunk) % g.P;
     auto issue_next = [&]() {
@@ -433,31 +508,37 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_tiled_kernel(AttnArgs a, i
     for (int i = 0; i < kRing; ++i)
         if (c_begin + i < c_end) issue_next();
 
-    // q of this lane's row as fp16 hi + lo, pre-scaled by scale * log2(e), in
+    // q of this lane's rows as fp16 hi + lo, pre-scaled by scale * log2(e), in
     // the B-operand layout (row = lane % 16, dims 8 (lane / 16) .. +7 per block)
-    half8 qh[C::NB], ql[C::NB];
+    half8 qh[RT][C::NB], ql[RT][C::NB];
     {
         const float qscale = a.scale * kLog2e;
-        const float* src = a.q + ((size_t)qi * a.n_heads + h) * D + 8 * (lane >> 4);
 #pragma unroll
-        for (int b = 0; b < C::NB; ++b)
+        for (int rt = 0; rt < RT; ++rt) {
+            const float* src = a.q + ((size_t)qi[rt] * a.n_heads + hh[rt]) * D + 8 * (lane >> 4);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float v = src[b * kBlock + i];          // in bounds: rows past the end read row 0
-                const float x = row_ok ? v * qscale : 0.0f;
-                qh[b][i] = (_Float16)x;
-                ql[b][i] = (_Float16)(x - (float)qh[b][i]);
-            }
+            for (int b = 0; b < C::NB; ++b)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float v = src[b * kBlock + i];      // in bounds: rows past the end read row 0
+                    const float x = row_ok[rt] ? v * qscale : 0.0f;
+                    qh[rt][b][i] = (_Float16)x;
+                    ql[rt][b][i] = (_Float16)(x - (float)qh[rt][b][i]);
+                }
+        }
     }
 
-    Row<D> st;
-    st.m = -INFINITY;
-    st.l = 0.0f;
+    Rows<D, RT> st;
 #pragma unroll
-    for (int nt = 0; nt < C::NT; ++nt) st.o[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int rt = 0; rt < RT; ++rt) {
+        st.m[rt] = -INFINITY;
+        st.l[rt] = 0.0f;
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt) st.o[rt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
 
     auto convert = [&](int c) {
-        convert_chunk<D>(ring + (c & (kRing - 1)) * C::SLOT, smem + (c & 1) * C::STAGE, t, a.ctx - c * kChunk);
+        convert_chunk<D, RT>(ring + (c & (kRing - 1)) * C::SLOT, smem + (c & 1) * C::STAGE, t, a.ctx - c * kChunk);
     };
     if (c_begin < c_end) {
         vm_wait<0>();
@@ -474,7 +555,8 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_tiled_kernel(AttnArgs a, i
         if (more) issue_next();
         SCHED_FENCE();
         if (wave_active)
-            chunk_step<D, decltype(masked)::value>(st, smem + (c & 1) * C::STAGE, qh, ql, lane, c * kChunk, last);
+            chunk_step<D, RT, decltype(masked)::value>(st, smem + (c & 1) * C::STAGE, qh, ql, lane, c * kChunk,
+                                                       last);
         SCHED_FENCE();
         if (more) vm_wait<(kRing - 2) * C::ND>(); else vm_wait<0>();
         lds_barrier();
@@ -485,35 +567,38 @@ __global__ __launch_bounds__(kThreads) void attn_mfma_tiled_kernel(AttnArgs a, i
     for (int c = c_begin; c < c_mask; ++c) step(c, std::false_type{});
     for (int c = c_mask; c < c_end; ++c) step(c, std::true_type{});
 
-    // row sum over the row's 4 lanes; every lane then holds (m, L) of its row
-    float L = xsum4(st.l);
-    float M = st.m;
-    if (bad) { M = NAN; L = NAN; }
-    if (!row_ok) return;
     const int grp = lane >> 4;
-    const size_t orow = (size_t)qi * a.n_heads + h;
-    if (n_splits == 1) {
-        const float inv = 1.0f / L;
-        float* dst = a.out + orow * D + 4 * grp;
 #pragma unroll
-        for (int nt = 0; nt < C::NT; ++nt) *reinterpret_cast<floatx4*>(dst + 16 * nt) = st.o[nt] * inv;
-        if (a.lse != nullptr && grp == 0) a.lse[orow] = (M + log2f(L)) * 0.69314718055994531f;
-    } else {
-        const size_t ps = orow * n_splits + split;
-        if (grp == 0) {
-            a.ws_m[ps] = M;
-            a.ws_l[ps] = L;
+    for (int rt = 0; rt < RT; ++rt) {
+        // row sum over the row's 4 lanes; every lane then holds (m, L) of its row
+        float L = xsum4(st.l[rt]);
+        float M = st.m[rt];
+        if (bad) { M = NAN; L = NAN; }
+        if (!row_ok[rt]) continue;
+        const size_t orow = (size_t)qi[rt] * a.n_heads + hh[rt];
+        if (n_splits == 1) {
+            const float inv = 1.0f / L;
+            float* dst = a.out + orow * D + 4 * grp;
+#pragma unroll
+            for (int nt = 0; nt < C::NT; ++nt) *reinterpret_cast<floatx4*>(dst + 16 * nt) = st.o[rt][nt] * inv;
+            if (a.lse != nullptr && grp == 0) a.lse[orow] = (M + log2f(L)) * 0.69314718055994531f;
+        } else {
+            const size_t ps = orow * n_splits + split;
+            if (grp == 0) {
+                a.ws_m[ps] = M;
+                a.ws_l[ps] = L;
+            }
+            float* dst = a.ws_acc + ps * D + 4 * grp;
+#pragma unroll
+            for (int nt = 0; nt < C::NT; ++nt) *reinterpret_cast<floatx4*>(dst + 16 * nt) = st.o[rt][nt];
         }
-        float* dst = a.ws_acc + ps * D + 4 * grp;
-#pragma unroll
-        for (int nt = 0; nt < C::NT; ++nt) *reinterpret_cast<floatx4*>(dst + 16 * nt) = st.o[nt];
     }
 }
 
-template <int D>
-hipError_t launch_d(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) {
-    using C = TCfg<D>;
-    auto kern = attn_mfma_tiled_kernel<D>;
+template <int D, int RT>
+hipError_t launch_dr(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) {
+    using C = TCfg<D, RT>;
+    auto kern = attn_mfma_tiled_kernel<D, RT>;
     if (C::LDS > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
@@ -521,7 +606,7 @@ hipError_t launch_d(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) {
     }
     const int row_tiles = (pl.rows + kRowsPerWg - 1) / kRowsPerWg;
     dim3 grid(row_tiles * pl.n_splits * a.g.n_kv);
-    hipLaunchKernelGGL(kern, grid, dim3(kThreads), C::LDS, stream, a, pl.chunks_per_split, pl.n_splits, pl.group,
+    hipLaunchKernelGGL(kern, grid, dim3(C::THREADS), C::LDS, stream, a, pl.chunks_per_split, pl.n_splits, pl.group,
                        pl.rows, row_tiles);
     return hipGetLastError();
 }
@@ -531,10 +616,12 @@ hipError_t launch_d(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) {
 int mfma_tiled_rows_per_wg() { return kRowsPerWg; }
 
 hipError_t launch_attn_mfma_tiled(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) {
+    // one row tile per wave: at head_dim 256 two tiles per wave need more than
+    // the 512 registers a wave can hold
     switch (a.g.D) {
-        case 64: return launch_d<64>(a, pl, stream);
-        case 128: return launch_d<128>(a, pl, stream);
-        case 256: return launch_d<256>(a, pl, stream);
+        case 64: return launch_dr<64, 1>(a, pl, stream);
+        case 128: return launch_dr<128, 1>(a, pl, stream);
+        case 256: return launch_dr<256, 1>(a, pl, stream);
         default: return hipErrorInvalidValue;
     }
 }
