@@ -243,30 +243,33 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] {w.name}: {n_layers} layers filled in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
 
-    def step(ev=None):
+    # The attention kernel is timed by events the library records around it,
+    # on one layer per step (rotating through the layers): a pair of event
+    # records between kernels costs about 5 us of queue time, which on every
+    # layer would inflate the step time being measured.
+    def step(ev=None, s=0):
         for i, lay in enumerate(layers):
             lay.append()
-            lay.attend(ws, args.kernel, None if ev is None else ev[i])
+            lay.attend(ws, args.kernel, ev if (ev is not None and i == s % n_layers) else None)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
     hip_ev = HipEvents()
-    evs = [[[hip_ev.create() for _ in range(2)] for _ in range(n_layers)] for _ in range(args.steps)]
+    evs = [[hip_ev.create() for _ in range(2)] for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for s in range(args.steps):
-        step(evs[s])
+        step(evs[s], s)
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
-    attn_ms = [hip_ev.elapsed_ms(e[0], e[1]) for st in evs for e in st]
-    for st in evs:
-        for e in st:
-            hip_ev.destroy(e[0])
-            hip_ev.destroy(e[1])
+    attn_ms = [hip_ev.elapsed_ms(e[0], e[1]) for e in evs]
+    for e in evs:
+        hip_ev.destroy(e[0])
+        hip_ev.destroy(e[1])
     avg_attn_us = 1000.0 * sum(attn_ms) / len(attn_ms)       # the attention kernel alone
     kname = kernel_name(w, args.kernel)
     traffic = measured_traffic(w.name, kname)
