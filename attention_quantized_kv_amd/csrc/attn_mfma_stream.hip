@@ -71,7 +71,7 @@ struct Cfg {
     static constexpr int LAND_VS = 1024;        // NB x 32 fp16, padded likewise
     static constexpr int PBUF = RT * 16 * kPStride * 4;
     static constexpr int WAVE_BYTES = LAND_K + LAND_KS + LAND_V + LAND_VS + PBUF;
-    static constexpr int Q_BYTES = RT * NB * 2 * 64 * 16;
+    static constexpr int Q_BYTES = RT == 1 ? 0 : RT * NB * 2 * 64 * 16;   // q staged in LDS only for RT > 1
     static constexpr int COMB_BYTES = (W / 2) * RT * 16 * D * 4;
     static constexpr int MAIN_BYTES = Q_BYTES + W * WAVE_BYTES > COMB_BYTES ? Q_BYTES + W * WAVE_BYTES : COMB_BYTES;
     static constexpr int ML_BYTES = W * RT * 16 * 2 * 4;
@@ -217,10 +217,15 @@ struct WaveState {
 template <int D, int RT, int JJ, bool MASK>
 __device__ inline void qk_step(floatx4 (&s)[RT][2], const Land& L, const half8* __restrict__ qlds,
                                const half8 (&qreg)[Cfg<D, RT>::NB][2], int lane, int j0, int first_last, int group,
-                               int rows) {
+                               int rows, int rt0) {
     using C = Cfg<D, RT>;
     const int g4 = lane >> 4;
     const int n16 = lane & 15;
+    // With several row tiles q is read from LDS per block.  The offset is
+    // made opaque so that the compiler does not hoist those loop-invariant
+    // reads out of the chunk loop (which would pin all of q in registers).
+    int qoff = lane;
+    if (RT > 1) asm volatile("" : "+v"(qoff));
     // K scales of the lane's token in each tile (NB halves)
     uint32_t ksw[2][C::NB / 2];
 #pragma unroll
@@ -252,8 +257,8 @@ __device__ inline void qk_step(floatx4 (&s)[RT][2], const Land& L, const half8* 
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             // one row tile: q lives in registers; more: read it from LDS
-            const half8 qh = RT == 1 ? qreg[b][0] : qlds[((rt * C::NB + b) * 2 + 0) * 64 + lane];
-            const half8 ql = RT == 1 ? qreg[b][1] : qlds[((rt * C::NB + b) * 2 + 1) * 64 + lane];
+            const half8 qh = RT == 1 ? qreg[b][0] : qlds[((rt * C::NB + b) * 2 + 0) * 64 + qoff];
+            const half8 ql = RT == 1 ? qreg[b][1] : qlds[((rt * C::NB + b) * 2 + 1) * 64 + qoff];
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
                 floatx4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh, kb[tt], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
@@ -269,7 +274,7 @@ __device__ inline void qk_step(floatx4 (&s)[RT][2], const Land& L, const half8* 
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int jj = 0; jj < JJ; ++jj) {
-                const int row = logical_row<JJ>(rt, 4 * g4 + jj);
+                const int row = logical_row<JJ>(rt0 + rt, 4 * g4 + jj);
                 const int last = row >= 0 && row < rows ? first_last + row / group : -1;
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt)
@@ -294,17 +299,21 @@ __device__ inline void softmax_step(WaveState<D, RT>& st, floatx4 (&s)[RT][2], f
             grow |= mnew[rt][jj] > st.m[rt][jj] + kTau;
         }
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        // rows whose maximum did not move get alpha = 1: one straight pass
+        // over the accumulators per row tile, no per-row branches
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
+        for (int rt = 0; rt < RT; ++rt) {
+            floatx4 alpha = {1.0f, 1.0f, 1.0f, 1.0f};
 #pragma unroll
             for (int jj = 0; jj < JJ; ++jj) {
-                if (!(mnew[rt][jj] > st.m[rt][jj])) continue;
-                const float alpha = fast_exp2(st.m[rt][jj] - mnew[rt][jj]);
-                st.l[rt][jj] *= alpha;
-#pragma unroll
-                for (int nt = 0; nt < C::NT; ++nt) st.o[rt][nt][jj] *= alpha;
-                st.m[rt][jj] = mnew[rt][jj];
+                const bool up = mnew[rt][jj] > st.m[rt][jj];
+                alpha[jj] = up ? fast_exp2(st.m[rt][jj] - mnew[rt][jj]) : 1.0f;
+                st.l[rt][jj] *= alpha[jj];
+                st.m[rt][jj] = up ? mnew[rt][jj] : st.m[rt][jj];
             }
+#pragma unroll
+            for (int nt = 0; nt < C::NT; ++nt) st.o[rt][nt] *= alpha;
+        }
     }
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
@@ -369,11 +378,16 @@ __device__ inline void pv_step(WaveState<D, RT>& st, const Land& L, const float*
     }
 }
 
-template <int D, int RT, int JJ>
+template <int D, int RT, int JJ, int RG>
 __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_stream_kernel(AttnArgs a, int cps, int n_splits,
                                                                            int group, int rows) {
     using C = Cfg<D, RT>;
     constexpr int W = C::W;
+    // RG row groups of RT*16 rows; the WPG waves of group gi share its rows
+    // and deal its chunks among themselves.  Every group streams the same
+    // chunks, so a chunk read by a second group mostly comes from L2.
+    constexpr int WPG = W / RG;
+    static_assert(RG == 1 || RT == 1, "row groups take one row tile per wave");
     extern __shared__ __align__(16) uint8_t smem[];
     const Geom& g = a.g;
     const int lane = threadIdx.x & 63;
@@ -397,8 +411,9 @@ __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_stream_kernel(AttnA
     // and the addresses in flight at any time stay close (better DRAM and
     // translation locality than one contiguous run per wave).  Start the
     // first loads before staging q.
-    const int stride = n_splits * W;
-    const int c0 = split * W + wave;
+    const int gi = wave / WPG, wig = wave % WPG;
+    const int stride = n_splits * WPG;
+    const int c0 = split * WPG + wig;
     const int c1 = total_chunks;
     (void)cps;
     // Page-table entries: lane k of `ents` holds the entry of the wave's
@@ -423,37 +438,48 @@ __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_stream_kernel(AttnA
         }
     }
 
-    // ---- stage q rows as fp16 hi/lo in the MFMA A layout, pre-scaled by scale*log2(e)
+    // ---- q as fp16 hi/lo in the MFMA A layout, pre-scaled by scale*log2(e):
+    // one row tile per wave is loaded straight into the wave's registers
+    // (lane l: row of MFMA row l % 16, dims 8 (l / 16) .. +7 of each block);
+    // several row tiles are staged in LDS and read per block.
     const float qscale = a.scale * kLog2e;
-    for (int e = threadIdx.x; e < RT * C::NB * 64; e += W * 64) {
-        const int l = e & 63, rb = e >> 6, b = rb % C::NB, rt = rb / C::NB;
-        const int row = logical_row<JJ>(rt, l & 15);
-        half8 hi, lo;
-        if (row >= 0 && row < rows) {
-            const int qi = row / group, h = kvh * group + row % group;
-            const float* src = a.q + ((size_t)qi * a.n_heads + h) * D + b * kBlock + 8 * (l >> 4);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float x = src[i] * qscale;
-                hi[i] = (_Float16)x;
-                lo[i] = (_Float16)(x - (float)hi[i]);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) { hi[i] = (_Float16)0.0f; lo[i] = (_Float16)0.0f; }
-        }
-        qlds[(rb * 2 + 0) * 64 + l] = hi;
-        qlds[(rb * 2 + 1) * 64 + l] = lo;
-    }
-    __syncthreads();
-
     half8 qreg[C::NB][2];
     if (RT == 1) {
+        const int row = logical_row<JJ>(gi, lane & 15);
+        const bool ok = row >= 0 && row < rows;
+        const int qi = ok ? row / group : 0, h = kvh * group + (ok ? row % group : 0);
+        const float* src = a.q + ((size_t)qi * a.n_heads + h) * D + 8 * (lane >> 4);
 #pragma unroll
-        for (int b = 0; b < C::NB; ++b) {
-            qreg[b][0] = qlds[(b * 2 + 0) * 64 + lane];
-            qreg[b][1] = qlds[(b * 2 + 1) * 64 + lane];
+        for (int b = 0; b < C::NB; ++b)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float v = src[b * kBlock + i];          // in bounds: rows past the end read row 0
+                const float x = ok ? v * qscale : 0.0f;
+                qreg[b][0][i] = (_Float16)x;
+                qreg[b][1][i] = (_Float16)(x - (float)qreg[b][0][i]);
+            }
+    } else {
+        for (int e = threadIdx.x; e < RT * C::NB * 64; e += W * 64) {
+            const int l = e & 63, rb = e >> 6, b = rb % C::NB, rt = rb / C::NB;
+            const int row = logical_row<JJ>(rt, l & 15);
+            half8 hi, lo;
+            if (row >= 0 && row < rows) {
+                const int qi = row / group, h = kvh * group + row % group;
+                const float* src = a.q + ((size_t)qi * a.n_heads + h) * D + b * kBlock + 8 * (l >> 4);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float x = src[i] * qscale;
+                    hi[i] = (_Float16)x;
+                    lo[i] = (_Float16)(x - (float)hi[i]);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) { hi[i] = (_Float16)0.0f; lo[i] = (_Float16)0.0f; }
+            }
+            qlds[(rb * 2 + 0) * 64 + l] = hi;
+            qlds[(rb * 2 + 1) * 64 + l] = lo;
         }
+        __syncthreads();
     }
 
     WaveState<D, RT> st;
@@ -482,8 +508,8 @@ __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_stream_kernel(AttnA
         const int slot_next = ((c + stride) * kChunk) % g.P;
         floatx4 s[RT][2];
         vm_wait<C::V_ISSUES>();                 // K(c) landed (V(c) may still fly)
-        if (mask) qk_step<D, RT, JJ, true>(s, land, qlds, qreg, lane, j0, first_last, group, rows);
-        else qk_step<D, RT, JJ, false>(s, land, qlds, qreg, lane, j0, first_last, group, rows);
+        if (mask) qk_step<D, RT, JJ, true>(s, land, qlds, qreg, lane, j0, first_last, group, rows, gi);
+        else qk_step<D, RT, JJ, false>(s, land, qlds, qreg, lane, j0, first_last, group, rows, gi);
         lds_fence();                            // K(c) read out: the zone is free
         if (ok_next) issue_k<D, RT>(land, u_next, g, slot_next, lane);
         softmax_step<D, RT, JJ>(st, s, plds, lane);
@@ -519,10 +545,11 @@ __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_stream_kernel(AttnA
             const int row = 16 * rt + 4 * g4 + jj;
             float mm = -INFINITY;
 #pragma unroll
-            for (int w = 0; w < W; ++w) mm = fmaxf(mm, mls[(w * RT * 16 + row) * 2]);
+            for (int j = 0; j < WPG; ++j) mm = fmaxf(mm, mls[((gi * WPG + j) * RT * 16 + row) * 2]);
             float lt = 0.0f;
 #pragma unroll
-            for (int w = 0; w < W; ++w) {
+            for (int j = 0; j < WPG; ++j) {
+                const int w = gi * WPG + j;
                 const float mw = mls[(w * RT * 16 + row) * 2], lw = mls[(w * RT * 16 + row) * 2 + 1];
                 lt += lw == 0.0f ? 0.0f : lw * exp2f(mw - mm);
             }
@@ -551,22 +578,24 @@ __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_stream_kernel(AttnA
                 for (int jj = 0; jj < JJ; ++jj)
                     st.o[rt][nt][jj] += ob[((size_t)slot * RT * 16 + 16 * rt + 4 * g4 + jj) * D + 16 * nt + n16];
     };
-    // tree: waves [h, 2h) hand their sums to waves [0, h), h = W/2 .. 1
+    // tree inside each row group: waves [h, 2h) of the group hand their sums
+    // to waves [0, h), h = WPG/2 .. 1; group gi uses buffer slots
+    // gi*WPG/2 .. (gi+1)*WPG/2 - 1
 #pragma unroll
-    for (int h = W / 2; h >= 1; h /= 2) {
-        if (wave >= h && wave < 2 * h) put(wave - h);
+    for (int h = WPG / 2; h >= 1; h /= 2) {
+        if (wig >= h && wig < 2 * h) put(gi * (WPG / 2) + wig - h);
         __syncthreads();
-        if (wave < h) add(wave);
+        if (wig < h) add(gi * (WPG / 2) + wig);
         __syncthreads();
     }
-    if (wave != 0) return;
+    if (wig != 0) return;
 
     // ---- write the partial of each row this workgroup serves
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int jj = 0; jj < JJ; ++jj) {
-            const int row = logical_row<JJ>(rt, 4 * g4 + jj);
+            const int row = logical_row<JJ>(gi + rt, 4 * g4 + jj);
             if (row < 0 || row >= rows) continue;
             const int qi = row / group, h = kvh * group + row % group;
             const size_t ps = ((size_t)qi * a.n_heads + h) * n_splits + split;
@@ -579,10 +608,10 @@ __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_stream_kernel(AttnA
         }
 }
 
-template <int D, int RT, int JJ>
+template <int D, int RT, int JJ, int RG>
 hipError_t launch_dr(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) {
     using C = Cfg<D, RT>;
-    auto kern = attn_mfma_stream_kernel<D, RT, JJ>;
+    auto kern = attn_mfma_stream_kernel<D, RT, JJ, RG>;
     if (C::LDS_BYTES > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
@@ -594,21 +623,21 @@ hipError_t launch_dr(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) 
     return hipGetLastError();
 }
 
+// One row tile per wave: up to 8 rows two per lane group (JJ = 2), up to
+// 16 rows one per MFMA row, more rows in 2 or 4 row groups.
 template <int D>
 hipError_t launch_d(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) {
-    if (pl.rows <= 8) return launch_dr<D, 1, 2>(a, pl, stream);
-    switch ((pl.rows + 15) / 16) {
-        case 1: return launch_dr<D, 1, 4>(a, pl, stream);
-        case 2: return launch_dr<D, 2, 4>(a, pl, stream);
-        case 3: return launch_dr<D, 3, 4>(a, pl, stream);
-        case 4: return launch_dr<D, 4, 4>(a, pl, stream);
-        default: return hipErrorInvalidValue;
-    }
+    if (pl.rows <= 8) return launch_dr<D, 1, 2, 1>(a, pl, stream);
+    if (pl.rows <= 16) return launch_dr<D, 1, 4, 1>(a, pl, stream);
+    if (pl.rows <= 32) return launch_dr<D, 1, 4, 2>(a, pl, stream);
+    if (pl.rows <= 64) return launch_dr<D, 1, 4, 4>(a, pl, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-int mfma_stream_waves(int rows) { return rows <= 16 ? 8 : 4; }
+int mfma_stream_row_groups(int rows) { return rows <= 16 ? 1 : rows <= 32 ? 2 : 4; }
+int mfma_stream_waves(int rows) { return 8 / mfma_stream_row_groups(rows); }
 
 hipError_t launch_attn_mfma_stream(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) {
     switch (a.g.D) {

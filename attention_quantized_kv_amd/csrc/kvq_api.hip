@@ -49,9 +49,9 @@ int auto_chunks_per_split(int kernel, int total_chunks, int n_kv, int n_q, int r
         return (int)(per < 1 ? 1 : per);
     }
     if (kernel == 2) {
-        // one wave per split of one KV head, all query rows at once; ~2048 waves
-        long per = units / 2048;
-        (void)rows;
+        // ~2048 waves: every row group of a workgroup streams the split's
+        // chunks, so a chunk costs one wave per row group
+        long per = units * kvq::mfma_stream_row_groups(rows) / 2048;
         return (int)(per < 1 ? 1 : per);
     }
     // LDS-tiled chunk kernel: a workgroup per (row tile, KV head, split);

@@ -102,7 +102,9 @@ hipError_t launch_attn_valu(const AttnArgs& a, const AttnPlan& pl, hipStream_t s
 hipError_t launch_attn_mfma_stream(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream);
 hipError_t launch_attn_mfma_tiled(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream);
 hipError_t launch_merge(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream);
-// Waves per workgroup of the streaming MFMA kernel for a given row count.
+// Streaming MFMA kernel: row groups per workgroup, and waves sharing one row
+// group (each partial folds that many waves' chunks), for a given row count.
+int mfma_stream_row_groups(int rows);
 int mfma_stream_waves(int rows);
 // Query rows per workgroup of the LDS-tiled MFMA kernel.
 int mfma_tiled_rows_per_wg();
