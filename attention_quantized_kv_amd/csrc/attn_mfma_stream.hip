@@ -15,14 +15,18 @@
 // every K/V byte, so the cache is read once per KV head.
 //
 // Data path per 32-token chunk and wave (D = head_dim, NB = D/32 blocks):
-//  * global -> LDS directly (global_load_lds_dwordx4) into the wave's own
-//    landing zone: two 16-token K tiles, their K scales, the V chunk and its
-//    V scales.  Each instruction moves one contiguous 1 KiB (16 bytes per
-//    lane) thanks to the pool layout, and data in flight costs no VGPRs.
-//    K of chunk c+1 is requested as soon as chunk c's K has been read out of
-//    LDS (after its QK step), V of chunk c+1 as soon as chunk c's V has been
-//    read (after its PV step), so each load has about a chunk of work to hide
-//    behind, plus the other wave on the SIMD.
+//  * global -> LDS directly (global_load_lds_dwordx4), one contiguous 1 KiB
+//    wave request (16 bytes per lane) per piece thanks to the pool layout,
+//    so data in flight costs no VGPRs.  A chunk is 3*KL code pieces (K tile
+//    0/1 of each 64-dim slice, then the V slices) plus a K-scale and a
+//    V-scale piece.  The code pieces stream through a per-wave ring of R
+//    slots in the order they are consumed: as soon as a piece has been read
+//    out of LDS, the piece R places further on is requested into its slot.
+//    The HBM system delivers the most when each wave keeps only a few KiB in
+//    flight (more outstanding requests lower the throughput), so the ring is
+//    kept short; the scale pieces of chunk c+1 are requested once chunk c's
+//    have been used.  The wait counts are computed at compile time from the
+//    fixed request order (Waits below).
 //  * S = Q K^T on v_mfma_f32_16x16x32_f16: K = 32 is exactly one quant block,
 //    so the int8 codes go in unscaled (exact in fp16) and the block's fp16
 //    scale multiplies the fp32 result.  q is split into fp16 hi + lo parts
@@ -58,29 +62,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 // at the end.
 constexpr float kTau = 4.0f;
 
-template <int D, int RT>
-struct Cfg {
-    static constexpr int NB = D / kBlock;       // quant blocks per row
-    static constexpr int KL = D / 64;           // 1 KiB loads: per K tile, per V chunk
-    static constexpr int NT = D / 16;           // 16-wide output tiles
-    static constexpr int W = RT == 1 ? 8 : 4;   // waves per workgroup (kThreadsFor / 64)
-    // per-wave landing zone and P buffer (bytes)
-    static constexpr int LAND_K = 2 * KL * 1024;
-    static constexpr int LAND_KS = 1024;        // 32 x NB fp16, padded to one full-wave DMA
-    static constexpr int LAND_V = KL * 1024;
-    static constexpr int LAND_VS = 1024;        // NB x 32 fp16, padded likewise
-    static constexpr int PBUF = RT * 16 * kPStride * 4;
-    static constexpr int WAVE_BYTES = LAND_K + LAND_KS + LAND_V + LAND_VS + PBUF;
-    static constexpr int Q_BYTES = RT == 1 ? 0 : RT * NB * 2 * 64 * 16;   // q staged in LDS only for RT > 1
-    static constexpr int COMB_BYTES = (W / 2) * RT * 16 * D * 4;
-    static constexpr int MAIN_BYTES = Q_BYTES + W * WAVE_BYTES > COMB_BYTES ? Q_BYTES + W * WAVE_BYTES : COMB_BYTES;
-    static constexpr int ML_BYTES = W * RT * 16 * 2 * 4;
-    static constexpr int LDS_BYTES = MAIN_BYTES + ML_BYTES;
-    // vector-memory instructions per request
-    static constexpr int K_ISSUES = 2 * KL + 1;
-    static constexpr int V_ISSUES = KL + 1;
-};
-
 // MFMA row placement.  Row tile rt holds MFMA rows 0..15; lane group g4 of the
 // S / O layouts owns rows 4*g4 .. 4*g4+3.  With at most 8 query rows (JJ = 2)
 // the rows go to MFMA rows {0,1, 4,5, 8,9, 12,13}, so each lane holds 2 real
@@ -91,9 +72,6 @@ __device__ inline int logical_row(int rt, int prow) {
     if (JJ == 4) return 16 * rt + prow;
     return (prow & 3) < 2 ? 8 * rt + 2 * (prow >> 2) + (prow & 3) : -1;
 }
-
-template <int RT>
-constexpr int kThreadsFor = (RT == 1 ? 8 : 4) * 64;   // workgroup size (must match Cfg::W)
 
 template <int CTRL>
 __device__ inline float dpp(float x) {
@@ -172,60 +150,107 @@ __device__ inline half8 v_codes_to_half(uint32_t x, uint32_t magic) {
     return h * mul + add;
 }
 
-// Per-wave LDS landing zone of one chunk.
+template <int D, int R>
+struct Cfg {
+    static constexpr int NB = D / kBlock;       // quant blocks per row
+    static constexpr int KL = D / 64;           // 64-dim slices (1 KiB pieces per K tile / V chunk)
+    static constexpr int NT = D / 16;           // 16-wide output tiles
+    static constexpr int NP = 3 * KL;           // code pieces per chunk: K(t0,p), K(t1,p) for each p, then V(u)
+    static constexpr int W = 8;                 // waves per workgroup (two per SIMD)
+    static_assert(NP % R == 0 && R <= NP, "ring slots must divide the pieces of a chunk");
+    // per-wave LDS: code ring, K scales, V scales, P transpose buffer (bytes)
+    static constexpr int RING = R * 1024;
+    static constexpr int LAND_KS = 1024;        // 32 x NB fp16, padded to one full-wave request
+    static constexpr int LAND_VS = 1024;        // NB x 32 fp16, padded likewise
+    static constexpr int PBUF = 16 * kPStride * 4;
+    static constexpr int WAVE_BYTES = RING + LAND_KS + LAND_VS + PBUF;
+    static constexpr int COMB_BYTES = (W / 2) * 16 * D * 4;
+    static constexpr int MAIN_BYTES = W * WAVE_BYTES > COMB_BYTES ? W * WAVE_BYTES : COMB_BYTES;
+    static constexpr int ML_BYTES = W * 16 * 2 * 4;
+    static constexpr int LDS_BYTES = MAIN_BYTES + ML_BYTES;
+};
+
+// Wait counts.  Per chunk a wave issues its requests in a fixed order: the
+// QK step consumes code pieces 2p, 2p+1 (slice p, both tiles) and requests
+// the pieces R places further on; then the next chunk's K scales; the PV
+// step consumes piece 2KL+u and requests the one R further on; then the next
+// chunk's V scales.  Piece J of chunk k was requested when piece J-R was
+// consumed, so the number of requests issued after it by the time it is
+// consumed is fixed; s_waitcnt vmcnt(that count) guarantees it has landed
+// (requests complete in order).  The first chunk waits for everything once,
+// the last chunk (nothing further requested) waits with 0.
+template <int KL, int R>
+struct Waits {
+    static constexpr int NP = 3 * KL, NI = 3 * KL + 2;
+    static constexpr int issue_pos(int j) { return j < 2 * KL ? j : j + 1; }          // slot of "consume j" in a chunk's requests
+    static constexpr int event_pos(int J) { return J < 2 * KL ? 2 * (J / 2) : 2 * KL + 1 + (J - 2 * KL); }
+    static constexpr int after(int J) {
+        const int m = ((J - R) % NP + NP) % NP;
+        return event_pos(J) - issue_pos(m) - 1 + (J < R ? NI : 0);
+    }
+    static constexpr int mn(int a, int b) { return a < b ? a : b; }
+    // QK slice p (and, for p = 0, this chunk's K scales, issued at 2KL of the
+    // chunk before)
+    static constexpr int qk(int p) { return p == 0 ? mn(mn(after(0), after(1)), NI - 2 * KL - 1) : mn(after(2 * p), after(2 * p + 1)); }
+    // PV slice u (and, for u = 0, this chunk's V scales, issued last in the chunk before)
+    static constexpr int pv(int u) { return u == 0 ? mn(after(2 * KL), NI - KL - 1) : after(2 * KL + u); }
+};
+
+// Per-wave LDS of the stream.
 struct Land {
-    uint8_t* k;     // [2 tiles][KL][1 KiB]
+    uint8_t* ring;  // [R][1 KiB] code pieces
     uint8_t* ks;    // [32 tokens][NB] fp16 (then repeats)
-    uint8_t* v;     // [KL][1 KiB]
     uint8_t* vs;    // [NB][32 tokens] fp16 (then repeats)
 };
 
-template <int D, int RT>
-__device__ inline void issue_k(const Land& L, const uint8_t* unit, const Geom& g, int slot0, int lane) {
-    using C = Cfg<D, RT>;
-    const uint8_t* src = unit + (int64_t)(slot0 / kTile) * kTile * D + lane * 16;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int p = 0; p < C::KL; ++p) dma16(src + tt * kTile * D + p * 1024, L.k + (tt * C::KL + p) * 1024);
-    // 32 tokens x NB scales = 4*NB pieces of 16 bytes.  Every lane takes part
-    // (lanes past 4*NB repeat a piece): a DMA under a lane-dependent branch
-    // can get its LDS base merged with a neighbouring DMA's by the compiler.
-    dma16(unit + g.k_scales_off() + (int64_t)slot0 * C::NB * 2 + (lane % (4 * C::NB)) * 16, L.ks);
+// Requests code piece j of a chunk (slot0 = its first slot in the page) into
+// ring slot j % R.  Full-wave request (see the scale pieces below).
+template <int D, int R>
+__device__ inline void issue_piece(const Land& L, const uint8_t* unit, const Geom& g, int slot0, int j, int lane) {
+    using C = Cfg<D, R>;
+    const uint8_t* src;
+    if (j < 2 * C::KL) {
+        const int p = j / 2, tt = j % 2;
+        src = unit + (int64_t)(slot0 / kTile + tt) * kTile * D + p * 1024 + lane * 16;
+    } else {
+        src = unit + g.v_codes_off() + (int64_t)(slot0 / kChunk) * kChunk * D / 2 + (j - 2 * C::KL) * 1024 + lane * 16;
+    }
+    dma16(src, L.ring + (j % R) * 1024);
 }
 
-template <int D, int RT>
-__device__ inline void issue_v(const Land& L, const uint8_t* unit, const Geom& g, int slot0, int lane) {
-    using C = Cfg<D, RT>;
-    const uint8_t* src = unit + g.v_codes_off() + (int64_t)(slot0 / kChunk) * kChunk * D / 2 + lane * 16;
-#pragma unroll
-    for (int u = 0; u < C::KL; ++u) dma16(src + u * 1024, L.v + u * 1024);
+// 32 tokens x NB scales = 4*NB pieces of 16 bytes.  Every lane takes part
+// (lanes past 4*NB repeat a piece): a direct-to-LDS load under a
+// lane-dependent branch can get its LDS base merged with a neighbouring one's.
+template <int D, int R>
+__device__ inline void issue_kscales(const Land& L, const uint8_t* unit, const Geom& g, int slot0, int lane) {
+    using C = Cfg<D, R>;
+    dma16(unit + g.k_scales_off() + (int64_t)slot0 * C::NB * 2 + (lane % (4 * C::NB)) * 16, L.ks);
+}
+template <int D, int R>
+__device__ inline void issue_vscales(const Land& L, const uint8_t* unit, const Geom& g, int slot0, int lane) {
+    using C = Cfg<D, R>;
     dma16(unit + g.v_scales_off() + (int64_t)(slot0 / kChunk) * C::NB * kChunk * 2 + (lane % (4 * C::NB)) * 16,
           L.vs);
 }
 
-template <int D, int RT>
+template <int D, int R>
 struct WaveState {
-    floatx4 o[RT][Cfg<D, RT>::NT];   // unnormalized output, MFMA C layout
-    float m[RT][4];                  // reference max of each of the lane's 4 rows per tile
-    float l[RT][4];                  // this lane's share of the row sums
+    floatx4 o[Cfg<D, R>::NT];   // unnormalized output, MFMA C layout
+    float m[4];                 // reference max of each of the lane's 4 rows
+    float l[4];                 // this lane's share of the row sums
 };
 
 // S = (q_hi + q_lo) K^T for the chunk's two 16-token tiles.  MASK: some key
 // of the chunk lies beyond the last key of some row (causal edge, or
-// positions past ctx_len).
-template <int D, int RT, int JJ, bool MASK>
-__device__ inline void qk_step(floatx4 (&s)[RT][2], const Land& L, const half8* __restrict__ qlds,
-                               const half8 (&qreg)[Cfg<D, RT>::NB][2], int lane, int j0, int first_last, int group,
-                               int rows, int rt0) {
-    using C = Cfg<D, RT>;
+// positions past ctx_len).  wait(p) runs before slice p's pieces are read,
+// done(p) after they have been read out of LDS.
+template <int D, int R, int JJ, bool MASK, class Wait, class Done>
+__device__ inline void qk_step(floatx4 (&s)[2], const Land& L, const half8 (&qreg)[Cfg<D, R>::NB][2], int lane,
+                               int j0, int first_last, int group, int rows, int rt0, Wait wait, Done done) {
+    using C = Cfg<D, R>;
     const int g4 = lane >> 4;
     const int n16 = lane & 15;
-    // With several row tiles q is read from LDS per block.  The offset is
-    // made opaque so that the compiler does not hoist those loop-invariant
-    // reads out of the chunk loop (which would pin all of q in registers).
-    int qoff = lane;
-    if (RT > 1) asm volatile("" : "+v"(qoff));
+    wait(0);
     // K scales of the lane's token in each tile (NB halves)
     uint32_t ksw[2][C::NB / 2];
 #pragma unroll
@@ -235,16 +260,17 @@ __device__ inline void qk_step(floatx4 (&s)[RT][2], const Land& L, const half8* 
         for (int w = 0; w < C::NB / 2; ++w) ksw[tt][w] = src[w];
     }
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) s[rt][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int tt = 0; tt < 2; ++tt) s[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
     u32x4 kr[2];
 #pragma unroll
     for (int b = 0; b < C::NB; ++b) {
         if ((b & 1) == 0) {
+            const int p = b / 2;
+            if (p > 0) wait(p);
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
-                kr[tt] = *reinterpret_cast<const u32x4*>(L.k + (tt * C::KL + b / 2) * 1024 + lane * 16);
+                kr[tt] = *reinterpret_cast<const u32x4*>(L.ring + ((2 * p + tt) % R) * 1024 + lane * 16);
+            done(p);
         }
         half8 kb[2];
         float ksc[2];
@@ -255,139 +281,143 @@ __device__ inline void qk_step(floatx4 (&s)[RT][2], const Land& L, const half8* 
             ksc[tt] = (b & 1) ? (float)sw.y : (float)sw.x;
         }
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            // one row tile: q lives in registers; more: read it from LDS
-            const half8 qh = RT == 1 ? qreg[b][0] : qlds[((rt * C::NB + b) * 2 + 0) * 64 + qoff];
-            const half8 ql = RT == 1 ? qreg[b][1] : qlds[((rt * C::NB + b) * 2 + 1) * 64 + qoff];
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                floatx4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh, kb[tt], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-                c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql, kb[tt], c, 0, 0, 0);
-                s[rt][tt] += ksc[tt] * c;
-            }
+        for (int tt = 0; tt < 2; ++tt) {
+            floatx4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qreg[b][0], kb[tt], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qreg[b][1], kb[tt], c, 0, 0, 0);
+            s[tt] += ksc[tt] * c;
         }
         SCHED_FENCE();
     }
     // causal / tail mask: key j visible to row r iff j <= first_last + r / group
     if (MASK) {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
+        for (int jj = 0; jj < JJ; ++jj) {
+            const int row = logical_row<JJ>(rt0, 4 * g4 + jj);
+            const int last = row >= 0 && row < rows ? first_last + row / group : -1;
 #pragma unroll
-            for (int jj = 0; jj < JJ; ++jj) {
-                const int row = logical_row<JJ>(rt0 + rt, 4 * g4 + jj);
-                const int last = row >= 0 && row < rows ? first_last + row / group : -1;
-#pragma unroll
-                for (int tt = 0; tt < 2; ++tt)
-                    if (j0 + tt * kTile + n16 > last) s[rt][tt][jj] = -INFINITY;
-            }
+            for (int tt = 0; tt < 2; ++tt)
+                if (j0 + tt * kTile + n16 > last) s[tt][jj] = -INFINITY;
+        }
     }
 }
 
 // Online softmax over the chunk's scores; writes P to the wave's LDS buffer.
-template <int D, int RT, int JJ>
-__device__ inline void softmax_step(WaveState<D, RT>& st, floatx4 (&s)[RT][2], float* __restrict__ plds, int lane) {
-    using C = Cfg<D, RT>;
+template <int D, int R, int JJ>
+__device__ inline void softmax_step(WaveState<D, R>& st, floatx4 (&s)[2], float* __restrict__ plds, int lane) {
+    using C = Cfg<D, R>;
     const int g4 = lane >> 4;
     const int n16 = lane & 15;
-    float mnew[RT][4];
+    float mnew[4];
     bool grow = false;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int jj = 0; jj < JJ; ++jj) {
-            mnew[rt][jj] = row16_max(fmaxf(s[rt][0][jj], s[rt][1][jj]));
-            grow |= mnew[rt][jj] > st.m[rt][jj] + kTau;
-        }
+    for (int jj = 0; jj < JJ; ++jj) {
+        mnew[jj] = row16_max(fmaxf(s[0][jj], s[1][jj]));
+        grow |= mnew[jj] > st.m[jj] + kTau;
+    }
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
         // rows whose maximum did not move get alpha = 1: one straight pass
-        // over the accumulators per row tile, no per-row branches
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            floatx4 alpha = {1.0f, 1.0f, 1.0f, 1.0f};
-#pragma unroll
-            for (int jj = 0; jj < JJ; ++jj) {
-                const bool up = mnew[rt][jj] > st.m[rt][jj];
-                alpha[jj] = up ? fast_exp2(st.m[rt][jj] - mnew[rt][jj]) : 1.0f;
-                st.l[rt][jj] *= alpha[jj];
-                st.m[rt][jj] = up ? mnew[rt][jj] : st.m[rt][jj];
-            }
-#pragma unroll
-            for (int nt = 0; nt < C::NT; ++nt) st.o[rt][nt] *= alpha;
-        }
-    }
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+        // over the accumulators, no per-row branches
+        floatx4 alpha = {1.0f, 1.0f, 1.0f, 1.0f};
 #pragma unroll
         for (int jj = 0; jj < JJ; ++jj) {
-            const float mref = (st.m[rt][jj] == -INFINITY ? 0.0f : st.m[rt][jj]) + kTau;
-            const float p0 = fast_exp2(s[rt][0][jj] - mref);
-            const float p1 = fast_exp2(s[rt][1][jj] - mref);
-            st.l[rt][jj] += p0 + p1;
-            float* prow = plds + (rt * 16 + 4 * g4 + jj) * kPStride;
-            prow[n16] = p0;
-            prow[kTile + n16] = p1;
+            const bool up = mnew[jj] > st.m[jj];
+            alpha[jj] = up ? fast_exp2(st.m[jj] - mnew[jj]) : 1.0f;
+            st.l[jj] *= alpha[jj];
+            st.m[jj] = up ? mnew[jj] : st.m[jj];
         }
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt) st.o[nt] *= alpha;
+    }
+#pragma unroll
+    for (int jj = 0; jj < JJ; ++jj) {
+        const float mref = (st.m[jj] == -INFINITY ? 0.0f : st.m[jj]) + kTau;
+        const float p0 = fast_exp2(s[0][jj] - mref);
+        const float p1 = fast_exp2(s[1][jj] - mref);
+        st.l[jj] += p0 + p1;
+        float* prow = plds + (4 * g4 + jj) * kPStride;
+        prow[n16] = p0;
+        prow[kTile + n16] = p1;
+    }
     lds_fence();
 }
 
-// O += (P * vscale) Vcodes for the chunk.
-template <int D, int RT, bool MASK>
-__device__ inline void pv_step(WaveState<D, RT>& st, const Land& L, const float* __restrict__ plds, int lane) {
-    using C = Cfg<D, RT>;
+// O += (P * vscale) Vcodes for the chunk.  wait(u) / done(u) around the
+// read of V slice u.
+template <int D, int R, bool MASK, class Wait, class Done>
+__device__ inline void pv_step(WaveState<D, R>& st, const Land& L, const float* __restrict__ plds, int lane,
+                               Wait wait, Done done) {
+    using C = Cfg<D, R>;
     const int g4 = lane >> 4;
     const int n16 = lane & 15;
     uint32_t magic = 0x64006400u;
     asm volatile("" : "+v"(magic));          // keep the constant in a VGPR
-    float pf[RT][8];
+    float pf[8];
+    {
+        const float* prow = plds + n16 * kPStride + 8 * g4;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        const float* prow = plds + (rt * 16 + n16) * kPStride + 8 * g4;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pf[rt][i] = prow[i];
+        for (int i = 0; i < 8; ++i) pf[i] = prow[i];
     }
     u32x4 vr;
 #pragma unroll
     for (int b = 0; b < C::NB; ++b) {
-        if ((b & 1) == 0) vr = *reinterpret_cast<const u32x4*>(L.v + (b / 2) * 1024 + lane * 16);
+        if ((b & 1) == 0) {
+            const int u = b / 2;
+            wait(u);
+            vr = *reinterpret_cast<const u32x4*>(L.ring + ((2 * C::KL + u) % R) * 1024 + lane * 16);
+            done(u);
+        }
         // V scales of the lane's 8 tokens (8*g4 .. 8*g4+7) for block b
         const half8 sc = *reinterpret_cast<const half8*>(L.vs + (b * kChunk + 8 * g4) * 2);
         // P' = p * vscale: one fused fp32 multiply rounded once to fp16
-        half8 a[RT];
+        half8 a;
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                float x0 = fmaf(pf[rt][k], (float)sc[k], 0.0f);
-                float x1 = fmaf(pf[rt][k + 4], (float)sc[k + 4], 0.0f);
-                if (MASK) {             // masked keys may hold unwritten scales
-                    x0 = pf[rt][k] == 0.0f ? 0.0f : x0;
-                    x1 = pf[rt][k + 4] == 0.0f ? 0.0f : x1;
-                }
-                a[rt][2 * k] = (_Float16)x0;
-                a[rt][2 * k + 1] = (_Float16)x1;
+        for (int k = 0; k < 4; ++k) {
+            float x0 = fmaf(pf[k], (float)sc[k], 0.0f);
+            float x1 = fmaf(pf[k + 4], (float)sc[k + 4], 0.0f);
+            if (MASK) {             // masked keys may hold unwritten scales
+                x0 = pf[k] == 0.0f ? 0.0f : x0;
+                x1 = pf[k + 4] == 0.0f ? 0.0f : x1;
             }
+            a[2 * k] = (_Float16)x0;
+            a[2 * k + 1] = (_Float16)x1;
+        }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int nt = 2 * b + h;
             const half8 bv = v_codes_to_half(vr[nt % 4], magic);
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-                st.o[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[rt], bv, st.o[rt][nt], 0, 0, 0);
+            st.o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bv, st.o[nt], 0, 0, 0);
         }
         SCHED_FENCE();
     }
 }
 
-template <int D, int RT, int JJ, int RG>
-__global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_stream_kernel(AttnArgs a, int cps, int n_splits,
-                                                                           int group, int rows) {
-    using C = Cfg<D, RT>;
+// Runs vm_wait<Waits::qk(p)> (or pv) for a p known only after unrolling.
+template <class WT, int P = 0>
+__device__ inline void wait_qk(int p) {
+    if constexpr (P < WT::NP / 3) {
+        if (p == P) { vm_wait<WT::qk(P)>(); return; }
+        wait_qk<WT, P + 1>(p);
+    }
+}
+template <class WT, int P = 0>
+__device__ inline void wait_pv(int p) {
+    if constexpr (P < WT::NP / 3) {
+        if (p == P) { vm_wait<WT::pv(P)>(); return; }
+        wait_pv<WT, P + 1>(p);
+    }
+}
+
+template <int D, int JJ, int RG, int R>
+__global__ __launch_bounds__(512) void attn_mfma_stream_kernel(AttnArgs a, int cps, int n_splits, int group,
+                                                               int rows) {
+    using C = Cfg<D, R>;
+    using WT = Waits<C::KL, R>;
     constexpr int W = C::W;
-    // RG row groups of RT*16 rows; the WPG waves of group gi share its rows
-    // and deal its chunks among themselves.  Every group streams the same
+    static_assert(W * 64 == 512, "launch bounds");
+    // RG row groups of 16 rows; the WPG waves of group gi share its rows and
+    // deal its chunks among themselves.  Every group streams the same
     // chunks, so a chunk read by a second group mostly comes from L2.
     constexpr int WPG = W / RG;
-    static_assert(RG == 1 || RT == 1, "row groups take one row tile per wave");
     extern __shared__ __align__(16) uint8_t smem[];
     const Geom& g = a.g;
     const int lane = threadIdx.x & 63;
@@ -397,20 +427,17 @@ __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_stream_kernel(AttnA
     const int total_chunks = (a.ctx + kChunk - 1) / kChunk;
     const int first_last = a.ctx - a.n_q;             // last key of query 0
 
-    // LDS: [Q hi/lo | per wave: landing zone + P buffer] (reused by the final
-    // combine) | [m, l per wave and row]
-    half8* qlds = reinterpret_cast<half8*>(smem);
-    uint8_t* wbase = smem + C::Q_BYTES + wave * C::WAVE_BYTES;
-    const Land land = {wbase, wbase + C::LAND_K, wbase + C::LAND_K + C::LAND_KS,
-                       wbase + C::LAND_K + C::LAND_KS + C::LAND_V};
-    float* plds = reinterpret_cast<float*>(wbase + C::LAND_K + C::LAND_KS + C::LAND_V + C::LAND_VS);
-    float* mls = reinterpret_cast<float*>(smem + C::MAIN_BYTES);     // [wave][RT*16][2]
+    // LDS: [per wave: ring + scales + P buffer] (reused by the final combine)
+    // | [m, l per wave and row]
+    uint8_t* wbase = smem + wave * C::WAVE_BYTES;
+    const Land land = {wbase, wbase + C::RING, wbase + C::RING + C::LAND_KS};
+    float* plds = reinterpret_cast<float*>(wbase + C::RING + C::LAND_KS + C::LAND_VS);
+    float* mls = reinterpret_cast<float*>(smem + C::MAIN_BYTES);     // [wave][16][2]
 
-    // ---- this wave's chunks: wave g of the KV head takes chunks g, g + N,
-    // g + 2N, ... (N waves per head), so all waves sweep the context together
-    // and the addresses in flight at any time stay close (better DRAM and
-    // translation locality than one contiguous run per wave).  Start the
-    // first loads before staging q.
+    // ---- this wave's chunks: wave g of a row group takes the group's chunks
+    // g, g + N, g + 2N, ... (N waves per group and KV head), so all waves
+    // sweep the context together and the addresses in flight at any time
+    // stay close.
     const int gi = wave / WPG, wig = wave % WPG;
     const int stride = n_splits * WPG;
     const int c0 = split * WPG + wig;
@@ -419,7 +446,7 @@ __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_stream_kernel(AttnA
     // Page-table entries: lane k of `ents` holds the entry of the wave's
     // chunk number kb + k (batches of 64, one gather load per batch), and the
     // loop picks them out with readlane -- no memory access, hence no wait,
-    // between the K/V requests in flight.
+    // between the requests in flight.
     auto load_ents = [&](int kb) -> int {
         const int ck = c0 + (kb + lane) * stride;
         return ck < c1 ? a.page_table[(ck * kChunk) / g.P] : -1;
@@ -430,21 +457,24 @@ __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_stream_kernel(AttnA
     };
     int ents = load_ents(0);
     bool ok_cur = false;
+    const uint8_t* u_cur = nullptr;
     if (c0 < c1) {
-        const uint8_t* u0 = unit_at(__builtin_amdgcn_readlane(ents, 0), ok_cur);
+        u_cur = unit_at(__builtin_amdgcn_readlane(ents, 0), ok_cur);
         if (ok_cur) {
-            issue_k<D, RT>(land, u0, g, (c0 * kChunk) % g.P, lane);
-            issue_v<D, RT>(land, u0, g, (c0 * kChunk) % g.P, lane);
+            const int slot0 = (c0 * kChunk) % g.P;
+            issue_kscales<D, R>(land, u_cur, g, slot0, lane);
+            issue_vscales<D, R>(land, u_cur, g, slot0, lane);
+#pragma unroll
+            for (int j = 0; j < R; ++j) issue_piece<D, R>(land, u_cur, g, slot0, j, lane);
         }
     }
 
-    // ---- q as fp16 hi/lo in the MFMA A layout, pre-scaled by scale*log2(e):
-    // one row tile per wave is loaded straight into the wave's registers
-    // (lane l: row of MFMA row l % 16, dims 8 (l / 16) .. +7 of each block);
-    // several row tiles are staged in LDS and read per block.
+    // ---- q as fp16 hi/lo in the MFMA A layout, pre-scaled by scale*log2(e),
+    // straight into the wave's registers (lane l: the row at MFMA row l % 16,
+    // dims 8 (l / 16) .. +7 of each block)
     const float qscale = a.scale * kLog2e;
     half8 qreg[C::NB][2];
-    if (RT == 1) {
+    {
         const int row = logical_row<JJ>(gi, lane & 15);
         const bool ok = row >= 0 && row < rows;
         const int qi = ok ? row / group : 0, h = kvh * group + (ok ? row % group : 0);
@@ -458,42 +488,16 @@ __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_stream_kernel(AttnA
                 qreg[b][0][i] = (_Float16)x;
                 qreg[b][1][i] = (_Float16)(x - (float)qreg[b][0][i]);
             }
-    } else {
-        for (int e = threadIdx.x; e < RT * C::NB * 64; e += W * 64) {
-            const int l = e & 63, rb = e >> 6, b = rb % C::NB, rt = rb / C::NB;
-            const int row = logical_row<JJ>(rt, l & 15);
-            half8 hi, lo;
-            if (row >= 0 && row < rows) {
-                const int qi = row / group, h = kvh * group + row % group;
-                const float* src = a.q + ((size_t)qi * a.n_heads + h) * D + b * kBlock + 8 * (l >> 4);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float x = src[i] * qscale;
-                    hi[i] = (_Float16)x;
-                    lo[i] = (_Float16)(x - (float)hi[i]);
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) { hi[i] = (_Float16)0.0f; lo[i] = (_Float16)0.0f; }
-            }
-            qlds[(rb * 2 + 0) * 64 + l] = hi;
-            qlds[(rb * 2 + 1) * 64 + l] = lo;
-        }
-        __syncthreads();
     }
 
-    WaveState<D, RT> st;
+    WaveState<D, R> st;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
+    for (int jj = 0; jj < 4; ++jj) { st.m[jj] = -INFINITY; st.l[jj] = 0.0f; }
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) { st.m[rt][jj] = -INFINITY; st.l[rt][jj] = 0.0f; }
-#pragma unroll
-        for (int nt = 0; nt < C::NT; ++nt) st.o[rt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int nt = 0; nt < C::NT; ++nt) st.o[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    // ---- stream: K(c+1) is requested after QK(c), V(c+1) after PV(c).  A
-    // page-table entry outside the pool stops the wave (nothing is loaded
-    // from it) and turns its partial into NaN.
+    // ---- stream.  A page-table entry outside the pool stops the wave
+    // (nothing is loaded from it) and turns its partial into NaN.
     bool bad = c0 < c1 && !ok_cur;
     for (int c = c0, k = 0; c < c1 && !bad; c += stride, ++k) {
         const int j0 = c * kChunk;
@@ -504,79 +508,95 @@ __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_stream_kernel(AttnA
             asm volatile("" : "+v"(ents));      // consume it here, so the loop's other path has nothing to wait for
         }
         bool ok_next = false;
-        const uint8_t* u_next = has_next ? unit_at(__builtin_amdgcn_readlane(ents, (k + 1) & 63), ok_next) : nullptr;
-        const int slot_next = ((c + stride) * kChunk) % g.P;
-        floatx4 s[RT][2];
-        vm_wait<C::V_ISSUES>();                 // K(c) landed (V(c) may still fly)
-        if (mask) qk_step<D, RT, JJ, true>(s, land, qlds, qreg, lane, j0, first_last, group, rows, gi);
-        else qk_step<D, RT, JJ, false>(s, land, qlds, qreg, lane, j0, first_last, group, rows, gi);
-        lds_fence();                            // K(c) read out: the zone is free
-        if (ok_next) issue_k<D, RT>(land, u_next, g, slot_next, lane);
-        softmax_step<D, RT, JJ>(st, s, plds, lane);
-        if (ok_next) vm_wait<C::K_ISSUES>(); else vm_wait<0>();   // V(c) landed
-        if (mask) pv_step<D, RT, true>(st, land, plds, lane);
-        else pv_step<D, RT, false>(st, land, plds, lane);
-        lds_fence();                            // V(c) read out
-        if (ok_next) issue_v<D, RT>(land, u_next, g, slot_next, lane);
-        if (c + stride < c1 && !ok_next) bad = true;
+        const uint8_t* u_next = has_next ? unit_at(__builtin_amdgcn_readlane(ents, (k + 1) & 63), ok_next) : u_cur;
+        const bool more = has_next && ok_next;  // requests for the next chunk go out in this iteration
+        const bool first = k == 0;
+        const int slot_cur = (c * kChunk) % g.P, slot_next = ((c + stride) * kChunk) % g.P;
+        // consuming piece J requests piece J + R: of this chunk, or of the next
+        auto refill = [&](int J) {
+            const int jn = J + R;
+            if (jn < C::NP) issue_piece<D, R>(land, u_cur, g, slot_cur, jn, lane);
+            else if (more) issue_piece<D, R>(land, u_next, g, slot_next, jn - C::NP, lane);
+        };
+        auto qk_wait = [&](int p) {
+            if (!more || (first && p == 0)) vm_wait<0>();
+            else wait_qk<WT>(p);
+        };
+        auto qk_done = [&](int p) {
+            lds_fence();                        // slice p read out: its slots are free
+            refill(2 * p);
+            refill(2 * p + 1);
+        };
+        auto pv_wait = [&](int u) {
+            if (!more) vm_wait<0>();
+            else wait_pv<WT>(u);
+        };
+        auto pv_done = [&](int u) {
+            lds_fence();
+            refill(2 * C::KL + u);
+        };
+        floatx4 s[2];
+        if (mask) qk_step<D, R, JJ, true>(s, land, qreg, lane, j0, first_last, group, rows, gi, qk_wait, qk_done);
+        else qk_step<D, R, JJ, false>(s, land, qreg, lane, j0, first_last, group, rows, gi, qk_wait, qk_done);
+        lds_fence();                            // K scales read out
+        if (more) issue_kscales<D, R>(land, u_next, g, slot_next, lane);
+        softmax_step<D, R, JJ>(st, s, plds, lane);
+        if (mask) pv_step<D, R, true>(st, land, plds, lane, pv_wait, pv_done);
+        else pv_step<D, R, false>(st, land, plds, lane, pv_wait, pv_done);
+        lds_fence();                            // V scales read out
+        if (more) issue_vscales<D, R>(land, u_next, g, slot_next, lane);
+        if (has_next && !ok_next) bad = true;
+        u_cur = u_next;
     }
     vm_wait<0>();
 
-    // ---- finish the row sums, combine the W waves in a fixed order
+    // ---- finish the row sums, combine the group's waves in a fixed order
     const int g4 = lane >> 4, n16 = lane & 15;
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int jj = 0; jj < JJ; ++jj) {
-            st.l[rt][jj] = row16_sum(st.l[rt][jj]) * 16.0f;        // weights carried 2^-kTau
-            if (bad) { st.m[rt][jj] = NAN; st.l[rt][jj] = NAN; }
-            if (n16 == 0) {
-                const int row = 16 * rt + 4 * g4 + jj;
-                mls[(wave * RT * 16 + row) * 2 + 0] = st.m[rt][jj];
-                mls[(wave * RT * 16 + row) * 2 + 1] = st.l[rt][jj];
-            }
+    for (int jj = 0; jj < JJ; ++jj) {
+        st.l[jj] = row16_sum(st.l[jj]) * 16.0f;        // weights carried 2^-kTau
+        if (bad) { st.m[jj] = NAN; st.l[jj] = NAN; }
+        if (n16 == 0) {
+            const int row = 4 * g4 + jj;
+            mls[(wave * 16 + row) * 2 + 0] = st.m[jj];
+            mls[(wave * 16 + row) * 2 + 1] = st.l[jj];
         }
+    }
     __syncthreads();                       // every wave is done with its landing zone
-    float M[RT][4], Ltot[RT][4];
+    float M[4], Ltot[4];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
+    for (int jj = 0; jj < JJ; ++jj) {
+        const int row = 4 * g4 + jj;
+        float mm = -INFINITY;
 #pragma unroll
-        for (int jj = 0; jj < JJ; ++jj) {
-            const int row = 16 * rt + 4 * g4 + jj;
-            float mm = -INFINITY;
+        for (int j = 0; j < WPG; ++j) mm = fmaxf(mm, mls[((gi * WPG + j) * 16 + row) * 2]);
+        float lt = 0.0f;
 #pragma unroll
-            for (int j = 0; j < WPG; ++j) mm = fmaxf(mm, mls[((gi * WPG + j) * RT * 16 + row) * 2]);
-            float lt = 0.0f;
-#pragma unroll
-            for (int j = 0; j < WPG; ++j) {
-                const int w = gi * WPG + j;
-                const float mw = mls[(w * RT * 16 + row) * 2], lw = mls[(w * RT * 16 + row) * 2 + 1];
-                lt += lw == 0.0f ? 0.0f : lw * exp2f(mw - mm);
-            }
-            M[rt][jj] = mm;
-            Ltot[rt][jj] = lt;
-            const float f = st.l[rt][jj] == 0.0f ? 0.0f : exp2f(st.m[rt][jj] - mm);
-#pragma unroll
-            for (int nt = 0; nt < C::NT; ++nt) st.o[rt][nt][jj] *= f;
+        for (int j = 0; j < WPG; ++j) {
+            const int w = gi * WPG + j;
+            const float mw = mls[(w * 16 + row) * 2], lw = mls[(w * 16 + row) * 2 + 1];
+            lt += lw == 0.0f ? 0.0f : lw * exp2f(mw - mm);
         }
-    float* ob = reinterpret_cast<float*>(smem);          // [W/2][RT*16][D]
+        M[jj] = mm;
+        Ltot[jj] = lt;
+        const float f = st.l[jj] == 0.0f ? 0.0f : exp2f(st.m[jj] - mm);
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt) st.o[nt][jj] *= f;
+    }
+    float* ob = reinterpret_cast<float*>(smem);          // [W/2][16][D]
     auto put = [&](int slot) {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
+        for (int nt = 0; nt < C::NT; ++nt)
 #pragma unroll
-            for (int nt = 0; nt < C::NT; ++nt)
-#pragma unroll
-                for (int jj = 0; jj < JJ; ++jj)
-                    ob[((size_t)slot * RT * 16 + 16 * rt + 4 * g4 + jj) * D + 16 * nt + n16] = st.o[rt][nt][jj];
+            for (int jj = 0; jj < JJ; ++jj)
+                ob[((size_t)slot * 16 + 4 * g4 + jj) * D + 16 * nt + n16] = st.o[nt][jj];
     };
     auto add = [&](int slot) {
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
+        for (int nt = 0; nt < C::NT; ++nt)
 #pragma unroll
-            for (int nt = 0; nt < C::NT; ++nt)
-#pragma unroll
-                for (int jj = 0; jj < JJ; ++jj)
-                    st.o[rt][nt][jj] += ob[((size_t)slot * RT * 16 + 16 * rt + 4 * g4 + jj) * D + 16 * nt + n16];
+            for (int jj = 0; jj < JJ; ++jj)
+                st.o[nt][jj] += ob[((size_t)slot * 16 + 4 * g4 + jj) * D + 16 * nt + n16];
     };
     // tree inside each row group: waves [h, 2h) of the group hand their sums
     // to waves [0, h), h = WPG/2 .. 1; group gi uses buffer slots
@@ -590,28 +610,27 @@ __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_stream_kernel(AttnA
     }
     if (wig != 0) return;
 
-    // ---- write the partial of each row this workgroup serves
+    // ---- write the partial of each row this row group serves
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int jj = 0; jj < JJ; ++jj) {
-            const int row = logical_row<JJ>(gi + rt, 4 * g4 + jj);
-            if (row < 0 || row >= rows) continue;
-            const int qi = row / group, h = kvh * group + row % group;
-            const size_t ps = ((size_t)qi * a.n_heads + h) * n_splits + split;
-            if (n16 == 0) {
-                a.ws_m[ps] = M[rt][jj];
-                a.ws_l[ps] = Ltot[rt][jj];
-            }
-#pragma unroll
-            for (int nt = 0; nt < C::NT; ++nt) a.ws_acc[ps * D + 16 * nt + n16] = st.o[rt][nt][jj];
+    for (int jj = 0; jj < JJ; ++jj) {
+        const int row = logical_row<JJ>(gi, 4 * g4 + jj);
+        if (row < 0 || row >= rows) continue;
+        const int qi = row / group, h = kvh * group + row % group;
+        const size_t ps = ((size_t)qi * a.n_heads + h) * n_splits + split;
+        if (n16 == 0) {
+            a.ws_m[ps] = M[jj];
+            a.ws_l[ps] = Ltot[jj];
         }
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt) a.ws_acc[ps * D + 16 * nt + n16] = st.o[nt][jj];
+    }
 }
 
-template <int D, int RT, int JJ, int RG>
+template <int D, int JJ, int RG>
 hipError_t launch_dr(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) {
-    using C = Cfg<D, RT>;
-    auto kern = attn_mfma_stream_kernel<D, RT, JJ, RG>;
+    constexpr int R = D == 64 ? 3 : D == 128 ? 3 : 4;   // ring slots: a few KiB in flight per wave
+    using C = Cfg<D, R>;
+    auto kern = attn_mfma_stream_kernel<D, JJ, RG, R>;
     if (C::LDS_BYTES > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
@@ -623,14 +642,14 @@ hipError_t launch_dr(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) 
     return hipGetLastError();
 }
 
-// One row tile per wave: up to 8 rows two per lane group (JJ = 2), up to
-// 16 rows one per MFMA row, more rows in 2 or 4 row groups.
+// Up to 8 rows two per lane group (JJ = 2), up to 16 rows one per MFMA row,
+// more rows in 2 or 4 row groups of 16.
 template <int D>
 hipError_t launch_d(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) {
-    if (pl.rows <= 8) return launch_dr<D, 1, 2, 1>(a, pl, stream);
-    if (pl.rows <= 16) return launch_dr<D, 1, 4, 1>(a, pl, stream);
-    if (pl.rows <= 32) return launch_dr<D, 1, 4, 2>(a, pl, stream);
-    if (pl.rows <= 64) return launch_dr<D, 1, 4, 4>(a, pl, stream);
+    if (pl.rows <= 8) return launch_dr<D, 2, 1>(a, pl, stream);
+    if (pl.rows <= 16) return launch_dr<D, 4, 1>(a, pl, stream);
+    if (pl.rows <= 32) return launch_dr<D, 4, 2>(a, pl, stream);
+    if (pl.rows <= 64) return launch_dr<D, 4, 4>(a, pl, stream);
     return hipErrorInvalidValue;
 }
 
