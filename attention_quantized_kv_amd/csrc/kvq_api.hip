@@ -39,8 +39,17 @@ int check_layout(const kvq_layout* L, kvq::Geom* g) {
     return KVQ_OK;
 }
 
-// Split heuristic: enough independent wavefronts to cover 256 CUs several
-// times over, with partials small next to the cache bytes.
+// Compute units of the current device (256 on an MI355X).
+int device_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+        cus = 256;
+    return cus;
+}
+
+// Split heuristic: enough independent wavefronts to cover the CUs, with
+// partials small next to the cache bytes.
 int auto_chunks_per_split(int kernel, int total_chunks, int n_kv, int n_q, int rows) {
     long units = (long)total_chunks * n_kv;
     if (kernel == 1) {
@@ -49,9 +58,14 @@ int auto_chunks_per_split(int kernel, int total_chunks, int n_kv, int n_q, int r
         return (int)(per < 1 ? 1 : per);
     }
     if (kernel == 2) {
-        // ~2048 waves: every row group of a workgroup streams the split's
-        // chunks, so a chunk costs one wave per row group
-        long per = units * kvq::mfma_stream_row_groups(rows) / 2048;
+        // one 8-wave workgroup fits a CU (registers): at most one workgroup
+        // per CU and KV head-split, so that all run in a single round; each
+        // wave of a row group takes cps chunks of its split
+        const long cus = device_cus();
+        long splits = cus / n_kv;
+        if (splits < 1) splits = 1;
+        const long wpg = kvq::mfma_stream_waves(rows);
+        long per = ((long)total_chunks + wpg * splits - 1) / (wpg * splits);
         return (int)(per < 1 ? 1 : per);
     }
     // LDS-tiled chunk kernel: a workgroup per (row tile, KV head, split);
