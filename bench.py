@@ -102,13 +102,15 @@ class Layer:
     def append(self):
         self.kvq.kvq_append(self.L, self.pool, self.pt, self.w.cached, self.k_new, self.v_new)
 
+    cps = 0
+
     def attend(self, ws, kernel, events=None):
         """kvq_attn_ex with the automatic plan (kernel 0: the same choice as
         kvq_decode_attn / kvq_prefill_attn) or a forced kernel; `events`
         (begin, end) are recorded by the library around the attention kernel
         itself, excluding the split merge."""
         self.kvq.kvq_attn_ex(self.L, self.pool, self.pt, self.w.ctx, self.q, self.w.scale, self.out, self.lse,
-                             ws, kernel=kernel, events=events)
+                             ws, kernel=kernel, chunks_per_split=self.cps, events=events)
 
 
 KERNEL_SOURCES = {"attn_mfma_stream": "attn_mfma_stream.hip", "attn_mfma_tiled": "attn_mfma_tiled.hip",
@@ -197,6 +199,7 @@ def main():
                     choices=["tiny", "decode65k", "decode262k", "verify131k", "prefill262k"])
     ap.add_argument("--layers", type=int, default=None, help="layers in the stack (default: the workload's)")
     ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA streaming, 3 MFMA tiled")
+    ap.add_argument("--cps", type=int, default=0, help="32-token chunks per split (0: the library's choice)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--shuffle-pages", action="store_true",
@@ -237,8 +240,8 @@ def main():
 
     t0 = time.time()
     layers = [Layer(w, i, dev, shuffle_pages=args.shuffle_pages) for i in range(n_layers)]
-    ws_n = kvq.kvq_workspace_bytes_ex(layers[0].L, w.n_heads, w.ctx, w.n_q, args.kernel, 0) if args.kernel \
-        else kvq.kvq_workspace_bytes(layers[0].L, w.n_heads, w.ctx, w.n_q, prefill)
+    Layer.cps = args.cps
+    ws_n = kvq.kvq_workspace_bytes_ex(layers[0].L, w.n_heads, w.ctx, w.n_q, args.kernel, args.cps)
     ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     print(f"[bench] {w.name}: {n_layers} layers filled in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
@@ -284,6 +287,7 @@ def main():
         "config": {"workload": w.name, "layers": n_layers, "n_heads": w.n_heads, "n_kv_heads": w.n_kv,
                    "head_dim": w.head_dim, "ctx": w.ctx, "n_q": w.n_q, "page_size": w.page_size,
                    "kv_format": "K Q8_0 + V Q4_0", "kernel": args.kernel or "auto",
+                   "chunks_per_split": args.cps or "auto",
                    "page_table": "shuffled" if args.shuffle_pages else "in order"},
     }
     if not prefill:
