@@ -41,6 +41,8 @@
 // and one partial per workgroup is written.
 #include <hip/hip_fp16.h>
 
+#include <type_traits>
+
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -78,14 +80,29 @@ __device__ inline float dpp(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
+// max(x, x of the lane that DPP control CTRL names), one v_max_f32_dpp (the
+// builtin route adds a move and a NaN-quieting max per step).  s_nop 1 covers
+// the two wait states a DPP read needs after the VALU write of its source.
+#define KVQ_MAX_DPP(CTRL)                                                                  \
+    __device__ inline float max_dpp_##CTRL(float x) {                                     \
+        float r;                                                                          \
+        asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 " KVQ_DPP_##CTRL " row_mask:0xf bank_mask:0xf" \
+            : "=v"(r) : "v"(x));                                                          \
+        return r;                                                                         \
+    }
+#define KVQ_DPP_ror8 "row_ror:8"
+#define KVQ_DPP_ror4 "row_ror:4"
+#define KVQ_DPP_swap2 "quad_perm:[2,3,0,1]"
+#define KVQ_DPP_swap1 "quad_perm:[1,0,3,2]"
+KVQ_MAX_DPP(ror8)
+KVQ_MAX_DPP(ror4)
+KVQ_MAX_DPP(swap2)
+KVQ_MAX_DPP(swap1)
+
 // Reductions over the 16 lanes of a DPP row (rotate by 8, by 4, then swap
 // pairs inside quads): every lane ends with the row's result.
 __device__ inline float row16_max(float x) {
-    x = fmaxf(x, dpp<0x128>(x));
-    x = fmaxf(x, dpp<0x124>(x));
-    x = fmaxf(x, dpp<0x4E>(x));
-    x = fmaxf(x, dpp<0xB1>(x));
-    return x;
+    return max_dpp_swap1(max_dpp_swap2(max_dpp_ror4(max_dpp_ror8(x))));
 }
 __device__ inline float row16_sum(float x) {
     x += dpp<0x128>(x);
@@ -177,8 +194,9 @@ struct Cfg {
 // chunk's V scales.  Piece J of chunk k was requested when piece J-R was
 // consumed, so the number of requests issued after it by the time it is
 // consumed is fixed; s_waitcnt vmcnt(that count) guarantees it has landed
-// (requests complete in order).  The first chunk waits for everything once,
-// the last chunk (nothing further requested) waits with 0.
+// (requests complete in order).  The first chunk's requests go out in the
+// same order before the loop, so it uses the same counts; the last chunk
+// (nothing further requested) waits with 0.
 template <int KL, int R>
 struct Waits {
     static constexpr int NP = 3 * KL, NI = 3 * KL + 2;
@@ -203,18 +221,30 @@ struct Land {
     uint8_t* vs;    // [NB][32 tokens] fp16 (then repeats)
 };
 
-// Requests code piece j of a chunk (slot0 = its first slot in the page) into
-// ring slot j % R.  Full-wave request (see the scale pieces below).
+// Where one chunk's data sits in the pool: the start of its K code tiles, V
+// code chunk, K scales and V scales (unit base + region offset + the chunk's
+// first slot times the bytes per slot of that region).
+struct ChunkPtr {
+    const uint8_t* k;
+    const uint8_t* v;
+    const uint8_t* ks;
+    const uint8_t* vs;
+};
+template <int D>
+__device__ inline ChunkPtr chunk_ptr(const uint8_t* unit, const Geom& g, int slot0) {
+    constexpr int NB = D / kBlock;
+    return {unit + (uint32_t)slot0 * D, unit + g.v_codes_off() + (uint32_t)slot0 * (D / 2),
+            unit + g.k_scales_off() + (uint32_t)slot0 * (2 * NB), unit + g.v_scales_off() + (uint32_t)slot0 * (2 * NB)};
+}
+
+// Requests code piece j of a chunk into ring slot j % R.  Full-wave request
+// (see the scale pieces below).
 template <int D, int R>
-__device__ inline void issue_piece(const Land& L, const uint8_t* unit, const Geom& g, int slot0, int j, int lane) {
+__device__ inline void issue_piece(const Land& L, const ChunkPtr& cp, int j, int lane) {
     using C = Cfg<D, R>;
     const uint8_t* src;
-    if (j < 2 * C::KL) {
-        const int p = j / 2, tt = j % 2;
-        src = unit + (int64_t)(slot0 / kTile + tt) * kTile * D + p * 1024 + lane * 16;
-    } else {
-        src = unit + g.v_codes_off() + (int64_t)(slot0 / kChunk) * kChunk * D / 2 + (j - 2 * C::KL) * 1024 + lane * 16;
-    }
+    if (j < 2 * C::KL) src = cp.k + (j % 2) * kTile * D + (j / 2) * 1024 + lane * 16;
+    else src = cp.v + (j - 2 * C::KL) * 1024 + lane * 16;
     dma16(src, L.ring + (j % R) * 1024);
 }
 
@@ -222,15 +252,14 @@ __device__ inline void issue_piece(const Land& L, const uint8_t* unit, const Geo
 // (lanes past 4*NB repeat a piece): a direct-to-LDS load under a
 // lane-dependent branch can get its LDS base merged with a neighbouring one's.
 template <int D, int R>
-__device__ inline void issue_kscales(const Land& L, const uint8_t* unit, const Geom& g, int slot0, int lane) {
+__device__ inline void issue_kscales(const Land& L, const ChunkPtr& cp, int lane) {
     using C = Cfg<D, R>;
-    dma16(unit + g.k_scales_off() + (int64_t)slot0 * C::NB * 2 + (lane % (4 * C::NB)) * 16, L.ks);
+    dma16(cp.ks + (lane % (4 * C::NB)) * 16, L.ks);
 }
 template <int D, int R>
-__device__ inline void issue_vscales(const Land& L, const uint8_t* unit, const Geom& g, int slot0, int lane) {
+__device__ inline void issue_vscales(const Land& L, const ChunkPtr& cp, int lane) {
     using C = Cfg<D, R>;
-    dma16(unit + g.v_scales_off() + (int64_t)(slot0 / kChunk) * C::NB * kChunk * 2 + (lane % (4 * C::NB)) * 16,
-          L.vs);
+    dma16(cp.vs + (lane % (4 * C::NB)) * 16, L.vs);
 }
 
 template <int D, int R>
@@ -456,16 +485,27 @@ __global__ __launch_bounds__(512) void attn_mfma_stream_kernel(AttnArgs a, int c
         return a.pool + g.unit_index(ok ? phys : 0, kvh) * g.unit_bytes();
     };
     int ents = load_ents(0);
+    // first slot of the current chunk in its page; it advances by dslot (mod P)
+    // from one chunk of the wave to the next
+    int slot_cur = (c0 * kChunk) % g.P;
+    const int dslot = (stride * kChunk) % g.P;
     bool ok_cur = false;
     const uint8_t* u_cur = nullptr;
     if (c0 < c1) {
         u_cur = unit_at(__builtin_amdgcn_readlane(ents, 0), ok_cur);
         if (ok_cur) {
-            const int slot0 = (c0 * kChunk) % g.P;
-            issue_kscales<D, R>(land, u_cur, g, slot0, lane);
-            issue_vscales<D, R>(land, u_cur, g, slot0, lane);
+            // the first chunk's requests in the order a previous chunk would
+            // have issued them (refills of pieces NP-R.., K scales after the QK
+            // slices, V scales last), so the steady-state wait counts hold
+            const ChunkPtr cp = chunk_ptr<D>(u_cur, g, slot_cur);
 #pragma unroll
-            for (int j = 0; j < R; ++j) issue_piece<D, R>(land, u_cur, g, slot0, j, lane);
+            for (int J = 0; J < 2 * C::KL; ++J)
+                if (J + R >= C::NP) issue_piece<D, R>(land, cp, J + R - C::NP, lane);
+            issue_kscales<D, R>(land, cp, lane);
+#pragma unroll
+            for (int J = 2 * C::KL; J < C::NP; ++J)
+                if (J + R >= C::NP) issue_piece<D, R>(land, cp, J + R - C::NP, lane);
+            issue_vscales<D, R>(land, cp, lane);
         }
     }
 
@@ -499,9 +539,11 @@ __global__ __launch_bounds__(512) void attn_mfma_stream_kernel(AttnArgs a, int c
     // ---- stream.  A page-table entry outside the pool stops the wave
     // (nothing is loaded from it) and turns its partial into NaN.
     bool bad = c0 < c1 && !ok_cur;
-    for (int c = c0, k = 0; c < c1 && !bad; c += stride, ++k) {
+    int c = c0, k = 0;
+    // one chunk: MASK when some key of it lies past the last key of some row
+    auto chunk = [&](auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
         const int j0 = c * kChunk;
-        const bool mask = j0 + kChunk - 1 > first_last;
         const bool has_next = c + stride < c1;
         if (has_next && ((k + 1) & 63) == 0) {  // every 64 chunks
             ents = load_ents(k + 1);
@@ -510,16 +552,16 @@ __global__ __launch_bounds__(512) void attn_mfma_stream_kernel(AttnArgs a, int c
         bool ok_next = false;
         const uint8_t* u_next = has_next ? unit_at(__builtin_amdgcn_readlane(ents, (k + 1) & 63), ok_next) : u_cur;
         const bool more = has_next && ok_next;  // requests for the next chunk go out in this iteration
-        const bool first = k == 0;
-        const int slot_cur = (c * kChunk) % g.P, slot_next = ((c + stride) * kChunk) % g.P;
+        const int slot_next = slot_cur + dslot >= g.P ? slot_cur + dslot - g.P : slot_cur + dslot;
+        const ChunkPtr cp = chunk_ptr<D>(u_cur, g, slot_cur), np = chunk_ptr<D>(u_next, g, slot_next);
         // consuming piece J requests piece J + R: of this chunk, or of the next
         auto refill = [&](int J) {
             const int jn = J + R;
-            if (jn < C::NP) issue_piece<D, R>(land, u_cur, g, slot_cur, jn, lane);
-            else if (more) issue_piece<D, R>(land, u_next, g, slot_next, jn - C::NP, lane);
+            if (jn < C::NP) issue_piece<D, R>(land, cp, jn, lane);
+            else if (more) issue_piece<D, R>(land, np, jn - C::NP, lane);
         };
         auto qk_wait = [&](int p) {
-            if (!more || (first && p == 0)) vm_wait<0>();
+            if (!more) vm_wait<0>();
             else wait_qk<WT>(p);
         };
         auto qk_done = [&](int p) {
@@ -536,18 +578,23 @@ __global__ __launch_bounds__(512) void attn_mfma_stream_kernel(AttnArgs a, int c
             refill(2 * C::KL + u);
         };
         floatx4 s[2];
-        if (mask) qk_step<D, R, JJ, true>(s, land, qreg, lane, j0, first_last, group, rows, gi, qk_wait, qk_done);
-        else qk_step<D, R, JJ, false>(s, land, qreg, lane, j0, first_last, group, rows, gi, qk_wait, qk_done);
+        qk_step<D, R, JJ, MASK>(s, land, qreg, lane, j0, first_last, group, rows, gi, qk_wait, qk_done);
         lds_fence();                            // K scales read out
-        if (more) issue_kscales<D, R>(land, u_next, g, slot_next, lane);
+        if (more) issue_kscales<D, R>(land, np, lane);
         softmax_step<D, R, JJ>(st, s, plds, lane);
-        if (mask) pv_step<D, R, true>(st, land, plds, lane, pv_wait, pv_done);
-        else pv_step<D, R, false>(st, land, plds, lane, pv_wait, pv_done);
+        pv_step<D, R, MASK>(st, land, plds, lane, pv_wait, pv_done);
         lds_fence();                            // V scales read out
-        if (more) issue_vscales<D, R>(land, u_next, g, slot_next, lane);
+        if (more) issue_vscales<D, R>(land, np, lane);
         if (has_next && !ok_next) bad = true;
         u_cur = u_next;
-    }
+        slot_cur = slot_next;
+        c += stride;
+        ++k;
+    };
+    // chunks wholly visible to every row first, then the masked ones
+    const int c_mask = first_last >= kChunk - 1 ? (first_last - (kChunk - 1)) / kChunk + 1 : 0;
+    while (c < c1 && c < c_mask && !bad) chunk(std::false_type{});
+    while (c < c1 && !bad) chunk(std::true_type{});
     vm_wait<0>();
 
     // ---- finish the row sums, combine the group's waves in a fixed order
