@@ -119,6 +119,14 @@ __device__ inline float row16_sum(float x) {
 // Waits for this wave's outstanding LDS reads; also a compiler memory fence.
 __device__ inline void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// Workgroup barrier for LDS data only: unlike __syncthreads() it does not wait
+// for the direct-to-LDS loads in flight (the release fence there would).
+__device__ inline void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Waits until at most N vector-memory requests of this wave are outstanding
 // (direct-to-LDS loads count); also a compiler memory fence, since the
 // compiler cannot see that later LDS reads depend on those loads.
@@ -173,7 +181,6 @@ struct Cfg {
     static constexpr int KL = D / 64;           // 64-dim slices (1 KiB pieces per K tile / V chunk)
     static constexpr int NT = D / 16;           // 16-wide output tiles
     static constexpr int NP = 3 * KL;           // code pieces per chunk: K(t0,p), K(t1,p) for each p, then V(u)
-    static constexpr int W = 8;                 // waves per workgroup (two per SIMD)
     static_assert(NP % R == 0 && R <= NP, "ring slots must divide the pieces of a chunk");
     // per-wave LDS: code ring, K scales, V scales, P transpose buffer (bytes)
     static constexpr int RING = R * 1024;
@@ -181,10 +188,25 @@ struct Cfg {
     static constexpr int LAND_VS = 1024;        // NB x 32 fp16, padded likewise
     static constexpr int PBUF = 16 * kPStride * 4;
     static constexpr int WAVE_BYTES = RING + LAND_KS + LAND_VS + PBUF;
-    static constexpr int COMB_BYTES = (W / 2) * 16 * D * 4;
-    static constexpr int MAIN_BYTES = W * WAVE_BYTES > COMB_BYTES ? W * WAVE_BYTES : COMB_BYTES;
-    static constexpr int ML_BYTES = W * 16 * 2 * 4;
-    static constexpr int LDS_BYTES = MAIN_BYTES + ML_BYTES;
+    static constexpr int Q_BYTES = NB * 2 * 1024;   // one row group's q, fp16 hi/lo, MFMA A layout
+};
+
+// Workgroup LDS: W per-wave areas (reused by the final combine) | q of each
+// of the RG row groups | (m, l) per wave and row.  The combine first folds the
+// waves past the largest power of two P2 <= WPG into the first ones, then
+// halves P2 down to one wave; SLOTS partial sums per group are in flight.
+template <int D, int R, int W, int RG>
+struct WgLds {
+    using C = Cfg<D, R>;
+    static constexpr int WPG = W / RG;
+    static constexpr int P2 = WPG >= 8 ? 8 : WPG >= 4 ? 4 : WPG >= 2 ? 2 : 1;
+    static_assert(WPG < 16, "power-of-two fold");
+    static constexpr int SLOTS = (P2 / 2 > WPG - P2 ? P2 / 2 : WPG - P2) > 0 ? (P2 / 2 > WPG - P2 ? P2 / 2 : WPG - P2) : 1;
+    static constexpr int COMB_BYTES = RG * SLOTS * 16 * D * 4;
+    static constexpr int MAIN_BYTES = W * C::WAVE_BYTES > COMB_BYTES ? W * C::WAVE_BYTES : COMB_BYTES;
+    static constexpr int Q_OFF = MAIN_BYTES;
+    static constexpr int ML_OFF = Q_OFF + RG * C::Q_BYTES;
+    static constexpr int BYTES = ML_OFF + W * 16 * 2 * 4;
 };
 
 // Wait counts.  Per chunk a wave issues its requests in a fixed order: the
@@ -274,7 +296,7 @@ struct WaveState {
 // positions past ctx_len).  wait(p) runs before slice p's pieces are read,
 // done(p) after they have been read out of LDS.
 template <int D, int R, int JJ, bool MASK, class Wait, class Done>
-__device__ inline void qk_step(floatx4 (&s)[2], const Land& L, const half8 (&qreg)[Cfg<D, R>::NB][2], int lane,
+__device__ inline void qk_step(floatx4 (&s)[2], const Land& L, const uint8_t* __restrict__ qlds, int lane,
                                int j0, int first_last, int group, int rows, int rt0, Wait wait, Done done) {
     using C = Cfg<D, R>;
     const int g4 = lane >> 4;
@@ -309,10 +331,12 @@ __device__ inline void qk_step(floatx4 (&s)[2], const Land& L, const half8 (&qre
             const half2v sw = as_h2(ksw[tt][b / 2]);
             ksc[tt] = (b & 1) ? (float)sw.y : (float)sw.x;
         }
+        const half8 qh = *reinterpret_cast<const half8*>(qlds + (2 * b) * 1024 + lane * 16);
+        const half8 ql = *reinterpret_cast<const half8*>(qlds + (2 * b + 1) * 1024 + lane * 16);
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-            floatx4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qreg[b][0], kb[tt], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-            c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qreg[b][1], kb[tt], c, 0, 0, 0);
+            floatx4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh, kb[tt], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql, kb[tt], c, 0, 0, 0);
             s[tt] += ksc[tt] * c;
         }
         SCHED_FENCE();
@@ -436,13 +460,12 @@ __device__ inline void wait_pv(int p) {
     }
 }
 
-template <int D, int JJ, int RG, int R>
-__global__ __launch_bounds__(512) void attn_mfma_stream_kernel(AttnArgs a, int cps, int n_splits, int group,
-                                                               int rows) {
+template <int D, int JJ, int RG, int R, int W>
+__global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, int cps, int n_splits, int group,
+                                                                  int rows) {
     using C = Cfg<D, R>;
     using WT = Waits<C::KL, R>;
-    constexpr int W = C::W;
-    static_assert(W * 64 == 512, "launch bounds");
+    using WL = WgLds<D, R, W, RG>;
     // RG row groups of 16 rows; the WPG waves of group gi share its rows and
     // deal its chunks among themselves.  Every group streams the same
     // chunks, so a chunk read by a second group mostly comes from L2.
@@ -457,11 +480,11 @@ __global__ __launch_bounds__(512) void attn_mfma_stream_kernel(AttnArgs a, int c
     const int first_last = a.ctx - a.n_q;             // last key of query 0
 
     // LDS: [per wave: ring + scales + P buffer] (reused by the final combine)
-    // | [m, l per wave and row]
+    // | [q of each row group] | [m, l per wave and row]
     uint8_t* wbase = smem + wave * C::WAVE_BYTES;
     const Land land = {wbase, wbase + C::RING, wbase + C::RING + C::LAND_KS};
     float* plds = reinterpret_cast<float*>(wbase + C::RING + C::LAND_KS + C::LAND_VS);
-    float* mls = reinterpret_cast<float*>(smem + C::MAIN_BYTES);     // [wave][16][2]
+    float* mls = reinterpret_cast<float*>(smem + WL::ML_OFF);        // [wave][16][2]
 
     // ---- this wave's chunks: wave g of a row group takes the group's chunks
     // g, g + N, g + 2N, ... (N waves per group and KV head), so all waves
@@ -484,7 +507,30 @@ __global__ __launch_bounds__(512) void attn_mfma_stream_kernel(AttnArgs a, int c
         ok = phys >= 0 && phys < g.n_pages;
         return a.pool + g.unit_index(ok ? phys : 0, kvh) * g.unit_bytes();
     };
+    // ---- q as fp16 hi/lo in the MFMA A layout, pre-scaled by scale*log2(e),
+    // once per row group in LDS: 1 KiB per (block, hi/lo), lane l's 16 bytes
+    // = the row at MFMA row l % 16, dims 8 (l / 16) .. +7 of the block.  The
+    // group's waves take the blocks round-robin.  The loads go out before the
+    // page-table gather, so both arrive in one round trip.
+    const float qscale = a.scale * kLog2e;
+    const uint8_t* qlds = smem + WL::Q_OFF + gi * C::Q_BYTES;
+    constexpr int QB = (C::NB + WPG - 1) / WPG;      // blocks per wave
+    float qv[QB][8];
+    const int q_row = logical_row<JJ>(gi, lane & 15);
+    const bool q_ok = q_row >= 0 && q_row < rows;
+    {
+        const int qi = q_ok ? q_row / group : 0, h = kvh * group + (q_ok ? q_row % group : 0);
+        const float* src = a.q + ((size_t)qi * a.n_heads + h) * D + 8 * (lane >> 4);
+#pragma unroll
+        for (int i = 0; i < QB; ++i) {
+            const int b = wig + i * WPG < C::NB ? wig + i * WPG : 0;   // waves with no block left reload block 0
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qv[i][e] = src[b * kBlock + e];   // rows past the end read row 0
+        }
+    }
+
     int ents = load_ents(0);
+    asm volatile("" : "+v"(ents));             // wait for it (and q) here, before any chunk request
     // first slot of the current chunk in its page; it advances by dslot (mod P)
     // from one chunk of the wave to the next
     int slot_cur = (c0 * kChunk) % g.P;
@@ -509,26 +555,23 @@ __global__ __launch_bounds__(512) void attn_mfma_stream_kernel(AttnArgs a, int c
         }
     }
 
-    // ---- q as fp16 hi/lo in the MFMA A layout, pre-scaled by scale*log2(e),
-    // straight into the wave's registers (lane l: the row at MFMA row l % 16,
-    // dims 8 (l / 16) .. +7 of each block)
-    const float qscale = a.scale * kLog2e;
-    half8 qreg[C::NB][2];
-    {
-        const int row = logical_row<JJ>(gi, lane & 15);
-        const bool ok = row >= 0 && row < rows;
-        const int qi = ok ? row / group : 0, h = kvh * group + (ok ? row % group : 0);
-        const float* src = a.q + ((size_t)qi * a.n_heads + h) * D + 8 * (lane >> 4);
+    // q into LDS (hi + lo fp16 halves; rows past the end are zero)
 #pragma unroll
-        for (int b = 0; b < C::NB; ++b)
+    for (int i = 0; i < QB; ++i) {
+        const int b = wig + i * WPG;
+        if (b >= C::NB) break;
+        half8 hi, lo;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float v = src[b * kBlock + i];          // in bounds: rows past the end read row 0
-                const float x = ok ? v * qscale : 0.0f;
-                qreg[b][0][i] = (_Float16)x;
-                qreg[b][1][i] = (_Float16)(x - (float)qreg[b][0][i]);
-            }
+        for (int e = 0; e < 8; ++e) {
+            const float x = q_ok ? qv[i][e] * qscale : 0.0f;
+            hi[e] = (_Float16)x;
+            lo[e] = (_Float16)(x - (float)hi[e]);
+        }
+        uint8_t* dst = smem + WL::Q_OFF + gi * C::Q_BYTES + (2 * b) * 1024 + lane * 16;
+        *reinterpret_cast<half8*>(dst) = hi;
+        *reinterpret_cast<half8*>(dst + 1024) = lo;
     }
+    lds_barrier();                             // q visible to the group; the first chunk stays in flight
 
     WaveState<D, R> st;
 #pragma unroll
@@ -578,7 +621,7 @@ __global__ __launch_bounds__(512) void attn_mfma_stream_kernel(AttnArgs a, int c
             refill(2 * C::KL + u);
         };
         floatx4 s[2];
-        qk_step<D, R, JJ, MASK>(s, land, qreg, lane, j0, first_last, group, rows, gi, qk_wait, qk_done);
+        qk_step<D, R, JJ, MASK>(s, land, qlds, lane, j0, first_last, group, rows, gi, qk_wait, qk_done);
         lds_fence();                            // K scales read out
         if (more) issue_kscales<D, R>(land, np, lane);
         softmax_step<D, R, JJ>(st, s, plds, lane);
@@ -630,7 +673,7 @@ __global__ __launch_bounds__(512) void attn_mfma_stream_kernel(AttnArgs a, int c
 #pragma unroll
         for (int nt = 0; nt < C::NT; ++nt) st.o[nt][jj] *= f;
     }
-    float* ob = reinterpret_cast<float*>(smem);          // [W/2][16][D]
+    float* ob = reinterpret_cast<float*>(smem);          // [RG * SLOTS][16][D]
     auto put = [&](int slot) {
 #pragma unroll
         for (int nt = 0; nt < C::NT; ++nt)
@@ -645,14 +688,21 @@ __global__ __launch_bounds__(512) void attn_mfma_stream_kernel(AttnArgs a, int c
             for (int jj = 0; jj < JJ; ++jj)
                 st.o[nt][jj] += ob[((size_t)slot * 16 + 4 * g4 + jj) * D + 16 * nt + n16];
     };
-    // tree inside each row group: waves [h, 2h) of the group hand their sums
-    // to waves [0, h), h = WPG/2 .. 1; group gi uses buffer slots
-    // gi*WPG/2 .. (gi+1)*WPG/2 - 1
-#pragma unroll
-    for (int h = WPG / 2; h >= 1; h /= 2) {
-        if (wig >= h && wig < 2 * h) put(gi * (WPG / 2) + wig - h);
+    // inside each row group: waves [P2, WPG) first hand their sums to waves
+    // [0, WPG - P2), then waves [h, 2h) to waves [0, h) for h = P2/2 .. 1;
+    // group gi uses buffer slots gi*SLOTS .. (gi+1)*SLOTS - 1
+    constexpr int P2 = WL::P2;
+    if constexpr (WPG > P2) {
+        if (wig >= P2) put(gi * WL::SLOTS + wig - P2);
         __syncthreads();
-        if (wig < h) add(gi * (WPG / 2) + wig);
+        if (wig < WPG - P2) add(gi * WL::SLOTS + wig);
+        __syncthreads();
+    }
+#pragma unroll
+    for (int h = P2 / 2; h >= 1; h /= 2) {
+        if (wig >= h && wig < 2 * h) put(gi * WL::SLOTS + wig - h);
+        __syncthreads();
+        if (wig < h) add(gi * WL::SLOTS + wig);
         __syncthreads();
     }
     if (wig != 0) return;
@@ -673,18 +723,25 @@ __global__ __launch_bounds__(512) void attn_mfma_stream_kernel(AttnArgs a, int c
     }
 }
 
+// Waves per workgroup: two per SIMD, one workgroup per CU.  (With at most 8
+// rows three waves per SIMD would fit in the registers, but 12 waves with
+// 4 KiB in flight each read HBM more slowly than 8.)
+template <int JJ>
+constexpr int stream_waves() { return 8; }
+
 template <int D, int JJ, int RG>
 hipError_t launch_dr(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) {
     constexpr int R = D == 64 ? 3 : D == 128 ? 3 : 4;   // ring slots: a few KiB in flight per wave
-    using C = Cfg<D, R>;
-    auto kern = attn_mfma_stream_kernel<D, JJ, RG, R>;
-    if (C::LDS_BYTES > 64 * 1024) {
+    constexpr int W = stream_waves<JJ>();
+    using WL = WgLds<D, R, W, RG>;
+    auto kern = attn_mfma_stream_kernel<D, JJ, RG, R, W>;
+    if (WL::BYTES > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS_BYTES);
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, WL::BYTES);
         if (e != hipSuccess) return e;
     }
     dim3 grid(pl.n_splits * a.g.n_kv);
-    hipLaunchKernelGGL(kern, grid, dim3(C::W * 64), C::LDS_BYTES, stream, a, pl.chunks_per_split, pl.n_splits,
+    hipLaunchKernelGGL(kern, grid, dim3(W * 64), WL::BYTES, stream, a, pl.chunks_per_split, pl.n_splits,
                        pl.group, pl.rows);
     return hipGetLastError();
 }
@@ -703,7 +760,9 @@ hipError_t launch_d(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) {
 }  // namespace
 
 int mfma_stream_row_groups(int rows) { return rows <= 16 ? 1 : rows <= 32 ? 2 : 4; }
-int mfma_stream_waves(int rows) { return 8 / mfma_stream_row_groups(rows); }
+int mfma_stream_waves(int rows) {
+    return (rows <= 8 ? stream_waves<2>() : stream_waves<4>()) / mfma_stream_row_groups(rows);
+}
 
 hipError_t launch_attn_mfma_stream(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) {
     switch (a.g.D) {
