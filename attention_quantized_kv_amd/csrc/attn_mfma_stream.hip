@@ -587,6 +587,13 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
     auto chunk = [&](auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
         const int j0 = c * kChunk;
+        // The two waves of a SIMD (w and w + W/2) take turns at the higher
+        // issue priority, chunk by chunk.  With the hardware's oldest-first
+        // choice alone, the second wave of every SIMD ends several percent
+        // later than the first (and, with two row groups, the groups drift
+        // apart and lose their shared L2 reads).
+        if (((k ^ (wave >= W / 2 ? 1 : 0)) & 1) != 0) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
         const bool has_next = c + stride < c1;
         if (has_next && ((k + 1) & 63) == 0) {  // every 64 chunks
             ents = load_ents(k + 1);
