@@ -28,6 +28,7 @@ KERNEL_AUTO, KERNEL_VALU, KERNEL_MFMA_STREAM, KERNEL_MFMA_TILED = 0, 1, 2, 3
 EXPORTS = (
     "kvq_unit_bytes", "kvq_pool_bytes", "kvq_append", "kvq_workspace_bytes",
     "kvq_decode_attn", "kvq_prefill_attn", "kvq_workspace_bytes_ex", "kvq_attn_ex",
+    "kvq_append_attn_workspace_bytes", "kvq_append_attn",
     "kvq_status_str", "kvq_last_error", "kvq_version",
 )
 
@@ -80,6 +81,8 @@ def lib() -> ctypes.CDLL:
         "kvq_decode_attn": [LP, P, P, i32, i32, i32, i32, P, ctypes.c_float, P, P, P, sz, P],
         "kvq_prefill_attn": [LP, P, P, i32, i32, i32, i32, P, ctypes.c_float, P, P, P, sz, P],
         "kvq_attn_ex": [LP, P, P, i32, i32, i32, i32, P, ctypes.c_float, P, P, P, sz, OP, P],
+        "kvq_append_attn_workspace_bytes": [LP, i32, i32, i32, OP, SZP],
+        "kvq_append_attn": [LP, P, P, i32, i32, i32, P, P, i32, P, ctypes.c_float, P, P, P, sz, OP, P],
         "kvq_status_str": [ctypes.c_int],
         "kvq_last_error": [],
         "kvq_version": [],
@@ -240,3 +243,37 @@ def kvq_attn_ex(layout: Layout, pool, page_table, ctx_len: int, q, scale: float,
     _check(lib().kvq_attn_ex(ctypes.byref(layout), _ptr(pool), _ptr(page_table), nt, int(ctx_len),
                              n_heads, n_q, _ptr(q), float(scale), _ptr(out), _ptr(lse), _ptr(ws),
                              ws_bytes, ctypes.byref(opts), _stream(stream)), "kvq_attn_ex")
+
+
+def kvq_append_attn_workspace_bytes(layout: Layout, n_heads: int, pos0: int, n_new: int,
+                                    kernel: int = 0, chunks_per_split: int = 0) -> int:
+    out = ctypes.c_size_t(0)
+    opts = AttnOpts(kernel, chunks_per_split)
+    _check(lib().kvq_append_attn_workspace_bytes(ctypes.byref(layout), n_heads, int(pos0), int(n_new),
+                                                 ctypes.byref(opts), ctypes.byref(out)),
+           "kvq_append_attn_workspace_bytes")
+    return out.value
+
+
+def kvq_append_attn(layout: Layout, pool, page_table, pos0: int, k, v, q, scale: float, out, lse=None,
+                    ws=None, kernel: int = 0, chunks_per_split: int = 0, stream=None, n_table=None,
+                    events=None):
+    """One decode step: append k, v [n_new][n_kv][D] at pos0, then attend the
+    n_new queries q [n_new][n_heads][D] over pos0 + n_new keys.  events as for
+    kvq_attn_ex (recorded around the split pass over the cached keys)."""
+    import torch
+    _need(k, "k", torch.float32)
+    _need(v, "v", torch.float32)
+    n_q, n_heads, ws_bytes = _attn_args(pool, page_table, q, out, lse, ws)
+    if k.shape[0] != n_q or v.shape[0] != n_q:
+        raise ValueError("k, v and q must hold the same number of rows")
+    nt = _n_table(page_table) if n_table is None else n_table
+    opts = AttnOpts(kernel, chunks_per_split)
+    if events is not None:
+        if not events[0] or not events[1]:
+            raise ValueError("events must be two created hipEvent_t handles")
+        opts.kernel_begin_event = events[0]
+        opts.kernel_end_event = events[1]
+    _check(lib().kvq_append_attn(ctypes.byref(layout), _ptr(pool), _ptr(page_table), nt, int(pos0), n_q,
+                                 _ptr(k), _ptr(v), n_heads, _ptr(q), float(scale), _ptr(out), _ptr(lse),
+                                 _ptr(ws), ws_bytes, ctypes.byref(opts), _stream(stream)), "kvq_append_attn")

@@ -342,6 +342,7 @@ __device__ inline void qk_step(floatx4 (&s)[2], const Land& L, const uint8_t* __
         SCHED_FENCE();
     }
     // causal / tail mask: key j visible to row r iff j <= first_last + r / group
+    // (group is huge when every row sees all keys)
     if (MASK) {
 #pragma unroll
         for (int jj = 0; jj < JJ; ++jj) {
@@ -477,7 +478,9 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
     const int split = blockIdx.x % n_splits;
     const int kvh = blockIdx.x / n_splits;
     const int total_chunks = (a.ctx + kChunk - 1) / kChunk;
-    const int first_last = a.ctx - a.n_q;             // last key of query 0
+    // last key of query 0; query i sees i keys more (causal), or all keys
+    const int first_last = a.causal ? a.ctx - a.n_q : a.ctx - 1;
+    const int mask_group = a.causal ? group : 0x7fffffff;
 
     // LDS: [per wave: ring + scales + P buffer] (reused by the final combine)
     // | [q of each row group] | [m, l per wave and row]
@@ -628,7 +631,7 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
             refill(2 * C::KL + u);
         };
         floatx4 s[2];
-        qk_step<D, R, JJ, MASK>(s, land, qlds, lane, j0, first_last, group, rows, gi, qk_wait, qk_done);
+        qk_step<D, R, JJ, MASK>(s, land, qlds, lane, j0, first_last, mask_group, rows, gi, qk_wait, qk_done);
         lds_fence();                            // K scales read out
         if (more) issue_kscales<D, R>(land, np, lane);
         softmax_step<D, R, JJ>(st, s, plds, lane);

@@ -191,6 +191,40 @@ int attn_impl(const kvq_layout* L, const void* d_pool, const int32_t* d_page_tab
     return ok();
 }
 
+// Fused append + attention.  The streaming kernel can take the cached keys
+// alone (every new row sees all of them) and the merge kernel adds the new
+// rows; other kernel choices run kvq_append and then the attention call.
+bool append_attn_fused(const kvq_layout* L, int32_t n_heads, int32_t n_new, const kvq_attn_opts* opts) {
+    const int kernel = opts ? opts->kernel : 0;
+    return (kernel == 0 || kernel == 2) && n_new * (n_heads / L->n_kv_heads) <= 64;
+}
+
+// Plan of the cached part (fused) or of the whole attention (otherwise).
+int append_attn_plan(const kvq_layout* L, int32_t n_heads, int32_t pos0, int32_t n_new, const kvq_attn_opts* opts,
+                     bool fused, kvq::AttnPlan* pl) {
+    if (!fused) return make_plan(L, n_heads, pos0 + n_new, n_new, false, opts, pl);
+    kvq_attn_opts o = opts ? *opts : kvq_attn_opts{0, 0, nullptr, nullptr};
+    o.kernel = 2;
+    if (pos0 > 0) return make_plan(L, n_heads, pos0, n_new, false, &o, pl);
+    int st = make_plan(L, n_heads, kvq::kChunk, n_new, false, &o, pl);   // checks only: no cached keys
+    pl->n_splits = 0;
+    return st;
+}
+
+int check_append_attn(const kvq_layout* L, int32_t n_table, int32_t pos0, int32_t n_new, int32_t n_heads) {
+    if (n_heads < 1 || n_heads % L->n_kv_heads != 0)
+        return fail(KVQ_ERR_INVALID_ARG, "n_heads %d must be a positive multiple of n_kv_heads %d", n_heads, L->n_kv_heads);
+    if (n_new < 1 || n_new > KVQ_MAX_NQ_DECODE)
+        return fail(KVQ_ERR_INVALID_ARG, "n_new %d must be in [1, %d]", n_new, KVQ_MAX_NQ_DECODE);
+    if (pos0 < 0) return fail(KVQ_ERR_INVALID_ARG, "pos0 %d < 0", pos0);
+    if (n_table < 1) return fail(KVQ_ERR_INVALID_ARG, "n_table %d < 1", n_table);
+    if ((int64_t)pos0 + n_new > (int64_t)n_table * L->page_size)
+        return fail(KVQ_ERR_CAPACITY, "positions up to %lld exceed the page table (%d pages of %d)",
+                    (long long)pos0 + n_new, n_table, L->page_size);
+    if ((int64_t)pos0 + n_new > INT32_MAX) return fail(KVQ_ERR_CAPACITY, "positions overflow int32");
+    return KVQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -272,6 +306,83 @@ int kvq_prefill_attn(const kvq_layout* layout, const void* d_pool, const int32_t
                      float* d_out, float* d_lse, void* d_ws, size_t ws_bytes, void* stream) {
     return attn_impl(layout, d_pool, d_page_table, n_table, ctx_len, n_heads, n_q, d_q, scale, d_out, d_lse,
                      d_ws, ws_bytes, true, nullptr, stream);
+}
+
+int kvq_append_attn_workspace_bytes(const kvq_layout* layout, int32_t n_heads, int32_t pos0, int32_t n_new,
+                                    const kvq_attn_opts* opts, size_t* bytes) {
+    kvq::Geom g;
+    int st = check_layout(layout, &g);
+    if (st) return st;
+    if (bytes == nullptr) return fail(KVQ_ERR_INVALID_ARG, "bytes is NULL");
+    st = check_append_attn(layout, INT32_MAX / layout->page_size, pos0, n_new, n_heads);
+    if (st) return st;
+    const bool fused = append_attn_fused(layout, n_heads, n_new, opts);
+    kvq::AttnPlan pl;
+    st = append_attn_plan(layout, n_heads, pos0, n_new, opts, fused, &pl);
+    if (st) return st;
+    *bytes = pl.n_splits > 0 ? kvq::ws_bytes_for(pl, n_new, n_heads, layout->head_dim) : 0;
+    return ok();
+}
+
+int kvq_append_attn(const kvq_layout* layout, void* d_pool, const int32_t* d_page_table, int32_t n_table,
+                    int32_t pos0, int32_t n_new, const float* d_k, const float* d_v, int32_t n_heads,
+                    const float* d_q, float scale, float* d_out, float* d_lse, void* d_ws, size_t ws_bytes,
+                    const kvq_attn_opts* opts, void* stream) {
+    kvq::Geom g;
+    int st = check_layout(layout, &g);
+    if (st) return st;
+    if (d_pool == nullptr || d_page_table == nullptr || d_k == nullptr || d_v == nullptr || d_q == nullptr ||
+        d_out == nullptr)
+        return fail(KVQ_ERR_INVALID_ARG, "pool, page_table, k, v, q and out must be non-NULL");
+    st = check_append_attn(layout, n_table, pos0, n_new, n_heads);
+    if (st) return st;
+    if (((uintptr_t)d_pool & 255) != 0) return fail(KVQ_ERR_INVALID_ARG, "pool must be 256-byte aligned");
+    const bool fused = append_attn_fused(layout, n_heads, n_new, opts);
+    if (!fused) {
+        st = kvq_append(layout, d_pool, d_page_table, n_table, pos0, n_new, d_k, d_v, stream);
+        if (st) return st;
+        return attn_impl(layout, d_pool, d_page_table, n_table, pos0 + n_new, n_heads, n_new, d_q, scale, d_out,
+                         d_lse, d_ws, ws_bytes, false, opts, stream);
+    }
+    kvq::AttnPlan pl;
+    st = append_attn_plan(layout, n_heads, pos0, n_new, opts, true, &pl);
+    if (st) return st;
+    const size_t need = pl.n_splits > 0 ? kvq::ws_bytes_for(pl, n_new, n_heads, layout->head_dim) : 0;
+    if (need > 0 && (d_ws == nullptr || ws_bytes < need))
+        return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, ws_bytes,
+                    d_ws == nullptr ? " (NULL)" : "");
+    if (((uintptr_t)d_ws & 15) != 0) return fail(KVQ_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+
+    kvq::AttnArgs a;
+    a.g = g;
+    a.pool = static_cast<const uint8_t*>(d_pool);
+    a.page_table = d_page_table;
+    a.ctx = pos0;
+    a.n_heads = n_heads;
+    a.n_q = n_new;
+    a.q = d_q;
+    a.scale = scale;
+    a.out = d_out;
+    a.lse = d_lse;
+    a.causal = 0;
+    const size_t rows = (size_t)n_new * n_heads;
+    const size_t ml = (rows * pl.n_splits * sizeof(float) + 255) / 256 * 256;
+    uint8_t* ws = static_cast<uint8_t*>(d_ws);
+    a.ws_m = reinterpret_cast<float*>(ws);
+    a.ws_l = reinterpret_cast<float*>(ws + ml);
+    a.ws_acc = reinterpret_cast<float*>(ws + 2 * ml);
+    const kvq::NewRows nr{static_cast<uint8_t*>(d_pool), d_k, d_v, pos0, n_new};
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    if (opts != nullptr && opts->kernel_begin_event != nullptr)
+        e = hipEventRecord(static_cast<hipEvent_t>(opts->kernel_begin_event), s);
+    if (e == hipSuccess && pl.n_splits > 0) e = kvq::launch_attn_mfma_stream(a, pl, s);
+    if (e == hipSuccess && opts != nullptr && opts->kernel_end_event != nullptr)
+        e = hipEventRecord(static_cast<hipEvent_t>(opts->kernel_end_event), s);
+    if (e == hipSuccess) e = kvq::launch_merge_new(a, nr, pl.n_splits, s);
+    if (e != hipSuccess) return fail(KVQ_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return ok();
 }
 
 int kvq_attn_ex(const kvq_layout* layout, const void* d_pool, const int32_t* d_page_table, int32_t n_table,

@@ -84,6 +84,21 @@ struct AttnArgs {
     float* ws_acc;   // [n_q*n_heads][n_splits][D]
     float* ws_m;     // [n_q*n_heads][n_splits]   log2-domain running max
     float* ws_l;     // [n_q*n_heads][n_splits]   sum of exp2(s - m)
+    // 1: the n_q query rows are the last n_q positions of the ctx keys (key j
+    // visible to query i iff j <= ctx - n_q + i).  0: every row sees all ctx
+    // keys (the cached part of a fused append + attention call).
+    int causal = 1;
+};
+
+// Rows appended by the fused append + attention call.  The merge kernel
+// quantizes them, writes their codes into the pool and adds their keys
+// (causally among themselves) to the split partials over the cached keys.
+struct NewRows {
+    uint8_t* pool;   // the pool, writable
+    const float* k;  // [n_new][n_kv][D]
+    const float* v;  // [n_new][n_kv][D]
+    int pos0;        // position of the first new row (= cached keys)
+    int n_new;       // = n_q
 };
 
 // Workspace bytes for a plan.
@@ -102,6 +117,9 @@ hipError_t launch_attn_valu(const AttnArgs& a, const AttnPlan& pl, hipStream_t s
 hipError_t launch_attn_mfma_stream(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream);
 hipError_t launch_attn_mfma_tiled(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream);
 hipError_t launch_merge(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream);
+// Merge of n_splits partials (0: none) with the new rows' keys, and the
+// rows' quantized write into the pool.
+hipError_t launch_merge_new(const AttnArgs& a, const NewRows& nr, int n_splits, hipStream_t stream);
 // Streaming MFMA kernel: row groups per workgroup, and waves sharing one row
 // group (each partial folds that many waves' chunks), for a given row count.
 int mfma_stream_row_groups(int rows);

@@ -14,51 +14,10 @@
 // xor-shuffles.  The two rows of a pair share every V byte (their nibbles sit
 // side by side in the chunk layout), so one thread writes that byte, merging
 // with the old nibble when only one row of the pair is new.
-#include <hip/hip_fp16.h>
-
-#include "kvq_internal.h"
-
-// Every product and sum below is rounded on its own.
-#pragma clang fp contract(off)
+#include "kvq_quant.h"
 
 namespace kvq {
 namespace {
-
-// Round half away from zero.  t - trunc(t) is exact in fp32.
-__device__ inline float round_half_away(float t) {
-    float r = truncf(t);
-    if (fabsf(t - r) >= 0.5f) r += copysignf(1.0f, t);
-    return r;
-}
-
-__device__ inline float block_max(float x) {
-#pragma unroll
-    for (int o = 16; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-    return x;
-}
-
-// Largest magnitude of the block and the lowest index holding it.
-__device__ inline void block_argmax_abs(float ax, int idx, float* amax, int* aidx) {
-#pragma unroll
-    for (int o = 16; o > 0; o >>= 1) {
-        float oax = __shfl_xor(ax, o, 64);
-        int oidx = __shfl_xor(idx, o, 64);
-        if (oax > ax || (oax == ax && oidx < idx)) { ax = oax; idx = oidx; }
-    }
-    *amax = ax;
-    *aidx = idx;
-}
-
-__device__ inline uint16_t f16_bits(float x) { return __half_as_ushort(__float2half_rn(x)); }
-
-// x * y rounded to fp32 on its own.  The empty asm hides the product from the
-// optimizer, which otherwise fuses it with a following add into one FMA
-// (single rounding) regardless of contraction pragmas.
-__device__ inline float mul_rounded(float x, float y) {
-    float p = x * y;
-    asm volatile("" : "+v"(p));
-    return p;
-}
 
 template <int D>
 __global__ __launch_bounds__(D) void append_kernel(Geom g, uint8_t* __restrict__ pool,
@@ -89,26 +48,14 @@ __global__ __launch_bounds__(D) void append_kernel(Geom g, uint8_t* __restrict__
         const size_t src = ((size_t)(pos - pos0) * g.n_kv + kvh) * D + d;
 
         // K: Q8_0
-        const float xk = k[src];
-        const float amax_k = block_max(fabsf(xk));
-        const float dk = __fdiv_rn(amax_k, 127.0f);
-        const float idk = dk != 0.0f ? __fdiv_rn(1.0f, dk) : 0.0f;
-        const int ck = (int)round_half_away(mul_rounded(xk, idk));
-        unit[k_code_pos(g, slot, d)] = (uint8_t)(int8_t)ck;
-        if ((d & (kBlock - 1)) == 0) k_scales[slot * nb + d / kBlock] = f16_bits(dk);
+        const QCode qk = quant_q8_0(k[src]);
+        unit[k_code_pos(g, slot, d)] = (uint8_t)(int8_t)qk.code;
+        if ((d & (kBlock - 1)) == 0) k_scales[slot * nb + d / kBlock] = f16_bits(qk.d);
 
         // V: Q4_0
-        const float xv = v[src];
-        float amax_v;
-        int aidx;
-        block_argmax_abs(fabsf(xv), d & (kBlock - 1), &amax_v, &aidx);
-        float m = __shfl(xv, (lane & ~(kBlock - 1)) + aidx, 64);
-        if (amax_v == 0.0f) m = 0.0f;                       // all-zero block: m = +0
-        const float dv = __fdiv_rn(m, -8.0f);
-        const float idv = dv != 0.0f ? __fdiv_rn(1.0f, dv) : 0.0f;
-        const float t = mul_rounded(xv, idv) + 8.5f;
-        vcode[r] = min(15, __float2int_rz(t));
-        if ((d & (kBlock - 1)) == 0) v_scales[v_scale_idx(g, slot, d / kBlock)] = f16_bits(dv);
+        const QCode qv = quant_q4_0(v[src], lane);
+        vcode[r] = qv.code;
+        if ((d & (kBlock - 1)) == 0) v_scales[v_scale_idx(g, slot, d / kBlock)] = f16_bits(qv.d);
     }
 
     int nib;

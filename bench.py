@@ -5,10 +5,12 @@ MI355X.
 Default workload: a 16-layer stack of full-attention layers, 24 query heads /
 4 KV heads x head_dim 256, 262,144 cached tokens per layer (436,207,616 bytes
 of quantized KV per layer, 6.98 GB for the stack).  One step = for every
-layer, kvq_append of the new token's K/V row (position 262,143) followed by
-kvq_decode_attn of one query over all 262,144 tokens (split over pages, merged
-by online log-sum-exp).  Each layer has its own pool, so consecutive layers
-never share cache lines and every step streams the whole 6.98 GB from HBM.
+layer, the decode step kvq_append_attn: the new token's K/V row (position
+262,143) is quantized into the cache and one query attends over all 262,144
+tokens (split over pages, merged by online log-sum-exp) -- two kernels per
+layer; --unfused runs kvq_append and then the attention call instead.  Each
+layer has its own pool, so consecutive layers never share cache lines and
+every step streams the whole 6.98 GB from HBM.
 
 Prints one JSON line: effective KV GB/s (algorithmic bytes / time), us per
 layer, the roofline of the decode kernel measured with HIP events on the
@@ -103,6 +105,13 @@ class Layer:
         self.kvq.kvq_append(self.L, self.pool, self.pt, self.w.cached, self.k_new, self.v_new)
 
     cps = 0
+
+    def decode_step(self, ws, kernel, events=None):
+        """kvq_append_attn: append the new rows and attend in one call; `events`
+        (begin, end) are recorded around the split pass over the cached keys."""
+        self.kvq.kvq_append_attn(self.L, self.pool, self.pt, self.w.cached, self.k_new, self.v_new, self.q,
+                                 self.w.scale, self.out, self.lse, ws, kernel=kernel, chunks_per_split=self.cps,
+                                 events=events)
 
     def attend(self, ws, kernel, events=None):
         """kvq_attn_ex with the automatic plan (kernel 0: the same choice as
@@ -200,6 +209,8 @@ def main():
     ap.add_argument("--layers", type=int, default=None, help="layers in the stack (default: the workload's)")
     ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA streaming, 3 MFMA tiled")
     ap.add_argument("--cps", type=int, default=0, help="32-token chunks per split (0: the library's choice)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="decode / verify: kvq_append, then the attention call (three kernels per layer)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--shuffle-pages", action="store_true",
@@ -241,7 +252,11 @@ def main():
     t0 = time.time()
     layers = [Layer(w, i, dev, shuffle_pages=args.shuffle_pages) for i in range(n_layers)]
     Layer.cps = args.cps
-    ws_n = kvq.kvq_workspace_bytes_ex(layers[0].L, w.n_heads, w.ctx, w.n_q, args.kernel, args.cps)
+    fused = not prefill and not args.unfused
+    if fused:
+        ws_n = kvq.kvq_append_attn_workspace_bytes(layers[0].L, w.n_heads, w.cached, w.n_q, args.kernel, args.cps)
+    else:
+        ws_n = kvq.kvq_workspace_bytes_ex(layers[0].L, w.n_heads, w.ctx, w.n_q, args.kernel, args.cps)
     ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     print(f"[bench] {w.name}: {n_layers} layers filled in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
@@ -252,8 +267,12 @@ def main():
     # layer would inflate the step time being measured.
     def step(ev=None, s=0):
         for i, lay in enumerate(layers):
-            lay.append()
-            lay.attend(ws, args.kernel, ev if (ev is not None and i == s % n_layers) else None)
+            e = ev if (ev is not None and i == s % n_layers) else None
+            if fused:
+                lay.decode_step(ws, args.kernel, e)
+            else:
+                lay.append()
+                lay.attend(ws, args.kernel, e)
 
     for _ in range(args.warmup):
         step()
@@ -279,6 +298,8 @@ def main():
 
     ms_per_step = total_ms / args.steps
     bytes_layer = w.ctx * kv_bytes_per_token_layer(w.n_kv, w.head_dim)
+    # bytes the timed kernel reads: the fused step's split pass reads the cached keys only
+    bytes_kernel = (w.cached if fused else w.ctx) * kv_bytes_per_token_layer(w.n_kv, w.head_dim)
     us_per_layer = 1000.0 * ms_per_step / n_layers
     flops_layer = attention_flops(w)
     rec = {
@@ -288,18 +309,20 @@ def main():
                    "head_dim": w.head_dim, "ctx": w.ctx, "n_q": w.n_q, "page_size": w.page_size,
                    "kv_format": "K Q8_0 + V Q4_0", "kernel": args.kernel or "auto",
                    "chunks_per_split": args.cps or "auto",
+                   "step": ("kvq_append_attn (append + attention, 2 kernels)" if fused else
+                            "kvq_append, then attention" if not prefill else "attention"),
                    "page_table": "shuffled" if args.shuffle_pages else "in order"},
     }
     if not prefill:
         value = n_layers * bytes_layer * args.steps / (total_ms / 1e3) / 1e9
-        achieved = bytes_layer / (avg_attn_us / 1e6) / 1e9
+        achieved = bytes_kernel / (avg_attn_us / 1e6) / 1e9
         rec.update({
             "metric": "quantized-KV decode attention: effective KV GB/s (% HBM peak), us/layer @262k",
             "value": round(value, 2), "unit": "GB/s",
         })
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": kname, "bytes_per_launch": bytes_layer,
+                "kernel": kname, "bytes_per_launch": bytes_kernel,
                 "avg_launch_us": round(avg_attn_us, 3)}
         extra = {"us_per_layer": round(us_per_layer, 3), "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
                  "ctx_tokens_per_s": round(w.ctx / (us_per_layer / 1e6), 1),

@@ -193,6 +193,37 @@ int kvq_attn_ex(const kvq_layout *layout, const void *d_pool,
                 float *d_out, float *d_lse,
                 void *d_ws, size_t ws_bytes, const kvq_attn_opts *opts, void *stream);
 
+/*
+ * One decode step: kvq_append of n_new rows at pos0, then attention of the
+ * n_new queries over the pos0 + n_new keys -- exactly kvq_append followed by
+ * kvq_attn_ex(ctx_len = pos0 + n_new, n_q = n_new), in two launches instead
+ * of three ("Qwen 27B (IQ4_XS, Q8/Q4 KV) on a 16GB RX 9070 XT at 262k
+ * context, via adaptive KV streaming": quantize on append, paged decode
+ * attention, online log-sum-exp across pages).  With the streaming kernel
+ * (opts->kernel 0 or 2, n_new * group <= 64) the split pass reads the pos0
+ * cached keys only, and the merge pass quantizes the new rows (the same codes
+ * and scales kvq_append writes), scores them, folds them into the softmax and
+ * writes them into the pool.  Other kernel choices run kvq_append and the
+ * attention one after the other.
+ *   pos0, n_new, d_k, d_v  as for kvq_append (1 <= n_new <= KVQ_MAX_NQ_DECODE)
+ *   d_q, d_out, d_lse      as for attention with n_q = n_new
+ *   d_ws   workspace of at least kvq_append_attn_workspace_bytes() bytes
+ *          (NULL if that is 0); opts as for kvq_attn_ex, may be NULL.
+ * The rows' V nibbles are written with atomic and/or on their pool dwords;
+ * the same ordering rules as kvq_append apply.  Errors: as kvq_append and
+ * kvq_attn_ex (INVALID_ARG also for n_new outside [1, KVQ_MAX_NQ_DECODE]).
+ */
+int kvq_append_attn_workspace_bytes(const kvq_layout *layout, int32_t n_heads, int32_t pos0,
+                                    int32_t n_new, const kvq_attn_opts *opts, size_t *bytes);
+
+int kvq_append_attn(const kvq_layout *layout, void *d_pool,
+                    const int32_t *d_page_table, int32_t n_table,
+                    int32_t pos0, int32_t n_new,
+                    const float *d_k, const float *d_v,
+                    int32_t n_heads, const float *d_q, float scale,
+                    float *d_out, float *d_lse,
+                    void *d_ws, size_t ws_bytes, const kvq_attn_opts *opts, void *stream);
+
 /* Status name, and the detail of the last failure on this thread. */
 const char *kvq_status_str(int status);
 const char *kvq_last_error(void);

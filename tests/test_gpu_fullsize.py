@@ -1,6 +1,8 @@
 """GPU: the workloads at their full sizes, in the launch configuration the
 benchmark times (automatic kernel and split plan, in-order page table, cache
-filled by kvq_append in chunks and the new rows appended at their position).
+filled by kvq_append in chunks and the new rows appended at their position;
+for the decode and verify workloads also through the fused decode step,
+kvq_append_attn, which appends the new rows and attends in one call).
 
 Inputs come from the seeded host generators (synth), so the oracle sees the
 same fp32 values.  Checked against the oracle:
@@ -23,7 +25,7 @@ pytestmark = pytest.mark.gpu
 FILL_CHUNK = 16384
 
 
-def _run(w):
+def _run(w, fused=False):
     import torch
     import attention_quantized_kv_amd as kvq
     k, v = synth.layer_kv(w, 0)
@@ -34,11 +36,18 @@ def _run(w):
     for r in range(0, w.cached, FILL_CHUNK):
         n = min(FILL_CHUNK, w.cached - r)
         kvq.kvq_append(L, pool, pt_dev, r, torch.from_numpy(k[r:r + n]).cuda(), torch.from_numpy(v[r:r + n]).cuda())
-    kvq.kvq_append(L, pool, pt_dev, w.cached, torch.from_numpy(k[w.cached:]).cuda(),
-                   torch.from_numpy(v[w.cached:]).cuda())
     qd = torch.from_numpy(q).cuda()
     out = torch.full((w.n_q, w.n_heads, w.head_dim), float("nan"), device="cuda")
     lse = torch.full((w.n_q, w.n_heads), float("nan"), device="cuda")
+    if fused:                                   # the decode step: append + attention in one call
+        ws = torch.empty(max(kvq.kvq_append_attn_workspace_bytes(L, w.n_heads, w.cached, w.n_q), 256),
+                         dtype=torch.uint8, device="cuda")
+        kvq.kvq_append_attn(L, pool, pt_dev, w.cached, torch.from_numpy(k[w.cached:]).cuda(),
+                            torch.from_numpy(v[w.cached:]).cuda(), qd, w.scale, out, lse, ws)
+        torch.cuda.synchronize()
+        return k, v, q, L, pool, pt, out.cpu().numpy(), lse.cpu().numpy()
+    kvq.kvq_append(L, pool, pt_dev, w.cached, torch.from_numpy(k[w.cached:]).cuda(),
+                   torch.from_numpy(v[w.cached:]).cuda())
     prefill = w.n_q > kvq.KVQ_MAX_NQ_DECODE
     ws = torch.empty(max(kvq.kvq_workspace_bytes(L, w.n_heads, w.ctx, w.n_q, prefill), 1), dtype=torch.uint8,
                      device="cuda")
@@ -74,10 +83,12 @@ def _rows(w):
     return [(i, h) for i in qs for h in hs]
 
 
-@pytest.mark.parametrize("name", ["tiny", "decode65k", "decode262k", "verify131k", "prefill262k"])
-def test_full_size(name):
+@pytest.mark.parametrize("name,fused", [("tiny", False), ("decode65k", False), ("decode262k", False),
+                                        ("verify131k", False), ("prefill262k", False), ("tiny", True),
+                                        ("decode262k", True), ("verify131k", True)])
+def test_full_size(name, fused):
     w = synth.WORKLOADS[name]
-    k, v, q, L, pool, pt, out, lse = _run(w)
+    k, v, q, L, pool, pt, out, lse = _run(w, fused)
     cache = oracle.QuantCache.from_float(k, v)
     del k, v
     _check_codes(w, cache, L, pool, pt)
@@ -85,4 +96,4 @@ def test_full_size(name):
     ref, ref_lse = oracle.attention(q, cache, w.scale, rows=rows)
     got = np.stack([out[i, h] for i, h in rows])
     got_lse = np.array([lse[i, h] for i, h in rows])
-    tu.assert_close(got, ref, got_lse, ref_lse, f"{name} ({len(rows)} rows)")
+    tu.assert_close(got, ref, got_lse, ref_lse, f"{name}{' fused' if fused else ''} ({len(rows)} rows)")
