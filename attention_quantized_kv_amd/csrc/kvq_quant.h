@@ -6,7 +6,8 @@
 // in include/kvq.h.
 //
 // One value per lane: a block is 32 consecutive lanes (an aligned half
-// wavefront), so block reductions are five xor-shuffles.  Every product,
+// wavefront), reduced in five lane exchanges (DPP inside 16-lane rows, a
+// permlane swap across them).  Every product,
 // quotient and sum is IEEE fp32 rounded on its own (no contraction), so codes
 // and scales are bit-reproducible wherever these functions run.
 #pragma once
@@ -24,22 +25,95 @@ __device__ inline float round_half_away(float t) {
     return r;
 }
 
-__device__ inline float block_max32(float x) {
-#pragma unroll
-    for (int o = 16; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-    return x;
+// Lane exchanges without LDS round trips: DPP within a 16-lane row, and the
+// gfx950 permlane swaps across rows (a 32-lane half and the whole wave).
+template <int CTRL>
+__device__ inline int dpp_i(int x) {
+    return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ inline float dpp_f(float x) {
+    return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, x)));
+}
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;   // lane i <-> 7-i inside each 8 lanes
+constexpr int kDppMirror = 0x140;       // lane i <-> 15-i inside each 16 lanes
+
+// The value of lane ^ 16 (the other 16-lane row of the 32-lane half).
+// v_permlane16_swap a, b swaps a's odd rows with b's even rows: with a = b =
+// x, an even row finds its partner in b and an odd row in a.  Inline asm: the
+// builtin's second result is folded into the first by the optimiser.
+__device__ inline int xor16_i(int x, int lane) {
+    int a = x, b = x;
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+    return (lane & 16) ? a : b;
+}
+// The value of lane ^ 32 (the other half of the wave), likewise.
+__device__ inline int xor32_i(int x, int lane) {
+    int a = x, b = x;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+    return (lane & 32) ? a : b;
+}
+__device__ inline float xor16_f(float x, int lane) {
+    return __builtin_bit_cast(float, xor16_i(__builtin_bit_cast(int, x), lane));
+}
+__device__ inline float xor32_f(float x, int lane) {
+    return __builtin_bit_cast(float, xor32_i(__builtin_bit_cast(int, x), lane));
 }
 
-// Largest magnitude of the block and the lowest index holding it.
-__device__ inline void block_argmax_abs32(float ax, int idx, float* amax, int* aidx) {
-#pragma unroll
-    for (int o = 16; o > 0; o >>= 1) {
-        float oax = __shfl_xor(ax, o, 64);
-        int oidx = __shfl_xor(idx, o, 64);
-        if (oax > ax || (oax == ax && oidx < idx)) { ax = oax; idx = oidx; }
-    }
-    *amax = ax;
-    *aidx = idx;
+// Maximum over the 32-lane half holding this lane (every lane gets it).
+__device__ inline float block_max32(float x, int lane) {
+    x = fmaxf(x, dpp_f<kDppXor1>(x));
+    x = fmaxf(x, dpp_f<kDppXor2>(x));
+    x = fmaxf(x, dpp_f<kDppHalfMirror>(x));
+    x = fmaxf(x, dpp_f<kDppMirror>(x));
+    return fmaxf(x, xor16_f(x, lane));
+}
+
+// Sum over the whole wave (every lane gets it; the order is fixed).
+__device__ inline float wave_sum(float x, int lane) {
+    x += dpp_f<kDppXor1>(x);
+    x += dpp_f<kDppXor2>(x);
+    x += dpp_f<kDppHalfMirror>(x);
+    x += dpp_f<kDppMirror>(x);
+    x += xor16_f(x, lane);
+    return x + xor32_f(x, lane);
+}
+
+// Maximum over the whole wave.
+__device__ inline float wave_max(float x, int lane) {
+    x = fmaxf(x, dpp_f<kDppXor1>(x));
+    x = fmaxf(x, dpp_f<kDppXor2>(x));
+    x = fmaxf(x, dpp_f<kDppHalfMirror>(x));
+    x = fmaxf(x, dpp_f<kDppMirror>(x));
+    x = fmaxf(x, xor16_f(x, lane));
+    return fmaxf(x, xor32_f(x, lane));
+}
+
+// Over the 32-lane half: the value of largest magnitude, lowest index on ties
+// (idx = position in the block).  The pair rule is symmetric, so both lanes
+// of every exchange keep the same winner and the order of the steps does not
+// matter.
+struct ArgMax {
+    float ax;   // |x|
+    float x;    // the signed value
+    int idx;
+};
+__device__ inline ArgMax pick(ArgMax a, ArgMax b) {
+    return (b.ax > a.ax || (b.ax == a.ax && b.idx < a.idx)) ? b : a;
+}
+template <int CTRL>
+__device__ inline ArgMax dpp_am(ArgMax a) {
+    return {dpp_f<CTRL>(a.ax), dpp_f<CTRL>(a.x), dpp_i<CTRL>(a.idx)};
+}
+__device__ inline ArgMax block_argmax_abs32(float x, int lane) {
+    ArgMax a{fabsf(x), x, lane & (kBlock - 1)};
+    a = pick(a, dpp_am<kDppXor1>(a));
+    a = pick(a, dpp_am<kDppXor2>(a));
+    a = pick(a, dpp_am<kDppHalfMirror>(a));
+    a = pick(a, dpp_am<kDppMirror>(a));
+    return pick(a, ArgMax{xor16_f(a.ax, lane), xor16_f(a.x, lane), xor16_i(a.idx, lane)});
 }
 
 __device__ inline uint16_t f16_bits(float x) { return __half_as_ushort(__float2half_rn(x)); }
@@ -62,24 +136,20 @@ struct QCode {
 
 // Q8_0: d = amax / 127, code = round-half-away(x / d) in [-127, 127]
 // (x * (1/d), both rounded; an all-zero block has d = 0 and codes 0).
-__device__ inline QCode quant_q8_0(float x) {
+__device__ inline QCode quant_q8_0(float x, int lane_in_wave) {
 #pragma clang fp contract(off)
-    const float amax = block_max32(fabsf(x));
+    const float amax = block_max32(fabsf(x), lane_in_wave);
     const float d = __fdiv_rn(amax, 127.0f);
     const float id = d != 0.0f ? __fdiv_rn(1.0f, d) : 0.0f;
     return {(int)round_half_away(mul_rounded(x, id)), d};
 }
 
 // Q4_0: m = the value of largest magnitude (lowest index on ties), d = m / -8,
-// code = min(15, trunc(x * (1/d) + 8.5)) in [0, 15].  lane_in_wave picks the
-// shuffle source: the block is lanes (lane & ~31) .. +31.
+// code = min(15, trunc(x * (1/d) + 8.5)) in [0, 15].
 __device__ inline QCode quant_q4_0(float x, int lane_in_wave) {
 #pragma clang fp contract(off)
-    float amax;
-    int aidx;
-    block_argmax_abs32(fabsf(x), lane_in_wave & (kBlock - 1), &amax, &aidx);
-    float m = __shfl(x, (lane_in_wave & ~(kBlock - 1)) + aidx, 64);
-    if (amax == 0.0f) m = 0.0f;                        // all-zero block: m = +0
+    const ArgMax am = block_argmax_abs32(x, lane_in_wave);
+    const float m = am.ax == 0.0f ? 0.0f : am.x;        // all-zero block: m = +0
     const float d = __fdiv_rn(m, -8.0f);
     const float id = d != 0.0f ? __fdiv_rn(1.0f, d) : 0.0f;
     const float t = mul_rounded(x, id) + 8.5f;

@@ -46,13 +46,11 @@ __global__ __launch_bounds__(D) void merge_kernel(AttnArgs a, int n_splits) {
             // splits with no visible key (l = 0) do not count; a NaN partial
             // (page outside the pool) propagates through its weight
             float bm = lk != 0.0f ? mk : -INFINITY;
-#pragma unroll
-            for (int off = 32; off >= 1; off /= 2) bm = fmaxf(bm, __shfl_xor(bm, off));
+            bm = wave_max(bm, t);
             const float Mn = fmaxf(M, bm);
             const float wk = lk != 0.0f ? exp2f(mk - Mn) : 0.0f;
             float sl = wk * lk;
-#pragma unroll
-            for (int off = 32; off >= 1; off /= 2) sl += __shfl_xor(sl, off);
+            sl = wave_sum(sl, t);
             const float al = M == -INFINITY ? 0.0f : exp2f(M - Mn);
             L = L * al + sl;
             M = Mn;
@@ -133,13 +131,11 @@ __global__ __launch_bounds__(D) void merge_new_kernel(AttnArgs a, NewRows nr, in
 #pragma unroll
     for (int j = 0; j < kMaxNew; ++j) {
         if (j >= n_vis) break;                         // uniform
-        const QCode ck = quant_q8_0(kx[j]);
+        const QCode ck = quant_q8_0(kx[j], lane);
         const QCode cv = quant_q4_0(vx[j], lane);
         const float kd = __half2float(__float2half_rn(ck.d)), vd = __half2float(__float2half_rn(cv.d));
         vhat[j] = (float)(cv.code - 8) * vd;
-        float p = xq * ((float)ck.code * kd);
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) p += __shfl_xor(p, o, 64);
+        const float p = wave_sum(xq * ((float)ck.code * kd), lane);
         if (lane == 0) red_s[j][wv] = p;
         if (writer && j == qi && phys >= 0 && phys < g.n_pages) {
             uint8_t* unit = nr.pool + g.unit_index(phys, kvh) * g.unit_bytes();
@@ -172,13 +168,11 @@ __global__ __launch_bounds__(D) void merge_new_kernel(AttnArgs a, NewRows nr, in
         }
         if (t < 64) {
             float bm = lk != 0.0f ? mk : -INFINITY;
-#pragma unroll
-            for (int off = 32; off >= 1; off /= 2) bm = fmaxf(bm, __shfl_xor(bm, off));
+            bm = wave_max(bm, t);
             const float Mn = fmaxf(M, bm);
             const float wk = lk != 0.0f ? exp2f(mk - Mn) : 0.0f;
             float sl = wk * lk;
-#pragma unroll
-            for (int off = 32; off >= 1; off /= 2) sl += __shfl_xor(sl, off);
+            sl = wave_sum(sl, t);
             const float al = M == -INFINITY ? 0.0f : exp2f(M - Mn);
             L = L * al + sl;
             M = Mn;

@@ -48,7 +48,7 @@ __global__ __launch_bounds__(D) void append_kernel(Geom g, uint8_t* __restrict__
         const size_t src = ((size_t)(pos - pos0) * g.n_kv + kvh) * D + d;
 
         // K: Q8_0
-        const QCode qk = quant_q8_0(k[src]);
+        const QCode qk = quant_q8_0(k[src], lane);
         unit[k_code_pos(g, slot, d)] = (uint8_t)(int8_t)qk.code;
         if ((d & (kBlock - 1)) == 0) k_scales[slot * nb + d / kBlock] = f16_bits(qk.d);
 
