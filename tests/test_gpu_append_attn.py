@@ -136,3 +136,29 @@ def test_rejects_bad_arguments():
     with pytest.raises(kvq.KvqError) as e:          # position 256 is past the page table
         kvq.kvq_append_attn(L, pool, pt_dev, 256, kv1, kv1, q1, 0.125, out1)
     assert e.value.status == kvq.KVQ_ERR_CAPACITY
+
+
+def test_workspace_garbage_and_reuse():
+    """The streaming kernel's arrival counters live in the workspace: any old
+    bytes there (random, or the previous call's counters) must not matter."""
+    import torch
+    import attention_quantized_kv_amd as kvq
+    rng = np.random.default_rng(41)
+    D, n_kv, G, P, ctx = 128, 2, 4, 64, 3000
+    k = rng.standard_normal((ctx, n_kv, D)).astype(np.float32)
+    v = rng.standard_normal((ctx, n_kv, D)).astype(np.float32)
+    L = tu.layout(n_kv, D, P, (ctx + P - 1) // P)
+    pool = tu.alloc_pool(L)
+    pt_dev, _ = tu.page_table_for(ctx, P, L.n_pages)
+    kvq.kvq_append(L, pool, pt_dev, 0, torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda())
+    cache = oracle.QuantCache.from_float(k, v)
+    nbytes = kvq.kvq_workspace_bytes(L, n_kv * G, ctx, 1)
+    ws = torch.from_numpy(rng.integers(0, 256, nbytes, dtype=np.uint8)).cuda()
+    for it in range(3):
+        q = rng.standard_normal((1, n_kv * G, D)).astype(np.float32)
+        out = torch.full((1, n_kv * G, D), float("nan"), device="cuda")
+        lse = torch.full((1, n_kv * G), float("nan"), device="cuda")
+        kvq.kvq_decode_attn(L, pool, pt_dev, ctx, torch.from_numpy(q).cuda(), 0.09, out, lse, ws)
+        torch.cuda.synchronize()
+        ref, ref_lse, _ = oracle.attention(q, cache, 0.09)
+        tu.assert_close(out.cpu().numpy(), ref, lse.cpu().numpy(), ref_lse, f"call {it}")
