@@ -206,7 +206,11 @@ struct WgLds {
     static constexpr int MAIN_BYTES = W * C::WAVE_BYTES > COMB_BYTES ? W * C::WAVE_BYTES : COMB_BYTES;
     static constexpr int Q_OFF = MAIN_BYTES;
     static constexpr int ML_OFF = Q_OFF + RG * C::Q_BYTES;
-    static constexpr int BYTES = ML_OFF + W * 16 * 2 * 4;
+    // one row group: the workgroup's chunk list (page entries) and the index
+    // of the next chunk to hand out
+    static constexpr int LIST = 256;
+    static constexpr int LIST_OFF = ML_OFF + W * 16 * 2 * 4;
+    static constexpr int BYTES = LIST_OFF + (RG == 1 ? (LIST + 4) * 4 : 0);
 };
 
 // Wait counts.  Per chunk a wave issues its requests in a fixed order: the
@@ -498,6 +502,22 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
     const int c0 = split * WPG + wig;
     const int c1 = total_chunks;
     (void)cps;
+    // One row group: the workgroup's chunks -- list entry p is chunk
+    // split * W + p % W + (p / W) * stride, the chunks its waves would take
+    // round-robin -- are handed out in list order from an LDS counter as the
+    // waves ask for their next chunk, so a wave that falls behind (the second
+    // wave of a SIMD, mostly) takes fewer.  Each wave starts with entry `wave`.
+    const int n_list = W * (c1 / stride) + min(max(c1 % stride - split * W, 0), W);
+    const bool dyn = RG == 1 && n_list <= WL::LIST;
+    int* const lst = reinterpret_cast<int*>(smem + WL::LIST_OFF);     // [LIST] page entries
+    int* const lctr = lst + WL::LIST;                                   // next list entry to hand out
+    auto list_chunk = [&](int p) { return split * W + p % W + (p / W) * stride; };
+    // one list entry for the whole wave: a single lane takes it
+    auto pop = [&]() {
+        int v = 0;
+        if (lane == 0) v = atomicAdd(lctr, 1);
+        return __builtin_amdgcn_readlane(v, 0);
+    };
     // Page-table entries: lane k of `ents` holds the entry of the wave's
     // chunk number kb + k (batches of 64, one gather load per batch), and the
     // loop picks them out with readlane -- no memory access, hence no wait,
@@ -532,6 +552,10 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
         }
     }
 
+    if (dyn) {
+        for (int p = threadIdx.x; p < n_list; p += W * 64) lst[p] = a.page_table[(list_chunk(p) * kChunk) / g.P];
+        if (threadIdx.x == 0) lctr[0] = W;
+    }
     int ents = load_ents(0);
     asm volatile("" : "+v"(ents));             // wait for it (and q) here, before any chunk request
     // first slot of the current chunk in its page; it advances by dslot (mod P)
@@ -586,6 +610,8 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
     // (nothing is loaded from it) and turns its partial into NaN.
     bool bad = c0 < c1 && !ok_cur;
     int c = c0, k = 0;
+    // list mode: the wave's next list entry (handed out one chunk ahead)
+    int p_next = dyn && c0 < c1 ? pop() : 0;
     // one chunk: MASK when some key of it lies past the last key of some row
     auto chunk = [&](auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
@@ -597,15 +623,30 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
         // apart and lose their shared L2 reads).
         if (((k ^ (wave >= W / 2 ? 1 : 0)) & 1) != 0) __builtin_amdgcn_s_setprio(1);
         else __builtin_amdgcn_s_setprio(0);
-        const bool has_next = c + stride < c1;
-        if (has_next && ((k + 1) & 63) == 0) {  // every 64 chunks
-            ents = load_ents(k + 1);
-            asm volatile("" : "+v"(ents));      // consume it here, so the loop's other path has nothing to wait for
+        bool has_next, ok_next = false;
+        const uint8_t* u_next = u_cur;
+        int slot_next = slot_cur, cn = c1, p_nn = 0;
+        if (dyn) {
+            has_next = p_next < n_list;
+            if (has_next) {
+                cn = list_chunk(p_next);
+                u_next = unit_at(lst[p_next], ok_next);
+                slot_next = (cn * kChunk) % g.P;
+                p_nn = pop();                   // the entry after it
+            }
+        } else {
+            has_next = c + stride < c1;
+            if (has_next && ((k + 1) & 63) == 0) {  // every 64 chunks
+                ents = load_ents(k + 1);
+                asm volatile("" : "+v"(ents));      // consume it here, so the loop's other path has nothing to wait for
+            }
+            if (has_next) {
+                cn = c + stride;
+                u_next = unit_at(__builtin_amdgcn_readlane(ents, (k + 1) & 63), ok_next);
+                slot_next = slot_cur + dslot >= g.P ? slot_cur + dslot - g.P : slot_cur + dslot;
+            }
         }
-        bool ok_next = false;
-        const uint8_t* u_next = has_next ? unit_at(__builtin_amdgcn_readlane(ents, (k + 1) & 63), ok_next) : u_cur;
         const bool more = has_next && ok_next;  // requests for the next chunk go out in this iteration
-        const int slot_next = slot_cur + dslot >= g.P ? slot_cur + dslot - g.P : slot_cur + dslot;
         const ChunkPtr cp = chunk_ptr<D>(u_cur, g, slot_cur), np = chunk_ptr<D>(u_next, g, slot_next);
         // consuming piece J requests piece J + R: of this chunk, or of the next
         auto refill = [&](int J) {
@@ -641,7 +682,8 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
         if (has_next && !ok_next) bad = true;
         u_cur = u_next;
         slot_cur = slot_next;
-        c += stride;
+        c = cn;
+        p_next = p_nn;
         ++k;
     };
     // chunks wholly visible to every row first, then the masked ones
