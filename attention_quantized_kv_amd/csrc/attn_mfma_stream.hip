@@ -508,6 +508,9 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
     // waves ask for their next chunk, so a wave that falls behind (the second
     // wave of a SIMD, mostly) takes fewer.  Each wave starts with entry `wave`.
     const int n_list = W * (c1 / stride) + min(max(c1 % stride - split * W, 0), W);
+    // (Several row groups keep the fixed round-robin: handed out per group,
+    // the groups drift apart and lose the L2 hits of reading the same chunks
+    // at about the same time.)
     const bool dyn = RG == 1 && n_list <= WL::LIST;
     int* const lst = reinterpret_cast<int*>(smem + WL::LIST_OFF);     // [LIST] page entries
     int* const lctr = lst + WL::LIST;                                   // next list entry to hand out
