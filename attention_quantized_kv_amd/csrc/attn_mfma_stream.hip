@@ -728,6 +728,39 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
 #pragma unroll
         for (int nt = 0; nt < C::NT; ++nt) st.o[nt][jj] *= f;
     }
+    if constexpr (JJ == 2 && RG == 1 && JJ * 4 * D * W * 4 <= WL::MAIN_BYTES) {
+        // At most 8 rows: every wave puts its rows at once, compactly
+        // ([wave][jj][g4][dim]), and after one barrier the workgroup's threads
+        // sum the waves in wave order and write the partial directly.
+        float* cb = reinterpret_cast<float*>(smem);
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt)
+#pragma unroll
+            for (int jj = 0; jj < JJ; ++jj) cb[((wave * JJ + jj) * 4 + g4) * D + 16 * nt + n16] = st.o[nt][jj];
+        if (wave == 0 && n16 == 0) {
+#pragma unroll
+            for (int jj = 0; jj < JJ; ++jj) {
+                const int row = logical_row<JJ>(0, 4 * g4 + jj);
+                if (row < 0 || row >= rows) continue;
+                const size_t ps = ((size_t)(row / group) * a.n_heads + kvh * group + row % group) * n_splits + split;
+                a.ws_m[ps] = M[jj];
+                a.ws_l[ps] = Ltot[jj];
+            }
+        }
+        __syncthreads();
+        constexpr int ITEMS = JJ * 4 * D;
+        for (int item = threadIdx.x; item < ITEMS; item += W * 64) {
+            const int jj = item / (4 * D), gg = (item / D) % 4, dim = item % D;
+            const int row = logical_row<JJ>(0, 4 * gg + jj);
+            if (row < 0 || row >= rows) continue;
+            float sum = 0.0f;
+#pragma unroll
+            for (int w = 0; w < W; ++w) sum += cb[w * ITEMS + item];
+            const size_t ps = ((size_t)(row / group) * a.n_heads + kvh * group + row % group) * n_splits + split;
+            a.ws_acc[ps * D + dim] = sum;
+        }
+        return;
+    }
     float* ob = reinterpret_cast<float*>(smem);          // [RG * SLOTS][16][D]
     auto put = [&](int slot) {
 #pragma unroll
