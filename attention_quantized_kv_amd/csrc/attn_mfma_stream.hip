@@ -195,7 +195,7 @@ struct Cfg {
 // of the RG row groups | (m, l) per wave and row.  The combine first folds the
 // waves past the largest power of two P2 <= WPG into the first ones, then
 // halves P2 down to one wave; SLOTS partial sums per group are in flight.
-template <int D, int R, int W, int RG>
+template <int D, int R, int W, int RG, int JJ>
 struct WgLds {
     using C = Cfg<D, R>;
     static constexpr int WPG = W / RG;
@@ -210,7 +210,13 @@ struct WgLds {
     // of the next chunk to hand out
     static constexpr int LIST = 256;
     static constexpr int LIST_OFF = ML_OFF + W * 16 * 2 * 4;
-    static constexpr int BYTES = LIST_OFF + (RG == 1 ? (LIST + 4) * 4 : 0);
+    // up to 8 rows (JJ = 2): the waves' rows for the one-barrier combine, in
+    // a region of their own so that a wave can store them while others still
+    // stream
+    static constexpr bool SMALL_COMBINE = JJ == 2 && RG == 1;
+    static constexpr int CB_OFF = LIST_OFF + (RG == 1 ? (LIST + 4) * 4 : 0);
+    static constexpr int BYTES = CB_OFF + (SMALL_COMBINE ? W * 8 * D * 4 : 0);
+    static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
 // Wait counts.  Per chunk a wave issues its requests in a fixed order: the
@@ -470,7 +476,7 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
                                                                   int rows) {
     using C = Cfg<D, R>;
     using WT = Waits<C::KL, R>;
-    using WL = WgLds<D, R, W, RG>;
+    using WL = WgLds<D, R, W, RG, JJ>;
     // RG row groups of 16 rows; the WPG waves of group gi share its rows and
     // deal its chunks among themselves.  Every group streams the same
     // chunks, so a chunk read by a second group mostly comes from L2.
@@ -701,6 +707,63 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
     for (int jj = 0; jj < JJ; ++jj) {
         st.l[jj] = row16_sum(st.l[jj]) * 16.0f;        // weights carried 2^-kTau
         if (bad) { st.m[jj] = NAN; st.l[jj] = NAN; }
+    }
+    if constexpr (WL::SMALL_COMBINE) {
+        // At most 8 rows: every wave stores its unscaled rows ([wave][row
+        // slot][dim], row slot = 4 jj + g4) and their (m, l) ([row slot][wave]);
+        // after one barrier each thread takes 4 consecutive dims of one row:
+        // it forms the row's wave factors 2^(m_w - M) and sums the waves in
+        // wave order.
+        constexpr int SLOTW = JJ * 4 * D;             // floats per wave
+        float* cb = reinterpret_cast<float*>(smem + WL::CB_OFF);
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt)
+#pragma unroll
+            for (int jj = 0; jj < JJ; ++jj) cb[wave * SLOTW + (4 * jj + g4) * D + 16 * nt + n16] = st.o[nt][jj];
+        if (n16 == 0) {
+#pragma unroll
+            for (int jj = 0; jj < JJ; ++jj) {
+                float* d = mls + ((4 * jj + g4) * W + wave) * 2;
+                d[0] = st.m[jj];
+                d[1] = st.l[jj];
+            }
+        }
+        __syncthreads();
+        for (int unit = threadIdx.x; unit < JJ * 4 * (D / 4); unit += W * 64) {
+            const int slot = unit / (D / 4), dim = 4 * (unit % (D / 4));
+            const int jj = slot / 4, gg = slot % 4;
+            const int row = logical_row<JJ>(0, 4 * gg + jj);
+            if (row < 0 || row >= rows) continue;
+            float mw[W], lw[W];
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+                mw[w] = mls[(slot * W + w) * 2];
+                lw[w] = mls[(slot * W + w) * 2 + 1];
+            }
+            float mm = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < W; ++w) mm = fmaxf(mm, mw[w]);
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+            float lt = 0.0f;
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+                // NaN (a bad page) propagates; a wave without keys (l = 0) adds nothing
+                const float f = lw[w] == 0.0f ? 0.0f : fast_exp2(mw[w] - mm);
+                lt += lw[w] * f;
+                const floatx4 o = *reinterpret_cast<const floatx4*>(cb + w * SLOTW + slot * D + dim);
+                acc += f * o;
+            }
+            const size_t ps = ((size_t)(row / group) * a.n_heads + kvh * group + row % group) * n_splits + split;
+            *reinterpret_cast<floatx4*>(a.ws_acc + ps * D + dim) = acc;
+            if (dim == 0) {
+                a.ws_m[ps] = mm;
+                a.ws_l[ps] = lt;
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int jj = 0; jj < JJ; ++jj) {
         if (n16 == 0) {
             const int row = 4 * g4 + jj;
             mls[(wave * 16 + row) * 2 + 0] = st.m[jj];
@@ -727,39 +790,6 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
         const float f = st.l[jj] == 0.0f ? 0.0f : exp2f(st.m[jj] - mm);
 #pragma unroll
         for (int nt = 0; nt < C::NT; ++nt) st.o[nt][jj] *= f;
-    }
-    if constexpr (JJ == 2 && RG == 1 && JJ * 4 * D * W * 4 <= WL::MAIN_BYTES) {
-        // At most 8 rows: every wave puts its rows at once, compactly
-        // ([wave][jj][g4][dim]), and after one barrier the workgroup's threads
-        // sum the waves in wave order and write the partial directly.
-        float* cb = reinterpret_cast<float*>(smem);
-#pragma unroll
-        for (int nt = 0; nt < C::NT; ++nt)
-#pragma unroll
-            for (int jj = 0; jj < JJ; ++jj) cb[((wave * JJ + jj) * 4 + g4) * D + 16 * nt + n16] = st.o[nt][jj];
-        if (wave == 0 && n16 == 0) {
-#pragma unroll
-            for (int jj = 0; jj < JJ; ++jj) {
-                const int row = logical_row<JJ>(0, 4 * g4 + jj);
-                if (row < 0 || row >= rows) continue;
-                const size_t ps = ((size_t)(row / group) * a.n_heads + kvh * group + row % group) * n_splits + split;
-                a.ws_m[ps] = M[jj];
-                a.ws_l[ps] = Ltot[jj];
-            }
-        }
-        __syncthreads();
-        constexpr int ITEMS = JJ * 4 * D;
-        for (int item = threadIdx.x; item < ITEMS; item += W * 64) {
-            const int jj = item / (4 * D), gg = (item / D) % 4, dim = item % D;
-            const int row = logical_row<JJ>(0, 4 * gg + jj);
-            if (row < 0 || row >= rows) continue;
-            float sum = 0.0f;
-#pragma unroll
-            for (int w = 0; w < W; ++w) sum += cb[w * ITEMS + item];
-            const size_t ps = ((size_t)(row / group) * a.n_heads + kvh * group + row % group) * n_splits + split;
-            a.ws_acc[ps * D + dim] = sum;
-        }
-        return;
     }
     float* ob = reinterpret_cast<float*>(smem);          // [RG * SLOTS][16][D]
     auto put = [&](int slot) {
@@ -821,7 +851,7 @@ template <int D, int JJ, int RG>
 hipError_t launch_dr(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) {
     constexpr int R = D == 64 ? 3 : D == 128 ? 3 : 4;   // ring slots: a few KiB in flight per wave
     constexpr int W = stream_waves<JJ>();
-    using WL = WgLds<D, R, W, RG>;
+    using WL = WgLds<D, R, W, RG, JJ>;
     auto kern = attn_mfma_stream_kernel<D, JJ, RG, R, W>;
     if (WL::BYTES > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
