@@ -854,8 +854,7 @@ hipError_t launch_dr(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) 
     using WL = WgLds<D, R, W, RG, JJ>;
     auto kern = attn_mfma_stream_kernel<D, JJ, RG, R, W>;
     if (WL::BYTES > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, WL::BYTES);
+        hipError_t e = allow_lds<attn_mfma_stream_kernel<D, JJ, RG, R, W>>(WL::BYTES);
         if (e != hipSuccess) return e;
     }
     dim3 grid(pl.n_splits * a.g.n_kv);

@@ -600,8 +600,7 @@ hipError_t launch_dr(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) 
     using C = TCfg<D, RT>;
     auto kern = attn_mfma_tiled_kernel<D, RT>;
     if (C::LDS > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
+        hipError_t e = allow_lds<attn_mfma_tiled_kernel<D, RT>>(C::LDS);
         if (e != hipSuccess) return e;
     }
     const int row_tiles = (pl.rows + kRowsPerWg - 1) / kRowsPerWg;

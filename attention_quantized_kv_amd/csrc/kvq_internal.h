@@ -110,6 +110,21 @@ inline size_t ws_bytes_for(const AttnPlan& pl, int n_q, int n_heads, int D) {
     return acc + 2 * ((ml + 255) / 256 * 256);
 }
 
+// Raises kernel Kern's dynamic LDS limit to `bytes`, once per kernel and
+// device (so that a launch inside a stream capture makes no such call).
+template <auto Kern>
+inline hipError_t allow_lds(int bytes) {
+    static unsigned int done = 0;   // bit d: set on device d
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const unsigned int bit = dev < 32 ? 1u << dev : 0u;
+    if (bit != 0 && (__atomic_load_n(&done, __ATOMIC_ACQUIRE) & bit) != 0) return hipSuccess;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(Kern), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && bit != 0) __atomic_fetch_or(&done, bit, __ATOMIC_RELEASE);
+    return e;
+}
+
 // Kernel launchers (each returns the hipError_t of its launch).
 hipError_t launch_append(const Geom& g, uint8_t* pool, const int32_t* page_table, int pos0,
                          int n_new, const float* k, const float* v, hipStream_t stream);

@@ -215,6 +215,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--shuffle-pages", action="store_true",
                     help="random page table (pages scattered over the pool) instead of in-order pages")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step (every layer) in a HIP graph and time its replays; the attention "
+                         "kernel is then timed by library events in a separate eager pass")
     ap.add_argument("--copy-gib", type=float, default=0.0,
                     help="only copy a buffer of this many GiB --steps times (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -288,6 +291,22 @@ def main():
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
+    if args.graph:
+        # the step's launches recorded once, replayed as one graph per step
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(max(args.warmup, 1)):
+            graph.replay()
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(args.steps):
+            graph.replay()
+        stop.record()
+        torch.cuda.synchronize()
+        eager_ms = total_ms
+        total_ms = start.elapsed_time(stop)
     attn_ms = [hip_ev.elapsed_ms(e[0], e[1]) for e in evs]
     for e in evs:
         hip_ev.destroy(e[0])
@@ -311,7 +330,8 @@ def main():
                    "chunks_per_split": args.cps or "auto",
                    "step": ("kvq_append_attn (append + attention, 2 kernels)" if fused else
                             "kvq_append, then attention" if not prefill else "attention"),
-                   "page_table": "shuffled" if args.shuffle_pages else "in order"},
+                   "page_table": "shuffled" if args.shuffle_pages else "in order",
+                   "launch": "hipGraph replay of the step" if args.graph else "eager"},
     }
     if not prefill:
         value = n_layers * bytes_layer * args.steps / (total_ms / 1e3) / 1e9
@@ -342,6 +362,8 @@ def main():
                 "higher_is_better": True, "scaling": "weak", "vs_baseline": None})
     rec["roofline"] = roof
     rec.update(extra)
+    if args.graph:
+        rec["eager_us_per_layer"] = round(1000.0 * eager_ms / args.steps / n_layers, 3)
     del layers
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
