@@ -22,6 +22,7 @@ KVQ_ERR_WORKSPACE = -3
 KVQ_ERR_CAPACITY = -4
 KVQ_ERR_HIP = -5
 KVQ_MAX_NQ_DECODE = 8
+KVQ_MAX_SEQS = 64
 
 KERNEL_AUTO, KERNEL_VALU, KERNEL_MFMA_STREAM, KERNEL_MFMA_TILED = 0, 1, 2, 3
 
@@ -29,6 +30,7 @@ EXPORTS = (
     "kvq_unit_bytes", "kvq_pool_bytes", "kvq_append", "kvq_workspace_bytes",
     "kvq_decode_attn", "kvq_prefill_attn", "kvq_workspace_bytes_ex", "kvq_attn_ex",
     "kvq_append_attn_workspace_bytes", "kvq_append_attn",
+    "kvq_decode_attn_batch_workspace_bytes", "kvq_decode_attn_batch",
     "kvq_status_str", "kvq_last_error", "kvq_version",
 )
 
@@ -83,6 +85,8 @@ def lib() -> ctypes.CDLL:
         "kvq_attn_ex": [LP, P, P, i32, i32, i32, i32, P, ctypes.c_float, P, P, P, sz, OP, P],
         "kvq_append_attn_workspace_bytes": [LP, i32, i32, i32, OP, SZP],
         "kvq_append_attn": [LP, P, P, i32, i32, i32, P, P, i32, P, ctypes.c_float, P, P, P, sz, OP, P],
+        "kvq_decode_attn_batch_workspace_bytes": [LP, i32, P, i32, i32, SZP],
+        "kvq_decode_attn_batch": [LP, P, P, i32, i32, P, i32, i32, P, ctypes.c_float, P, P, P, sz, OP, P],
         "kvq_status_str": [ctypes.c_int],
         "kvq_last_error": [],
         "kvq_version": [],
@@ -277,3 +281,50 @@ def kvq_append_attn(layout: Layout, pool, page_table, pos0: int, k, v, q, scale:
     _check(lib().kvq_append_attn(ctypes.byref(layout), _ptr(pool), _ptr(page_table), nt, int(pos0), n_q,
                                  _ptr(k), _ptr(v), n_heads, _ptr(q), float(scale), _ptr(out), _ptr(lse),
                                  _ptr(ws), ws_bytes, ctypes.byref(opts), _stream(stream)), "kvq_append_attn")
+
+
+def _ctx_array(ctx_lens):
+    vals = [int(c) for c in ctx_lens]
+    return (ctypes.c_int32 * max(len(vals), 1))(*vals), len(vals)
+
+
+def kvq_decode_attn_batch_workspace_bytes(layout: Layout, ctx_lens, n_heads: int, n_q: int) -> int:
+    """Workspace bytes of kvq_decode_attn_batch for these sequences."""
+    arr, n = _ctx_array(ctx_lens)
+    out = ctypes.c_size_t(0)
+    _check(lib().kvq_decode_attn_batch_workspace_bytes(ctypes.byref(layout), n, ctypes.cast(arr, ctypes.c_void_p),
+                                                       int(n_heads), int(n_q), ctypes.byref(out)),
+           "kvq_decode_attn_batch_workspace_bytes")
+    return out.value
+
+
+def kvq_decode_attn_batch(layout: Layout, pool, page_tables, ctx_lens, q, scale: float, out, lse=None,
+                          ws=None, stream=None, events=None):
+    """Decode of several sequences in one call: page_tables int32 [n_seqs][n_table]
+    (device), ctx_lens a host sequence of n_seqs ints, q and out
+    [n_seqs][n_q][n_heads][D], lse [n_seqs][n_q][n_heads] or None; events as
+    for kvq_attn_ex (recorded around the streaming kernel)."""
+    import torch
+    _need(pool, "pool", torch.uint8)
+    _need(page_tables, "page_tables", torch.int32)
+    _need(q, "q", torch.float32)
+    _need(out, "out", torch.float32)
+    _need(lse, "lse", torch.float32)
+    _need(ws, "workspace", torch.uint8)
+    if page_tables.dim() != 2 or q.dim() != 4:
+        raise ValueError("page_tables must be [n_seqs][n_table] and q [n_seqs][n_q][n_heads][D]")
+    arr, n = _ctx_array(ctx_lens)
+    if page_tables.shape[0] != n or q.shape[0] != n:
+        raise ValueError("page_tables, ctx_lens and q must cover the same sequences")
+    ws_bytes = 0 if ws is None else ws.numel()
+    opts = AttnOpts(0, 0)
+    if events is not None:
+        if not events[0] or not events[1]:
+            raise ValueError("events must be two created hipEvent_t handles")
+        opts.kernel_begin_event = events[0]
+        opts.kernel_end_event = events[1]
+    _check(lib().kvq_decode_attn_batch(ctypes.byref(layout), _ptr(pool), _ptr(page_tables),
+                                       int(page_tables.shape[1]), n, ctypes.cast(arr, ctypes.c_void_p),
+                                       int(q.shape[2]), int(q.shape[1]), _ptr(q), float(scale), _ptr(out),
+                                       _ptr(lse), _ptr(ws), ws_bytes, ctypes.byref(opts), _stream(stream)),
+           "kvq_decode_attn_batch")

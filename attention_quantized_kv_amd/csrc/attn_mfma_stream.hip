@@ -471,9 +471,9 @@ __device__ inline void wait_pv(int p) {
     }
 }
 
-template <int D, int JJ, int RG, int R, int W>
+template <int D, int JJ, int RG, int R, int W, class Batch>
 __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, int cps, int n_splits, int group,
-                                                                  int rows) {
+                                                                  int rows, Batch sb) {
     using C = Cfg<D, R>;
     using WT = Waits<C::KL, R>;
     using WL = WgLds<D, R, W, RG, JJ>;
@@ -485,8 +485,22 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
     const Geom& g = a.g;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave: scalar
-    const int split = blockIdx.x % n_splits;
-    const int kvh = blockIdx.x / n_splits;
+    int wg = blockIdx.x;
+    if constexpr (!std::is_same_v<Batch, NoBatch>) {
+        // batched decode: this workgroup serves sequence b, whose keys, page
+        // table row, queries and partials start where the table says
+        const int b = seq_of(sb.wg0, sb.n, wg);
+        wg -= sb.wg0[b];
+        n_splits = sb.n_splits[b];
+        a.ctx = sb.ctx[b];
+        a.page_table += (size_t)b * sb.n_table;
+        a.q += (size_t)b * a.n_q * a.n_heads * D;
+        a.ws_m += sb.part0[b];
+        a.ws_l += sb.part0[b];
+        a.ws_acc += (size_t)sb.part0[b] * D;
+    }
+    const int split = wg % n_splits;
+    const int kvh = wg / n_splits;
     const int total_chunks = (a.ctx + kChunk - 1) / kChunk;
     // last key of query 0; query i sees i keys more (causal), or all keys
     const int first_last = a.causal ? a.ctx - a.n_q : a.ctx - 1;
@@ -847,31 +861,40 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
 template <int JJ>
 constexpr int stream_waves() { return 8; }
 
-template <int D, int JJ, int RG>
-hipError_t launch_dr(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) {
+template <int D, int JJ, int RG, class Batch>
+hipError_t launch_dr(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream, const Batch& sb, int n_wg) {
     constexpr int R = D == 64 ? 3 : D == 128 ? 3 : 4;   // ring slots: a few KiB in flight per wave
     constexpr int W = stream_waves<JJ>();
     using WL = WgLds<D, R, W, RG, JJ>;
-    auto kern = attn_mfma_stream_kernel<D, JJ, RG, R, W>;
+    auto kern = attn_mfma_stream_kernel<D, JJ, RG, R, W, Batch>;
     if (WL::BYTES > 64 * 1024) {
-        hipError_t e = allow_lds<attn_mfma_stream_kernel<D, JJ, RG, R, W>>(WL::BYTES);
+        hipError_t e = allow_lds<attn_mfma_stream_kernel<D, JJ, RG, R, W, Batch>>(WL::BYTES);
         if (e != hipSuccess) return e;
     }
-    dim3 grid(pl.n_splits * a.g.n_kv);
-    hipLaunchKernelGGL(kern, grid, dim3(W * 64), WL::BYTES, stream, a, pl.chunks_per_split, pl.n_splits,
-                       pl.group, pl.rows);
+    hipLaunchKernelGGL(kern, dim3(n_wg), dim3(W * 64), WL::BYTES, stream, a, pl.chunks_per_split, pl.n_splits,
+                       pl.group, pl.rows, sb);
     return hipGetLastError();
 }
 
 // Up to 8 rows two per lane group (JJ = 2), up to 16 rows one per MFMA row,
 // more rows in 2 or 4 row groups of 16.
-template <int D>
-hipError_t launch_d(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) {
-    if (pl.rows <= 8) return launch_dr<D, 2, 1>(a, pl, stream);
-    if (pl.rows <= 16) return launch_dr<D, 4, 1>(a, pl, stream);
-    if (pl.rows <= 32) return launch_dr<D, 4, 2>(a, pl, stream);
-    if (pl.rows <= 64) return launch_dr<D, 4, 4>(a, pl, stream);
+template <int D, class Batch>
+hipError_t launch_d(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream, const Batch& sb, int n_wg) {
+    if (pl.rows <= 8) return launch_dr<D, 2, 1>(a, pl, stream, sb, n_wg);
+    if (pl.rows <= 16) return launch_dr<D, 4, 1>(a, pl, stream, sb, n_wg);
+    if (pl.rows <= 32) return launch_dr<D, 4, 2>(a, pl, stream, sb, n_wg);
+    if (pl.rows <= 64) return launch_dr<D, 4, 4>(a, pl, stream, sb, n_wg);
     return hipErrorInvalidValue;
+}
+
+template <class Batch>
+hipError_t launch_any(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream, const Batch& sb, int n_wg) {
+    switch (a.g.D) {
+        case 64: return launch_d<64>(a, pl, stream, sb, n_wg);
+        case 128: return launch_d<128>(a, pl, stream, sb, n_wg);
+        case 256: return launch_d<256>(a, pl, stream, sb, n_wg);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
@@ -881,13 +904,9 @@ int mfma_stream_waves(int rows) {
     return (rows <= 8 ? stream_waves<2>() : stream_waves<4>()) / mfma_stream_row_groups(rows);
 }
 
-hipError_t launch_attn_mfma_stream(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) {
-    switch (a.g.D) {
-        case 64: return launch_d<64>(a, pl, stream);
-        case 128: return launch_d<128>(a, pl, stream);
-        case 256: return launch_d<256>(a, pl, stream);
-        default: return hipErrorInvalidValue;
-    }
+hipError_t launch_attn_mfma_stream(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream, const SeqBatch* batch) {
+    if (batch != nullptr && batch->n > 0) return launch_any(a, pl, stream, *batch, batch->wg0[batch->n]);
+    return launch_any(a, pl, stream, NoBatch{}, pl.n_splits * a.g.n_kv);
 }
 
 }  // namespace kvq

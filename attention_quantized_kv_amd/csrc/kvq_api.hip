@@ -4,6 +4,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
+
 #include "../../include/kvq.h"
 #include "kvq_internal.h"
 
@@ -22,6 +24,13 @@ int fail(int status, const char* fmt, ...) {
 int ok() {
     g_err[0] = '\0';
     return KVQ_OK;
+}
+
+// The current detail, copied (for a message that wraps it).
+const char* kvq_last_error_copy() {
+    thread_local char copy[512];
+    snprintf(copy, sizeof(copy), "%s", g_err);
+    return copy;
 }
 
 int check_layout(const kvq_layout* L, kvq::Geom* g) {
@@ -225,6 +234,56 @@ int check_append_attn(const kvq_layout* L, int32_t n_table, int32_t pos0, int32_
     return KVQ_OK;
 }
 
+// Batched decode plan: every sequence's split count from its share of the
+// context (about one workgroup per CU and KV head in all), the workgroup and
+// partial offsets of each, and the partials in all (for the workspace).
+int batch_plan(const kvq_layout* L, int32_t n_table, int32_t n_seqs, const int32_t* ctx_lens, int32_t n_heads,
+               int32_t n_q, kvq::AttnPlan* pl, kvq::SeqBatch* sb, size_t* parts) {
+    kvq::Geom g;
+    int st = check_layout(L, &g);
+    if (st) return st;
+    if (n_seqs < 1 || n_seqs > KVQ_MAX_SEQS)
+        return fail(KVQ_ERR_INVALID_ARG, "n_seqs %d outside [1, %d]", n_seqs, KVQ_MAX_SEQS);
+    if (ctx_lens == nullptr) return fail(KVQ_ERR_INVALID_ARG, "ctx_lens is NULL");
+    if (n_q < 1 || n_q > KVQ_MAX_NQ_DECODE)
+        return fail(KVQ_ERR_INVALID_ARG, "batched decode takes 1 <= n_q <= %d (got %d)", KVQ_MAX_NQ_DECODE, n_q);
+    long total = 0;
+    for (int b = 0; b < n_seqs; ++b) {
+        st = check_attn_shape(L, n_table, ctx_lens[b], n_heads, n_q, false);
+        if (st) return fail(st, "sequence %d: %s", b, kvq_last_error_copy());
+        total += (ctx_lens[b] + kvq::kChunk - 1) / kvq::kChunk;
+    }
+    kvq_attn_opts opts{2, 1, nullptr, nullptr};
+    st = make_plan(L, n_heads, ctx_lens[0], n_q, false, &opts, pl);   // kernel, group, rows
+    if (st) return st;
+    const int wpg = kvq::mfma_stream_waves(pl->rows);
+    long per_head = device_cus() / L->n_kv_heads;
+    if (per_head < 1) per_head = 1;
+    sb->n = n_seqs;
+    sb->n_table = n_table;
+    long wg = 0, part = 0;
+    for (int b = 0; b < n_seqs; ++b) {
+        const long chunks = (ctx_lens[b] + kvq::kChunk - 1) / kvq::kChunk;
+        long want = (per_head * chunks + total / 2) / total;
+        if (want < 1) want = 1;
+        const long cps = (chunks + wpg * want - 1) / (wpg * want);
+        const long splits = (chunks + wpg * cps - 1) / (wpg * cps);
+        sb->wg0[b] = (int)wg;
+        sb->ctx[b] = ctx_lens[b];
+        sb->n_splits[b] = (int)splits;
+        sb->part0[b] = (int)part;
+        wg += splits * L->n_kv_heads;
+        part += (long)n_q * n_heads * splits;
+    }
+    sb->wg0[n_seqs] = (int)wg;
+    *parts = (size_t)part;
+    return KVQ_OK;
+}
+
+size_t batch_ws_bytes(size_t parts, int D) {
+    return 2 * ((parts * sizeof(float) + 255) / 256 * 256) + parts * (size_t)D * sizeof(float);
+}
+
 }  // namespace
 
 extern "C" {
@@ -391,6 +450,73 @@ int kvq_attn_ex(const kvq_layout* layout, const void* d_pool, const int32_t* d_p
                 void* stream) {
     return attn_impl(layout, d_pool, d_page_table, n_table, ctx_len, n_heads, n_q, d_q, scale, d_out, d_lse,
                      d_ws, ws_bytes, n_q > KVQ_MAX_NQ_DECODE, opts, stream);
+}
+
+int kvq_decode_attn_batch_workspace_bytes(const kvq_layout* layout, int32_t n_seqs, const int32_t* ctx_lens,
+                                          int32_t n_heads, int32_t n_q, size_t* bytes) {
+    if (bytes == nullptr) return fail(KVQ_ERR_INVALID_ARG, "bytes is NULL");
+    kvq::AttnPlan pl;
+    kvq::SeqBatch sb;
+    size_t parts = 0;
+    // the plan does not depend on the page table: pass a table that fits
+    int32_t n_table = 1;
+    if (layout != nullptr && ctx_lens != nullptr && n_seqs >= 1 && n_seqs <= KVQ_MAX_SEQS && layout->page_size > 0)
+        for (int b = 0; b < n_seqs; ++b)
+            n_table = std::max(n_table, (ctx_lens[b] + layout->page_size - 1) / layout->page_size);
+    int st = batch_plan(layout, n_table, n_seqs, ctx_lens, n_heads, n_q, &pl, &sb, &parts);
+    if (st) return st;
+    *bytes = batch_ws_bytes(parts, layout->head_dim);
+    return ok();
+}
+
+int kvq_decode_attn_batch(const kvq_layout* layout, const void* d_pool, const int32_t* d_page_tables, int32_t n_table,
+                          int32_t n_seqs, const int32_t* ctx_lens, int32_t n_heads, int32_t n_q,
+                          const float* d_q, float scale, float* d_out, float* d_lse,
+                          void* d_ws, size_t ws_bytes, const kvq_attn_opts* opts, void* stream) {
+    if (d_pool == nullptr || d_page_tables == nullptr || d_q == nullptr || d_out == nullptr)
+        return fail(KVQ_ERR_INVALID_ARG, "pool, page_tables, q and out must be non-NULL");
+    if (opts != nullptr && opts->kernel != 0 && opts->kernel != 2)
+        return fail(KVQ_ERR_INVALID_ARG, "batched decode runs the streaming kernel (kernel 0 or 2, got %d)",
+                    opts->kernel);
+    kvq::AttnPlan pl;
+    kvq::SeqBatch sb;
+    size_t parts = 0;
+    int st = batch_plan(layout, n_table, n_seqs, ctx_lens, n_heads, n_q, &pl, &sb, &parts);
+    if (st) return st;
+    const size_t need = batch_ws_bytes(parts, layout->head_dim);
+    if (d_ws == nullptr || ws_bytes < need)
+        return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, ws_bytes,
+                    d_ws == nullptr ? " (NULL)" : "");
+    if (((uintptr_t)d_pool & 255) != 0) return fail(KVQ_ERR_INVALID_ARG, "pool must be 256-byte aligned");
+    if (((uintptr_t)d_ws & 15) != 0) return fail(KVQ_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    kvq::Geom g;
+    check_layout(layout, &g);
+    kvq::AttnArgs a;
+    a.g = g;
+    a.pool = static_cast<const uint8_t*>(d_pool);
+    a.page_table = d_page_tables;
+    a.ctx = sb.ctx[0];
+    a.n_heads = n_heads;
+    a.n_q = n_q;
+    a.q = d_q;
+    a.scale = scale;
+    a.out = d_out;
+    a.lse = d_lse;
+    uint8_t* ws = static_cast<uint8_t*>(d_ws);
+    const size_t ml = (parts * sizeof(float) + 255) / 256 * 256;
+    a.ws_m = reinterpret_cast<float*>(ws);
+    a.ws_l = reinterpret_cast<float*>(ws + ml);
+    a.ws_acc = reinterpret_cast<float*>(ws + 2 * ml);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    if (opts != nullptr && opts->kernel_begin_event != nullptr)
+        e = hipEventRecord(static_cast<hipEvent_t>(opts->kernel_begin_event), s);
+    if (e == hipSuccess) e = kvq::launch_attn_mfma_stream(a, pl, s, &sb);
+    if (e == hipSuccess && opts != nullptr && opts->kernel_end_event != nullptr)
+        e = hipEventRecord(static_cast<hipEvent_t>(opts->kernel_end_event), s);
+    if (e == hipSuccess) e = kvq::launch_merge(a, pl, s, &sb);
+    if (e != hipSuccess) return fail(KVQ_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return ok();
 }
 
 }  // extern "C"

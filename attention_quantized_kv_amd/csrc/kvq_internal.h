@@ -101,6 +101,29 @@ struct NewRows {
     int n_new;       // = n_q
 };
 
+// Several sequences in one launch (batched decode): each has its own context
+// length, page-table row and split count; the streaming kernel's workgroups
+// and the merge kernel's rows are dealt to the sequences in order.  n = 0: a
+// single-sequence call, where AttnArgs and the plan say everything.
+constexpr int kMaxSeqs = 64;
+struct SeqBatch {
+    int n = 0;                 // sequences in the launch
+    int n_table = 0;           // page-table entries per sequence (row stride of the page tables)
+    int wg0[kMaxSeqs + 1];     // first streaming workgroup of sequence b; wg0[n] = the grid
+    int ctx[kMaxSeqs];         // keys of sequence b
+    int n_splits[kMaxSeqs];    // partials per query row of sequence b
+    int part0[kMaxSeqs];       // first partial of sequence b (rows of all sequences are n_q * n_heads)
+};
+struct NoBatch {};             // the kernel argument of single-sequence launches
+
+// Index of the sequence that owns item `i` of a launch, given each sequence's
+// first item (first[0] = 0, first[n] = the total); uniform across the wave.
+__device__ inline int seq_of(const int* first, int n, int i) {
+    int b = 0;
+    while (b + 1 < n && i >= first[b + 1]) ++b;
+    return b;
+}
+
 // Workspace bytes for a plan.
 inline size_t ws_bytes_for(const AttnPlan& pl, int n_q, int n_heads, int D) {
     if (pl.n_splits <= 1 && pl.kernel == 3) return 0;
@@ -129,9 +152,10 @@ inline hipError_t allow_lds(int bytes) {
 hipError_t launch_append(const Geom& g, uint8_t* pool, const int32_t* page_table, int pos0,
                          int n_new, const float* k, const float* v, hipStream_t stream);
 hipError_t launch_attn_valu(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream);
-hipError_t launch_attn_mfma_stream(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream);
+hipError_t launch_attn_mfma_stream(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream,
+                                   const SeqBatch* batch = nullptr);
 hipError_t launch_attn_mfma_tiled(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream);
-hipError_t launch_merge(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream);
+hipError_t launch_merge(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream, const SeqBatch* batch = nullptr);
 // Merge of n_splits partials (0: none) with the new rows' keys, and the
 // rows' quantized write into the pool.
 hipError_t launch_merge_new(const AttnArgs& a, const NewRows& nr, int n_splits, hipStream_t stream);

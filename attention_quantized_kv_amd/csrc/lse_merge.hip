@@ -11,6 +11,8 @@
 //
 // Splits with no visible key (l = 0) are skipped; a NaN partial (a page-table
 // entry outside the pool) propagates to the output.
+#include <type_traits>
+
 #include "kvq_quant.h"
 
 namespace kvq {
@@ -25,15 +27,24 @@ constexpr float kLog2eM = 1.4426950408889634f;
 // memory round trip), while wave 0 folds the batch's (m, l) into weights:
 // M' = max(M, max_s m_s), w_s = 2^(m_s - M'), L' = L 2^(M - M') + sum w_s l_s;
 // then o' = o 2^(M - M') + sum w_s acc_s.  The folding order is fixed.
-template <int D>
-__global__ __launch_bounds__(D) void merge_kernel(AttnArgs a, int n_splits) {
+// Batched launches: row b * n_q * n_heads + r is row r of sequence b, whose
+// partials start at partial b.part0[b] and number n_splits[b] per row.
+template <int D, class Batch>
+__global__ __launch_bounds__(D) void merge_kernel(AttnArgs a, int n_splits, Batch sb) {
     __shared__ float w_s[kBatch];
     __shared__ float alpha_s, l_s, m_s;
     const int row = blockIdx.x;
     const int t = threadIdx.x;
-    const float* m = a.ws_m + (size_t)row * n_splits;
-    const float* l = a.ws_l + (size_t)row * n_splits;
-    const float* acc = a.ws_acc + (size_t)row * n_splits * D + t;
+    size_t p0 = (size_t)row * n_splits;            // this row's first partial
+    if constexpr (!std::is_same_v<Batch, NoBatch>) {
+        const int rps = a.n_q * a.n_heads;
+        const int b = row / rps;
+        n_splits = sb.n_splits[b];
+        p0 = (size_t)sb.part0[b] + (size_t)(row - b * rps) * n_splits;
+    }
+    const float* m = a.ws_m + p0;
+    const float* l = a.ws_l + p0;
+    const float* acc = a.ws_acc + p0 * D + t;
     float M = -INFINITY, L = 0.0f, o = 0.0f;       // wave 0 keeps M, L; every thread its o
     for (int s0 = 0; s0 < n_splits; s0 += kBatch) {
         const int nb = min(kBatch, n_splits - s0);
@@ -233,15 +244,22 @@ hipError_t launch_merge_new(const AttnArgs& a, const NewRows& nr, int n_splits, 
     return hipGetLastError();
 }
 
-hipError_t launch_merge(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) {
-    dim3 grid(a.n_q * a.n_heads);
+template <class Batch>
+hipError_t launch_merge_b(const AttnArgs& a, int n_splits, int n_rows, hipStream_t stream, const Batch& sb) {
+    dim3 grid(n_rows);
     switch (a.g.D) {
-        case 64: hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(64), 0, stream, a, pl.n_splits); break;
-        case 128: hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(128), 0, stream, a, pl.n_splits); break;
-        case 256: hipLaunchKernelGGL(merge_kernel<256>, grid, dim3(256), 0, stream, a, pl.n_splits); break;
+        case 64: hipLaunchKernelGGL((merge_kernel<64, Batch>), grid, dim3(64), 0, stream, a, n_splits, sb); break;
+        case 128: hipLaunchKernelGGL((merge_kernel<128, Batch>), grid, dim3(128), 0, stream, a, n_splits, sb); break;
+        case 256: hipLaunchKernelGGL((merge_kernel<256, Batch>), grid, dim3(256), 0, stream, a, n_splits, sb); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_merge(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream, const SeqBatch* batch) {
+    if (batch != nullptr && batch->n > 0)
+        return launch_merge_b(a, 0, batch->n * a.n_q * a.n_heads, stream, *batch);
+    return launch_merge_b(a, pl.n_splits, a.n_q * a.n_heads, stream, NoBatch{});
 }
 
 }  // namespace kvq

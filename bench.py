@@ -122,6 +122,40 @@ class Layer:
                              ws, kernel=kernel, chunks_per_split=self.cps, events=events)
 
 
+class BatchLayer:
+    """One layer of the batched-decode workload: n_seqs sequences of ctx tokens
+    in one pool, page p of sequence b at physical page p * n_seqs + b (the
+    requests' pages interleaved, as in a serving pool)."""
+
+    def __init__(self, w, layer, device, fill_chunk=16384):
+        import torch
+        import attention_quantized_kv_amd as kvq
+        self.kvq = kvq
+        self.w = w
+        pages = w.n_pages
+        self.L = kvq.Layout(w.n_kv, w.head_dim, w.page_size, pages * w.n_seqs)
+        self.pool = torch.empty(kvq.kvq_pool_bytes(self.L), dtype=torch.uint8, device=device)
+        pt = torch.arange(pages)[None, :] * w.n_seqs + torch.arange(w.n_seqs)[:, None]
+        self.pt = pt.to(torch.int32).to(device).contiguous()
+        base = (w.wid * 1000 + layer) * 1_000_003
+        for b in range(w.n_seqs):
+            for r in range(0, w.ctx, fill_chunk):
+                n = min(fill_chunk, w.ctx - r)
+                k = device_normal((n, w.n_kv, w.head_dim), base + 4 * (b * w.ctx + r) + 1, device)
+                v = device_normal((n, w.n_kv, w.head_dim), base + 4 * (b * w.ctx + r) + 2, device)
+                kvq.kvq_append(self.L, self.pool, self.pt[b], r, k, v)
+        self.q = device_normal((w.n_seqs, w.n_q, w.n_heads, w.head_dim), base + 9, device)
+        self.out = torch.empty_like(self.q)
+        self.lse = torch.empty((w.n_seqs, w.n_q, w.n_heads), dtype=torch.float32, device=device)
+        self.ctx_lens = [w.ctx] * w.n_seqs
+
+    def attend(self, ws, kernel, events=None):
+        """kvq_decode_attn_batch over every sequence; `events` (begin, end) are
+        recorded around the streaming kernel."""
+        self.kvq.kvq_decode_attn_batch(self.L, self.pool, self.pt, self.ctx_lens, self.q, self.w.scale,
+                                       self.out, self.lse, ws, events=events)
+
+
 KERNEL_SOURCES = {"attn_mfma_stream": "attn_mfma_stream.hip", "attn_mfma_tiled": "attn_mfma_tiled.hip",
                   "attn_valu": "attn_valu.hip"}
 
@@ -175,6 +209,8 @@ def cpu_baseline(w, min_seconds: float, max_reps: int = 8):
     if w.n_q <= 8:
         rows = [(i, h) for i in range(w.n_q) for h in range(w.n_heads)]
         desc = f"one {w.ctx}-token layer, all {len(rows)} query rows"
+        if w.n_seqs > 1:
+            desc = f"one of the {w.n_seqs} sequences of a layer ({w.ctx} tokens), all {len(rows)} query rows"
         bytes_per_rep = w.ctx * kv_bytes_per_token_layer(w.n_kv, w.head_dim)
     else:
         rng = __import__("numpy").random.default_rng(0)
@@ -205,7 +241,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="decode262k",
-                    choices=["tiny", "decode65k", "decode262k", "verify131k", "prefill262k"])
+                    choices=["tiny", "decode65k", "decode262k", "verify131k", "prefill262k", "batch16x16k"])
     ap.add_argument("--layers", type=int, default=None, help="layers in the stack (default: the workload's)")
     ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA streaming, 3 MFMA tiled")
     ap.add_argument("--cps", type=int, default=0, help="32-token chunks per split (0: the library's choice)")
@@ -253,10 +289,16 @@ def main():
     torch.cuda.set_device(dev)
 
     t0 = time.time()
-    layers = [Layer(w, i, dev, shuffle_pages=args.shuffle_pages) for i in range(n_layers)]
+    batched = w.n_seqs > 1
+    if batched:
+        layers = [BatchLayer(w, i, dev) for i in range(n_layers)]
+    else:
+        layers = [Layer(w, i, dev, shuffle_pages=args.shuffle_pages) for i in range(n_layers)]
     Layer.cps = args.cps
-    fused = not prefill and not args.unfused
-    if fused:
+    fused = not prefill and not args.unfused and not batched
+    if batched:
+        ws_n = kvq.kvq_decode_attn_batch_workspace_bytes(layers[0].L, layers[0].ctx_lens, w.n_heads, w.n_q)
+    elif fused:
         ws_n = kvq.kvq_append_attn_workspace_bytes(layers[0].L, w.n_heads, w.cached, w.n_q, args.kernel, args.cps)
     else:
         ws_n = kvq.kvq_workspace_bytes_ex(layers[0].L, w.n_heads, w.ctx, w.n_q, args.kernel, args.cps)
@@ -271,7 +313,9 @@ def main():
     def step(ev=None, s=0):
         for i, lay in enumerate(layers):
             e = ev if (ev is not None and i == s % n_layers) else None
-            if fused:
+            if batched:
+                lay.attend(ws, args.kernel, e)
+            elif fused:
                 lay.decode_step(ws, args.kernel, e)
             else:
                 lay.append()
@@ -316,28 +360,31 @@ def main():
     traffic = measured_traffic(w.name, kname)
 
     ms_per_step = total_ms / args.steps
-    bytes_layer = w.ctx * kv_bytes_per_token_layer(w.n_kv, w.head_dim)
+    bytes_layer = w.n_seqs * w.ctx * kv_bytes_per_token_layer(w.n_kv, w.head_dim)
     # bytes the timed kernel reads: the fused step's split pass reads the cached keys only
-    bytes_kernel = (w.cached if fused else w.ctx) * kv_bytes_per_token_layer(w.n_kv, w.head_dim)
+    bytes_kernel = w.n_seqs * (w.cached if fused else w.ctx) * kv_bytes_per_token_layer(w.n_kv, w.head_dim)
     us_per_layer = 1000.0 * ms_per_step / n_layers
     flops_layer = attention_flops(w)
     rec = {
         "data": "synthetic",
         "dtype": "f16 MFMA / f32" if args.kernel in (0, 2, 3) else "f32",
-        "config": {"workload": w.name, "layers": n_layers, "n_heads": w.n_heads, "n_kv_heads": w.n_kv,
+        "config": {"workload": w.name, "layers": n_layers, **({"n_seqs": w.n_seqs} if batched else {}), "n_heads": w.n_heads, "n_kv_heads": w.n_kv,
                    "head_dim": w.head_dim, "ctx": w.ctx, "n_q": w.n_q, "page_size": w.page_size,
                    "kv_format": "K Q8_0 + V Q4_0", "kernel": args.kernel or "auto",
                    "chunks_per_split": args.cps or "auto",
                    "step": ("kvq_append_attn (append + attention, 2 kernels)" if fused else
-                            "kvq_append, then attention" if not prefill else "attention"),
-                   "page_table": "shuffled" if args.shuffle_pages else "in order",
+                            f"kvq_decode_attn_batch over {w.n_seqs} sequences (2 kernels; cache filled beforehand)"
+                            if batched else "kvq_append, then attention" if not prefill else "attention"),
+                   "page_table": ("interleaved: page p of sequence b at p * n_seqs + b" if batched else
+                                  "shuffled" if args.shuffle_pages else "in order"),
                    "launch": "hipGraph replay of the step" if args.graph else "eager"},
     }
     if not prefill:
         value = n_layers * bytes_layer * args.steps / (total_ms / 1e3) / 1e9
         achieved = bytes_kernel / (avg_attn_us / 1e6) / 1e9
         rec.update({
-            "metric": "quantized-KV decode attention: effective KV GB/s (% HBM peak), us/layer @262k",
+            "metric": ("quantized-KV batched decode attention: effective KV GB/s (% HBM peak)" if batched else
+                       "quantized-KV decode attention: effective KV GB/s (% HBM peak), us/layer @262k"),
             "value": round(value, 2), "unit": "GB/s",
         })
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -368,7 +415,7 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, max_reps=8 * w.n_seqs)
     print(json.dumps(rec), flush=True)
 
 

@@ -42,6 +42,7 @@ extern "C" {
 
 #define KVQ_BLOCK 32          /* values per quantization block */
 #define KVQ_MAX_NQ_DECODE 8   /* largest n_q accepted by kvq_decode_attn */
+#define KVQ_MAX_SEQS 64       /* largest n_seqs accepted by kvq_decode_attn_batch */
 
 typedef enum {
     KVQ_OK = 0,
@@ -223,6 +224,43 @@ int kvq_append_attn(const kvq_layout *layout, void *d_pool,
                     int32_t n_heads, const float *d_q, float scale,
                     float *d_out, float *d_lse,
                     void *d_ws, size_t ws_bytes, const kvq_attn_opts *opts, void *stream);
+
+/*
+ * Batched decode: n_seqs independent sequences in one call, each with its own
+ * context length and page-table row, all in one page pool (sequences normally
+ * own disjoint pages).  For every sequence b it computes exactly what
+ * kvq_decode_attn computes for that sequence alone ("Qwen 27B (IQ4_XS, Q8/Q4
+ * KV) on a 16GB RX 9070 XT at 262k context, via adaptive KV streaming", third
+ * paragraph: paged decode attention; the server there answers several
+ * requests at once): query i of b sits at position ctx_lens[b] - n_q + i.
+ *   d_page_tables  int32 [n_seqs][n_table], device; row b is sequence b's table
+ *   ctx_lens       int32 [n_seqs], HOST memory (the split plan is made on the
+ *                  host); n_q <= ctx_lens[b] <= n_table * page_size
+ *   d_q            fp32 [n_seqs][n_q][n_heads][head_dim]
+ *   d_out          fp32 [n_seqs][n_q][n_heads][head_dim]
+ *   d_lse          fp32 [n_seqs][n_q][n_heads], may be NULL
+ *   d_ws           workspace of at least kvq_decode_attn_batch_workspace_bytes()
+ *                  bytes for the same n_seqs, ctx_lens, n_heads and n_q
+ *   opts           may be NULL; as for kvq_attn_ex, except that kernel must be
+ *                  0 or 2 and chunks_per_split is ignored (the events bracket
+ *                  the streaming kernel of all sequences)
+ * 1 <= n_seqs <= KVQ_MAX_SEQS, 1 <= n_q <= KVQ_MAX_NQ_DECODE, and
+ * n_q * (n_heads / n_kv_heads) <= 64 (the streaming kernel runs every
+ * sequence; a sequence's share of the workgroups follows its context length).
+ * Errors: INVALID_ARG (nulls, n_seqs or n_q out of range, a ctx_lens[b] <
+ * n_q, opts->kernel other than 0 or 2), UNSUPPORTED, CAPACITY (a ctx_lens[b] > n_table * page_size),
+ * WORKSPACE, HIP.
+ */
+int kvq_decode_attn_batch_workspace_bytes(const kvq_layout *layout, int32_t n_seqs, const int32_t *ctx_lens,
+                                          int32_t n_heads, int32_t n_q, size_t *bytes);
+
+int kvq_decode_attn_batch(const kvq_layout *layout, const void *d_pool,
+                          const int32_t *d_page_tables, int32_t n_table,
+                          int32_t n_seqs, const int32_t *ctx_lens,
+                          int32_t n_heads, int32_t n_q,
+                          const float *d_q, float scale,
+                          float *d_out, float *d_lse,
+                          void *d_ws, size_t ws_bytes, const kvq_attn_opts *opts, void *stream);
 
 /* Status name, and the detail of the last failure on this thread. */
 const char *kvq_status_str(int status);

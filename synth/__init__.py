@@ -72,7 +72,8 @@ def with_outliers(x: np.ndarray, channels: np.ndarray, factor: float = 20.0) -> 
 @dataclass(frozen=True)
 class Workload:
     """One workload: a cache of ``cached`` tokens, ``n_new`` rows appended at
-    position ``cached``, then ``n_q`` queries ending at ``cached + n_new``."""
+    position ``cached``, then ``n_q`` queries ending at ``cached + n_new``;
+    ``n_seqs`` such sequences per layer (batched decode) when above 1."""
     name: str
     wid: int
     layers: int
@@ -84,6 +85,7 @@ class Workload:
     n_q: int
     page_size: int = 256
     outliers: bool = False
+    n_seqs: int = 1
 
     @property
     def ctx(self) -> int:
@@ -109,6 +111,9 @@ WORKLOADS = {
     "verify131k": Workload("verify131k", 4, 16, 24, 4, 256, 131072, 4, 4),
     # chunked prefill: 2,048 rows appended after 260,096 tokens, 1% outliers x20
     "prefill262k": Workload("prefill262k", 5, 1, 24, 4, 256, 260096, 2048, 2048, outliers=True),
+    # batched decode: 16 sequences of 16,384 tokens per layer (the KV bytes of
+    # decode262k spread over 16 requests)
+    "batch16x16k": Workload("batch16x16k", 6, 16, 24, 4, 256, 16383, 1, 1, n_seqs=16),
 }
 
 

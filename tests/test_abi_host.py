@@ -99,6 +99,37 @@ def test_attention_validation():
     assert call(fn=lib.kvq_prefill_attn, nq=9, ws=None)[0] == kvq.KVQ_ERR_WORKSPACE
 
 
+def test_batch_decode_validation():
+    lib = kvq.lib()
+    L = kvq.Layout(4, 256, 256, 64)
+    ctx = (ctypes.c_int32 * 4)(1000, 1, 2048, 300)
+
+    def call(pool=FAKE, pt=FAKE, nt=8, ns=4, cl=ctx, nh=24, nq=1, q=FAKE, out=FAKE, ws=FAKE, wsb=1 << 30,
+             opts=None):
+        return _status(lib.kvq_decode_attn_batch, ctypes.byref(L), pool, pt, nt, ns,
+                       None if cl is None else ctypes.cast(cl, ctypes.c_void_p), nh, nq, q,
+                       ctypes.c_float(0.0625), out, None, ws, wsb, opts, None)
+
+    assert call(pool=None)[0] == kvq.KVQ_ERR_INVALID_ARG
+    assert call(pt=None)[0] == kvq.KVQ_ERR_INVALID_ARG
+    assert call(cl=None)[0] == kvq.KVQ_ERR_INVALID_ARG
+    assert call(ns=0)[0] == kvq.KVQ_ERR_INVALID_ARG
+    assert call(ns=kvq.KVQ_MAX_SEQS + 1)[0] == kvq.KVQ_ERR_INVALID_ARG
+    assert call(nq=9)[0] == kvq.KVQ_ERR_INVALID_ARG
+    st, msg = call(nq=2)                                            # sequence 1 has a single key
+    assert st == kvq.KVQ_ERR_INVALID_ARG and "sequence 1" in msg
+    st, msg = call(nt=4)                                            # sequence 2 needs 8 pages
+    assert st == kvq.KVQ_ERR_CAPACITY and "sequence 2" in msg
+    assert call(nh=24 * 3)[0] == kvq.KVQ_ERR_UNSUPPORTED             # 18 heads per KV head
+    assert call(ws=None)[0] == kvq.KVQ_ERR_WORKSPACE
+    assert call(opts=ctypes.byref(kvq.AttnOpts(3, 0)))[0] == kvq.KVQ_ERR_INVALID_ARG   # tiled kernel
+    # the workspace query: bytes grow with the partials of every sequence
+    one = kvq.kvq_decode_attn_batch_workspace_bytes(L, [1000], 24, 1)
+    four = kvq.kvq_decode_attn_batch_workspace_bytes(L, [1000, 1, 2048, 300], 24, 1)
+    assert 0 < one < four
+    assert call(wsb=four - 1)[0] == kvq.KVQ_ERR_WORKSPACE
+
+
 def test_status_strings():
     lib = kvq.lib()
     for st, name in [(0, "KVQ_OK"), (-1, "KVQ_ERR_INVALID_ARG"), (-2, "KVQ_ERR_UNSUPPORTED"),
