@@ -30,7 +30,7 @@ EXPORTS = (
     "kvq_unit_bytes", "kvq_pool_bytes", "kvq_append", "kvq_workspace_bytes",
     "kvq_decode_attn", "kvq_prefill_attn", "kvq_workspace_bytes_ex", "kvq_attn_ex",
     "kvq_append_attn_workspace_bytes", "kvq_append_attn",
-    "kvq_decode_attn_batch_workspace_bytes", "kvq_decode_attn_batch",
+    "kvq_decode_attn_batch_workspace_bytes", "kvq_decode_attn_batch", "kvq_stage_pages",
     "kvq_status_str", "kvq_last_error", "kvq_version",
 )
 
@@ -87,6 +87,7 @@ def lib() -> ctypes.CDLL:
         "kvq_append_attn": [LP, P, P, i32, i32, i32, P, P, i32, P, ctypes.c_float, P, P, P, sz, OP, P],
         "kvq_decode_attn_batch_workspace_bytes": [LP, i32, P, i32, i32, SZP],
         "kvq_decode_attn_batch": [LP, P, P, i32, i32, P, i32, i32, P, ctypes.c_float, P, P, P, sz, OP, P],
+        "kvq_stage_pages": [LP, P, P, i32, LP, P, i32, P],
         "kvq_status_str": [ctypes.c_int],
         "kvq_last_error": [],
         "kvq_version": [],
@@ -328,3 +329,24 @@ def kvq_decode_attn_batch(layout: Layout, pool, page_tables, ctx_lens, q, scale:
                                        int(q.shape[2]), int(q.shape[1]), _ptr(q), float(scale), _ptr(out),
                                        _ptr(lse), _ptr(ws), ws_bytes, ctypes.byref(opts), _stream(stream)),
            "kvq_decode_attn_batch")
+
+
+def kvq_stage_pages(host_layout: Layout, host_pool, host_page_table, dev_layout: Layout, dev_pool,
+                    dst_first: int = 0, n_copy=None, stream=None):
+    """Copy the pages host_page_table names (a host int32 sequence or tensor)
+    from host_pool (a CPU uint8 tensor, pinned for overlap) to consecutive
+    pages of dev_pool starting at dst_first, asynchronously on `stream`."""
+    import torch
+    if host_pool.is_cuda:
+        raise ValueError("host_pool must be a host tensor")
+    if not host_pool.is_contiguous() or host_pool.dtype != torch.uint8:
+        raise ValueError("host_pool must be a contiguous uint8 tensor")
+    _need(dev_pool, "dev_pool", torch.uint8)
+    vals = [int(x) for x in (host_page_table.tolist() if hasattr(host_page_table, "tolist") else host_page_table)]
+    n = len(vals) if n_copy is None else int(n_copy)
+    if n > len(vals):
+        raise ValueError(f"n_copy {n} exceeds the {len(vals)} page-table entries")
+    arr = (ctypes.c_int32 * max(len(vals), 1))(*vals)
+    _check(lib().kvq_stage_pages(ctypes.byref(host_layout), ctypes.c_void_p(host_pool.data_ptr()),
+                                 ctypes.cast(arr, ctypes.c_void_p), n, ctypes.byref(dev_layout), _ptr(dev_pool),
+                                 int(dst_first), _stream(stream)), "kvq_stage_pages")

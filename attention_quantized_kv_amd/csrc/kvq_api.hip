@@ -519,4 +519,40 @@ int kvq_decode_attn_batch(const kvq_layout* layout, const void* d_pool, const in
     return ok();
 }
 
+int kvq_stage_pages(const kvq_layout* host_layout, const void* h_pool, const int32_t* h_page_table, int32_t n_copy,
+                    const kvq_layout* dev_layout, void* d_pool, int32_t dst_first, void* stream) {
+    kvq::Geom gh, gd;
+    int st = check_layout(host_layout, &gh);
+    if (st) return st;
+    st = check_layout(dev_layout, &gd);
+    if (st) return st;
+    if (h_pool == nullptr || d_pool == nullptr || h_page_table == nullptr)
+        return fail(KVQ_ERR_INVALID_ARG, "pools and page table must be non-NULL");
+    if (n_copy < 0) return fail(KVQ_ERR_INVALID_ARG, "n_copy %d < 0", n_copy);
+    if (gh.D != gd.D || gh.P != gd.P || gh.n_kv != gd.n_kv)
+        return fail(KVQ_ERR_INVALID_ARG, "host and device layouts differ (head_dim, page_size or n_kv_heads)");
+    if (dst_first < 0 || (int64_t)dst_first + n_copy > gd.n_pages)
+        return fail(KVQ_ERR_INVALID_ARG, "device pages %d..%d outside the pool of %d", dst_first,
+                    dst_first + n_copy - 1, gd.n_pages);
+    for (int i = 0; i < n_copy; ++i)
+        if (h_page_table[i] < 0 || h_page_table[i] >= gh.n_pages)
+            return fail(KVQ_ERR_INVALID_ARG, "host page %d (entry %d) outside the pool of %d", h_page_table[i], i,
+                        gh.n_pages);
+    if (n_copy == 0) return ok();
+    // one page of the pool = the units of all KV heads, contiguous
+    const size_t page_bytes = (size_t)gh.unit_bytes() * gh.n_kv;
+    const uint8_t* src = static_cast<const uint8_t*>(h_pool);
+    uint8_t* dst = static_cast<uint8_t*>(d_pool) + (size_t)dst_first * page_bytes;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int i = 0; i < n_copy;) {
+        int j = i + 1;
+        while (j < n_copy && h_page_table[j] == h_page_table[j - 1] + 1) ++j;   // a run of consecutive pages
+        const hipError_t e = hipMemcpyAsync(dst + (size_t)i * page_bytes, src + (size_t)h_page_table[i] * page_bytes,
+                                            (size_t)(j - i) * page_bytes, hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return fail(KVQ_ERR_HIP, "hipMemcpyAsync failed: %s", hipGetErrorString(e));
+        i = j;
+    }
+    return ok();
+}
+
 }  // extern "C"

@@ -235,13 +235,124 @@ def cpu_baseline(w, min_seconds: float, max_reps: int = 8):
             "sample": f"{desc}, {reps} repetition(s), {t_total:.1f} s"}
 
 
+def bench_stream(args, w, n_layers):
+    """Host-resident KV streaming: every layer's cache sits in pinned host
+    memory; per step each layer's pages are staged (kvq_stage_pages) into one
+    of two device buffers on a copy stream while the previous layer's
+    attention runs on the compute stream, ordered by events."""
+    import torch
+    import attention_quantized_kv_amd as kvq
+    dev = torch.device("cuda", 0)
+    L = kvq.Layout(w.n_kv, w.head_dim, w.page_size, w.n_pages)
+    nbytes = kvq.kvq_pool_bytes(L)
+    fill = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    pt_dev = torch.arange(w.n_pages, dtype=torch.int32, device=dev)
+    hosts, qs = [], []
+    t0 = time.time()
+    for layer in range(n_layers):
+        base = (w.wid * 1000 + layer) * 1_000_003
+        for r in range(0, w.ctx, 16384):
+            n = min(16384, w.ctx - r)
+            k = device_normal((n, w.n_kv, w.head_dim), base + 2 * r + 1, dev)
+            v = device_normal((n, w.n_kv, w.head_dim), base + 2 * r + 2, dev)
+            kvq.kvq_append(L, fill, pt_dev, r, k, v)
+        h = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+        h.copy_(fill)
+        hosts.append(h)
+        qs.append(device_normal((w.n_q, w.n_heads, w.head_dim), base + 9, dev))
+    del fill
+    torch.cuda.synchronize()
+    print(f"[bench] {w.name}: {n_layers} host-resident layers filled in {time.time() - t0:.1f} s",
+          file=sys.stderr, flush=True)
+    host_table = list(range(w.n_pages))          # the layer's pages, in order: one copy per layer
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(2)]
+    out = torch.empty((w.n_q, w.n_heads, w.head_dim), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.n_q, w.n_heads), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(kvq.kvq_workspace_bytes(L, w.n_heads, w.ctx, w.n_q), 256), dtype=torch.uint8, device=dev)
+    compute = torch.cuda.current_stream()
+    copy = torch.cuda.Stream()
+    copied = [torch.cuda.Event(), torch.cuda.Event()]
+    used = [torch.cuda.Event(), torch.cuda.Event()]
+
+    def step(ev=None, s=0):
+        for e in used:
+            e.record(compute)
+        with torch.cuda.stream(copy):
+            kvq.kvq_stage_pages(L, hosts[0], host_table, L, bufs[0], stream=copy)
+            copied[0].record(copy)
+        for i in range(n_layers):
+            b = i % 2
+            if i + 1 < n_layers:
+                nb = (i + 1) % 2
+                with torch.cuda.stream(copy):
+                    copy.wait_event(used[nb])
+                    kvq.kvq_stage_pages(L, hosts[i + 1], host_table, L, bufs[nb], stream=copy)
+                    copied[nb].record(copy)
+            compute.wait_event(copied[b])
+            e = ev if (ev is not None and i == s % n_layers) else None
+            kvq.kvq_attn_ex(L, bufs[b], pt_dev, w.ctx, qs[i], w.scale, out, lse, ws, events=e)
+            used[b].record(compute)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    hip_ev = HipEvents()
+    evs = [[hip_ev.create() for _ in range(2)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for s in range(args.steps):
+        step(evs[s], s)
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    attn_us = 1000.0 * sum(hip_ev.elapsed_ms(e[0], e[1]) for e in evs) / len(evs)
+    for e in evs:
+        hip_ev.destroy(e[0])
+        hip_ev.destroy(e[1])
+    # the link's rate for one plain pinned copy of a layer, for reference
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(4):
+        bufs[0].copy_(hosts[0], non_blocking=True)
+    stop.record()
+    torch.cuda.synchronize()
+    copy_gbs = 4 * nbytes / (start.elapsed_time(stop) / 1e3) / 1e9
+    bytes_layer = w.ctx * kv_bytes_per_token_layer(w.n_kv, w.head_dim)
+    us_per_layer = 1000.0 * total_ms / args.steps / n_layers
+    value = bytes_layer / (us_per_layer / 1e6) / 1e9
+    rec = {
+        "data": "synthetic", "dtype": "f16 MFMA / f32",
+        "config": {"workload": w.name, "layers": n_layers, "n_heads": w.n_heads, "n_kv_heads": w.n_kv,
+                   "head_dim": w.head_dim, "ctx": w.ctx, "n_q": w.n_q, "page_size": w.page_size,
+                   "kv_format": "K Q8_0 + V Q4_0", "kernel": "auto",
+                   "step": "per layer: kvq_stage_pages host -> device (copy stream) overlapped with the "
+                           "previous layer's kvq_attn_ex (two device buffers, events)",
+                   "kv_home": "pinned host memory"},
+        "metric": "host-resident KV streaming decode: KV GB/s over the host link, attention overlapped",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None,
+        "roofline": {"bound": "hbm", "achieved": round(bytes_layer / (attn_us / 1e6) / 1e9, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(bytes_layer / (attn_us / 1e6) / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "attn_mfma_stream", "bytes_per_launch": bytes_layer,
+                     "avg_launch_us": round(attn_us, 3)},
+        "us_per_layer": round(us_per_layer, 3),
+        "link": {"streamed_GBps": round(value, 2), "plain_pinned_copy_GBps": round(copy_gbs, 2),
+                 "frac_of_plain_copy": round(value / copy_gbs, 4)},
+        "kv_bytes_per_layer": bytes_layer,
+    }
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="decode262k",
-                    choices=["tiny", "decode65k", "decode262k", "verify131k", "prefill262k", "batch16x16k"])
+                    choices=["tiny", "decode65k", "decode262k", "verify131k", "prefill262k", "batch16x16k",
+                             "stream262k"])
     ap.add_argument("--layers", type=int, default=None, help="layers in the stack (default: the workload's)")
     ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA streaming, 3 MFMA tiled")
     ap.add_argument("--cps", type=int, default=0, help="32-token chunks per split (0: the library's choice)")
@@ -284,6 +395,13 @@ def main():
 
     w = synth.WORKLOADS[args.workload]
     n_layers = args.layers or w.layers
+    if w.host_resident:
+        rec = bench_stream(args, w, n_layers)
+        if not args.no_cpu_baseline:
+            print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+            rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        print(json.dumps(rec), flush=True)
+        return
     prefill = w.n_q > kvq.KVQ_MAX_NQ_DECODE
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)

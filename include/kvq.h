@@ -262,6 +262,31 @@ int kvq_decode_attn_batch(const kvq_layout *layout, const void *d_pool,
                           float *d_out, float *d_lse,
                           void *d_ws, size_t ws_bytes, const kvq_attn_opts *opts, void *stream);
 
+/*
+ * Host-resident KV streaming ("Qwen 27B (IQ4_XS, Q8/Q4 KV) on a 16GB RX 9070
+ * XT at 262k context, via adaptive KV streaming", first paragraph: the cache
+ * lives in host memory and its pages stream to the GPU as attention needs
+ * them).  Copies logical pages 0 .. n_copy-1 of a sequence, whose physical
+ * pages in a host pool are h_page_table[0 .. n_copy-1], to consecutive
+ * physical pages dst_first .. dst_first + n_copy - 1 of a device pool, as
+ * asynchronous copies on `stream` (runs of consecutive host pages go as one
+ * copy).  Attention then reads the device pool with the page table
+ * dst_first + i.
+ *   host_layout, h_pool   the host pool (pinned memory for copies that overlap
+ *                         the GPU's work; pageable memory also works, with
+ *                         copies the runtime may serialize)
+ *   h_page_table          int32 [n_copy], HOST memory
+ *   dev_layout, d_pool    the device pool; n_kv_heads, head_dim and page_size
+ *                         must equal the host pool's
+ * The source pages must not change until the copies are done (an event
+ * recorded on `stream` after this call tells when).  Errors: INVALID_ARG
+ * (nulls, n_copy < 0, layouts that differ, a host page outside the host pool,
+ * destination pages past the device pool), HIP.  n_copy == 0 is a no-op.
+ */
+int kvq_stage_pages(const kvq_layout *host_layout, const void *h_pool, const int32_t *h_page_table,
+                    int32_t n_copy, const kvq_layout *dev_layout, void *d_pool, int32_t dst_first,
+                    void *stream);
+
 /* Status name, and the detail of the last failure on this thread. */
 const char *kvq_status_str(int status);
 const char *kvq_last_error(void);

@@ -73,7 +73,8 @@ def with_outliers(x: np.ndarray, channels: np.ndarray, factor: float = 20.0) -> 
 class Workload:
     """One workload: a cache of ``cached`` tokens, ``n_new`` rows appended at
     position ``cached``, then ``n_q`` queries ending at ``cached + n_new``;
-    ``n_seqs`` such sequences per layer (batched decode) when above 1."""
+    ``n_seqs`` such sequences per layer (batched decode) when above 1;
+    ``host_resident``: the caches live in host memory and stream in."""
     name: str
     wid: int
     layers: int
@@ -86,6 +87,7 @@ class Workload:
     page_size: int = 256
     outliers: bool = False
     n_seqs: int = 1
+    host_resident: bool = False
 
     @property
     def ctx(self) -> int:
@@ -114,6 +116,9 @@ WORKLOADS = {
     # batched decode: 16 sequences of 16,384 tokens per layer (the KV bytes of
     # decode262k spread over 16 requests)
     "batch16x16k": Workload("batch16x16k", 6, 16, 24, 4, 256, 16383, 1, 1, n_seqs=16),
+    # decode262k with every layer's cache in pinned host memory, streamed to
+    # the GPU layer by layer while the previous layer's attention runs
+    "stream262k": Workload("stream262k", 7, 16, 24, 4, 256, 262144, 0, 1, host_resident=True),
 }
 
 

@@ -130,6 +130,29 @@ def test_batch_decode_validation():
     assert call(wsb=four - 1)[0] == kvq.KVQ_ERR_WORKSPACE
 
 
+def test_stage_pages_validation():
+    lib = kvq.lib()
+    H = kvq.Layout(4, 256, 256, 16)
+    D = kvq.Layout(4, 256, 256, 8)
+    pt = (ctypes.c_int32 * 4)(3, 4, 5, 9)
+
+    def call(hl=H, hp=FAKE, t=pt, n=4, dl=D, dp=FAKE, first=0):
+        return _status(lib.kvq_stage_pages, ctypes.byref(hl), hp, None if t is None else ctypes.cast(t, ctypes.c_void_p),
+                       n, ctypes.byref(dl), dp, first, None)
+
+    assert call(hp=None)[0] == kvq.KVQ_ERR_INVALID_ARG
+    assert call(dp=None)[0] == kvq.KVQ_ERR_INVALID_ARG
+    assert call(t=None)[0] == kvq.KVQ_ERR_INVALID_ARG
+    assert call(n=-1)[0] == kvq.KVQ_ERR_INVALID_ARG
+    assert call(dl=kvq.Layout(4, 128, 256, 8))[0] == kvq.KVQ_ERR_INVALID_ARG     # head_dim differs
+    assert call(dl=kvq.Layout(2, 256, 256, 8))[0] == kvq.KVQ_ERR_INVALID_ARG     # KV heads differ
+    assert call(first=5)[0] == kvq.KVQ_ERR_INVALID_ARG                           # pages 5..8 of 8
+    bad = (ctypes.c_int32 * 4)(3, 4, 16, 9)                                      # page 16 of 16
+    st, msg = call(t=bad)
+    assert st == kvq.KVQ_ERR_INVALID_ARG and "entry 2" in msg
+    assert call(n=0)[0] == kvq.KVQ_OK                                            # no-op, no copy
+
+
 def test_status_strings():
     lib = kvq.lib()
     for st, name in [(0, "KVQ_OK"), (-1, "KVQ_ERR_INVALID_ARG"), (-2, "KVQ_ERR_UNSUPPORTED"),
