@@ -69,6 +69,13 @@ def _load():
         getattr(lib, name).restype = i64
     lib.orc_q8_0_block_bytes.restype = i64
     lib.orc_q4_0_block_bytes.restype = i64
+    lib.orc_int2_block_bytes.restype = i64
+    lib.orc_quantize_int2.argtypes = [P, i64, P, P, P]
+    lib.orc_quantize_int2.restype = None
+    lib.orc_dequant_int2.argtypes = [P, P, P, i64, P]
+    lib.orc_dequant_int2.restype = None
+    lib.orc_attention_dense.argtypes = [i32, i32, i32, i32, i32, P, P, P, f64, i32, P, P, P]
+    lib.orc_attention_dense.restype = ctypes.c_int
     lib.orc_attention.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, f64, i32, P, P, P]
     lib.orc_attention.restype = ctypes.c_int
     lib.orc_attention_partial.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, f64,
@@ -138,6 +145,31 @@ def quantize_q4_0(x: np.ndarray):
     return codes, scales
 
 
+BLOCK2 = 128     # values per INT2 block
+
+
+def quantize_int2(x: np.ndarray):
+    """INT2 codes (uint8 0..3, one per value), fp16 scale bits and fp16 zero
+    bits ([..., D/128]); blocks of 128 along the last axis."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    assert x.shape[-1] % BLOCK2 == 0
+    nb = x.size // BLOCK2
+    codes = np.empty(x.shape, dtype=np.uint8)
+    scales = np.empty(x.shape[:-1] + (x.shape[-1] // BLOCK2,), dtype=np.uint16)
+    zeros = np.empty_like(scales)
+    _load().orc_quantize_int2(_ptr(x), nb, _ptr(codes), _ptr(scales), _ptr(zeros))
+    return codes, scales, zeros
+
+
+def dequant_int2(codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    zeros = np.ascontiguousarray(zeros, dtype=np.uint16)
+    out = np.empty(codes.shape, dtype=np.float64)
+    _load().orc_dequant_int2(_ptr(codes), _ptr(scales), _ptr(zeros), codes.size // BLOCK2, _ptr(out))
+    return out
+
+
 def dequant_q8_0(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     codes = np.ascontiguousarray(codes, dtype=np.int8)
     scales = np.ascontiguousarray(scales, dtype=np.uint16)
@@ -174,6 +206,11 @@ def q4_0_block_bytes() -> int:
     return int(_load().orc_q4_0_block_bytes())
 
 
+def int2_block_bytes() -> int:
+    """Bytes per 128 values of the INT2 codec."""
+    return int(_load().orc_int2_block_bytes())
+
+
 # --------------------------------------------------------------------------
 # attention
 # --------------------------------------------------------------------------
@@ -202,6 +239,50 @@ class QuantCache:
         return dequant_q4_0(self.v_codes, self.v_scales)
 
 
+class Int2Cache:
+    """One layer's INT2 cache (K and V both INT2), logical token-major layout."""
+
+    def __init__(self, kc, ks, kz, vc, vs, vz):
+        self.k = (kc, ks, kz)
+        self.v = (vc, vs, vz)
+        self.ctx, self.n_kv, self.D = kc.shape
+
+    @classmethod
+    def from_float(cls, k: np.ndarray, v: np.ndarray) -> "Int2Cache":
+        return cls(*quantize_int2(k), *quantize_int2(v))
+
+    def k_hat(self) -> np.ndarray:
+        return dequant_int2(*self.k)
+
+    def v_hat(self) -> np.ndarray:
+        return dequant_int2(*self.v)
+
+
+def attention_dense(q: np.ndarray, k_hat: np.ndarray, v_hat: np.ndarray, scale: float, rows=None,
+                    ctx: int | None = None):
+    """attention() over given dequantized K and V [ctx][n_kv][D] (fp64)."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    k_hat = np.ascontiguousarray(k_hat, dtype=np.float64)
+    v_hat = np.ascontiguousarray(v_hat, dtype=np.float64)
+    n_q, n_heads, D = q.shape
+    full, n_kv, Dk = k_hat.shape
+    ctx = full if ctx is None else int(ctx)
+    assert D == Dk and v_hat.shape == k_hat.shape and n_heads % n_kv == 0 and 1 <= n_q <= ctx <= full
+    lib = _load()
+    if rows is None:
+        out = np.empty((n_q, n_heads, D), dtype=np.float64)
+        lse = np.empty((n_q, n_heads), dtype=np.float64)
+        threads = lib.orc_attention_dense(n_q, n_heads, n_kv, D, ctx, _ptr(q), _ptr(k_hat), _ptr(v_hat),
+                                          float(scale), 0, None, _ptr(out), _ptr(lse))
+        return out, lse, threads
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 2))
+    out = np.empty((r.shape[0], D), dtype=np.float64)
+    lse = np.empty((r.shape[0],), dtype=np.float64)
+    lib.orc_attention_dense(n_q, n_heads, n_kv, D, ctx, _ptr(q), _ptr(k_hat), _ptr(v_hat), float(scale),
+                            r.shape[0], _ptr(r), _ptr(out), _ptr(lse))
+    return out, lse
+
+
 def attention(q: np.ndarray, cache: QuantCache, scale: float, rows=None, ctx: int | None = None):
     """Exact attention (fp64) of q [n_q][n_heads][D] over the first ``ctx``
     cached tokens (default: all).  Query i sits at position ctx - n_q + i and
@@ -211,6 +292,8 @@ def attention(q: np.ndarray, cache: QuantCache, scale: float, rows=None, ctx: in
     Without rows returns (out [n_q][n_heads][D], lse [n_q][n_heads]) and the
     thread count as a third element.
     """
+    if isinstance(cache, Int2Cache):
+        return attention_dense(q, cache.k_hat(), cache.v_hat(), scale, rows=rows, ctx=ctx)
     q = np.ascontiguousarray(q, dtype=np.float32)
     n_q, n_heads, D = q.shape
     ctx = cache.ctx if ctx is None else int(ctx)

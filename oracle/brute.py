@@ -72,6 +72,26 @@ def quant_q4_0_block(xs):
     return codes, f16_bits(d)
 
 
+BLOCK2 = 128
+
+
+def quant_int2_block(xs):
+    """One block of 128 fp32 values -> (codes 0..3, fp16 scale bits, fp16 zero
+    bits): d = (max - min) / 3, code = the nearest of the 4 levels (ties
+    upward), clamped at 3; the INT2 codec of the oracle ("OSCAR2 KV Cache
+    benchmark", compression-ratio table: 36 bytes per 128 values)."""
+    assert len(xs) == BLOCK2
+    xs = [f32(x) for x in xs]
+    mn, mx = min(xs), max(xs)
+    d = f32(f32(mx - mn) / 3.0)
+    idv = f32(1.0 / d) if d != 0.0 else 0.0
+    codes = []
+    for x in xs:
+        t = f32(f32(f32(x - mn) * idv) + 0.5)
+        codes.append(min(3, int(math.floor(t))))
+    return codes, f16_bits(d), f16_bits(mn)
+
+
 def quantize_rows(rows, kind):
     """rows: list of lists (each a multiple of 32 long) -> (codes rows, scale rows)."""
     fn = quant_q8_0_block if kind == "q8_0" else quant_q4_0_block

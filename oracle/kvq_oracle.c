@@ -165,6 +165,54 @@ int64_t orc_kv_bytes_per_token_f16(int64_t layers, int64_t kv_heads, int64_t hea
 int64_t orc_q8_0_block_bytes(void) { return 2 + ORC_BLOCK; }
 int64_t orc_q4_0_block_bytes(void) { return 2 + ORC_BLOCK / 2; }
 
+/* ------------------------------------------------------------------------ */
+/* INT2 codec (a 2-bit cache for K and V alike).  [OSCAR2] compression-ratio */
+/* table: 36 bytes per 128 values (2.25 bit), with fp16 zero-point metadata; */
+/* the same codec for K and V.  Readings where the page is silent: a block  */
+/* is 128 consecutive values of one (token, KV head) row; per block         */
+/* mn = min x, mx = max x, d = (mx - mn) / 3 in fp32; id = 1/d (0 when d =  */
+/* 0); code = min(3, trunc(fp32(fp32(fp32(x - mn) * id) + 0.5))), i.e. the  */
+/* nearest of the 4 levels with ties upward; stored: scale fp16(d) and zero  */
+/* fp16(mn), nearest even; value = zero + scale * code.                     */
+/* codes: one value 0..3 per byte here (the packing is a storage matter).   */
+/* ------------------------------------------------------------------------ */
+#define ORC_BLOCK2 128
+
+void orc_quantize_int2(const float *x, int64_t n_blocks, uint8_t *codes, uint16_t *scales, uint16_t *zeros)
+{
+    for (int64_t b = 0; b < n_blocks; ++b) {
+        const float *xb = x + b * ORC_BLOCK2;
+        float mn = xb[0], mx = xb[0];
+        for (int i = 1; i < ORC_BLOCK2; ++i) {
+            if (xb[i] < mn) mn = xb[i];
+            if (xb[i] > mx) mx = xb[i];
+        }
+        float d = (mx - mn) / 3.0f;
+        float id = (d != 0.0f) ? 1.0f / d : 0.0f;
+        for (int i = 0; i < ORC_BLOCK2; ++i) {
+            float t = xb[i] - mn;
+            t = t * id;
+            t = t + 0.5f;
+            int c = (int)t;                                /* t >= 0.5: this is floor */
+            codes[b * ORC_BLOCK2 + i] = (uint8_t)(c > 3 ? 3 : c);
+        }
+        scales[b] = orc_f32_to_f16(d);
+        zeros[b] = orc_f32_to_f16(mn);
+    }
+}
+
+void orc_dequant_int2(const uint8_t *codes, const uint16_t *scales, const uint16_t *zeros, int64_t n_blocks,
+                      double *out)
+{
+    for (int64_t b = 0; b < n_blocks; ++b) {
+        double h = (double)orc_f16_to_f32(scales[b]), z = (double)orc_f16_to_f32(zeros[b]);
+        for (int i = 0; i < ORC_BLOCK2; ++i) out[b * ORC_BLOCK2 + i] = z + h * (double)codes[b * ORC_BLOCK2 + i];
+    }
+}
+
+/* Bytes per 128 values: 32 bytes of 2-bit codes, an fp16 scale, an fp16 zero. */
+int64_t orc_int2_block_bytes(void) { return ORC_BLOCK2 / 4 + 2 + 2; }
+
 int64_t orc_kv_bytes_per_token_q8k_q4v(int64_t layers, int64_t kv_heads, int64_t head_dim)
 {
     int64_t blocks = head_dim / ORC_BLOCK;
@@ -189,10 +237,13 @@ typedef struct {
     const int8_t *kc; const uint16_t *ks;
     const uint8_t *vc; const uint16_t *vs;
     double scale;
+    /* given dequantized values [ctx][n_kv][D] (any codec), or NULL */
+    const double *kd, *vd;
 } orc_problem;
 
 static double khat(const orc_problem *p, int64_t j, int kv, int d)
 {
+    if (p->kd) return p->kd[(j * p->n_kv + kv) * p->D + d];
     int nb = p->D / ORC_BLOCK;
     double h = (double)orc_f16_to_f32(p->ks[(j * p->n_kv + kv) * nb + d / ORC_BLOCK]);
     return h * (double)p->kc[(j * p->n_kv + kv) * p->D + d];
@@ -200,6 +251,7 @@ static double khat(const orc_problem *p, int64_t j, int kv, int d)
 
 static double vhat(const orc_problem *p, int64_t j, int kv, int d)
 {
+    if (p->vd) return p->vd[(j * p->n_kv + kv) * p->D + d];
     int nb = p->D / ORC_BLOCK;
     double h = (double)orc_f16_to_f32(p->vs[(j * p->n_kv + kv) * nb + d / ORC_BLOCK]);
     return h * ((double)p->vc[(j * p->n_kv + kv) * p->D + d] - 8.0);
@@ -248,12 +300,31 @@ static void partial_row(const orc_problem *p, int i, int h, int64_t j0, int64_t 
 /* Full attention for a list of query rows.  rows = n_rows (i, h) pairs, or
  * NULL for every row in (i, h) order.  out: [n_rows][D]; lse: [n_rows]
  * (natural log of the sum of exp(score)).  Returns the thread count used. */
+static int attention_rows(const orc_problem *pp, int32_t n_rows, const int32_t *rows, double *out, double *lse);
+
 int orc_attention(int32_t n_q, int32_t n_heads, int32_t n_kv, int32_t D, int32_t ctx,
                   const float *q, const int8_t *kc, const uint16_t *ks,
                   const uint8_t *vc, const uint16_t *vs, double scale,
                   int32_t n_rows, const int32_t *rows, double *out, double *lse)
 {
-    orc_problem p = {n_q, n_heads, n_kv, D, ctx, q, kc, ks, vc, vs, scale};
+    orc_problem p = {n_q, n_heads, n_kv, D, ctx, q, kc, ks, vc, vs, scale, NULL, NULL};
+    return attention_rows(&p, n_rows, rows, out, lse);
+}
+
+/* The same attention over given dequantized K and V ([ctx][n_kv][D], fp64):
+ * the plain definition for any codec (the INT2 cache uses it). */
+int orc_attention_dense(int32_t n_q, int32_t n_heads, int32_t n_kv, int32_t D, int32_t ctx,
+                        const float *q, const double *khat_in, const double *vhat_in, double scale,
+                        int32_t n_rows, const int32_t *rows, double *out, double *lse)
+{
+    orc_problem p = {n_q, n_heads, n_kv, D, ctx, q, NULL, NULL, NULL, NULL, scale, khat_in, vhat_in};
+    return attention_rows(&p, n_rows, rows, out, lse);
+}
+
+static int attention_rows(const orc_problem *pp, int32_t n_rows, const int32_t *rows, double *out, double *lse)
+{
+    const orc_problem p = *pp;
+    const int32_t n_heads = p.n_heads, D = p.D, ctx = p.ctx, n_q = p.n_q;
     int64_t total = rows ? n_rows : (int64_t)n_q * n_heads;
     int threads = 1;
 #pragma omp parallel
@@ -284,7 +355,7 @@ void orc_attention_partial(int32_t n_q, int32_t n_heads, int32_t n_kv, int32_t D
                            const uint8_t *vc, const uint16_t *vs, double scale,
                            int64_t j0, int64_t j1, double *m, double *l, double *acc)
 {
-    orc_problem p = {n_q, n_heads, n_kv, D, ctx, q, kc, ks, vc, vs, scale};
+    orc_problem p = {n_q, n_heads, n_kv, D, ctx, q, kc, ks, vc, vs, scale, NULL, NULL};
     int64_t total = (int64_t)n_q * n_heads;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t r = 0; r < total; ++r)
