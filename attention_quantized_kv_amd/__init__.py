@@ -41,14 +41,18 @@ class KvqError(RuntimeError):
         self.status = status
 
 
+KVQ_CODEC_Q8K_Q4V, KVQ_CODEC_INT2 = 0, 1
+
+
 class Layout(ctypes.Structure):
-    """kvq_layout: n_kv_heads, head_dim, page_size, n_pages."""
+    """kvq_layout: n_kv_heads, head_dim, page_size, n_pages, codec (0: K Q8_0 +
+    V Q4_0, the default; 1: K and V INT2)."""
     _fields_ = [("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("page_size", ctypes.c_int32), ("n_pages", ctypes.c_int32)]
+                ("page_size", ctypes.c_int32), ("n_pages", ctypes.c_int32), ("codec", ctypes.c_int32)]
 
     def __repr__(self):
         return (f"Layout(n_kv_heads={self.n_kv_heads}, head_dim={self.head_dim}, "
-                f"page_size={self.page_size}, n_pages={self.n_pages})")
+                f"page_size={self.page_size}, n_pages={self.n_pages}, codec={self.codec})")
 
 
 class AttnOpts(ctypes.Structure):

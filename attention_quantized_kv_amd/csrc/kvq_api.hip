@@ -42,7 +42,11 @@ int check_layout(const kvq_layout* L, kvq::Geom* g) {
         return fail(KVQ_ERR_UNSUPPORTED, "head_dim %d not built (64, 128, 256)", L->head_dim);
     if (L->page_size % kvq::kChunk != 0 || L->page_size > 1024)
         return fail(KVQ_ERR_UNSUPPORTED, "page_size %d must be a multiple of 32 in [32, 1024]", L->page_size);
-    *g = kvq::Geom{L->head_dim, L->page_size, L->n_kv_heads, L->n_pages};
+    if (L->codec != KVQ_CODEC_Q8K_Q4V && L->codec != KVQ_CODEC_INT2)
+        return fail(KVQ_ERR_INVALID_ARG, "unknown codec %d", L->codec);
+    if (L->codec == KVQ_CODEC_INT2 && L->head_dim % kvq::kBlock2 != 0)
+        return fail(KVQ_ERR_UNSUPPORTED, "the INT2 codec takes head_dim 128 or 256 (got %d)", L->head_dim);
+    *g = kvq::Geom{L->head_dim, L->page_size, L->n_kv_heads, L->n_pages, L->codec};
     const double total = (double)g->unit_bytes() * L->n_kv_heads * L->n_pages;
     if (total > 9.0e18) return fail(KVQ_ERR_INVALID_ARG, "pool size overflows");
     return KVQ_OK;
@@ -95,6 +99,8 @@ int make_plan(const kvq_layout* L, int n_heads, int ctx, int n_q, bool prefill,
     const int group = n_heads / L->n_kv_heads;
     const int rows = n_q * group;
     int kernel = opts ? opts->kernel : 0;
+    if (L->codec == KVQ_CODEC_INT2)
+        return fail(KVQ_ERR_UNSUPPORTED, "attention over the INT2 codec is not built yet");
     if (kernel == 0) kernel = (!prefill && rows <= 64) ? 2 : 3;
     if (kernel < 1 || kernel > 3) return fail(KVQ_ERR_INVALID_ARG, "unknown kernel %d", kernel);
     if (group > 16) return fail(KVQ_ERR_UNSUPPORTED, "group size %d > 16", group);
@@ -205,7 +211,7 @@ int attn_impl(const kvq_layout* L, const void* d_pool, const int32_t* d_page_tab
 // rows; other kernel choices run kvq_append and then the attention call.
 bool append_attn_fused(const kvq_layout* L, int32_t n_heads, int32_t n_new, const kvq_attn_opts* opts) {
     const int kernel = opts ? opts->kernel : 0;
-    return (kernel == 0 || kernel == 2) && n_new * (n_heads / L->n_kv_heads) <= 64;
+    return L->codec == KVQ_CODEC_Q8K_Q4V && (kernel == 0 || kernel == 2) && n_new * (n_heads / L->n_kv_heads) <= 64;
 }
 
 // Plan of the cached part (fused) or of the whole attention (otherwise).

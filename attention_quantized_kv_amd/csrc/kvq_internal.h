@@ -25,19 +25,44 @@ constexpr int kBlock = 32;       // values per quantization block
 constexpr int kTile = 16;        // tokens per K tile (MFMA N/M = 16)
 constexpr int kChunk = 32;       // tokens per V chunk (MFMA K = 32)
 
+constexpr int kBlock2 = 128;     // values per INT2 block
+
 struct Geom {
     int D;          // head_dim
     int P;          // page_size
     int n_kv;       // KV heads
     int n_pages;    // physical pages
+    int codec = 0;  // 0: K Q8_0 + V Q4_0; 1: K and V INT2
     __host__ __device__ int nb() const { return D / kBlock; }
     __host__ __device__ int64_t k_codes_off() const { return 0; }
     __host__ __device__ int64_t k_scales_off() const { return (int64_t)P * D; }
     __host__ __device__ int64_t v_codes_off() const { return (int64_t)P * D + (int64_t)P * nb() * 2; }
     __host__ __device__ int64_t v_scales_off() const { return v_codes_off() + (int64_t)P * D / 2; }
-    __host__ __device__ int64_t unit_bytes() const { return v_scales_off() + (int64_t)P * nb() * 2; }
+    __host__ __device__ int64_t unit_bytes() const {
+        return codec == 1 ? i2_v_zeros_off() + (int64_t)P * nb2() * 2 : v_scales_off() + (int64_t)P * nb() * 2;
+    }
     __host__ __device__ int64_t unit_index(int page, int kvh) const { return (int64_t)page * n_kv + kvh; }
+    // INT2 unit: K codes, V codes, K (scale, zero), V scales, V zeros
+    __host__ __device__ int nb2() const { return D / kBlock2; }
+    __host__ __device__ int64_t i2_v_codes_off() const { return (int64_t)P * D / 4; }
+    __host__ __device__ int64_t i2_k_params_off() const { return (int64_t)P * D / 2; }
+    __host__ __device__ int64_t i2_v_scales_off() const { return i2_k_params_off() + (int64_t)P * nb2() * 4; }
+    __host__ __device__ int64_t i2_v_zeros_off() const { return i2_v_scales_off() + (int64_t)P * nb2() * 2; }
 };
+
+// INT2 unit: byte offset of the 16-bit word holding K code (slot s, dim d),
+// and the code's bit position in it.
+__host__ __device__ inline int64_t i2_k_word(const Geom& g, int s, int d, int* bit) {
+    const int t = s / kTile, n = s % kTile, step = d / 32, grp = (d % 32) / 8;
+    *bit = 2 * (d % 8);
+    return (int64_t)t * kTile * g.D / 4 + (int64_t)(grp * 16 + n) * (g.D / 16) + step * 2;
+}
+// INT2 unit: the same for V code (slot s, dim d).
+__host__ __device__ inline int64_t i2_v_word(const Geom& g, int s, int d, int* bit) {
+    const int c = s / kChunk, grp = (s % kChunk) / 8, w = d / 16, n = d % 16;
+    *bit = 2 * (s % 8);
+    return g.i2_v_codes_off() + (int64_t)c * kChunk * g.D / 4 + (int64_t)(grp * 16 + n) * (g.D / 8) + w * 2;
+}
 
 // Byte offset (within a unit) of K code (slot s, dim d).
 __host__ __device__ inline int64_t k_code_pos(const Geom& g, int s, int d) {

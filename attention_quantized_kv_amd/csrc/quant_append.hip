@@ -66,10 +66,104 @@ __global__ __launch_bounds__(D) void append_kernel(Geom g, uint8_t* __restrict__
     unit[off] = (uint8_t)(lo | (hi << 4));
 }
 
+// INT2 codec (K and V alike; "OSCAR2 KV Cache benchmark", compression-ratio
+// table: 36 bytes per 128 values with fp16 zero-point metadata): per block of
+// 128 values mn = min, mx = max, d = (mx - mn) / 3, code = min(3,
+// floor((x - mn) * (1/d) + 0.5)), every operation rounded to fp32 on its own;
+// stored fp16(d) and fp16(mn).
+//
+// One workgroup per (group of 8 consecutive positions, KV head, block): the
+// 8 tokens of a group share every V code word (one 16-bit word holds a dim
+// of 8 tokens), so the group is written by one workgroup and needs no
+// atomics.  Wave e quantizes token e of the group, two values per lane; it
+// writes the token's K words (8 codes of 8 consecutive dims, gathered over 4
+// lanes) and scale/zero pairs, and leaves its V codes in LDS; after a
+// barrier 128 threads build each dim's V word, keeping the old codes of the
+// group's tokens that are not being appended.
+__global__ __launch_bounds__(512) void append_int2_kernel(Geom g, uint8_t* __restrict__ pool,
+                                                          const int32_t* __restrict__ page_table, int pos0,
+                                                          int n_new, const float* __restrict__ k,
+                                                          const float* __restrict__ v) {
+#pragma clang fp contract(off)
+    __shared__ uint8_t vcodes[8][kBlock2];
+    const int kvh = blockIdx.y, b = blockIdx.z;
+    const int base = 8 * (blockIdx.x + (pos0 >> 3));         // first position of the group
+    const int e = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int pos = base + e;
+    const bool mine = pos >= pos0 && pos < pos0 + n_new;     // uniform per wave
+    const int phys = page_table[base / g.P];
+    if (phys < 0 || phys >= g.n_pages) return;               // never touch a page outside the pool
+    uint8_t* unit = pool + g.unit_index(phys, kvh) * g.unit_bytes();
+    const int slot = pos % g.P;
+    const int nb2 = g.nb2();
+    if (mine) {
+        const size_t src = ((size_t)(pos - pos0) * g.n_kv + kvh) * g.D + kBlock2 * b + 2 * lane;
+        auto quant = [&](const float* x, int& c0, int& c1, uint16_t& hs, uint16_t& hz) {
+            const float x0 = x[src], x1 = x[src + 1];
+            const float mn = -wave_max(-fminf(x0, x1), lane);  // exact: negation and max
+            const float mx = wave_max(fmaxf(x0, x1), lane);
+            const float d = __fdiv_rn(mx - mn, 3.0f);
+            const float id = d != 0.0f ? __fdiv_rn(1.0f, d) : 0.0f;
+            c0 = min(3, (int)(mul_rounded(x0 - mn, id) + 0.5f));
+            c1 = min(3, (int)(mul_rounded(x1 - mn, id) + 0.5f));
+            hs = f16_bits(d);
+            hz = f16_bits(mn);
+        };
+        int c0, c1;
+        uint16_t hs, hz;
+        // K: lanes 4j..4j+3 hold dims 8j..8j+7 of the block: one 16-bit word
+        quant(k, c0, c1, hs, hz);
+        int w = (c0 << (4 * (lane & 3))) | (c1 << (4 * (lane & 3) + 2));
+        w |= __shfl_xor(w, 1);
+        w |= __shfl_xor(w, 2);
+        if ((lane & 3) == 0) {
+            int bit;
+            const int64_t off = i2_k_word(g, slot, kBlock2 * b + 2 * lane, &bit);
+            *reinterpret_cast<uint16_t*>(unit + off) = (uint16_t)w;
+        }
+        if (lane == 0) {
+            uint16_t* kp = reinterpret_cast<uint16_t*>(unit + g.i2_k_params_off()) + ((size_t)slot * nb2 + b) * 2;
+            kp[0] = hs;
+            kp[1] = hz;
+        }
+        // V: codes to LDS, scale and zero to the unit
+        quant(v, c0, c1, hs, hz);
+        vcodes[e][2 * lane] = (uint8_t)c0;
+        vcodes[e][2 * lane + 1] = (uint8_t)c1;
+        if (lane == 0) {
+            const size_t i = ((size_t)(slot / kChunk) * nb2 + b) * kChunk + slot % kChunk;
+            reinterpret_cast<uint16_t*>(unit + g.i2_v_scales_off())[i] = hs;
+            reinterpret_cast<uint16_t*>(unit + g.i2_v_zeros_off())[i] = hz;
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < kBlock2) {
+        const int dd = threadIdx.x;
+        int bit;
+        const int64_t off = i2_v_word(g, base % g.P, kBlock2 * b + dd, &bit);   // the group's word for this dim
+        uint16_t* word = reinterpret_cast<uint16_t*>(unit + off);
+        const bool all = base >= pos0 && base + 8 <= pos0 + n_new;
+        const int old = all ? 0 : *word;
+        int w = 0;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const bool has = base + t >= pos0 && base + t < pos0 + n_new;
+            w |= (has ? vcodes[t][dd] : (old >> (2 * t)) & 3) << (2 * t);
+        }
+        *word = (uint16_t)w;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_append(const Geom& g, uint8_t* pool, const int32_t* page_table, int pos0,
                          int n_new, const float* k, const float* v, hipStream_t stream) {
+    if (g.codec == 1) {
+        const int groups = ((pos0 + n_new - 1) >> 3) - (pos0 >> 3) + 1;
+        hipLaunchKernelGGL(append_int2_kernel, dim3(groups, g.n_kv, g.nb2()), dim3(512), 0, stream, g, pool,
+                           page_table, pos0, n_new, k, v);
+        return hipGetLastError();
+    }
     const int pairs = ((pos0 + n_new - 1) >> 1) - (pos0 >> 1) + 1;
     dim3 grid(pairs, g.n_kv);
     switch (g.D) {

@@ -56,15 +56,20 @@ typedef enum {
 /*
  * Shape of one layer's page pool.
  *   n_kv_heads  KV heads of the layer, >= 1
- *   head_dim    D, one of 64, 128, 256
+ *   head_dim    D, one of 64, 128, 256 (128 or 256 for KVQ_CODEC_INT2)
  *   page_size   tokens per page, a multiple of 32 in [32, 1024]
  *   n_pages     physical pages in the pool, >= 1
+ *   codec       how K and V are stored: KVQ_CODEC_Q8K_Q4V (0, the default
+ *               of a zero-initialised layout) or KVQ_CODEC_INT2
  */
+#define KVQ_CODEC_Q8K_Q4V 0   /* K Q8_0, V Q4_0, 32-value blocks */
+#define KVQ_CODEC_INT2 1      /* K and V INT2, 128-value blocks with an fp16 scale and zero-point */
 typedef struct {
     int32_t n_kv_heads;
     int32_t head_dim;
     int32_t page_size;
     int32_t n_pages;
+    int32_t codec;
 } kvq_layout;
 
 /*
@@ -92,6 +97,26 @@ typedef struct {
  * 26*P*D/16 bytes: 416 bytes per token at D = 256, matching Q8_0 (34 B) +
  * Q4_0 (18 B) per 32-value block ("Adaptive KV streaming lands on ROCm ...",
  * "Why it matters": 26,624 bytes per token over 16 layers).
+ *
+ * KVQ_CODEC_INT2 ("OSCAR2 KV Cache benchmark", compression-ratio table: a
+ * 2-bit cache of 36 bytes per 128 values with fp16 zero-point metadata, the
+ * same codec for K and V).  Per block of 128 values of one row: mn = min,
+ * mx = max, d = (mx - mn) / 3 (fp32), code = min(3, floor((x - mn) * (1/d)
+ * + 0.5)) (0 when d = 0; each operation rounded to fp32), stored scale =
+ * fp16(d) and zero = fp16(mn); the value is zero + scale * code.  Unit
+ * layout (nb2 = D/128), 2-bit codes packed from bit 0 up:
+ *   [0, P*D/4)               K codes, 16-token tiles t; inside a tile lane
+ *                            L = g*16 + n (g < 4, n < 16) has D/16 bytes:
+ *                            one 16-bit word per 32-dim step s < D/32 holding
+ *                            dims 32s+8g+(0..7) of token 16t+n.
+ *   next P*D/4 bytes         V codes, 32-token chunks c; inside a chunk lane
+ *                            L = g*16 + n has D/8 bytes: one 16-bit word per
+ *                            16-dim tile w < D/16 holding dim 16w+n of tokens
+ *                            32c+8g+(0..7).
+ *   next 4*P*nb2 bytes       K scale and zero, fp16 bits, [token][block][2].
+ *   next 2*P*nb2 bytes       V scales, fp16 bits, [chunk][block][32 tokens].
+ *   next 2*P*nb2 bytes       V zeros, fp16 bits, [chunk][block][32 tokens].
+ * The unit is 9*P*D/16 bytes: 144 bytes per token at D = 256.
  */
 int kvq_unit_bytes(const kvq_layout *layout, size_t *bytes);
 int kvq_pool_bytes(const kvq_layout *layout, size_t *bytes);

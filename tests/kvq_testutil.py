@@ -17,8 +17,8 @@ ATOL, RTOL = 2e-3, 1e-3
 LSE_ATOL, LSE_RTOL = 1e-4, 1e-5
 
 
-def layout(n_kv, D, P, n_pages) -> kvq.Layout:
-    return kvq.Layout(n_kv, D, P, n_pages)
+def layout(n_kv, D, P, n_pages, codec=0) -> kvq.Layout:
+    return kvq.Layout(n_kv, D, P, n_pages, codec)
 
 
 def alloc_pool(L: kvq.Layout, device="cuda", fill=0):
@@ -108,3 +108,43 @@ def assert_close(out, ref, lse=None, ref_lse=None, what=""):
             i = np.unravel_index(np.argmax(e - b), e.shape)
             raise AssertionError(f"{what}: lse outside tolerance at {i}: got {lse[i]!r} want {ref_lse[i]!r}")
     return float(err.max())
+
+
+def decode_pool_int2(pool_np: np.ndarray, L: kvq.Layout, page_table: np.ndarray, ctx: int):
+    """INT2 pool -> per token and KV head: K codes, scales, zeros, V codes,
+    scales, zeros ([ctx][n_kv][D] and [ctx][n_kv][D/128]), from the INT2 unit
+    layout described in include/kvq.h."""
+    D, P, n_kv = L.head_dim, L.page_size, L.n_kv_heads
+    nb2 = D // 128
+    ub = 9 * P * D // 16
+    kc = np.empty((ctx, n_kv, D), np.uint8)
+    vc = np.empty((ctx, n_kv, D), np.uint8)
+    ks = np.empty((ctx, n_kv, nb2), np.uint16)
+    kz = np.empty_like(ks)
+    vs = np.empty_like(ks)
+    vz = np.empty_like(ks)
+    k_par, v_sc = P * D // 2, P * D // 2 + 4 * P * nb2
+    v_ze = v_sc + 2 * P * nb2
+    dims = np.arange(D)
+    for j in range(ctx):
+        page, s = divmod(j, P)
+        for h in range(n_kv):
+            u = pool_np[(int(page_table[page]) * n_kv + h) * ub:][:ub]
+            # K: tile s // 16, lane (g, n) with n = s % 16 holds words for dims 32 step + 8 g + (0..7)
+            t, n = divmod(s, 16)
+            step, grp, e = dims // 32, (dims % 32) // 8, dims % 8
+            off = t * 16 * D // 4 + (grp * 16 + n) * (D // 16) + step * 2
+            words = u[off].astype(np.uint32) | (u[off + 1].astype(np.uint32) << 8)
+            kc[j, h] = (words >> (2 * e)) & 3
+            # V: chunk s // 32, lane (g, n) with g = (s % 32) // 8, n = d % 16, word d // 16
+            c, gi, ei = s // 32, (s % 32) // 8, s % 8
+            off = P * D // 4 + c * 32 * D // 4 + (gi * 16 + dims % 16) * (D // 8) + (dims // 16) * 2
+            words = u[off].astype(np.uint32) | (u[off + 1].astype(np.uint32) << 8)
+            vc[j, h] = (words >> (2 * ei)) & 3
+            kp = u[k_par + s * nb2 * 4:][:nb2 * 4].view(np.uint16).reshape(nb2, 2)
+            ks[j, h], kz[j, h] = kp[:, 0], kp[:, 1]
+            for b in range(nb2):
+                i = (c * nb2 + b) * 32 + s % 32
+                vs[j, h, b] = u[v_sc + 2 * i:v_sc + 2 * i + 2].view(np.uint16)[0]
+                vz[j, h, b] = u[v_ze + 2 * i:v_ze + 2 * i + 2].view(np.uint16)[0]
+    return kc, ks, kz, vc, vs, vz

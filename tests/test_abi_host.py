@@ -153,6 +153,18 @@ def test_stage_pages_validation():
     assert call(n=0)[0] == kvq.KVQ_OK                                            # no-op, no copy
 
 
+def test_int2_codec_layout():
+    for D in (128, 256):
+        L = kvq.Layout(3, D, 64, 5, kvq.KVQ_CODEC_INT2)
+        assert kvq.kvq_unit_bytes(L) == 9 * 64 * D // 16              # 36 bytes per 128 values, K and V
+        assert kvq.kvq_pool_bytes(L) == 3 * 5 * 9 * 64 * D // 16
+    lib = kvq.lib()
+    out = ctypes.c_size_t(0)
+    assert lib.kvq_unit_bytes(ctypes.byref(kvq.Layout(1, 64, 64, 1, kvq.KVQ_CODEC_INT2)),
+                              ctypes.byref(out)) == kvq.KVQ_ERR_UNSUPPORTED
+    assert lib.kvq_unit_bytes(ctypes.byref(kvq.Layout(1, 128, 64, 1, 2)), ctypes.byref(out)) == kvq.KVQ_ERR_INVALID_ARG
+
+
 def test_status_strings():
     lib = kvq.lib()
     for st, name in [(0, "KVQ_OK"), (-1, "KVQ_ERR_INVALID_ARG"), (-2, "KVQ_ERR_UNSUPPORTED"),
