@@ -50,18 +50,23 @@ struct Geom {
     __host__ __device__ int64_t i2_v_zeros_off() const { return i2_v_scales_off() + (int64_t)P * nb2() * 2; }
 };
 
-// INT2 unit: byte offset of the 16-bit word holding K code (slot s, dim d),
-// and the code's bit position in it.
-__host__ __device__ inline int64_t i2_k_word(const Geom& g, int s, int d, int* bit) {
+// INT2 code words: 8 codes each, two words per dword -- code e of word h
+// (0: the even word, 1: the odd one) at bit 16 (e / 4) + 8 h + 2 (e % 4).  A
+// shift by 2j (or 8 + 2j) and a mask 0x00030003 then yield codes (j, 4 + j)
+// of a word as the two halves of a dword.
+__host__ __device__ inline int i2_bit(int h, int e) { return 16 * (e / 4) + 8 * h + 2 * (e % 4); }
+// INT2 unit: byte offset of the dword holding K code (slot s, dim d), and
+// the code's bit in it.
+__host__ __device__ inline int64_t i2_k_dword(const Geom& g, int s, int d, int* bit) {
     const int t = s / kTile, n = s % kTile, step = d / 32, grp = (d % 32) / 8;
-    *bit = 2 * (d % 8);
-    return (int64_t)t * kTile * g.D / 4 + (int64_t)(grp * 16 + n) * (g.D / 16) + step * 2;
+    *bit = i2_bit(step & 1, d % 8);
+    return (int64_t)t * kTile * g.D / 4 + (int64_t)(grp * 16 + n) * (g.D / 16) + (step / 2) * 4;
 }
 // INT2 unit: the same for V code (slot s, dim d).
-__host__ __device__ inline int64_t i2_v_word(const Geom& g, int s, int d, int* bit) {
+__host__ __device__ inline int64_t i2_v_dword(const Geom& g, int s, int d, int* bit) {
     const int c = s / kChunk, grp = (s % kChunk) / 8, w = d / 16, n = d % 16;
-    *bit = 2 * (s % 8);
-    return g.i2_v_codes_off() + (int64_t)c * kChunk * g.D / 4 + (int64_t)(grp * 16 + n) * (g.D / 8) + w * 2;
+    *bit = i2_bit(w & 1, s % 8);
+    return g.i2_v_codes_off() + (int64_t)c * kChunk * g.D / 4 + (int64_t)(grp * 16 + n) * (g.D / 8) + (w / 2) * 4;
 }
 
 // Byte offset (within a unit) of K code (slot s, dim d).

@@ -73,63 +73,50 @@ __global__ __launch_bounds__(D) void append_kernel(Geom g, uint8_t* __restrict__
 // stored fp16(d) and fp16(mn).
 //
 // One workgroup per (group of 8 consecutive positions, KV head, block): the
-// 8 tokens of a group share every V code word (one 16-bit word holds a dim
-// of 8 tokens), so the group is written by one workgroup and needs no
-// atomics.  Wave e quantizes token e of the group, two values per lane; it
-// writes the token's K words (8 codes of 8 consecutive dims, gathered over 4
-// lanes) and scale/zero pairs, and leaves its V codes in LDS; after a
-// barrier 128 threads build each dim's V word, keeping the old codes of the
-// group's tokens that are not being appended.
+// 8 tokens of a group share every V code dword (a dword holds two dims of 8
+// tokens), so the group is written by one workgroup and needs no atomics.
+// Wave e quantizes token e of the group, two values per lane, writes its
+// scale/zero pairs and leaves its codes in LDS; after a barrier 64 threads
+// pack the tokens' K dwords (8 per token) and 64 threads the group's V
+// dwords, keeping the old codes of the group's tokens that are not being
+// appended.
 __global__ __launch_bounds__(512) void append_int2_kernel(Geom g, uint8_t* __restrict__ pool,
                                                           const int32_t* __restrict__ page_table, int pos0,
                                                           int n_new, const float* __restrict__ k,
                                                           const float* __restrict__ v) {
 #pragma clang fp contract(off)
+    __shared__ uint8_t kcodes[8][kBlock2];
     __shared__ uint8_t vcodes[8][kBlock2];
     const int kvh = blockIdx.y, b = blockIdx.z;
     const int base = 8 * (blockIdx.x + (pos0 >> 3));         // first position of the group
     const int e = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int pos = base + e;
-    const bool mine = pos >= pos0 && pos < pos0 + n_new;     // uniform per wave
+    auto mine = [&](int t) { return base + t >= pos0 && base + t < pos0 + n_new; };
     const int phys = page_table[base / g.P];
     if (phys < 0 || phys >= g.n_pages) return;               // never touch a page outside the pool
     uint8_t* unit = pool + g.unit_index(phys, kvh) * g.unit_bytes();
-    const int slot = pos % g.P;
     const int nb2 = g.nb2();
-    if (mine) {
+    if (mine(e)) {                                           // uniform per wave
+        const int pos = base + e, slot = pos % g.P;
         const size_t src = ((size_t)(pos - pos0) * g.n_kv + kvh) * g.D + kBlock2 * b + 2 * lane;
-        auto quant = [&](const float* x, int& c0, int& c1, uint16_t& hs, uint16_t& hz) {
+        auto quant = [&](const float* x, uint8_t (&codes)[8][kBlock2], uint16_t& hs, uint16_t& hz) {
             const float x0 = x[src], x1 = x[src + 1];
             const float mn = -wave_max(-fminf(x0, x1), lane);  // exact: negation and max
             const float mx = wave_max(fmaxf(x0, x1), lane);
             const float d = __fdiv_rn(mx - mn, 3.0f);
             const float id = d != 0.0f ? __fdiv_rn(1.0f, d) : 0.0f;
-            c0 = min(3, (int)(mul_rounded(x0 - mn, id) + 0.5f));
-            c1 = min(3, (int)(mul_rounded(x1 - mn, id) + 0.5f));
+            codes[e][2 * lane] = (uint8_t)min(3, (int)(mul_rounded(x0 - mn, id) + 0.5f));
+            codes[e][2 * lane + 1] = (uint8_t)min(3, (int)(mul_rounded(x1 - mn, id) + 0.5f));
             hs = f16_bits(d);
             hz = f16_bits(mn);
         };
-        int c0, c1;
         uint16_t hs, hz;
-        // K: lanes 4j..4j+3 hold dims 8j..8j+7 of the block: one 16-bit word
-        quant(k, c0, c1, hs, hz);
-        int w = (c0 << (4 * (lane & 3))) | (c1 << (4 * (lane & 3) + 2));
-        w |= __shfl_xor(w, 1);
-        w |= __shfl_xor(w, 2);
-        if ((lane & 3) == 0) {
-            int bit;
-            const int64_t off = i2_k_word(g, slot, kBlock2 * b + 2 * lane, &bit);
-            *reinterpret_cast<uint16_t*>(unit + off) = (uint16_t)w;
-        }
+        quant(k, kcodes, hs, hz);
         if (lane == 0) {
             uint16_t* kp = reinterpret_cast<uint16_t*>(unit + g.i2_k_params_off()) + ((size_t)slot * nb2 + b) * 2;
             kp[0] = hs;
             kp[1] = hz;
         }
-        // V: codes to LDS, scale and zero to the unit
-        quant(v, c0, c1, hs, hz);
-        vcodes[e][2 * lane] = (uint8_t)c0;
-        vcodes[e][2 * lane + 1] = (uint8_t)c1;
+        quant(v, vcodes, hs, hz);
         if (lane == 0) {
             const size_t i = ((size_t)(slot / kChunk) * nb2 + b) * kChunk + slot % kChunk;
             reinterpret_cast<uint16_t*>(unit + g.i2_v_scales_off())[i] = hs;
@@ -137,20 +124,39 @@ __global__ __launch_bounds__(512) void append_int2_kernel(Geom g, uint8_t* __res
         }
     }
     __syncthreads();
-    if (threadIdx.x < kBlock2) {
-        const int dd = threadIdx.x;
-        int bit;
-        const int64_t off = i2_v_word(g, base % g.P, kBlock2 * b + dd, &bit);   // the group's word for this dim
-        uint16_t* word = reinterpret_cast<uint16_t*>(unit + off);
-        const bool all = base >= pos0 && base + 8 <= pos0 + n_new;
-        const int old = all ? 0 : *word;
-        int w = 0;
+    const int t = threadIdx.x;
+    if (t < 64) {
+        // K dword (grp, i) of token te: words 2i, 2i+1 = 32-dim steps of this block
+        const int te = t >> 3, grp = (t >> 1) & 3, i = 2 * b + (t & 1);
+        if (mine(te)) {
+            uint32_t w = 0;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const bool has = base + t >= pos0 && base + t < pos0 + n_new;
-            w |= (has ? vcodes[t][dd] : (old >> (2 * t)) & 3) << (2 * t);
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int ee = 0; ee < 8; ++ee)
+                    w |= (uint32_t)kcodes[te][32 * (2 * i + h) - kBlock2 * b + 8 * grp + ee] << i2_bit(h, ee);
+            int bit;
+            const int64_t off = i2_k_dword(g, (base + te) % g.P, 32 * (2 * i) + 8 * grp, &bit);
+            *reinterpret_cast<uint32_t*>(unit + off) = w;
         }
-        *word = (uint16_t)w;
+    } else if (t < 128) {
+        // V dword (n, i) of the group: words 2i, 2i+1 = dims 16 (2i + h) + n, tokens 0..7
+        const int q = t - 64, n = q & 15, i = 4 * b + (q >> 4);
+        int bit;
+        const int64_t off = i2_v_dword(g, base % g.P, 16 * (2 * i) + n, &bit);
+        uint32_t* dw = reinterpret_cast<uint32_t*>(unit + off);
+        const bool all = base >= pos0 && base + 8 <= pos0 + n_new;
+        const uint32_t old = all ? 0u : *dw;
+        uint32_t w = 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int ee = 0; ee < 8; ++ee) {
+                const int sh = i2_bit(h, ee);
+                const uint32_t c = mine(ee) ? vcodes[ee][16 * (2 * i + h) + n - kBlock2 * b] : (old >> sh) & 3u;
+                w |= c << sh;
+            }
+        *dw = w;
     }
 }
 

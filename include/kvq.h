@@ -104,15 +104,16 @@ typedef struct {
  * mx = max, d = (mx - mn) / 3 (fp32), code = min(3, floor((x - mn) * (1/d)
  * + 0.5)) (0 when d = 0; each operation rounded to fp32), stored scale =
  * fp16(d) and zero = fp16(mn); the value is zero + scale * code.  Unit
- * layout (nb2 = D/128), 2-bit codes packed from bit 0 up:
+ * layout (nb2 = D/128).  Codes come in words of 8 codes, two words per
+ * dword: code e (< 8) of word 2i+h (h < 2) sits at bit
+ * 16*(e/4) + 8*h + 2*(e%4) of dword i.
  *   [0, P*D/4)               K codes, 16-token tiles t; inside a tile lane
  *                            L = g*16 + n (g < 4, n < 16) has D/16 bytes:
- *                            one 16-bit word per 32-dim step s < D/32 holding
- *                            dims 32s+8g+(0..7) of token 16t+n.
+ *                            word s < D/32 holds dims 32s+8g+e of token
+ *                            16t+n.
  *   next P*D/4 bytes         V codes, 32-token chunks c; inside a chunk lane
- *                            L = g*16 + n has D/8 bytes: one 16-bit word per
- *                            16-dim tile w < D/16 holding dim 16w+n of tokens
- *                            32c+8g+(0..7).
+ *                            L = g*16 + n has D/8 bytes: word w < D/16 holds
+ *                            dim 16w+n of tokens 32c+8g+e.
  *   next 4*P*nb2 bytes       K scale and zero, fp16 bits, [token][block][2].
  *   next 2*P*nb2 bytes       V scales, fp16 bits, [chunk][block][32 tokens].
  *   next 2*P*nb2 bytes       V zeros, fp16 bits, [chunk][block][32 tokens].

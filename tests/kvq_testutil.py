@@ -126,21 +126,26 @@ def decode_pool_int2(pool_np: np.ndarray, L: kvq.Layout, page_table: np.ndarray,
     k_par, v_sc = P * D // 2, P * D // 2 + 4 * P * nb2
     v_ze = v_sc + 2 * P * nb2
     dims = np.arange(D)
+
+    def code(u, word_off, word, e):
+        """Code e of word `word` of a lane area starting at byte word_off: word
+        2i+h lives in dword i, code e at bit 16 (e / 4) + 8 h + 2 (e % 4)."""
+        off = word_off + (word // 2) * 4
+        dw = (u[off].astype(np.uint32) | (u[off + 1].astype(np.uint32) << 8) |
+              (u[off + 2].astype(np.uint32) << 16) | (u[off + 3].astype(np.uint32) << 24))
+        return (dw >> (16 * (e // 4) + 8 * (word % 2) + 2 * (e % 4))) & 3
+
     for j in range(ctx):
         page, s = divmod(j, P)
         for h in range(n_kv):
             u = pool_np[(int(page_table[page]) * n_kv + h) * ub:][:ub]
-            # K: tile s // 16, lane (g, n) with n = s % 16 holds words for dims 32 step + 8 g + (0..7)
+            # K: tile s // 16, lane (g, n) with n = s % 16; word = 32-dim step, code e = dim % 8
             t, n = divmod(s, 16)
             step, grp, e = dims // 32, (dims % 32) // 8, dims % 8
-            off = t * 16 * D // 4 + (grp * 16 + n) * (D // 16) + step * 2
-            words = u[off].astype(np.uint32) | (u[off + 1].astype(np.uint32) << 8)
-            kc[j, h] = (words >> (2 * e)) & 3
-            # V: chunk s // 32, lane (g, n) with g = (s % 32) // 8, n = d % 16, word d // 16
+            kc[j, h] = code(u, t * 16 * D // 4 + (grp * 16 + n) * (D // 16), step, e)
+            # V: chunk s // 32, lane (g, n) with g = (s % 32) // 8, n = d % 16; word d // 16, code s % 8
             c, gi, ei = s // 32, (s % 32) // 8, s % 8
-            off = P * D // 4 + c * 32 * D // 4 + (gi * 16 + dims % 16) * (D // 8) + (dims // 16) * 2
-            words = u[off].astype(np.uint32) | (u[off + 1].astype(np.uint32) << 8)
-            vc[j, h] = (words >> (2 * ei)) & 3
+            vc[j, h] = code(u, P * D // 4 + c * 32 * D // 4 + (gi * 16 + dims % 16) * (D // 8), dims // 16, ei)
             kp = u[k_par + s * nb2 * 4:][:nb2 * 4].view(np.uint16).reshape(nb2, 2)
             ks[j, h], kz[j, h] = kp[:, 0], kp[:, 1]
             for b in range(nb2):
