@@ -70,14 +70,14 @@ int auto_chunks_per_split(int kernel, int total_chunks, int n_kv, int n_q, int r
         long per = units * n_q / 4096;
         return (int)(per < 1 ? 1 : per);
     }
-    if (kernel == 2) {
+    if (kernel == 2 || kernel == 4) {
         // one 8-wave workgroup fits a CU (registers): at most one workgroup
         // per CU and KV head-split, so that all run in a single round; each
         // wave of a row group takes cps chunks of its split
         const long cus = device_cus();
         long splits = cus / n_kv;
         if (splits < 1) splits = 1;
-        const long wpg = kvq::mfma_stream_waves(rows);
+        const long wpg = kernel == 4 ? kvq::int2_waves() : kvq::mfma_stream_waves(rows);
         long per = ((long)total_chunks + wpg * splits - 1) / (wpg * splits);
         return (int)(per < 1 ? 1 : per);
     }
@@ -99,10 +99,17 @@ int make_plan(const kvq_layout* L, int n_heads, int ctx, int n_q, bool prefill,
     const int group = n_heads / L->n_kv_heads;
     const int rows = n_q * group;
     int kernel = opts ? opts->kernel : 0;
-    if (L->codec == KVQ_CODEC_INT2)
-        return fail(KVQ_ERR_UNSUPPORTED, "attention over the INT2 codec is not built yet");
+    if (kernel < 0 || kernel > 4) return fail(KVQ_ERR_INVALID_ARG, "unknown kernel %d", kernel);
+    if (L->codec == KVQ_CODEC_INT2) {
+        if (prefill) return fail(KVQ_ERR_UNSUPPORTED, "prefill over the INT2 codec is not built (decode only)");
+        if (kernel != 0 && kernel != 4)
+            return fail(KVQ_ERR_UNSUPPORTED, "the INT2 codec runs kernel 4 (got kernel %d)", kernel);
+        if (rows > 16) return fail(KVQ_ERR_UNSUPPORTED, "INT2 decode takes n_q*group <= 16 (got %d)", rows);
+        kernel = 4;
+    } else if (kernel == 4) {
+        return fail(KVQ_ERR_INVALID_ARG, "kernel 4 reads the INT2 codec only");
+    }
     if (kernel == 0) kernel = (!prefill && rows <= 64) ? 2 : 3;
-    if (kernel < 1 || kernel > 3) return fail(KVQ_ERR_INVALID_ARG, "unknown kernel %d", kernel);
     if (group > 16) return fail(KVQ_ERR_UNSUPPORTED, "group size %d > 16", group);
     if (kernel == 2 && rows > 64) return fail(KVQ_ERR_UNSUPPORTED, "streaming MFMA kernel takes n_q*group <= 64 (got %d)", rows);
     const int total_chunks = (ctx + kvq::kChunk - 1) / kvq::kChunk;
@@ -113,7 +120,8 @@ int make_plan(const kvq_layout* L, int n_heads, int ctx, int n_q, bool prefill,
     pl->kernel = kernel;
     pl->chunks_per_split = cps;
     // the streaming MFMA kernel folds the waves of a workgroup into one partial
-    const int per_partial = kernel == 2 ? kvq::mfma_stream_waves(rows) * cps : cps;
+    const int per_partial = kernel == 2 ? kvq::mfma_stream_waves(rows) * cps
+                            : kernel == 4 ? kvq::int2_waves() * cps : cps;
     pl->n_splits = (total_chunks + per_partial - 1) / per_partial;
     pl->group = group;
     pl->rows = rows;
@@ -198,6 +206,7 @@ int attn_impl(const kvq_layout* L, const void* d_pool, const int32_t* d_page_tab
         case 1: e = kvq::launch_attn_valu(a, pl, s); break;
         case 2: e = kvq::launch_attn_mfma_stream(a, pl, s); break;
         case 3: e = kvq::launch_attn_mfma_tiled(a, pl, s); break;
+        case 4: e = kvq::launch_attn_int2(a, pl, s); break;
     }
     if (e == hipSuccess && opts != nullptr && opts->kernel_end_event != nullptr)
         e = hipEventRecord(static_cast<hipEvent_t>(opts->kernel_end_event), s);
@@ -248,6 +257,8 @@ int batch_plan(const kvq_layout* L, int32_t n_table, int32_t n_seqs, const int32
     kvq::Geom g;
     int st = check_layout(L, &g);
     if (st) return st;
+    if (L->codec != KVQ_CODEC_Q8K_Q4V)
+        return fail(KVQ_ERR_UNSUPPORTED, "batched decode reads the Q8_0/Q4_0 codec only");
     if (n_seqs < 1 || n_seqs > KVQ_MAX_SEQS)
         return fail(KVQ_ERR_INVALID_ARG, "n_seqs %d outside [1, %d]", n_seqs, KVQ_MAX_SEQS);
     if (ctx_lens == nullptr) return fail(KVQ_ERR_INVALID_ARG, "ctx_lens is NULL");

@@ -93,7 +93,7 @@ __host__ __device__ inline int v_scale_idx(const Geom& g, int s, int b) {
 
 // Launch plan for attention: which kernel and how the keys are split.
 struct AttnPlan {
-    int kernel;            // 1 VALU, 2 MFMA streaming, 3 MFMA LDS-tiled
+    int kernel;            // 1 VALU, 2 MFMA streaming, 3 MFMA LDS-tiled, 4 INT2 streaming
     int chunks_per_split;  // 32-token chunks per merged partial
     int n_splits;          // partials per query row
     int group;             // q heads per KV head
@@ -193,6 +193,9 @@ hipError_t launch_merge_new(const AttnArgs& a, const NewRows& nr, int n_splits, 
 // group (each partial folds that many waves' chunks), for a given row count.
 int mfma_stream_row_groups(int rows);
 int mfma_stream_waves(int rows);
+// Decode over the INT2 codec (rows <= 16) and its waves per workgroup.
+hipError_t launch_attn_int2(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream);
+int int2_waves();
 // Query rows per workgroup of the LDS-tiled MFMA kernel.
 int mfma_tiled_rows_per_wg();
 

@@ -165,6 +165,28 @@ def test_int2_codec_layout():
     assert lib.kvq_unit_bytes(ctypes.byref(kvq.Layout(1, 128, 64, 1, 2)), ctypes.byref(out)) == kvq.KVQ_ERR_INVALID_ARG
 
 
+def test_int2_attention_plan():
+    """Attention over the INT2 codec: decode with up to 16 rows per KV head
+    (kernel 0 or 4); prefill, more rows, the other kernels and batched
+    decode are rejected; kernel 4 needs the INT2 codec."""
+    L = kvq.Layout(2, 256, 64, 100, kvq.KVQ_CODEC_INT2)
+    assert kvq.kvq_workspace_bytes(L, 12, 5000, 1) > 0                  # 6 rows
+    assert kvq.kvq_workspace_bytes_ex(L, 16, 5000, 2, kernel=4) > 0     # 16 rows
+
+    def status(fn, *args, **kw):
+        with pytest.raises(kvq.KvqError) as e:
+            fn(*args, **kw)
+        return e.value.status
+    assert status(kvq.kvq_workspace_bytes, L, 12, 5000, 64, True) == kvq.KVQ_ERR_UNSUPPORTED    # prefill
+    assert status(kvq.kvq_workspace_bytes, L, 12, 5000, 3) == kvq.KVQ_ERR_UNSUPPORTED           # 18 rows
+    for kernel in (1, 2, 3):
+        assert status(kvq.kvq_workspace_bytes_ex, L, 12, 5000, 1, kernel=kernel) == kvq.KVQ_ERR_UNSUPPORTED
+    assert status(kvq.kvq_workspace_bytes_ex, L, 12, 5000, 1, kernel=5) == kvq.KVQ_ERR_INVALID_ARG
+    assert status(kvq.kvq_workspace_bytes_ex, kvq.Layout(2, 256, 64, 100), 12, 5000, 1,
+                  kernel=4) == kvq.KVQ_ERR_INVALID_ARG
+    assert status(kvq.kvq_decode_attn_batch_workspace_bytes, L, [100, 200], 12, 1) == kvq.KVQ_ERR_UNSUPPORTED
+
+
 def test_status_strings():
     lib = kvq.lib()
     for st, name in [(0, "KVQ_OK"), (-1, "KVQ_ERR_INVALID_ARG"), (-2, "KVQ_ERR_UNSUPPORTED"),
