@@ -14,24 +14,25 @@
 // the small integer codes:
 //   q . k  = sum_b d_b (q_b . c_b) + z_b sum(q_b)       (b: the 128-dim blocks)
 //   p V    = sum_t (p_t d_t) c_t + sum_t p_t z_t         (per V block of dims)
-// q_b . c_b is an MFMA over exact fp16 codes (q split into fp16 hi + lo, so
-// every product is exact in fp32); sum(q_b) is a per-row constant.  On the V
-// side P' = p d (fp32, rounded once to fp16) multiplies the codes, and the
-// zero-point term is one more MFMA per chunk, fp16(p) times the chunk's V
-// zero-points, whose output column b is the row's term for block b.
+// q_b . c_b is an MFMA over the codes as exact fp16 (q split into fp16 hi +
+// lo, so every product is exact in fp32); sum(q_b) is a per-row constant.  On
+// the V side P' = p d (fp32, rounded once to fp16) multiplies the codes (as
+// fp16 subnormals, below), and the zero-point term is one more MFMA per
+// chunk, fp16(p) times the chunk's V zero-points, whose output column b is
+// the row's term for block b.
 //
 // Work split as in the Q8_0/Q4_0 streaming kernel: a workgroup of W waves per
 // (KV head, split), the split's 32-token chunks dealt round-robin to its
 // waves, every query row of the KV head served from one read of each byte.
-// Per chunk a lane loads its share straight into registers (two chunk
-// buffers: chunk c+1 is requested before chunk c is computed):
-//   K codes  2 tiles x D/16 bytes   V codes  D/8 bytes
-//   K (scale, zero) of its token, per tile: 4 bytes per block
-//   V scales of its 8 tokens (MFMA A layout), 16 bytes per block
-//   V zero-points of its 8 tokens for block n16 % NB2: 16 bytes
-// Each code load is one contiguous 1 KiB (D = 256) wave request thanks to
-// the pool layout.
+// A wave streams its chunks global -> LDS directly (global_load_lds_dwordx4:
+// no registers held by data in flight) into a ring of NSLOT chunk slots,
+// NSLOT - 1 chunks ahead of the one it computes.  A chunk is 2 x 8D/1024
+// code requests of 1 KiB (K then V, contiguous in the pool thanks to its
+// layout) and one full-wave request for its parameters: K (scale, zero) per
+// token and block, V scales and V zero-points per block and token.
 #include <hip/hip_fp16.h>
+
+#include <type_traits>
 
 #include "kvq_internal.h"
 #include "kvq_mfma.h"
@@ -48,88 +49,146 @@ struct I2Cfg {
     static constexpr int NT = D / 16;         // 16-dim output tiles
 };
 
-// One chunk's loads of one lane.
+// One chunk in a wave's LDS ring (bytes).
 template <int D>
-struct I2Chunk {
-    uint32_t k[2][I2Cfg<D>::KD];
-    uint32_t v[I2Cfg<D>::VD];
-    uint32_t kp[2][I2Cfg<D>::NB2];   // (scale, zero) fp16 pair per block, token n16 of each tile
-    u32x4 vs[I2Cfg<D>::NB2];         // V scales of tokens 8 g4 .. 8 g4 + 7, per block
-    u32x4 vz;                        // V zero-points of the same tokens, block n16 % NB2
+struct I2Slot {
+    static constexpr int NB2 = D / kBlock2;
+    static constexpr int CODE = 8 * D;                 // 32 tokens x D/4 bytes of K (or V) codes
+    static constexpr int K_OFF = 0, V_OFF = CODE, P_OFF = 2 * CODE;
+    static constexpr int VS_OFF = P_OFF + 128 * NB2;   // after the K (scale, zero) pairs [32][NB2][2]
+    static constexpr int VZ_OFF = VS_OFF + 64 * NB2;   // V scales [NB2][32], then V zeros [NB2][32]
+    static constexpr int BYTES = 2 * CODE + 1024;      // the parameter request lands a full 1 KiB
+    static constexpr int CODE_REQS = CODE / 1024;      // 1 KiB requests per code region
+    static constexpr int REQS = 2 * CODE_REQS + 1;     // requests per chunk
+    static constexpr int PLANES = 16 * NB2;            // lanes whose parameter bytes are distinct
+    static_assert(CODE % 1024 == 0, "whole wave requests");
 };
 
-template <int N>
-__device__ inline void load_dwords(uint32_t (&d)[N], const uint8_t* p) {
-    if constexpr (N % 4 == 0) {
-#pragma unroll
-        for (int i = 0; i < N / 4; ++i) {
-            const u32x4 x = reinterpret_cast<const u32x4*>(p)[i];
-            d[4 * i] = x.x;
-            d[4 * i + 1] = x.y;
-            d[4 * i + 2] = x.z;
-            d[4 * i + 3] = x.w;
-        }
-    } else if constexpr (N == 2) {
-        const uint2 x = *reinterpret_cast<const uint2*>(p);
-        d[0] = x.x;
-        d[1] = x.y;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// 32-bit LDS address of a pointer into shared memory.
+__device__ inline uint32_t lds_off(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Reads of a ring slot.  They are written as LDS reads in asm blocks that wait
+// for their own results: the compiler, unable to tell ring slots apart, would
+// otherwise guard a read with a wait for every direct-to-LDS load in flight
+// (the next chunks'), which takes away the prefetch.  The slot's own data has
+// landed by then (an explicit vmcnt wait).
+//
+// K: the codes of the lane's token in both 16-token tiles and its (scale,
+// zero) pairs (at D = 128 the upper half of each code vector is unused).
+template <int D>
+__device__ inline void read_k(const uint8_t* sl, int lane, int n16, u32x4 (&kc)[2], u32x2 (&kp)[2]) {
+    using S = I2Slot<D>;
+    const uint32_t ak = lds_off(sl + S::K_OFF + lane * (D / 16));
+    const uint32_t ap = lds_off(sl + S::P_OFF + n16 * (S::NB2 * 4));
+    if constexpr (D == 256) {
+        asm volatile(
+            "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:1024\n\t"
+            "ds_read_b64 %2, %5\n\tds_read_b64 %3, %5 offset:128\n\ts_waitcnt lgkmcnt(0)"
+            : "=&v"(kc[0]), "=&v"(kc[1]), "=&v"(kp[0]), "=&v"(kp[1])
+            : "v"(ak), "v"(ap)
+            : "memory");
     } else {
-        static_assert(N == 1, "1, 2 or a multiple of 4 dwords");
-        d[0] = *reinterpret_cast<const uint32_t*>(p);
+        static_assert(D == 128, "head_dim 128 or 256");
+        u32x2 k0, k1;
+        uint32_t p0, p1;
+        asm volatile(
+            "ds_read_b64 %0, %4\n\tds_read_b64 %1, %4 offset:512\n\t"
+            "ds_read_b32 %2, %5\n\tds_read_b32 %3, %5 offset:64\n\ts_waitcnt lgkmcnt(0)"
+            : "=&v"(k0), "=&v"(k1), "=&v"(p0), "=&v"(p1)
+            : "v"(ak), "v"(ap)
+            : "memory");
+        kc[0] = u32x4{k0.x, k0.y, 0u, 0u};
+        kc[1] = u32x4{k1.x, k1.y, 0u, 0u};
+        kp[0] = u32x2{p0, 0u};
+        kp[1] = u32x2{p1, 0u};
+    }
+}
+// V: the lane's code dwords, its 8 tokens' zero-points for block n16 % NB2
+// and their scales per block (at D = 128 the second halves are unused).
+template <int D>
+__device__ inline void read_v(const uint8_t* sl, int lane, int n16, int g4, u32x4 (&vc)[2], u32x4& vz,
+                              u32x4 (&vs)[2]) {
+    using S = I2Slot<D>;
+    const uint32_t av = lds_off(sl + S::V_OFF + lane * (D / 8));
+    const uint32_t az = lds_off(sl + S::VZ_OFF + (n16 % S::NB2) * 64 + 16 * g4);
+    const uint32_t as = lds_off(sl + S::VS_OFF + 16 * g4);
+    if constexpr (D == 256) {
+        asm volatile(
+            "ds_read_b128 %0, %5\n\tds_read_b128 %1, %5 offset:16\n\tds_read_b128 %2, %6\n\t"
+            "ds_read_b128 %3, %7\n\tds_read_b128 %4, %7 offset:64\n\ts_waitcnt lgkmcnt(0)"
+            : "=&v"(vc[0]), "=&v"(vc[1]), "=&v"(vz), "=&v"(vs[0]), "=&v"(vs[1])
+            : "v"(av), "v"(az), "v"(as)
+            : "memory");
+    } else {
+        asm volatile(
+            "ds_read_b128 %0, %3\n\tds_read_b128 %1, %4\n\tds_read_b128 %2, %5\n\ts_waitcnt lgkmcnt(0)"
+            : "=&v"(vc[0]), "=&v"(vz), "=&v"(vs[0])
+            : "v"(av), "v"(az), "v"(as)
+            : "memory");
+        vc[1] = vc[0];
+        vs[1] = vs[0];
     }
 }
 
-// Requests chunk slot0 .. slot0 + 31 of a unit (slot0 a multiple of 32).
-template <int D>
-__device__ inline void load_chunk(I2Chunk<D>& r, const uint8_t* unit, const Geom& g, int slot0, int lane) {
-    using C = I2Cfg<D>;
-    const int g4 = lane >> 4, n16 = lane & 15;
-    const uint32_t s0 = (uint32_t)slot0;
-    // K tile t covers tokens 16t .. 16t+15 in 16 * D/4 bytes, lane l at l * D/16
-    const uint8_t* kc = unit + s0 * (D / 4) + lane * (D / 16);
-    load_dwords(r.k[0], kc);
-    load_dwords(r.k[1], kc + kTile * (D / 4));
-    // V chunk c covers tokens 32c .. 32c+31 in 32 * D/4 bytes, lane l at l * D/8
-    load_dwords(r.v, unit + g.i2_v_codes_off() + s0 * (D / 4) + lane * (D / 8));
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-        load_dwords(r.kp[tt], unit + g.i2_k_params_off() + (s0 + kTile * tt + n16) * (C::NB2 * 4));
-    const uint8_t* vsb = unit + g.i2_v_scales_off() + (s0 / kChunk) * (C::NB2 * kChunk * 2) + 16 * g4;
-#pragma unroll
-    for (int b = 0; b < C::NB2; ++b) r.vs[b] = *reinterpret_cast<const u32x4*>(vsb + b * (kChunk * 2));
-    r.vz = *reinterpret_cast<const u32x4*>(unit + g.i2_v_zeros_off() + (s0 / kChunk) * (C::NB2 * kChunk * 2) +
-                                           (n16 % C::NB2) * (kChunk * 2) + 16 * g4);
+// s_waitcnt vmcnt(n * REQS) for a run-time n in [0, NMAX].
+template <int REQS, int NMAX, int I = 0>
+__device__ inline void wait_chunks(int n) {
+    if constexpr (I <= NMAX) {
+        if (n == I) { vm_wait<I * REQS>(); return; }
+        wait_chunks<REQS, NMAX, I + 1>(n);
+    }
 }
 
 // The 8 codes of word H (0: low, 1: high byte of each half) of dword x as
-// fp16 MUL * code, exactly, in the order (c0, c4, c1, c5, c2, c6, c3, c7).
-// Code j sits at bits 2j (and code 4+j at bits 16+2j): masked in place under
-// the fp16 exponent of 2^(10-2j), whose mantissa step is then 1, it reads
-// 2^(10-2j) + code; one FMA per pair removes the offset.  The offsets live in
-// registers (magic), so each pair costs one v_and_or_b32 and one
-// v_pk_fma_f16.
-template <int H, int MUL>
-__device__ inline half8 i2_word_to_half(uint32_t x, const uint32_t (&magic)[4]) {
+// fp16, in the order (c0, c4, c1, c5, c2, c6, c3, c7).  Code j (and 4+j, in
+// the upper half) sits at bit 2j.
+//
+// K (i2_word_exact): masked in place under the fp16 exponent of 2^(10-2j),
+// whose mantissa step is then 1, it reads 2^(10-2j) + code; one packed
+// subtraction per pair leaves the code itself.
+//
+// V (i2_word_sub): masked in place with a zero exponent it reads the fp16
+// subnormal c * 4^j * 2^-24, exactly: one v_and_b32 per pair.  The weights'
+// elements 2j, 2j+1 carry 4^(2-j), so the products are p d_v c 2^-20 (p d_v *
+// 16 must stay in fp16: V scales below 4096).  The matrix cores keep only
+// about 16 bits of such tiny products in a sum, which the weighted values
+// tolerate (each weight is rounded to fp16 anyway) but the scores do not: K
+// codes take the exact form.
+constexpr float kVAcc = 1048576.0f;    // 2^20: P' . codes carries 2^-20
+template <int H>
+__device__ inline half8 i2_word_exact(uint32_t x, const uint32_t (&magic)[4]) {
     const uint32_t y = H ? x >> 8 : x;
     u32x4 w;
 #pragma unroll
     for (int j = 0; j < 4; ++j) w[j] = (y & (0x00030003u << (2 * j))) | magic[j];
-    const half8 h = __builtin_bit_cast(half8, w);
-    const _Float16 m = (_Float16)MUL;
-    const _Float16 a0 = (_Float16)(-1024.0f * MUL), a1 = (_Float16)(-256.0f * MUL);
-    const _Float16 a2 = (_Float16)(-64.0f * MUL), a3 = (_Float16)(-16.0f * MUL);
-    const half8 add = {a0, a0, a1, a1, a2, a2, a3, a3};
-    return h * half8{m, m, m, m, m, m, m, m} + add;
+    const _Float16 a0 = 1024.0f, a1 = 256.0f, a2 = 64.0f, a3 = 16.0f;
+    return __builtin_bit_cast(half8, w) - half8{a0, a0, a1, a1, a2, a2, a3, a3};
+}
+template <int H>
+__device__ inline half8 i2_word_sub(uint32_t x) {
+    const uint32_t y = H ? x >> 8 : x;
+    u32x4 w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = y & (0x00030003u << (2 * j));
+    return __builtin_bit_cast(half8, w);
 }
 
-template <int D, int JJ, int W>
+template <int D, int JJ, int W, int NSLOT>
 struct I2Lds {
     using C = I2Cfg<D>;
+    using S = I2Slot<D>;
+    // per wave: a ring of NSLOT chunk slots
+    static constexpr int RING = NSLOT * S::BYTES;
     // q per 32-dim step, MFMA A layout: up to 8 rows carry fp16 hi in MFMA
     // rows {0,1,4,5,..} and lo two rows further down (one operand); up to 16
     // rows a hi and a lo operand
     static constexpr int QSTEP = JJ == 2 ? 1024 : 2048;
-    static constexpr int QS_OFF = C::STEPS * QSTEP;            // sum of q per (row, block): [16][NB2] floats
+    static constexpr int Q_OFF = W * RING;
+    static constexpr int QS_OFF = Q_OFF + C::STEPS * QSTEP;    // sum of q per (row, block): [16][NB2] floats
     static constexpr int PB_OFF = QS_OFF + 16 * C::NB2 * 4;
     static constexpr int PBUF = 16 * kPStride * 4;              // per wave: P transpose buffer
     static constexpr int LOOP_BYTES = PB_OFF + W * PBUF;
@@ -140,10 +199,11 @@ struct I2Lds {
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <int D, int JJ, int W>
+template <int D, int JJ, int W, int NSLOT>
 __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_splits, int group, int rows) {
     using C = I2Cfg<D>;
-    using L = I2Lds<D, JJ, W>;
+    using S = I2Slot<D>;
+    using L = I2Lds<D, JJ, W, NSLOT>;
     extern __shared__ __align__(16) uint8_t smem[];
     const Geom& g = a.g;
     const int lane = threadIdx.x & 63;
@@ -163,9 +223,9 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
     int ents = load_ents(0);
 
     // ---- q: A operands and per-block sums in LDS.  Thread (r, b, i) takes
-    // dims 128 b + 8 i .. +7 of row r, pre-scaled by scale * log2(e), split
-    // into fp16 hi + lo, stored in the codes' element order (d0, d4, d1, d5,
-    // ...); the 16 threads of (r, b) sum hi + lo over the block.
+    // dims 128 b + 8 i .. +7 of row r, pre-scaled by scale * log2(e), in the
+    // codes' element order (d0, d4, d1, d5, ...), split into fp16 hi + lo; the
+    // 16 threads of (r, b) sum the block.
     const float qscale = a.scale * kLog2e;
     float* qsum = reinterpret_cast<float*>(smem + L::QS_OFF);
     {
@@ -183,13 +243,14 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
             float sum = 0.0f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
+                // element e: dim e/2 or 4 + e/2
                 const float v = x[(e & 1) ? 4 + e / 2 : e / 2];
                 hi[e] = (_Float16)v;
                 lo[e] = (_Float16)(v - (float)hi[e]);
-                sum += (float)hi[e] + (float)lo[e];
+                sum += v;
             }
             const int step = 4 * b + i / 4, gq = i % 4;
-            uint8_t* qd = smem + step * L::QSTEP;
+            uint8_t* qd = smem + L::Q_OFF + step * L::QSTEP;
             if constexpr (JJ == 2) {
                 const int n = 4 * (r / 2) + r % 2;     // MFMA row of row r (logical_row<2> inverse)
                 *reinterpret_cast<half8*>(qd + (gq * 16 + n) * 16) = hi;
@@ -217,17 +278,23 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
     for (int jj = 0; jj < 4; ++jj) { m[jj] = -INFINITY; l[jj] = 0.0f; }
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt) o[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+
     uint32_t magic[4] = {0x64006400u, 0x5C005C00u, 0x54005400u, 0x4C004C00u};   // fp16 2^10, 2^8, 2^6, 2^4
 #pragma unroll
-    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(magic[j]));              // keep them in VGPRs
+    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(magic[j]));              // kept in VGPRs
 
     // chunks wholly visible to every row come first
     const int c_mask = first_last >= kChunk - 1 ? (first_last - (kChunk - 1)) / kChunk + 1 : 0;
 
     // One chunk: S = q K^T, online softmax, O += P' V, corr += p z.
-    auto process = [&](const I2Chunk<D>& cur, int c) {
+    // MASK: some key of the chunk lies past the last key of some row.
+    auto process = [&](const uint8_t* sl, int c, auto mask_tag) {
+        constexpr bool mask = decltype(mask_tag)::value;
         const int j0 = c * kChunk;
-        const bool mask = c >= c_mask;
+        // K codes of the lane's token in each tile, and its (scale, zero) pairs
+        u32x4 kcode[2];
+        u32x2 kpar[2];
+        read_k<D>(sl, lane, n16, kcode, kpar);
         floatx4 s[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int b = 0; b < C::NB2; ++b) {
@@ -235,22 +302,23 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
                 const int step = 4 * b + st;
-                const uint8_t* qp = smem + step * L::QSTEP + lane * 16;
+                const uint8_t* qp = smem + L::Q_OFF + step * L::QSTEP + lane * 16;
                 const half8 qa = *reinterpret_cast<const half8*>(qp);
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt) {
-                    const half8 kb = (step & 1) ? i2_word_to_half<1, 1>(cur.k[tt][step / 2], magic)
-                                                : i2_word_to_half<0, 1>(cur.k[tt][step / 2], magic);
+                    const half8 kb = (step & 1) ? i2_word_exact<1>(kcode[tt][step / 2], magic)
+                                                : i2_word_exact<0>(kcode[tt][step / 2], magic);
                     acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa, kb, acc[tt], 0, 0, 0);
                     if constexpr (JJ == 4) {
                         const half8 ql = *reinterpret_cast<const half8*>(qp + 1024);
                         acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql, kb, acc[tt], 0, 0, 0);
                     }
                 }
+                SCHED_FENCE();
             }
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
-                const half2v dz = as_h2(cur.kp[tt][b]);
+                const half2v dz = as_h2(kpar[tt][b]);
                 const float d = (float)dz.x, z = (float)dz.y;
 #pragma unroll
                 for (int jj = 0; jj < JJ; ++jj) {
@@ -261,7 +329,7 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
             SCHED_FENCE();
         }
         // causal / tail mask: key j visible to row r iff j <= first_last + r / group
-        if (mask) {
+        if constexpr (mask) {
 #pragma unroll
             for (int jj = 0; jj < JJ; ++jj) {
                 const int row = logical_row<JJ>(0, 4 * g4 + jj);
@@ -280,6 +348,8 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
             grow |= mnew[jj] > m[jj] + kTau;
         }
         if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            // rows whose maximum did not move get alpha = 1: one straight pass
+            // over the accumulators, no per-row branches
             floatx4 alpha = {1.0f, 1.0f, 1.0f, 1.0f};
 #pragma unroll
             for (int jj = 0; jj < JJ; ++jj) {
@@ -309,23 +379,33 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
         for (int e = 0; e < 8; ++e) pf[e] = plds[n16 * kPStride + 8 * g4 + e];
         // zero-point term: fp16(p) times the zero-points (keys past the
         // context may hold unwritten zero-points: they get 0)
-        half8 az, bz = __builtin_bit_cast(half8, cur.vz);
+        u32x4 vcode[2], vzr, vsr[2];
+        read_v<D>(sl, lane, n16, g4, vcode, vzr, vsr);
+        half8 az, bz = __builtin_bit_cast(half8, vzr);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             az[e] = (_Float16)pf[e];
             if (mask && j0 + 8 * g4 + e >= a.ctx) bz[e] = (_Float16)0.0f;
         }
         corr = __builtin_amdgcn_mfma_f32_16x16x32_f16(az, bz, corr, 0, 0, 0);
+        // the codes' token order; token pair j carries 4^(2-j) (exact)
+        float ps[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float f = j < 2 ? (float)(1 << (4 - 2 * j)) : 1.0f / (float)(1 << (2 * j - 4));
+            ps[2 * j] = pf[j] * f;
+            ps[2 * j + 1] = pf[4 + j] * f;
+        }
 #pragma unroll
         for (int b = 0; b < C::NB2; ++b) {
-            // P' = p * d_v, rounded once to fp16, in the codes' token order
-            const half8 sc = __builtin_bit_cast(half8, cur.vs[b]);
+            // P' = p * d_v (times 4^(2-j)), one fp32 product rounded once to fp16
+            const half8 sc = __builtin_bit_cast(half8, vsr[b]);
             half8 ap;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                float x0 = pf[j] * (float)sc[j];
-                float x1 = pf[4 + j] * (float)sc[4 + j];
-                if (mask) {                      // masked keys may hold unwritten scales
+                float x0 = fmaf(ps[2 * j], (float)sc[j], 0.0f);
+                float x1 = fmaf(ps[2 * j + 1], (float)sc[4 + j], 0.0f);
+                if constexpr (mask) {            // masked keys may hold unwritten scales
                     x0 = pf[j] == 0.0f ? 0.0f : x0;
                     x1 = pf[4 + j] == 0.0f ? 0.0f : x1;
                 }
@@ -335,48 +415,82 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
 #pragma unroll
             for (int w = 0; w < 8; ++w) {
                 const int nt = 8 * b + w;
-                // codes carry 2^kTau = 16 (the weights carry 2^-kTau)
-                const half8 bv = (nt & 1) ? i2_word_to_half<1, 16>(cur.v[nt / 2], magic)
-                                          : i2_word_to_half<0, 16>(cur.v[nt / 2], magic);
+                const half8 bv = (nt & 1) ? i2_word_sub<1>(vcode[nt / 8][(nt / 2) % 4])
+                                          : i2_word_sub<0>(vcode[nt / 8][(nt / 2) % 4]);
                 o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap, bv, o[nt], 0, 0, 0);
+                if (w & 1) SCHED_FENCE();       // a few B operands live at a time
             }
             SCHED_FENCE();
         }
     };
 
-    // ---- stream, two chunk buffers.  A page-table entry outside the pool
-    // stops the wave (nothing is loaded from it) and turns its partial into NaN.
-    I2Chunk<D> buf0, buf1;
-    bool bad = false;
-    int c = c0, k = 0;
-    auto request = [&](I2Chunk<D>& r, int kk, int cc) {
-        const int phys = __builtin_amdgcn_readlane(ents, kk & 63);
-        if (phys < 0 || phys >= g.n_pages) return false;
-        load_chunk<D>(r, a.pool + g.unit_index(phys, kvh) * g.unit_bytes(), g, (cc * kChunk) % g.P, lane);
-        return true;
-    };
-    if (c < c1) bad = !request(buf0, 0, c);
-    // processes chunk c from cur after requesting the wave's next chunk into nxt
-    auto advance = [&](const I2Chunk<D>& cur, I2Chunk<D>& nxt) {
-        const int cn = c + stride;
-        bool ok = true;
-        if (cn < c1) {
-            if (((k + 1) & 63) == 0) {
-                ents = load_ents(k + 1);
-                asm volatile("" : "+v"(ents));
-            }
-            ok = request(nxt, k + 1, cn);
+    // ---- stream.  Chunk i of the wave (global chunk c0 + i stride) lands in
+    // ring slot i % NSLOT; computing chunk i first requests chunk
+    // i + NSLOT - 1 into the slot chunk i - 1 used.  A page-table entry
+    // outside the pool stops the requests there; the wave stops when it gets
+    // to that chunk and its partial turns into NaN.
+    uint8_t* const ring = smem + wave * L::RING;
+    const int n_mine = c0 < c1 ? (c1 - 1 - c0) / stride + 1 : 0;   // chunks of this wave
+    // the parameter request: lane l carries K (scale, zero) pairs, V scales
+    // or V zeros, 16 bytes at pbase + slot0 * pmul of the unit
+    int pbase, pmul;
+    {
+        const int pl = lane % S::PLANES;
+        if (pl < 8 * C::NB2) {
+            pbase = (int)g.i2_k_params_off() + 16 * pl;
+            pmul = 4 * C::NB2;
+        } else if (pl < 12 * C::NB2) {
+            pbase = (int)g.i2_v_scales_off() + 16 * (pl - 8 * C::NB2);
+            pmul = 2 * C::NB2;
+        } else {
+            pbase = (int)g.i2_v_zeros_off() + 16 * (pl - 12 * C::NB2);
+            pmul = 2 * C::NB2;
         }
-        process(cur, c);
-        c = cn;
-        ++k;
-        bad = !ok;
-    };
-    while (c < c1 && !bad) {
-        advance(buf0, buf1);
-        if (c >= c1 || bad) break;
-        advance(buf1, buf0);
     }
+    int n_req = 0;         // chunks requested so far
+    int stop = n_mine;     // first chunk not requested (a bad page), else n_mine
+    auto request = [&]() {
+        if (n_req >= stop) return;
+        if ((n_req & 63) == 0 && n_req > 0) {
+            // the next 64 entries; a load that waits for itself (and for the
+            // requests in flight), so no pending register outlives the branch
+            const int ck = c0 + (n_req + lane) * stride;
+            const int32_t* pe = a.page_table + (ck < c1 ? (ck * kChunk) / g.P : 0);
+            int v;
+            asm volatile("global_load_dword %0, %1, off\n\ts_waitcnt vmcnt(0)" : "=v"(v) : "v"(pe) : "memory");
+            ents = ck < c1 ? v : -1;
+        }
+        const int phys = __builtin_amdgcn_readlane(ents, n_req & 63);
+        if (phys < 0 || phys >= g.n_pages) { stop = n_req; return; }
+        const uint8_t* unit = a.pool + g.unit_index(phys, kvh) * g.unit_bytes();
+        const uint32_t s0 = (uint32_t)(((c0 + n_req * stride) * kChunk) % g.P);
+        uint8_t* sl = ring + (n_req % NSLOT) * S::BYTES;
+        const uint8_t* kc = unit + s0 * (D / 4) + lane * 16;
+        const uint8_t* vc = unit + g.i2_v_codes_off() + s0 * (D / 4) + lane * 16;
+#pragma unroll
+        for (int i = 0; i < S::CODE_REQS; ++i) dma16(kc + i * 1024, sl + S::K_OFF + i * 1024);
+#pragma unroll
+        for (int i = 0; i < S::CODE_REQS; ++i) dma16(vc + i * 1024, sl + S::V_OFF + i * 1024);
+        dma16(unit + pbase + s0 * pmul, sl + S::P_OFF);
+        ++n_req;
+    };
+#pragma unroll
+    for (int i = 0; i + 1 < NSLOT; ++i) request();
+
+    bool bad = false;
+    int ci = 0;            // the wave's chunk being computed
+    auto step = [&](auto mask_tag) {
+        request();         // chunk ci + NSLOT - 1, into the slot chunk ci - 1 has left
+        wait_chunks<S::REQS, NSLOT - 1>(n_req - ci - 1);   // chunk ci has landed
+        process(ring + (ci % NSLOT) * S::BYTES, c0 + ci * stride, mask_tag);
+        lds_fence();       // the slot is read out before it is requested again
+        ++ci;
+    };
+    const int n_full = c0 < c_mask ? min((c_mask - 1 - c0) / stride + 1, n_mine) : 0;
+    while (ci < n_full && ci < stop) step(std::false_type{});
+    while (ci < n_mine && ci < stop) step(std::true_type{});
+    bad = ci < n_mine;
+    vm_wait<0>();          // nothing in flight into LDS past this point
 
     // ---- finish: row sums, the zero-point term into o, then the W waves'
     // partials combined in wave order into one per workgroup
@@ -386,7 +500,8 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
         if (bad) { m[jj] = NAN; l[jj] = NAN; }
     }
     {
-        // corr column b (lane 16 g4 + b) times 2^kTau goes to the dims of block b
+        // o carries 2^-20 (the codes) and 2^-kTau (the weights); corr column
+        // b (lane 16 g4 + b) times 2^kTau goes to the dims of block b
         float cz[C::NB2][JJ];
 #pragma unroll
         for (int b = 0; b < C::NB2; ++b)
@@ -395,7 +510,7 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
 #pragma unroll
         for (int nt = 0; nt < C::NT; ++nt)
 #pragma unroll
-            for (int jj = 0; jj < JJ; ++jj) o[nt][jj] += cz[nt / 8][jj];
+            for (int jj = 0; jj < JJ; ++jj) o[nt][jj] = fmaf(o[nt][jj], 16.0f * kVAcc, cz[nt / 8][jj]);
     }
     __syncthreads();                                    // q and P buffers no longer read
     constexpr int SLOTW = JJ * 4 * D;                   // floats per wave
@@ -447,17 +562,18 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
 }
 
 constexpr int kInt2Waves = 8;   // two per SIMD, one workgroup per CU
+constexpr int kInt2Slots = 3;   // chunks in a wave's ring: two in flight while one is computed
 
 template <int D, int JJ>
 hipError_t launch_dj(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) {
-    constexpr int W = kInt2Waves;
-    using L = I2Lds<D, JJ, W>;
+    constexpr int W = kInt2Waves, NS = kInt2Slots;
+    using L = I2Lds<D, JJ, W, NS>;
     if (L::BYTES > 64 * 1024) {
-        hipError_t e = allow_lds<attn_int2_kernel<D, JJ, W>>(L::BYTES);
+        hipError_t e = allow_lds<attn_int2_kernel<D, JJ, W, NS>>(L::BYTES);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((attn_int2_kernel<D, JJ, W>), dim3(pl.n_splits * a.g.n_kv), dim3(W * 64), L::BYTES, stream, a,
-                       pl.n_splits, pl.group, pl.rows);
+    hipLaunchKernelGGL((attn_int2_kernel<D, JJ, W, NS>), dim3(pl.n_splits * a.g.n_kv), dim3(W * 64), L::BYTES, stream,
+                       a, pl.n_splits, pl.group, pl.rows);
     return hipGetLastError();
 }
 

@@ -49,28 +49,6 @@
 namespace kvq {
 namespace {
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void glb_void;
-
-// Workgroup barrier for LDS data only: unlike __syncthreads() it does not wait
-// for the direct-to-LDS loads in flight (the release fence there would).
-__device__ inline void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// Waits until at most N vector-memory requests of this wave are outstanding
-// (direct-to-LDS loads count); also a compiler memory fence, since the
-// compiler cannot see that later LDS reads depend on those loads.
-template <int N>
-__device__ inline void vm_wait() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
-
-// 16 bytes per lane, global -> LDS: lane i's bytes land at lds + 16 i.
-__device__ inline void dma16(const void* g, void* lds) {
-    __builtin_amdgcn_global_load_lds((glb_void*)g, (lds_void*)lds, 16, 0, 0);
-}
-
 // 8 int8 codes -> 8 fp16 values, exactly: flip the sign bit to get c + 128,
 // place each byte under the fp16 exponent of 1024 (0x64xx = 1024 + byte),
 // subtract 1152.

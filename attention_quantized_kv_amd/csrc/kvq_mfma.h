@@ -84,5 +84,27 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ inline half2v as_h2(uint32_t x) { return __builtin_bit_cast(half2v, x); }
 
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+
+// Workgroup barrier for LDS data only: unlike __syncthreads() it does not wait
+// for the direct-to-LDS loads in flight (the release fence there would).
+__device__ inline void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Waits until at most N vector-memory requests of this wave are outstanding
+// (direct-to-LDS loads count); also a compiler memory fence, since the
+// compiler cannot see that later LDS reads depend on those loads.
+template <int N>
+__device__ inline void vm_wait() { asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory"); }
+
+// 16 bytes per lane, global -> LDS: lane i's bytes land at lds + 16 i.
+__device__ inline void dma16(const void* g, void* lds) {
+    __builtin_amdgcn_global_load_lds((glb_void*)g, (lds_void*)lds, 16, 0, 0);
+}
+
 }  // namespace
 }  // namespace kvq

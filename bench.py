@@ -34,9 +34,12 @@ HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
 
 
-def kv_bytes_per_token_layer(n_kv: int, D: int) -> int:
+def kv_bytes_per_token_layer(n_kv: int, D: int, codec: int = 0) -> int:
     """Algorithmic bytes one token of one layer occupies: per 32-value block a
-    34-byte Q8_0 K block and an 18-byte Q4_0 V block."""
+    34-byte Q8_0 K block and an 18-byte Q4_0 V block; with the INT2 codec per
+    128-value block 36 bytes (32 of codes, fp16 scale and zero) for K and V."""
+    if codec == 1:
+        return n_kv * (D // 128) * 2 * 36
     return n_kv * (D // 32) * (34 + 18)
 
 
@@ -82,7 +85,7 @@ class Layer:
         import attention_quantized_kv_amd as kvq
         self.kvq = kvq
         self.w = w
-        self.L = kvq.Layout(w.n_kv, w.head_dim, w.page_size, w.n_pages)
+        self.L = kvq.Layout(w.n_kv, w.head_dim, w.page_size, w.n_pages, w.codec)
         self.pool = torch.empty(kvq.kvq_pool_bytes(self.L), dtype=torch.uint8, device=device)
         if shuffle_pages:
             perm = torch.randperm(w.n_pages, generator=torch.Generator().manual_seed(1000 + layer))
@@ -157,14 +160,17 @@ class BatchLayer:
 
 
 KERNEL_SOURCES = {"attn_mfma_stream": "attn_mfma_stream.hip", "attn_mfma_tiled": "attn_mfma_tiled.hip",
-                  "attn_valu": "attn_valu.hip"}
+                  "attn_valu": "attn_valu.hip", "attn_int2": "attn_int2.hip"}
 
 
 def kernel_name(w, kernel: int) -> str:
     """Name of the attention kernel the plan picks (mirrors the library's
     automatic choice: streaming MFMA for decode / verify with at most 64 query
-    rows per KV head, the LDS-tiled MFMA kernel otherwise)."""
+    rows per KV head, the LDS-tiled MFMA kernel otherwise; the INT2 kernel
+    for the 2-bit cache)."""
     rows = w.n_q * (w.n_heads // w.n_kv)
+    if w.codec == 1:
+        return "attn_int2"
     if kernel == 0:
         kernel = 2 if (w.n_q <= 8 and rows <= 64) else 3
     return {1: "attn_valu", 2: "attn_mfma_stream", 3: "attn_mfma_tiled"}[kernel]
@@ -203,7 +209,7 @@ def cpu_baseline(w, min_seconds: float, max_reps: int = 8):
     import oracle
     import synth
     k, v = synth.layer_kv(w, 0)
-    cache = oracle.QuantCache.from_float(k, v)
+    cache = (oracle.Int2Cache if w.codec == 1 else oracle.QuantCache).from_float(k, v)
     del k, v
     q = synth.layer_q(w, 0)
     if w.n_q <= 8:
@@ -211,7 +217,7 @@ def cpu_baseline(w, min_seconds: float, max_reps: int = 8):
         desc = f"one {w.ctx}-token layer, all {len(rows)} query rows"
         if w.n_seqs > 1:
             desc = f"one of the {w.n_seqs} sequences of a layer ({w.ctx} tokens), all {len(rows)} query rows"
-        bytes_per_rep = w.ctx * kv_bytes_per_token_layer(w.n_kv, w.head_dim)
+        bytes_per_rep = w.ctx * kv_bytes_per_token_layer(w.n_kv, w.head_dim, w.codec)
     else:
         rng = __import__("numpy").random.default_rng(0)
         sel = sorted({0, 255, 256, w.n_q - 1, *rng.integers(0, w.n_q, 12).tolist()})
@@ -317,7 +323,7 @@ def bench_stream(args, w, n_layers):
     stop.record()
     torch.cuda.synchronize()
     copy_gbs = 4 * nbytes / (start.elapsed_time(stop) / 1e3) / 1e9
-    bytes_layer = w.ctx * kv_bytes_per_token_layer(w.n_kv, w.head_dim)
+    bytes_layer = w.ctx * kv_bytes_per_token_layer(w.n_kv, w.head_dim, w.codec)
     us_per_layer = 1000.0 * total_ms / args.steps / n_layers
     value = bytes_layer / (us_per_layer / 1e6) / 1e9
     rec = {
@@ -352,7 +358,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="decode262k",
                     choices=["tiny", "decode65k", "decode262k", "verify131k", "prefill262k", "batch16x16k",
-                             "stream262k"])
+                             "stream262k", "int2decode262k"])
     ap.add_argument("--layers", type=int, default=None, help="layers in the stack (default: the workload's)")
     ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA streaming, 3 MFMA tiled")
     ap.add_argument("--cps", type=int, default=0, help="32-token chunks per split (0: the library's choice)")
@@ -413,7 +419,8 @@ def main():
     else:
         layers = [Layer(w, i, dev, shuffle_pages=args.shuffle_pages) for i in range(n_layers)]
     Layer.cps = args.cps
-    fused = not prefill and not args.unfused and not batched
+    # (the INT2 codec has no fused append + attention: append, then attend)
+    fused = not prefill and not args.unfused and not batched and w.codec == 0
     if batched:
         ws_n = kvq.kvq_decode_attn_batch_workspace_bytes(layers[0].L, layers[0].ctx_lens, w.n_heads, w.n_q)
     elif fused:
@@ -478,9 +485,9 @@ def main():
     traffic = measured_traffic(w.name, kname)
 
     ms_per_step = total_ms / args.steps
-    bytes_layer = w.n_seqs * w.ctx * kv_bytes_per_token_layer(w.n_kv, w.head_dim)
+    bytes_layer = w.n_seqs * w.ctx * kv_bytes_per_token_layer(w.n_kv, w.head_dim, w.codec)
     # bytes the timed kernel reads: the fused step's split pass reads the cached keys only
-    bytes_kernel = w.n_seqs * (w.cached if fused else w.ctx) * kv_bytes_per_token_layer(w.n_kv, w.head_dim)
+    bytes_kernel = w.n_seqs * (w.cached if fused else w.ctx) * kv_bytes_per_token_layer(w.n_kv, w.head_dim, w.codec)
     us_per_layer = 1000.0 * ms_per_step / n_layers
     flops_layer = attention_flops(w)
     rec = {
@@ -488,7 +495,8 @@ def main():
         "dtype": "f16 MFMA / f32" if args.kernel in (0, 2, 3) else "f32",
         "config": {"workload": w.name, "layers": n_layers, **({"n_seqs": w.n_seqs} if batched else {}), "n_heads": w.n_heads, "n_kv_heads": w.n_kv,
                    "head_dim": w.head_dim, "ctx": w.ctx, "n_q": w.n_q, "page_size": w.page_size,
-                   "kv_format": "K Q8_0 + V Q4_0", "kernel": args.kernel or "auto",
+                   "kv_format": ("K INT2 + V INT2 (128-value blocks, fp16 scale and zero)" if w.codec == 1
+                                 else "K Q8_0 + V Q4_0"), "kernel": args.kernel or "auto",
                    "chunks_per_split": args.cps or "auto",
                    "step": ("kvq_append_attn (append + attention, 2 kernels)" if fused else
                             f"kvq_decode_attn_batch over {w.n_seqs} sequences (2 kernels; cache filled beforehand)"

@@ -74,7 +74,8 @@ class Workload:
     """One workload: a cache of ``cached`` tokens, ``n_new`` rows appended at
     position ``cached``, then ``n_q`` queries ending at ``cached + n_new``;
     ``n_seqs`` such sequences per layer (batched decode) when above 1;
-    ``host_resident``: the caches live in host memory and stream in."""
+    ``host_resident``: the caches live in host memory and stream in;
+    ``codec``: how the cache stores K and V."""
     name: str
     wid: int
     layers: int
@@ -88,6 +89,7 @@ class Workload:
     outliers: bool = False
     n_seqs: int = 1
     host_resident: bool = False
+    codec: int = 0          # 0: K Q8_0 + V Q4_0; 1: K and V INT2 (128-value blocks)
 
     @property
     def ctx(self) -> int:
@@ -119,6 +121,9 @@ WORKLOADS = {
     # decode262k with every layer's cache in pinned host memory, streamed to
     # the GPU layer by layer while the previous layer's attention runs
     "stream262k": Workload("stream262k", 7, 16, 24, 4, 256, 262144, 0, 1, host_resident=True),
+    # decode262k over the 2-bit cache (K and V INT2: 144 bytes per token and
+    # KV head instead of 416)
+    "int2decode262k": Workload("int2decode262k", 8, 16, 24, 4, 256, 262143, 1, 1, codec=1),
 }
 
 

@@ -8,6 +8,9 @@ Inputs come from the seeded host generators (synth), so the oracle sees the
 same fp32 values.  Checked against the oracle:
   * K/V codes and scales of sampled pages (first, middle, the appended tail),
     bit for bit;
+  * for the 2-bit cache (int2decode262k: K and V INT2, decoded with the
+    header's layout) codes, scales and zero-points of sampled pages, bit for
+    bit, and the outputs of every query row;
   * attention outputs and lse of every query row for the decode and verify
     workloads, and of sampled rows (first and last queries of the chunk, the
     page edges 255/256, seeded random ones; heads of every KV group) for the
@@ -30,7 +33,7 @@ def _run(w, fused=False):
     import attention_quantized_kv_amd as kvq
     k, v = synth.layer_kv(w, 0)
     q = synth.layer_q(w, 0)
-    L = tu.layout(w.n_kv, w.head_dim, w.page_size, w.n_pages)
+    L = tu.layout(w.n_kv, w.head_dim, w.page_size, w.n_pages, codec=w.codec)
     pool = tu.alloc_pool(L)
     pt_dev, pt = tu.page_table_for(w.ctx, w.page_size, w.n_pages)
     for r in range(0, w.cached, FILL_CHUNK):
@@ -97,3 +100,23 @@ def test_full_size(name, fused):
     got = np.stack([out[i, h] for i, h in rows])
     got_lse = np.array([lse[i, h] for i, h in rows])
     tu.assert_close(got, ref, got_lse, ref_lse, f"{name}{' fused' if fused else ''} ({len(rows)} rows)")
+
+
+def test_full_size_int2():
+    w = synth.WORKLOADS["int2decode262k"]
+    k, v, q, L, pool, pt, out, lse = _run(w)
+    cache = oracle.Int2Cache.from_float(k, v)
+    del k, v
+    pool_np = pool.cpu().numpy()
+    names = ("K codes", "K scales", "K zeros", "V codes", "V scales", "V zeros")
+    for lp in sorted({0, w.n_pages // 2, w.cached // w.page_size, w.n_pages - 1}):
+        s0 = lp * w.page_size
+        n = min(w.page_size, w.ctx - s0)
+        got = tu.decode_pool_int2(pool_np, L, np.array([pt[lp]], dtype=np.int32), n)
+        for name, g, want in zip(names, got, cache.k + cache.v):
+            assert np.array_equal(g, want[s0:s0 + n]), f"{name} of page {lp}"
+    rows = _rows(w)
+    ref, ref_lse = oracle.attention(q, cache, w.scale, rows=rows)
+    got = np.stack([out[i, h] for i, h in rows])
+    got_lse = np.array([lse[i, h] for i, h in rows])
+    tu.assert_close(got, ref, got_lse, ref_lse, f"int2decode262k ({len(rows)} rows)")
