@@ -176,17 +176,31 @@ def kernel_name(w, kernel: int) -> str:
     return {1: "attn_valu", 2: "attn_mfma_stream", 3: "attn_mfma_tiled"}[kernel]
 
 
+def source_digest(kname: str):
+    """sha256 over the kernel's .hip file and the two headers every kernel
+    includes (kvq_internal.h, kvq_mfma.h), in that order; None if missing."""
+    import hashlib
+    csrc = os.path.join(ROOT, "attention_quantized_kv_amd", "csrc")
+    h = hashlib.sha256()
+    for name in (KERNEL_SOURCES[kname], "kvq_internal.h", "kvq_mfma.h"):
+        path = os.path.join(csrc, name)
+        if not os.path.exists(path):
+            return None
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
+
+
 def measured_traffic(workload: str, kname: str):
     """HBM bytes per launch of `kname` on `workload` from the committed
     rocprofv3 counter summary (profiles/hbm_traffic.txt: FETCH_SIZE and
     WRITE_SIZE scaled by the factors a plain copy of known size gives), or
-    None when there is no entry or the kernel source has changed since."""
-    import hashlib
+    None when there is no entry or the kernel sources have changed since."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
-    src = os.path.join(ROOT, "attention_quantized_kv_amd", "csrc", KERNEL_SOURCES[kname])
-    if not os.path.exists(path) or not os.path.exists(src):
+    if not os.path.exists(path):
         return None
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    digest = source_digest(kname)
+    if digest is None:
+        return None
     for line in open(path):
         f = line.split()
         if len(f) >= 8 and not line.startswith("#") and f[0] == workload and f[1] == kname:
