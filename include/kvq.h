@@ -121,10 +121,9 @@ typedef struct {
  * Attention over this codec: decode and verify only (kvq_decode_attn and
  * kvq_attn_ex with kernel 0 or 4, n_q * group <= 16); kvq_append_attn runs
  * kvq_append and then that decode; prefill and batched decode return
- * UNSUPPORTED for it.  Its kernel feeds fp16 matrix cores with operands
- * scaled by powers of two: every component of scale * q must lie within
- * +-700 and every V block scale below 4,096 (a V block range below 12,000),
- * else the output is not finite.
+ * UNSUPPORTED for it.  Its kernel feeds the attention weights to fp16 matrix
+ * cores scaled by up to 16: every V block scale must stay below 4,096 (a V
+ * block range below 12,000), else the output is not finite.
  */
 int kvq_unit_bytes(const kvq_layout *layout, size_t *bytes);
 int kvq_pool_bytes(const kvq_layout *layout, size_t *bytes);
