@@ -44,8 +44,6 @@ template <int D>
 struct I2Cfg {
     static constexpr int NB2 = D / kBlock2;   // 128-value blocks per row
     static constexpr int STEPS = D / 32;      // 32-dim MFMA steps of q . k
-    static constexpr int KD = D / 64;         // K code dwords per lane and 16-token tile
-    static constexpr int VD = D / 32;         // V code dwords per lane and 32-token chunk
     static constexpr int NT = D / 16;         // 16-dim output tiles
 };
 
