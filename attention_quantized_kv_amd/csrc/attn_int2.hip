@@ -197,8 +197,8 @@ struct I2Lds {
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <int D, int JJ, int W, int NSLOT>
-__global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_splits, int group, int rows) {
+template <int D, int JJ, int W, int NSLOT, class Batch>
+__global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_splits, int group, int rows, Batch sb) {
     using C = I2Cfg<D>;
     using S = I2Slot<D>;
     using L = I2Lds<D, JJ, W, NSLOT>;
@@ -207,7 +207,21 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g4 = lane >> 4, n16 = lane & 15;
-    const int split = blockIdx.x % n_splits, kvh = blockIdx.x / n_splits;
+    int wg = blockIdx.x;
+    if constexpr (!std::is_same_v<Batch, NoBatch>) {
+        // batched decode: this workgroup serves sequence b, whose keys, page
+        // table row, queries and partials start where the table says
+        const int b = seq_of(sb.wg0, sb.n, wg);
+        wg -= sb.wg0[b];
+        n_splits = sb.n_splits[b];
+        a.ctx = sb.ctx[b];
+        a.page_table += (size_t)b * sb.n_table;
+        a.q += (size_t)b * a.n_q * a.n_heads * D;
+        a.ws_m += sb.part0[b];
+        a.ws_l += sb.part0[b];
+        a.ws_acc += (size_t)sb.part0[b] * D;
+    }
+    const int split = wg % n_splits, kvh = wg / n_splits;
     const int c1 = (a.ctx + kChunk - 1) / kChunk;
     const int first_last = a.causal ? a.ctx - a.n_q : a.ctx - 1;   // last key of query 0
     const int mask_group = a.causal ? group : 0x7fffffff;
@@ -562,36 +576,42 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
 constexpr int kInt2Waves = 8;   // two per SIMD, one workgroup per CU
 constexpr int kInt2Slots = 3;   // chunks in a wave's ring: two in flight while one is computed
 
-template <int D, int JJ>
-hipError_t launch_dj(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) {
+template <int D, int JJ, class Batch>
+hipError_t launch_dj(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream, const Batch& sb, int n_wg) {
     constexpr int W = kInt2Waves, NS = kInt2Slots;
     using L = I2Lds<D, JJ, W, NS>;
     if (L::BYTES > 64 * 1024) {
-        hipError_t e = allow_lds<attn_int2_kernel<D, JJ, W, NS>>(L::BYTES);
+        hipError_t e = allow_lds<attn_int2_kernel<D, JJ, W, NS, Batch>>(L::BYTES);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((attn_int2_kernel<D, JJ, W, NS>), dim3(pl.n_splits * a.g.n_kv), dim3(W * 64), L::BYTES, stream,
-                       a, pl.n_splits, pl.group, pl.rows);
+    hipLaunchKernelGGL((attn_int2_kernel<D, JJ, W, NS, Batch>), dim3(n_wg), dim3(W * 64), L::BYTES, stream, a,
+                       pl.n_splits, pl.group, pl.rows, sb);
     return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_d(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) {
-    if (pl.rows <= 8) return launch_dj<D, 2>(a, pl, stream);
-    if (pl.rows <= 16) return launch_dj<D, 4>(a, pl, stream);
+template <int D, class Batch>
+hipError_t launch_d(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream, const Batch& sb, int n_wg) {
+    if (pl.rows <= 8) return launch_dj<D, 2>(a, pl, stream, sb, n_wg);
+    if (pl.rows <= 16) return launch_dj<D, 4>(a, pl, stream, sb, n_wg);
     return hipErrorInvalidValue;
+}
+
+template <class Batch>
+hipError_t launch_any(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream, const Batch& sb, int n_wg) {
+    switch (a.g.D) {
+        case 128: return launch_d<128>(a, pl, stream, sb, n_wg);
+        case 256: return launch_d<256>(a, pl, stream, sb, n_wg);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
 
 int int2_waves() { return kInt2Waves; }
 
-hipError_t launch_attn_int2(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) {
-    switch (a.g.D) {
-        case 128: return launch_d<128>(a, pl, stream);
-        case 256: return launch_d<256>(a, pl, stream);
-        default: return hipErrorInvalidValue;
-    }
+hipError_t launch_attn_int2(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream, const SeqBatch* batch) {
+    if (batch != nullptr && batch->n > 0) return launch_any(a, pl, stream, *batch, batch->wg0[batch->n]);
+    return launch_any(a, pl, stream, NoBatch{}, pl.n_splits * a.g.n_kv);
 }
 
 }  // namespace kvq

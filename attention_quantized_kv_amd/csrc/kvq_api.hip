@@ -257,8 +257,6 @@ int batch_plan(const kvq_layout* L, int32_t n_table, int32_t n_seqs, const int32
     kvq::Geom g;
     int st = check_layout(L, &g);
     if (st) return st;
-    if (L->codec != KVQ_CODEC_Q8K_Q4V)
-        return fail(KVQ_ERR_UNSUPPORTED, "batched decode reads the Q8_0/Q4_0 codec only");
     if (n_seqs < 1 || n_seqs > KVQ_MAX_SEQS)
         return fail(KVQ_ERR_INVALID_ARG, "n_seqs %d outside [1, %d]", n_seqs, KVQ_MAX_SEQS);
     if (ctx_lens == nullptr) return fail(KVQ_ERR_INVALID_ARG, "ctx_lens is NULL");
@@ -270,10 +268,11 @@ int batch_plan(const kvq_layout* L, int32_t n_table, int32_t n_seqs, const int32
         if (st) return fail(st, "sequence %d: %s", b, kvq_last_error_copy());
         total += (ctx_lens[b] + kvq::kChunk - 1) / kvq::kChunk;
     }
-    kvq_attn_opts opts{2, 1, nullptr, nullptr};
+    // the streaming kernel of the codec: 2 (Q8_0/Q4_0) or 4 (INT2)
+    kvq_attn_opts opts{L->codec == KVQ_CODEC_INT2 ? 4 : 2, 1, nullptr, nullptr};
     st = make_plan(L, n_heads, ctx_lens[0], n_q, false, &opts, pl);   // kernel, group, rows
     if (st) return st;
-    const int wpg = kvq::mfma_stream_waves(pl->rows);
+    const int wpg = pl->kernel == 4 ? kvq::int2_waves() : kvq::mfma_stream_waves(pl->rows);
     long per_head = device_cus() / L->n_kv_heads;
     if (per_head < 1) per_head = 1;
     sb->n = n_seqs;
@@ -492,9 +491,12 @@ int kvq_decode_attn_batch(const kvq_layout* layout, const void* d_pool, const in
                           void* d_ws, size_t ws_bytes, const kvq_attn_opts* opts, void* stream) {
     if (d_pool == nullptr || d_page_tables == nullptr || d_q == nullptr || d_out == nullptr)
         return fail(KVQ_ERR_INVALID_ARG, "pool, page_tables, q and out must be non-NULL");
-    if (opts != nullptr && opts->kernel != 0 && opts->kernel != 2)
-        return fail(KVQ_ERR_INVALID_ARG, "batched decode runs the streaming kernel (kernel 0 or 2, got %d)",
+    if (opts != nullptr && opts->kernel != 0 && opts->kernel != 2 && opts->kernel != 4)
+        return fail(KVQ_ERR_INVALID_ARG, "batched decode runs a streaming kernel (kernel 0, 2 or 4, got %d)",
                     opts->kernel);
+    if (layout != nullptr && opts != nullptr && opts->kernel != 0 &&
+        opts->kernel != (layout->codec == KVQ_CODEC_INT2 ? 4 : 2))
+        return fail(KVQ_ERR_UNSUPPORTED, "kernel %d does not read codec %d", opts->kernel, layout->codec);
     kvq::AttnPlan pl;
     kvq::SeqBatch sb;
     size_t parts = 0;
@@ -528,7 +530,8 @@ int kvq_decode_attn_batch(const kvq_layout* layout, const void* d_pool, const in
     hipError_t e = hipSuccess;
     if (opts != nullptr && opts->kernel_begin_event != nullptr)
         e = hipEventRecord(static_cast<hipEvent_t>(opts->kernel_begin_event), s);
-    if (e == hipSuccess) e = kvq::launch_attn_mfma_stream(a, pl, s, &sb);
+    if (e == hipSuccess)
+        e = pl.kernel == 4 ? kvq::launch_attn_int2(a, pl, s, &sb) : kvq::launch_attn_mfma_stream(a, pl, s, &sb);
     if (e == hipSuccess && opts != nullptr && opts->kernel_end_event != nullptr)
         e = hipEventRecord(static_cast<hipEvent_t>(opts->kernel_end_event), s);
     if (e == hipSuccess) e = kvq::launch_merge(a, pl, s, &sb);

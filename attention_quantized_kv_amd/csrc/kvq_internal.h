@@ -194,7 +194,8 @@ hipError_t launch_merge_new(const AttnArgs& a, const NewRows& nr, int n_splits, 
 int mfma_stream_row_groups(int rows);
 int mfma_stream_waves(int rows);
 // Decode over the INT2 codec (rows <= 16) and its waves per workgroup.
-hipError_t launch_attn_int2(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream);
+hipError_t launch_attn_int2(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream,
+                            const SeqBatch* batch = nullptr);
 int int2_waves();
 // Query rows per workgroup of the LDS-tiled MFMA kernel.
 int mfma_tiled_rows_per_wg();

@@ -118,9 +118,9 @@ typedef struct {
  *   next 2*P*nb2 bytes       V scales, fp16 bits, [chunk][block][32 tokens].
  *   next 2*P*nb2 bytes       V zeros, fp16 bits, [chunk][block][32 tokens].
  * The unit is 9*P*D/16 bytes: 144 bytes per token at D = 256.
- * Attention over this codec: decode and verify only (kvq_decode_attn and
- * kvq_attn_ex with kernel 0 or 4, n_q * group <= 16); kvq_append_attn runs
- * kvq_append and then that decode; prefill and batched decode return
+ * Attention over this codec: decode and verify only (kvq_decode_attn,
+ * kvq_decode_attn_batch and kvq_attn_ex with kernel 0 or 4, n_q * group <=
+ * 16); kvq_append_attn runs kvq_append and then that decode; prefill returns
  * UNSUPPORTED for it.  Its kernel feeds the attention weights to fp16 matrix
  * cores scaled by up to 16: every V block scale must stay below 4,096 (a V
  * block range below 12,000), else the output is not finite.
@@ -276,13 +276,17 @@ int kvq_append_attn(const kvq_layout *layout, void *d_pool,
  *   d_ws           workspace of at least kvq_decode_attn_batch_workspace_bytes()
  *                  bytes for the same n_seqs, ctx_lens, n_heads and n_q
  *   opts           may be NULL; as for kvq_attn_ex, except that kernel must be
- *                  0 or 2 and chunks_per_split is ignored (the events bracket
- *                  the streaming kernel of all sequences)
+ *                  0 or the codec's streaming kernel (2 for
+ *                  KVQ_CODEC_Q8K_Q4V, 4 for KVQ_CODEC_INT2) and
+ *                  chunks_per_split is ignored (the events bracket the
+ *                  streaming kernel of all sequences)
  * 1 <= n_seqs <= KVQ_MAX_SEQS, 1 <= n_q <= KVQ_MAX_NQ_DECODE, and
- * n_q * (n_heads / n_kv_heads) <= 64 (the streaming kernel runs every
- * sequence; a sequence's share of the workgroups follows its context length).
+ * n_q * (n_heads / n_kv_heads) <= 64 (16 for KVQ_CODEC_INT2; the streaming
+ * kernel runs every sequence; a sequence's share of the workgroups follows
+ * its context length).
  * Errors: INVALID_ARG (nulls, n_seqs or n_q out of range, a ctx_lens[b] <
- * n_q, opts->kernel other than 0 or 2), UNSUPPORTED, CAPACITY (a ctx_lens[b] > n_table * page_size),
+ * n_q, opts->kernel other than 0, 2 or 4), UNSUPPORTED (the other codec's
+ * kernel, too many rows), CAPACITY (a ctx_lens[b] > n_table * page_size),
  * WORKSPACE, HIP.
  */
 int kvq_decode_attn_batch_workspace_bytes(const kvq_layout *layout, int32_t n_seqs, const int32_t *ctx_lens,

@@ -166,9 +166,9 @@ def test_int2_codec_layout():
 
 
 def test_int2_attention_plan():
-    """Attention over the INT2 codec: decode with up to 16 rows per KV head
-    (kernel 0 or 4); prefill, more rows, the other kernels and batched
-    decode are rejected; kernel 4 needs the INT2 codec."""
+    """Attention over the INT2 codec: decode and batched decode with up to 16
+    rows per KV head (kernel 0 or 4); prefill, more rows and the other
+    kernels are rejected; kernel 4 needs the INT2 codec."""
     L = kvq.Layout(2, 256, 64, 100, kvq.KVQ_CODEC_INT2)
     assert kvq.kvq_workspace_bytes(L, 12, 5000, 1) > 0                  # 6 rows
     assert kvq.kvq_workspace_bytes_ex(L, 16, 5000, 2, kernel=4) > 0     # 16 rows
@@ -184,7 +184,8 @@ def test_int2_attention_plan():
     assert status(kvq.kvq_workspace_bytes_ex, L, 12, 5000, 1, kernel=5) == kvq.KVQ_ERR_INVALID_ARG
     assert status(kvq.kvq_workspace_bytes_ex, kvq.Layout(2, 256, 64, 100), 12, 5000, 1,
                   kernel=4) == kvq.KVQ_ERR_INVALID_ARG
-    assert status(kvq.kvq_decode_attn_batch_workspace_bytes, L, [100, 200], 12, 1) == kvq.KVQ_ERR_UNSUPPORTED
+    assert kvq.kvq_decode_attn_batch_workspace_bytes(L, [100, 200], 12, 1) > 0            # batched decode
+    assert status(kvq.kvq_decode_attn_batch_workspace_bytes, L, [100, 200], 12, 3) == kvq.KVQ_ERR_UNSUPPORTED
 
 
 def test_status_strings():

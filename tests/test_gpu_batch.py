@@ -6,6 +6,7 @@ lse must match the oracle run on that sequence alone.  Cases: ragged lengths
 from 8 to 20,000 keys (a single key in the largest batch), n_q = 1..8 (all
 four row layouts of the streaming kernel), the largest batch (64 sequences), and a page-table entry
 outside the pool in one sequence (that sequence NaN, the others exact).
+The same over the INT2 cache (its streaming kernel, up to 16 rows).
 """
 import math
 
@@ -19,14 +20,14 @@ pytestmark = pytest.mark.gpu
 
 
 class Batch:
-    def __init__(self, seed, ctx_lens, n_kv, D, P):
+    def __init__(self, seed, ctx_lens, n_kv, D, P, codec=0):
         import torch
         import attention_quantized_kv_amd as kvq
         self.kvq = kvq
         rng = np.random.default_rng(seed)
         pages = [(c + P - 1) // P for c in ctx_lens]
         n_pages = sum(pages) + 3
-        self.L = tu.layout(n_kv, D, P, n_pages)
+        self.L = tu.layout(n_kv, D, P, n_pages, codec=codec)
         self.pool = tu.alloc_pool(self.L, fill=0xFF)
         perm = rng.permutation(n_pages).astype(np.int32)
         n_table = max(pages)
@@ -42,7 +43,7 @@ class Batch:
             v = rng.standard_normal((c, n_kv, D)).astype(np.float32)
             kvq.kvq_append(self.L, self.pool, self.pt[b].contiguous(), 0, torch.from_numpy(k).cuda(),
                            torch.from_numpy(v).cuda())
-            self.caches.append(oracle.QuantCache.from_float(k, v))
+            self.caches.append((oracle.Int2Cache if codec == kvq.KVQ_CODEC_INT2 else oracle.QuantCache).from_float(k, v))
         self.ctx_lens, self.n_kv, self.D, self.rng = list(ctx_lens), n_kv, D, rng
 
     def run(self, G, n_q, pt=None):
@@ -93,3 +94,32 @@ def test_invalid_page_in_one_sequence(ragged):
             continue
         ref, ref_lse, _ = oracle.attention(q[b], ragged.caches[b], scale)
         tu.assert_close(out[b], ref, lse[b], ref_lse, f"sequence {b} beside the bad one")
+
+
+@pytest.fixture(scope="module")
+def ragged_int2():
+    import attention_quantized_kv_amd as kvq
+    return Batch(95, [8, 97, 3000, 257, 9000, 64, 2], n_kv=2, D=256, P=64, codec=kvq.KVQ_CODEC_INT2)
+
+
+@pytest.mark.parametrize("G,n_q", [(6, 1), (4, 2), (8, 2), (1, 1)])
+def test_int2_batch_matches_oracle_per_sequence(ragged_int2, G, n_q):
+    q, scale, out, lse = ragged_int2.run(G, n_q)
+    for b, c in enumerate(ragged_int2.ctx_lens):
+        ref, ref_lse, _ = oracle.attention(q[b], ragged_int2.caches[b], scale)
+        tu.assert_close(out[b], ref, lse[b], ref_lse, f"INT2 sequence {b} (ctx {c}), G={G} n_q={n_q}")
+
+
+def test_int2_batch_bad_page_and_d128():
+    import attention_quantized_kv_amd as kvq
+    bt = Batch(97, [1 + (53 * i) % 700 for i in range(20)], n_kv=1, D=128, P=32, codec=kvq.KVQ_CODEC_INT2)
+    bad = bt.pt.clone()
+    bad[5, 3] = bt.L.n_pages + 1              # sequence 5 only (it has more than 3 pages)
+    assert bt.ctx_lens[5] > 3 * 32
+    q, scale, out, lse = bt.run(4, 1, pt=bad)
+    assert np.isnan(out[5]).all() and np.isnan(lse[5]).all()
+    for b, c in enumerate(bt.ctx_lens):
+        if b == 5:
+            continue
+        ref, ref_lse, _ = oracle.attention(q[b], bt.caches[b], scale)
+        tu.assert_close(out[b], ref, lse[b], ref_lse, f"INT2 sequence {b} of 20 (ctx {c}) beside a bad one")
