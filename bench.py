@@ -136,7 +136,7 @@ class BatchLayer:
         self.kvq = kvq
         self.w = w
         pages = w.n_pages
-        self.L = kvq.Layout(w.n_kv, w.head_dim, w.page_size, pages * w.n_seqs)
+        self.L = kvq.Layout(w.n_kv, w.head_dim, w.page_size, pages * w.n_seqs, w.codec)
         self.pool = torch.empty(kvq.kvq_pool_bytes(self.L), dtype=torch.uint8, device=device)
         pt = torch.arange(pages)[None, :] * w.n_seqs + torch.arange(w.n_seqs)[:, None]
         self.pt = pt.to(torch.int32).to(device).contiguous()
@@ -372,7 +372,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="decode262k",
                     choices=["tiny", "decode65k", "decode262k", "verify131k", "prefill262k", "batch16x16k",
-                             "stream262k", "int2decode262k"])
+                             "stream262k", "int2decode262k", "int2batch16x16k"])
     ap.add_argument("--layers", type=int, default=None, help="layers in the stack (default: the workload's)")
     ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA streaming, 3 MFMA tiled")
     ap.add_argument("--cps", type=int, default=0, help="32-token chunks per split (0: the library's choice)")

@@ -124,6 +124,8 @@ WORKLOADS = {
     # decode262k over the 2-bit cache (K and V INT2: 144 bytes per token and
     # KV head instead of 416)
     "int2decode262k": Workload("int2decode262k", 8, 16, 24, 4, 256, 262143, 1, 1, codec=1),
+    # batch16x16k over the 2-bit cache
+    "int2batch16x16k": Workload("int2batch16x16k", 9, 16, 24, 4, 256, 16383, 1, 1, n_seqs=16, codec=1),
 }
 
 
