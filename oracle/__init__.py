@@ -258,6 +258,30 @@ class Int2Cache:
         return dequant_int2(*self.v)
 
 
+def hadamard_matrix(n: int) -> np.ndarray:
+    """The n x n Hadamard matrix of Sylvester's construction (n a power of
+    two): H_1 = [1], H_2m = [[H_m, H_m], [H_m, -H_m]].  Entries +-1, symmetric,
+    H H = n I."""
+    assert n >= 1 and n & (n - 1) == 0, "n must be a power of two"
+    h = np.ones((1, 1))
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def hadamard(x: np.ndarray) -> np.ndarray:
+    """The normalized Hadamard rotation of every row (last axis, a power of
+    two): y = x H / sqrt(n), fp64.  The rotation the pages bake into a model
+    so that the 2-bit cache holds rotated K and V ("OSCAR2 KV Cache
+    benchmark", rotation model conversion: a Hadamard rotation per head of
+    dimension 256).  H / sqrt(n) is orthogonal and symmetric, so it is its own
+    inverse: rotating q and k leaves every score unchanged, and rotating v
+    rotates the output, which one more rotation undoes."""
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[-1]
+    return x @ hadamard_matrix(n) / np.sqrt(n)
+
+
 def attention_dense(q: np.ndarray, k_hat: np.ndarray, v_hat: np.ndarray, scale: float, rows=None,
                     ctx: int | None = None):
     """attention() over given dequantized K and V [ctx][n_kv][D] (fp64)."""
