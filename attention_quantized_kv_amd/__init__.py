@@ -30,7 +30,7 @@ EXPORTS = (
     "kvq_unit_bytes", "kvq_pool_bytes", "kvq_append", "kvq_workspace_bytes",
     "kvq_decode_attn", "kvq_prefill_attn", "kvq_workspace_bytes_ex", "kvq_attn_ex",
     "kvq_append_attn_workspace_bytes", "kvq_append_attn",
-    "kvq_decode_attn_batch_workspace_bytes", "kvq_decode_attn_batch", "kvq_stage_pages",
+    "kvq_decode_attn_batch_workspace_bytes", "kvq_decode_attn_batch", "kvq_stage_pages", "kvq_hadamard",
     "kvq_status_str", "kvq_last_error", "kvq_version",
 )
 
@@ -92,6 +92,7 @@ def lib() -> ctypes.CDLL:
         "kvq_decode_attn_batch_workspace_bytes": [LP, i32, P, i32, i32, SZP],
         "kvq_decode_attn_batch": [LP, P, P, i32, i32, P, i32, i32, P, ctypes.c_float, P, P, P, sz, OP, P],
         "kvq_stage_pages": [LP, P, P, i32, LP, P, i32, P],
+        "kvq_hadamard": [P, ctypes.c_int64, i32, P],
         "kvq_status_str": [ctypes.c_int],
         "kvq_last_error": [],
         "kvq_version": [],
@@ -333,6 +334,16 @@ def kvq_decode_attn_batch(layout: Layout, pool, page_tables, ctx_lens, q, scale:
                                        int(q.shape[2]), int(q.shape[1]), _ptr(q), float(scale), _ptr(out),
                                        _ptr(lse), _ptr(ws), ws_bytes, ctypes.byref(opts), _stream(stream)),
            "kvq_decode_attn_batch")
+
+
+def kvq_hadamard(x, stream=None):
+    """Rotate every row of x (a contiguous fp32 device tensor whose last axis,
+    a power of two up to 1024, is the row) in place by H / sqrt(dim)."""
+    import torch
+    _need(x, "x", torch.float32)
+    dim = int(x.shape[-1]) if x.dim() > 0 else 0
+    n_rows = x.numel() // dim if dim > 0 else 0
+    _check(lib().kvq_hadamard(_ptr(x), n_rows, dim, _stream(stream)), "kvq_hadamard")
 
 
 def kvq_stage_pages(host_layout: Layout, host_pool, host_page_table, dev_layout: Layout, dev_pool,

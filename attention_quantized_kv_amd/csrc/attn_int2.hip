@@ -16,10 +16,11 @@
 //   p V    = sum_t (p_t d_t) c_t + sum_t p_t z_t         (per V block of dims)
 // q_b . c_b is an MFMA over the codes as exact fp16 (q split into fp16 hi +
 // lo, so every product is exact in fp32); sum(q_b) is a per-row constant.  On
-// the V side P' = p d (fp32, rounded once to fp16) multiplies the codes (as
-// fp16 subnormals, below), and the zero-point term is one more MFMA per
-// chunk, fp16(p) times the chunk's V zero-points, whose output column b is
-// the row's term for block b.
+// the V side P' = p d (fp32) multiplies the codes, and the zero-point term is
+// one more MFMA per chunk, p times the chunk's V zero-points, whose output
+// column b is the row's term for block b.  Both weights enter as fp16 hi +
+// lo: the two terms can be much larger than the value they sum to, so a
+// single fp16 rounding of the weights would not do.
 //
 // Work split as in the Q8_0/Q4_0 streaming kernel: a workgroup of W waves per
 // (KV head, split), the split's 32-token chunks dealt round-robin to its
@@ -141,39 +142,33 @@ __device__ inline void wait_chunks(int n) {
     }
 }
 
-// The 8 codes of word H (0: low, 1: high byte of each half) of dword x as
-// fp16, in the order (c0, c4, c1, c5, c2, c6, c3, c7).  Code j (and 4+j, in
-// the upper half) sits at bit 2j.
+// The 8 codes of word H of dword x as fp16 MUL * code, exactly, in the
+// order (c0, c2, c1, c3, c4, c6, c5, c7) (index bits 0 and 1 swapped: see
+// code_slot).  The dword is spread into nibbles, n0 = x & 0x33333333 and n1 =
+// (x >> 2) & 0x33333333; with the codes' interleave (code e of word h at bit
+// 16 (e/4) + 8h + 2 (e%4)) byte 2k + h of n0 holds codes 4k, 4k+2 of word h
+// and the same byte of n1 codes 4k+1, 4k+3.  A 2-bit code zero-extended to a
+// nibble is the e2m1 (fp4) value code/2, and gfx950 converts two fp4 values
+// with a scale into two fp16 at once: 2 MUL gives MUL * code exactly.  Both
+// words of a dword share n0 and n1: 11 operations per 16 codes.
 //
-// K (i2_word_exact): masked in place under the fp16 exponent of 2^(10-2j),
-// whose mantissa step is then 1, it reads 2^(10-2j) + code; one packed
-// subtraction per pair leaves the code itself.
-//
-// V (i2_word_sub): masked in place with a zero exponent it reads the fp16
-// subnormal c * 4^j * 2^-24, exactly: one v_and_b32 per pair.  The weights'
-// elements 2j, 2j+1 carry 4^(2-j), so the products are p d_v c 2^-20 (p d_v *
-// 16 must stay in fp16: V scales below 4096).  The matrix cores keep only
-// about 16 bits of such tiny products in a sum, which the weighted values
-// tolerate (each weight is rounded to fp16 anyway) but the scores do not: K
-// codes take the exact form.
-constexpr float kVAcc = 1048576.0f;    // 2^20: P' . codes carries 2^-20
-template <int H>
-__device__ inline half8 i2_word_exact(uint32_t x, const uint32_t (&magic)[4]) {
-    const uint32_t y = H ? x >> 8 : x;
-    u32x4 w;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) w[j] = (y & (0x00030003u << (2 * j))) | magic[j];
-    const _Float16 a0 = 1024.0f, a1 = 256.0f, a2 = 64.0f, a3 = 16.0f;
-    return __builtin_bit_cast(half8, w) - half8{a0, a0, a1, a1, a2, a2, a3, a3};
+// (Masked into an fp16 with a zero exponent instead, a code reads as the
+// subnormal c 4^j 2^-24 and needs no conversion, but the matrix cores
+// truncate such tiny products toward zero in a sum, about 16 bits down: a
+// bias that rotated caches turn into visible output errors.  The fp16
+// operands here are normal, and their sums are as exact as fp32.)
+template <int H, int MUL>
+__device__ inline half8 i2_word(uint32_t x) {
+    const uint32_t n0 = x & 0x33333333u, n1 = (x >> 2) & 0x33333333u;
+    constexpr float sc = 2.0f * MUL;
+    const half2v a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(n0, sc, H);
+    const half2v b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(n1, sc, H);
+    const half2v c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(n0, sc, 2 + H);
+    const half2v d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(n1, sc, 2 + H);
+    return half8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
-template <int H>
-__device__ inline half8 i2_word_sub(uint32_t x) {
-    const uint32_t y = H ? x >> 8 : x;
-    u32x4 w;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) w[j] = y & (0x00030003u << (2 * j));
-    return __builtin_bit_cast(half8, w);
-}
+// The code (of a word) in operand element s.
+__host__ __device__ constexpr int code_slot(int s) { return (s & 4) | ((s & 1) << 1) | ((s >> 1) & 1); }
 
 template <int D, int JJ, int W, int NSLOT>
 struct I2Lds {
@@ -236,7 +231,7 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
 
     // ---- q: A operands and per-block sums in LDS.  Thread (r, b, i) takes
     // dims 128 b + 8 i .. +7 of row r, pre-scaled by scale * log2(e), in the
-    // codes' element order (d0, d4, d1, d5, ...), split into fp16 hi + lo; the
+    // codes' element order (d0, d2, d1, d3, ...), split into fp16 hi + lo; the
     // 16 threads of (r, b) sum the block.
     const float qscale = a.scale * kLog2e;
     float* qsum = reinterpret_cast<float*>(smem + L::QS_OFF);
@@ -255,8 +250,7 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
             float sum = 0.0f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                // element e: dim e/2 or 4 + e/2
-                const float v = x[(e & 1) ? 4 + e / 2 : e / 2];
+                const float v = x[code_slot(e)];
                 hi[e] = (_Float16)v;
                 lo[e] = (_Float16)(v - (float)hi[e]);
                 sum += v;
@@ -291,10 +285,6 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt) o[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    uint32_t magic[4] = {0x64006400u, 0x5C005C00u, 0x54005400u, 0x4C004C00u};   // fp16 2^10, 2^8, 2^6, 2^4
-#pragma unroll
-    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(magic[j]));              // kept in VGPRs
-
     // chunks wholly visible to every row come first
     const int c_mask = first_last >= kChunk - 1 ? (first_last - (kChunk - 1)) / kChunk + 1 : 0;
 
@@ -318,8 +308,7 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
                 const half8 qa = *reinterpret_cast<const half8*>(qp);
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt) {
-                    const half8 kb = (step & 1) ? i2_word_exact<1>(kcode[tt][step / 2], magic)
-                                                : i2_word_exact<0>(kcode[tt][step / 2], magic);
+                    const half8 kb = (step & 1) ? i2_word<1, 1>(kcode[tt][step / 2]) : i2_word<0, 1>(kcode[tt][step / 2]);
                     acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa, kb, acc[tt], 0, 0, 0);
                     if constexpr (JJ == 4) {
                         const half8 ql = *reinterpret_cast<const half8*>(qp + 1024);
@@ -370,6 +359,10 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
                 l[jj] *= alpha[jj];
                 m[jj] = up ? mnew[jj] : m[jj];
             }
+            if constexpr (JJ == 2) {             // the lo rows follow their rows
+                alpha[2] = alpha[0];
+                alpha[3] = alpha[1];
+            }
 #pragma unroll
             for (int nt = 0; nt < C::NT; ++nt) o[nt] *= alpha;
             corr *= alpha;
@@ -385,51 +378,63 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
             prow[kTile + n16] = p1;
         }
         lds_fence();
-        // P in the A layout: row n16, tokens 8 g4 .. 8 g4 + 7
+        // P in the A layout: row n16, tokens 8 g4 .. 8 g4 + 7.  The weights
+        // enter the products as fp16 hi + lo: v = z + d c splits into terms
+        // larger than v itself (large zero-points after a rotation), so one
+        // fp16 rounding of the weights would cost too much.  Up to 8 rows
+        // (JJ = 2) the lo halves sit in the spare MFMA rows 4 g + {2, 3} (the
+        // rows' own lanes read row n16 - 2 and keep what fp16 missed); up to
+        // 16 rows a second MFMA takes them.
+        constexpr bool LO_ROWS = JJ == 2;
+        const bool lo_lane = LO_ROWS && (n16 & 2) != 0;
+        const int prow = LO_ROWS ? (n16 & ~2) : n16;
         float pf[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pf[e] = plds[n16 * kPStride + 8 * g4 + e];
-        // zero-point term: fp16(p) times the zero-points (keys past the
-        // context may hold unwritten zero-points: they get 0)
+        for (int e = 0; e < 8; ++e) pf[e] = plds[prow * kPStride + 8 * g4 + e];
+        // fp16 of x, or in a lo lane the part of x below it: x - s h with s =
+        // 0 or 1 (one mixed-precision FMA; x - 0 h is x itself, x <= 65504)
+        const float s_lo = lo_lane ? 1.0f : 0.0f;
+        auto part = [&](float x) -> _Float16 { return (_Float16)fmaf(-s_lo, (float)(_Float16)x, x); };
+        auto rest = [](float x) -> _Float16 { return (_Float16)fmaf(-1.0f, (float)(_Float16)x, x); };
+        // zero-point term: p times the zero-points (keys past the context may
+        // hold unwritten zero-points: they get 0)
         u32x4 vcode[2], vzr, vsr[2];
         read_v<D>(sl, lane, n16, g4, vcode, vzr, vsr);
         half8 az, bz = __builtin_bit_cast(half8, vzr);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            az[e] = (_Float16)pf[e];
+            az[e] = part(pf[e]);
             if (mask && j0 + 8 * g4 + e >= a.ctx) bz[e] = (_Float16)0.0f;
         }
         corr = __builtin_amdgcn_mfma_f32_16x16x32_f16(az, bz, corr, 0, 0, 0);
-        // the codes' token order; token pair j carries 4^(2-j) (exact)
-        float ps[8];
+        if constexpr (!LO_ROWS) {
+            half8 azl;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float f = j < 2 ? (float)(1 << (4 - 2 * j)) : 1.0f / (float)(1 << (2 * j - 4));
-            ps[2 * j] = pf[j] * f;
-            ps[2 * j + 1] = pf[4 + j] * f;
+            for (int e = 0; e < 8; ++e) azl[e] = rest(pf[e]);
+            corr = __builtin_amdgcn_mfma_f32_16x16x32_f16(azl, bz, corr, 0, 0, 0);
         }
 #pragma unroll
         for (int b = 0; b < C::NB2; ++b) {
-            // P' = p * d_v (times 4^(2-j)), one fp32 product rounded once to fp16
+            // P' = p * d_v in the codes' token order, one fp32 product, then
+            // fp16 hi + lo
             const half8 sc = __builtin_bit_cast(half8, vsr[b]);
-            half8 ap;
+            half8 ap, apl;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                float x0 = fmaf(ps[2 * j], (float)sc[j], 0.0f);
-                float x1 = fmaf(ps[2 * j + 1], (float)sc[4 + j], 0.0f);
-                if constexpr (mask) {            // masked keys may hold unwritten scales
-                    x0 = pf[j] == 0.0f ? 0.0f : x0;
-                    x1 = pf[4 + j] == 0.0f ? 0.0f : x1;
-                }
-                ap[2 * j] = (_Float16)x0;
-                ap[2 * j + 1] = (_Float16)x1;
+            for (int e = 0; e < 8; ++e) {
+                const int t = code_slot(e);
+                float x = fmaf(pf[t], (float)sc[t], 0.0f);
+                if constexpr (mask) x = pf[t] == 0.0f ? 0.0f : x;   // masked keys may hold unwritten scales
+                ap[e] = part(x);
+                if constexpr (!LO_ROWS) apl[e] = rest(x);
             }
 #pragma unroll
             for (int w = 0; w < 8; ++w) {
                 const int nt = 8 * b + w;
-                const half8 bv = (nt & 1) ? i2_word_sub<1>(vcode[nt / 8][(nt / 2) % 4])
-                                          : i2_word_sub<0>(vcode[nt / 8][(nt / 2) % 4]);
+                // codes carry 2^kTau = 16 (the weights carry 2^-kTau)
+                const half8 bv = (nt & 1) ? i2_word<1, 16>(vcode[nt / 8][(nt / 2) % 4])
+                                          : i2_word<0, 16>(vcode[nt / 8][(nt / 2) % 4]);
                 o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap, bv, o[nt], 0, 0, 0);
+                if constexpr (!LO_ROWS) o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(apl, bv, o[nt], 0, 0, 0);
                 if (w & 1) SCHED_FENCE();       // a few B operands live at a time
             }
             SCHED_FENCE();
@@ -511,9 +516,19 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
         l[jj] = row16_sum(l[jj]) * 16.0f;               // weights carried 2^-kTau
         if (bad) { m[jj] = NAN; l[jj] = NAN; }
     }
+    if constexpr (JJ == 2) {
+        // fold the lo rows into their rows
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt) {
+            o[nt][0] += o[nt][2];
+            o[nt][1] += o[nt][3];
+        }
+        corr[0] += corr[2];
+        corr[1] += corr[3];
+    }
     {
-        // o carries 2^-20 (the codes) and 2^-kTau (the weights); corr column
-        // b (lane 16 g4 + b) times 2^kTau goes to the dims of block b
+        // the weights carry 2^-kTau (o has it made up by the codes); corr
+        // column b (lane 16 g4 + b) times 2^kTau goes to the dims of block b
         float cz[C::NB2][JJ];
 #pragma unroll
         for (int b = 0; b < C::NB2; ++b)
@@ -522,7 +537,7 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
 #pragma unroll
         for (int nt = 0; nt < C::NT; ++nt)
 #pragma unroll
-            for (int jj = 0; jj < JJ; ++jj) o[nt][jj] = fmaf(o[nt][jj], 16.0f * kVAcc, cz[nt / 8][jj]);
+            for (int jj = 0; jj < JJ; ++jj) o[nt][jj] += cz[nt / 8][jj];
     }
     __syncthreads();                                    // q and P buffers no longer read
     constexpr int SLOTW = JJ * 4 * D;                   // floats per wave

@@ -539,6 +539,19 @@ int kvq_decode_attn_batch(const kvq_layout* layout, const void* d_pool, const in
     return ok();
 }
 
+int kvq_hadamard(float* d_x, int64_t n_rows, int32_t dim, void* stream) {
+    if (dim < 2 || dim > 1024 || (dim & (dim - 1)) != 0)
+        return fail(KVQ_ERR_INVALID_ARG, "dim %d must be a power of two in [2, 1024]", dim);
+    if (n_rows < 0 || n_rows > INT32_MAX)
+        return fail(KVQ_ERR_INVALID_ARG, "n_rows %lld outside [0, 2^31 - 1]", (long long)n_rows);
+    if (n_rows == 0) return ok();
+    if (d_x == nullptr) return fail(KVQ_ERR_INVALID_ARG, "x is NULL");
+    if (((uintptr_t)d_x & 3) != 0) return fail(KVQ_ERR_INVALID_ARG, "x must be 4-byte aligned");
+    const hipError_t e = kvq::launch_hadamard(d_x, n_rows, dim, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(KVQ_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 int kvq_stage_pages(const kvq_layout* host_layout, const void* h_pool, const int32_t* h_page_table, int32_t n_copy,
                     const kvq_layout* dev_layout, void* d_pool, int32_t dst_first, void* stream) {
     kvq::Geom gh, gd;

@@ -51,9 +51,10 @@ struct Geom {
 };
 
 // INT2 code words: 8 codes each, two words per dword -- code e of word h
-// (0: the even word, 1: the odd one) at bit 16 (e / 4) + 8 h + 2 (e % 4).  A
-// shift by 2j (or 8 + 2j) and a mask 0x00030003 then yield codes (j, 4 + j)
-// of a word as the two halves of a dword.
+// (0: the even word, 1: the odd one) at bit 16 (e / 4) + 8 h + 2 (e % 4).
+// Spread into nibbles (x & 0x33333333, (x >> 2) & 0x33333333), every byte
+// then holds two codes of one word as two fp4 values, ready for the gfx950
+// fp4 -> fp16 conversion.
 __host__ __device__ inline int i2_bit(int h, int e) { return 16 * (e / 4) + 8 * h + 2 * (e % 4); }
 // INT2 unit: byte offset of the dword holding K code (slot s, dim d), and
 // the code's bit in it.
@@ -193,6 +194,9 @@ hipError_t launch_merge_new(const AttnArgs& a, const NewRows& nr, int n_splits, 
 // group (each partial folds that many waves' chunks), for a given row count.
 int mfma_stream_row_groups(int rows);
 int mfma_stream_waves(int rows);
+// In-place normalized Hadamard rotation of n_rows rows of dim floats (dim a
+// power of two in [2, 1024], n_rows in [1, 2^31 - 1]).
+hipError_t launch_hadamard(float* x, int64_t n_rows, int dim, hipStream_t stream);
 // Decode over the INT2 codec (rows <= 16) and its waves per workgroup.
 hipError_t launch_attn_int2(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream,
                             const SeqBatch* batch = nullptr);

@@ -121,9 +121,7 @@ typedef struct {
  * Attention over this codec: decode and verify only (kvq_decode_attn,
  * kvq_decode_attn_batch and kvq_attn_ex with kernel 0 or 4, n_q * group <=
  * 16); kvq_append_attn runs kvq_append and then that decode; prefill returns
- * UNSUPPORTED for it.  Its kernel feeds the attention weights to fp16 matrix
- * cores scaled by up to 16: every V block scale must stay below 4,096 (a V
- * block range below 12,000), else the output is not finite.
+ * UNSUPPORTED for it.
  */
 int kvq_unit_bytes(const kvq_layout *layout, size_t *bytes);
 int kvq_pool_bytes(const kvq_layout *layout, size_t *bytes);
@@ -324,6 +322,24 @@ int kvq_decode_attn_batch(const kvq_layout *layout, const void *d_pool,
 int kvq_stage_pages(const kvq_layout *host_layout, const void *h_pool, const int32_t *h_page_table,
                     int32_t n_copy, const kvq_layout *dev_layout, void *d_pool, int32_t dst_first,
                     void *stream);
+
+/*
+ * kvq_hadamard -- rotate rows in place: x_r <- x_r H / sqrt(dim), H the dim x
+ * dim Hadamard matrix of Sylvester's construction (H_1 = [1], H_2m =
+ * [[H_m, H_m], [H_m, -H_m]]).  The 2-bit cache is meant to hold rotated K and
+ * V ("OSCAR2 KV Cache benchmark", rotation model conversion: a Hadamard
+ * rotation per head baked into the model), which spreads outlier channels
+ * over the whole row.  H / sqrt(dim) is orthogonal and its own inverse, so a
+ * caller that rotates k and v before kvq_append and q before the attention
+ * call gets the same scores and the rotated output, which one more
+ * kvq_hadamard turns back.
+ *   d_x     fp32 [n_rows][dim], device, contiguous rows; read and written
+ *   dim     a power of two in [2, 1024] (head_dim)
+ * fp32 butterflies in a fixed order, then one product by fp32(1/sqrt(dim)).
+ * Errors: INVALID_ARG (dim not such a power of two, n_rows < 0 or > 2^31 - 1,
+ * NULL or misaligned x), HIP.  n_rows == 0 is a no-op.
+ */
+int kvq_hadamard(float *d_x, int64_t n_rows, int32_t dim, void *stream);
 
 /* Status name, and the detail of the last failure on this thread. */
 const char *kvq_status_str(int status);

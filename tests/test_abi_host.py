@@ -188,6 +188,18 @@ def test_int2_attention_plan():
     assert status(kvq.kvq_decode_attn_batch_workspace_bytes, L, [100, 200], 12, 3) == kvq.KVQ_ERR_UNSUPPORTED
 
 
+def test_hadamard_arguments():
+    """kvq_hadamard rejects every bad argument before touching the GPU."""
+    lib = kvq.lib()
+    for dim in (0, 1, 3, 96, 2048):
+        assert lib.kvq_hadamard(FAKE, 4, dim, None) == kvq.KVQ_ERR_INVALID_ARG, dim
+    assert lib.kvq_hadamard(FAKE, -1, 64, None) == kvq.KVQ_ERR_INVALID_ARG
+    assert lib.kvq_hadamard(FAKE, 1 << 31, 64, None) == kvq.KVQ_ERR_INVALID_ARG
+    assert lib.kvq_hadamard(None, 4, 64, None) == kvq.KVQ_ERR_INVALID_ARG
+    assert lib.kvq_hadamard(ctypes.c_void_p(0x100002), 4, 64, None) == kvq.KVQ_ERR_INVALID_ARG   # misaligned
+    assert lib.kvq_hadamard(None, 0, 64, None) == kvq.KVQ_OK                                    # no-op
+
+
 def test_status_strings():
     lib = kvq.lib()
     for st, name in [(0, "KVQ_OK"), (-1, "KVQ_ERR_INVALID_ARG"), (-2, "KVQ_ERR_UNSUPPORTED"),

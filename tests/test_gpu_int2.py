@@ -176,8 +176,8 @@ def test_int2_append_attn():
 
 
 def test_int2_wide_value_ranges():
-    """Wide blocks inside the documented limit (V scales up to about 3,100, below
-    4,096; K x30): the output stays finite and matches the oracle."""
+    """Wide blocks (V scales up to about 3,000, K x30): the output stays
+    finite and matches the oracle."""
     import torch
     import attention_quantized_kv_amd as kvq
     rng = np.random.default_rng(12)
