@@ -61,27 +61,35 @@ constexpr int kRing = 4;         // raw chunks in flight per workgroup (direct-t
 template <int RT>
 constexpr int kThreadsFor = kRowsPerWg / (16 * RT) * 64;
 
-template <int D, int RT>
+template <int D, int RT, int CODEC>
 struct TCfg {
     static constexpr int W = kRowsPerWg / (16 * RT);   // waves per workgroup
     static constexpr int THREADS = W * 64;
-    static constexpr int NB = D / kBlock;       // quant blocks per row
+    static constexpr int NB = D / kBlock;       // 32-dim MFMA steps (quant blocks of Q8_0/Q4_0)
+    static constexpr int NB2 = D / kBlock2;     // 128-value INT2 blocks
     static constexpr int NT = D / 16;           // 16-wide output dim tiles
     static constexpr int KL = D / 64;           // 1 KiB pieces per K tile / V chunk
-    static constexpr int K_FRAG = 2 * NB * 64 * 16;   // [tile][block][lane] x 16 B
-    static constexpr int KS = 2 * NB * 16 * 2;        // [tile][block][16 keys] fp16
+    static constexpr int K_FRAG = 2 * NB * 64 * 16;   // [tile][step][lane] x 16 B
+    static constexpr int KS = 2 * NB * 16 * 2;        // [tile][step][16 keys] fp16 (INT2: the 128-block's d per step)
+    static constexpr int KZ = CODEC == 1 ? 2 * NB2 * 16 * 2 : 0;   // INT2: [tile][block][16 keys] fp16 zero-points
     static constexpr int V_FRAG = NT * 64 * 16;       // [dim tile][lane] x 16 B, hi then lo parts
-    static constexpr int STAGE = K_FRAG + KS + 2 * V_FRAG;
+    static constexpr int STAGE = K_FRAG + KS + KZ + 2 * V_FRAG;
     // raw chunk as it arrives by direct-to-LDS loads, one 1 KiB wave request
-    // each: [K tiles 2KL][K scales 1][V pieces KL][V scales 1]
-    static constexpr int N_DMA = 3 * KL + 2;
+    // each.  Q8_0/Q4_0: [K tiles 2KL][K scales 1][V pieces KL][V scales 1].
+    // INT2: [K codes 8D/1024][V codes 8D/1024][parameters 1]: K (scale, zero)
+    // [32 tokens][NB2][2], V scales [NB2][32], V zeros [NB2][32] (fp16).
+    static constexpr int CR = 8 * D / 1024;           // INT2: 1 KiB requests per code region
+    static constexpr int N_DMA = CODEC == 1 ? 2 * CR + 1 : 3 * KL + 2;
     static constexpr int ND = (N_DMA + W - 1) / W;    // requests per wave and chunk
     static constexpr int SLOT = N_DMA * 1024;
     static constexpr int OFF_KS = 2 * KL * 1024, OFF_V = OFF_KS + 1024, OFF_VS = OFF_V + KL * 1024;
+    static constexpr int I2_V = 8 * D, I2_P = 16 * D;                 // INT2 raw offsets: V codes, parameters
+    static constexpr int I2_VS = I2_P + 128 * NB2, I2_VZ = I2_VS + 64 * NB2;
     static constexpr int LDS = 2 * STAGE + kRing * SLOT;
     static constexpr int K_ITEMS = 128 * KL;    // 16-byte K-code pieces per chunk
     static constexpr int KS_ITEMS = 4 * NB;     // 16-byte K-scale pieces per chunk
     static_assert(KS_ITEMS <= THREADS, "one K-scale piece per thread");
+    static_assert(CODEC == 0 || (D % 128 == 0 && 32 * NB2 <= THREADS), "INT2: head_dim 128 or 256");
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -183,9 +191,9 @@ __device__ inline void lds_barrier() {
 // scale pieces, 4*NB of 16 bytes, are repeated across the remaining lanes.
 // A request's source is unit + off + mul * slot0, with off and mul fixed per
 // wave (computed once), slot0 = the chunk's first slot in its page.
-template <int D, int RT>
+template <int D, int RT, int CODEC>
 struct Requests {
-    using C = TCfg<D, RT>;
+    using C = TCfg<D, RT, CODEC>;
     int64_t off[C::ND];
     int mul[C::ND];
     int dst[C::ND];
@@ -196,6 +204,28 @@ struct Requests {
             int item = j * C::W + wave;
             while (item >= C::N_DMA) item -= C::N_DMA;
             dst[j] = item * 1024;
+            if constexpr (CODEC == 1) {
+                if (item < C::CR) {                         // K codes, piece item (chunk-contiguous)
+                    off[j] = (int64_t)item * 1024 + lane * 16;
+                    mul[j] = D / 4;
+                } else if (item < 2 * C::CR) {              // V codes
+                    off[j] = g.i2_v_codes_off() + (int64_t)(item - C::CR) * 1024 + lane * 16;
+                    mul[j] = D / 4;
+                } else {                                    // parameters: lane pl of 16 NB2
+                    const int pl = lane % (16 * C::NB2);
+                    if (pl < 8 * C::NB2) {
+                        off[j] = g.i2_k_params_off() + 16 * pl;
+                        mul[j] = 4 * C::NB2;
+                    } else if (pl < 12 * C::NB2) {
+                        off[j] = g.i2_v_scales_off() + 16 * (pl - 8 * C::NB2);
+                        mul[j] = 2 * C::NB2;
+                    } else {
+                        off[j] = g.i2_v_zeros_off() + 16 * (pl - 12 * C::NB2);
+                        mul[j] = 2 * C::NB2;
+                    }
+                }
+                continue;
+            }
             if (item < 2 * C::KL) {                     // K codes: tile tt, piece p
                 const int tt = item / C::KL, pc = item % C::KL;
                 off[j] = (int64_t)tt * kTile * D + pc * 1024 + lane * 16;
@@ -230,9 +260,79 @@ struct Requests {
 //  K scales: thread t < 4*NB spreads 8 of them to [tile][block][16 keys].
 // kvalid: tokens of the chunk that exist (< ctx); V of the others is zeroed so
 // that a masked key (weight 0) cannot meet an unwritten, non-finite scale.
+template <int D, int RT, int CODEC>
+__device__ inline void convert_chunk(const uint8_t* slot, uint8_t* stage, int t, int kvalid);
+
+// INT2 (the same stage layout; K codes exact, the scale per 128-value block
+// replicated over its four 32-dim steps, zero-points apart, V = z + d c):
+//  K: fragment (tile tt, step s, lane L = 16 g + n) = dims 32 s + 8 g .. +7 of
+//     token 16 tt + n, natural order: word s of lane L's raw K bytes, code e
+//     at bit 16 (e/4) + 8 (s%2) + 2 (e%4) of its dword.
+//  V: fragment (dim tile nt, lane fl = 16 G + n): dim 16 nt + n of keys 4G+i
+//     and 16+4G+i (i < 4); with the pool's interleave the four codes of one
+//     key group are one byte of one raw dword.  hi + lo of z + d c (fp32).
+//  Scales and zero-points: thread t < 32 NB2 takes (token, block).
 template <int D, int RT>
+__device__ inline void convert_chunk_int2(const uint8_t* slot, uint8_t* stage, int t, int kvalid) {
+    using C = TCfg<D, RT, 1>;
+    uint8_t* kf = stage;
+    _Float16* ksl = reinterpret_cast<_Float16*>(stage + C::K_FRAG);
+    _Float16* kzl = reinterpret_cast<_Float16*>(stage + C::K_FRAG + C::KS);
+    uint8_t* vf = stage + C::K_FRAG + C::KS + C::KZ;
+    constexpr int K_OUT = 2 * C::NB * 64;       // K fragments per chunk
+#pragma unroll
+    for (int it = 0; it < (K_OUT + C::THREADS - 1) / C::THREADS; ++it) {
+        const int item = it * C::THREADS + t;
+        if (K_OUT % C::THREADS != 0 && item >= K_OUT) break;
+        const int tt = item / (C::NB * 64), st = (item / 64) % C::NB, L = item % 64;
+        const uint32_t x = *reinterpret_cast<const uint32_t*>(slot + tt * (kTile * D / 4) + L * (D / 16) + (st / 2) * 4);
+        const uint32_t y = x >> (8 * (st & 1));
+        half8 h;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = (_Float16)(float)((y >> (16 * (e / 4) + 2 * (e % 4))) & 3u);
+        *reinterpret_cast<half8*>(kf + ((tt * C::NB + st) * 64 + L) * 16) = h;
+    }
+#pragma unroll
+    for (int it = 0; it < (C::NT * 64 + C::THREADS - 1) / C::THREADS; ++it) {
+        const int item = it * C::THREADS + t;
+        if (C::NT * 64 % C::THREADS != 0 && item >= C::NT * 64) break;
+        const int nt = item / 64, fl = item % 64, G = fl / 16, n = fl % 16, b = nt / 8;
+        const int sh = 16 * (G % 2) + 8 * (nt % 2);
+        // keys 4G+i (raw lane group G/2) and 16+4G+i (group 2+G/2), word nt
+        const uint8_t* vraw = slot + C::I2_V + n * (D / 8) + (nt / 2) * 4;
+        const uint32_t c1 = *reinterpret_cast<const uint32_t*>(vraw + (G / 2) * 16 * (D / 8)) >> sh;
+        const uint32_t c2 = *reinterpret_cast<const uint32_t*>(vraw + (2 + G / 2) * 16 * (D / 8)) >> sh;
+        const _Float16* vs = reinterpret_cast<const _Float16*>(slot + C::I2_VS) + b * kChunk;
+        const _Float16* vz = reinterpret_cast<const _Float16*>(slot + C::I2_VZ) + b * kChunk;
+        half8 hi, lo;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int key = i < 4 ? 4 * G + i : 16 + 4 * G + (i - 4);
+            const uint32_t c = ((i < 4 ? c1 : c2) >> (2 * (i % 4))) & 3u;
+            const float v = key < kvalid ? fmaf((float)vs[key], (float)c, (float)vz[key]) : 0.0f;
+            hi[i] = (_Float16)v;
+            lo[i] = (_Float16)(v - (float)hi[i]);
+        }
+        *reinterpret_cast<half8*>(vf + (nt * 64 + fl) * 16) = hi;
+        *reinterpret_cast<half8*>(vf + C::V_FRAG + (nt * 64 + fl) * 16) = lo;
+    }
+    if (t < kChunk * C::NB2) {
+        const int tok = t / C::NB2, b = t % C::NB2;
+        const half2v dz = as_h2(*reinterpret_cast<const uint32_t*>(slot + C::I2_P + (tok * C::NB2 + b) * 4));
+        const int tt = tok / kTile, key = tok % kTile;
+#pragma unroll
+        for (int st = 4 * b; st < 4 * b + 4; ++st) ksl[(tt * C::NB + st) * kTile + key] = dz.x;
+        kzl[(tt * C::NB2 + b) * kTile + key] = dz.y;
+    }
+}
+
+template <int D, int RT, int CODEC>
 __device__ inline void convert_chunk(const uint8_t* slot, uint8_t* stage, int t, int kvalid) {
-    using C = TCfg<D, RT>;
+    if constexpr (CODEC == 1) {
+        convert_chunk_int2<D, RT>(slot, stage, t, kvalid);
+        return;
+    }
+    using C = TCfg<D, RT, CODEC>;
     uint8_t* kf = stage;
     _Float16* ksl = reinterpret_cast<_Float16*>(stage + C::K_FRAG);
     uint8_t* vf = stage + C::K_FRAG + C::KS;
@@ -290,21 +390,23 @@ __device__ inline void convert_chunk(const uint8_t* slot, uint8_t* stage, int t,
 
 template <int D, int RT>
 struct Rows {
-    floatx4 o[RT][TCfg<D, RT>::NT];   // O^T: row tile rt, this lane's row, dims 16 nt + 4 (lane / 16) + i
+    floatx4 o[RT][D / 16];            // O^T: row tile rt, this lane's row, dims 16 nt + 4 (lane / 16) + i
     float m[RT];                      // reference max (log2 domain), equal on the row's 4 lanes
     float l[RT];                      // this lane's share of the row sum
 };
 
 // One chunk: S^T = K Q^T, online softmax, O^T += V^T P^T for the wave's RT
 // row tiles.  MASK: some key of the chunk lies beyond some row's last key.
-template <int D, int RT, bool MASK>
+template <int D, int RT, int CODEC, bool MASK>
 __device__ inline void chunk_step(Rows<D, RT>& st, const uint8_t* __restrict__ stage,
-                                  const half8 (&qh)[RT][TCfg<D, RT>::NB], const half8 (&ql)[RT][TCfg<D, RT>::NB],
-                                  int lane, int j0, const int (&last)[RT]) {
-    using C = TCfg<D, RT>;
+                                  const half8 (&qh)[RT][D / kBlock], const half8 (&ql)[RT][D / kBlock],
+                                  const float (&qsum)[RT][D / kBlock2 > 0 ? D / kBlock2 : 1], int lane, int j0,
+                                  const int (&last)[RT]) {
+    using C = TCfg<D, RT, CODEC>;
     const uint8_t* kf = stage;
     const _Float16* ksl = reinterpret_cast<const _Float16*>(stage + C::K_FRAG);
-    const uint8_t* vf = stage + C::K_FRAG + C::KS;
+    const _Float16* kzl = reinterpret_cast<const _Float16*>(stage + C::K_FRAG + C::KS);
+    const uint8_t* vf = stage + C::K_FRAG + C::KS + C::KZ;
     const int grp = lane >> 4;
     floatx4 s[RT][2];
 #pragma unroll
@@ -347,6 +449,20 @@ __device__ inline void chunk_step(Rows<D, RT>& st, const uint8_t* __restrict__ s
             for (int tt = 0; tt < 2; ++tt) { ka[tt] = kn[tt]; ks[tt] = ksn[tt]; }
         }
         SCHED_FENCE();      // one block of lookahead, no more (register budget)
+    }
+    if constexpr (CODEC == 1) {
+        // the zero-point term of the INT2 keys: z (key, block) times the
+        // block's sum of this lane's q row
+#pragma unroll
+        for (int b = 0; b < C::NB2; ++b)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                const half4 z = *reinterpret_cast<const half4*>(kzl + (tt * C::NB2 + b) * kTile + 4 * grp);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) s[rt][tt][i] = fmaf((float)z[i], qsum[rt][b], s[rt][tt][i]);
+            }
     }
     if (MASK) {
 #pragma unroll
@@ -428,10 +544,10 @@ __device__ inline void chunk_step(Rows<D, RT>& st, const uint8_t* __restrict__ s
     }
 }
 
-template <int D, int RT>
+template <int D, int RT, int CODEC>
 __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_tiled_kernel(AttnArgs a, int cps, int n_splits,
                                                                           int group, int rows, int row_tiles) {
-    using C = TCfg<D, RT>;
+    using C = TCfg<D, RT, CODEC>;
     extern __shared__ __align__(16) uint8_t smem[];
     const Geom& g = a.g;
     const int t = threadIdx.x;
@@ -492,7 +608,7 @@ __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_tiled_kernel(AttnAr
 
     bool bad = false;
     uint8_t* ring = smem + 2 * C::STAGE;
-    const Requests<D, RT> req(g, wave, lane);
+    const Requests<D, RT, CODEC> req(g, wave, lane);
     // position of the next chunk to request, advanced one chunk at a time
     int iss_c = c_begin, iss_page = (c_begin * kChunk) / g.P, iss_slot = (c_begin * kChunk) % g.P;
     auto issue_next = [&]() {
@@ -510,12 +626,18 @@ __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_tiled_kernel(AttnAr
 
     // q of this lane's rows as fp16 hi + lo, pre-scaled by scale * log2(e), in
     // the B-operand layout (row = lane % 16, dims 8 (lane / 16) .. +7 per block)
+    // (INT2: also the row's sum of the pre-scaled q over each 128-value
+    // block, for the zero-point term: this lane's 32 dims of it, then the
+    // row's 4 lanes)
     half8 qh[RT][C::NB], ql[RT][C::NB];
+    float qsum[RT][C::NB2 > 0 ? C::NB2 : 1];
     {
         const float qscale = a.scale * kLog2e;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             const float* src = a.q + ((size_t)qi[rt] * a.n_heads + hh[rt]) * D + 8 * (lane >> 4);
+#pragma unroll
+            for (int b = 0; b < (C::NB2 > 0 ? C::NB2 : 1); ++b) qsum[rt][b] = 0.0f;
 #pragma unroll
             for (int b = 0; b < C::NB; ++b)
 #pragma unroll
@@ -524,7 +646,12 @@ __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_tiled_kernel(AttnAr
                     const float x = row_ok[rt] ? v * qscale : 0.0f;
                     qh[rt][b][i] = (_Float16)x;
                     ql[rt][b][i] = (_Float16)(x - (float)qh[rt][b][i]);
+                    if constexpr (CODEC == 1) qsum[rt][b / 4] += x;
                 }
+            if constexpr (CODEC == 1) {
+#pragma unroll
+                for (int b = 0; b < C::NB2; ++b) qsum[rt][b] = xsum4(qsum[rt][b]);
+            }
         }
     }
 
@@ -538,7 +665,8 @@ __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_tiled_kernel(AttnAr
     }
 
     auto convert = [&](int c) {
-        convert_chunk<D, RT>(ring + (c & (kRing - 1)) * C::SLOT, smem + (c & 1) * C::STAGE, t, a.ctx - c * kChunk);
+        convert_chunk<D, RT, CODEC>(ring + (c & (kRing - 1)) * C::SLOT, smem + (c & 1) * C::STAGE, t,
+                                    a.ctx - c * kChunk);
     };
     if (c_begin < c_end) {
         vm_wait<0>();
@@ -555,8 +683,8 @@ __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_tiled_kernel(AttnAr
         if (more) issue_next();
         SCHED_FENCE();
         if (wave_active)
-            chunk_step<D, RT, decltype(masked)::value>(st, smem + (c & 1) * C::STAGE, qh, ql, lane, c * kChunk,
-                                                       last);
+            chunk_step<D, RT, CODEC, decltype(masked)::value>(st, smem + (c & 1) * C::STAGE, qh, ql, qsum, lane,
+                                                              c * kChunk, last);
         SCHED_FENCE();
         if (more) vm_wait<(kRing - 2) * C::ND>(); else vm_wait<0>();
         lds_barrier();
@@ -595,12 +723,12 @@ __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_tiled_kernel(AttnAr
     }
 }
 
-template <int D, int RT>
+template <int D, int RT, int CODEC>
 hipError_t launch_dr(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) {
-    using C = TCfg<D, RT>;
-    auto kern = attn_mfma_tiled_kernel<D, RT>;
+    using C = TCfg<D, RT, CODEC>;
+    auto kern = attn_mfma_tiled_kernel<D, RT, CODEC>;
     if (C::LDS > 64 * 1024) {
-        hipError_t e = allow_lds<attn_mfma_tiled_kernel<D, RT>>(C::LDS);
+        hipError_t e = allow_lds<attn_mfma_tiled_kernel<D, RT, CODEC>>(C::LDS);
         if (e != hipSuccess) return e;
     }
     const int row_tiles = (pl.rows + kRowsPerWg - 1) / kRowsPerWg;
@@ -617,10 +745,17 @@ int mfma_tiled_rows_per_wg() { return kRowsPerWg; }
 hipError_t launch_attn_mfma_tiled(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream) {
     // one row tile per wave: at head_dim 256 two tiles per wave need more than
     // the 512 registers a wave can hold
+    if (a.g.codec == 1) {
+        switch (a.g.D) {
+            case 128: return launch_dr<128, 1, 1>(a, pl, stream);
+            case 256: return launch_dr<256, 1, 1>(a, pl, stream);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (a.g.D) {
-        case 64: return launch_dr<64, 1>(a, pl, stream);
-        case 128: return launch_dr<128, 1>(a, pl, stream);
-        case 256: return launch_dr<256, 1>(a, pl, stream);
+        case 64: return launch_dr<64, 1, 0>(a, pl, stream);
+        case 128: return launch_dr<128, 1, 0>(a, pl, stream);
+        case 256: return launch_dr<256, 1, 0>(a, pl, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -101,11 +101,14 @@ int make_plan(const kvq_layout* L, int n_heads, int ctx, int n_q, bool prefill,
     int kernel = opts ? opts->kernel : 0;
     if (kernel < 0 || kernel > 4) return fail(KVQ_ERR_INVALID_ARG, "unknown kernel %d", kernel);
     if (L->codec == KVQ_CODEC_INT2) {
-        if (prefill) return fail(KVQ_ERR_UNSUPPORTED, "prefill over the INT2 codec is not built (decode only)");
-        if (kernel != 0 && kernel != 4)
-            return fail(KVQ_ERR_UNSUPPORTED, "the INT2 codec runs kernel 4 (got kernel %d)", kernel);
-        if (rows > 16) return fail(KVQ_ERR_UNSUPPORTED, "INT2 decode takes n_q*group <= 16 (got %d)", rows);
-        kernel = 4;
+        // kernel 4: the INT2 streaming kernel (decode and verify, up to 16
+        // rows per KV head); kernel 3: the LDS-tiled kernel (prefill, more rows)
+        if (kernel == 1 || kernel == 2)
+            return fail(KVQ_ERR_UNSUPPORTED, "the INT2 codec runs kernel 3 or 4 (got kernel %d)", kernel);
+        if (kernel == 4 && (prefill || rows > 16))
+            return fail(KVQ_ERR_UNSUPPORTED, "kernel 4 takes decode with n_q*group <= 16 (got %d rows%s)", rows,
+                        prefill ? ", prefill" : "");
+        if (kernel == 0) kernel = (!prefill && rows <= 16) ? 4 : 3;
     } else if (kernel == 4) {
         return fail(KVQ_ERR_INVALID_ARG, "kernel 4 reads the INT2 codec only");
     }

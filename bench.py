@@ -166,11 +166,11 @@ KERNEL_SOURCES = {"attn_mfma_stream": "attn_mfma_stream.hip", "attn_mfma_tiled":
 def kernel_name(w, kernel: int) -> str:
     """Name of the attention kernel the plan picks (mirrors the library's
     automatic choice: streaming MFMA for decode / verify with at most 64 query
-    rows per KV head, the LDS-tiled MFMA kernel otherwise; the INT2 kernel
-    for the 2-bit cache)."""
+    rows per KV head, the LDS-tiled MFMA kernel otherwise; over the 2-bit
+    cache its streaming kernel up to 16 rows, else the LDS-tiled one)."""
     rows = w.n_q * (w.n_heads // w.n_kv)
     if w.codec == 1:
-        return "attn_int2"
+        return "attn_int2" if (kernel in (0, 4) and w.n_q <= 8 and rows <= 16) else "attn_mfma_tiled"
     if kernel == 0:
         kernel = 2 if (w.n_q <= 8 and rows <= 64) else 3
     return {1: "attn_valu", 2: "attn_mfma_stream", 3: "attn_mfma_tiled"}[kernel]
@@ -372,7 +372,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="decode262k",
                     choices=["tiny", "decode65k", "decode262k", "verify131k", "prefill262k", "batch16x16k",
-                             "stream262k", "int2decode262k", "int2batch16x16k"])
+                             "stream262k", "int2decode262k", "int2batch16x16k", "int2prefill262k"])
     ap.add_argument("--layers", type=int, default=None, help="layers in the stack (default: the workload's)")
     ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA streaming, 3 MFMA tiled")
     ap.add_argument("--cps", type=int, default=0, help="32-token chunks per split (0: the library's choice)")

@@ -118,10 +118,11 @@ typedef struct {
  *   next 2*P*nb2 bytes       V scales, fp16 bits, [chunk][block][32 tokens].
  *   next 2*P*nb2 bytes       V zeros, fp16 bits, [chunk][block][32 tokens].
  * The unit is 9*P*D/16 bytes: 144 bytes per token at D = 256.
- * Attention over this codec: decode and verify only (kvq_decode_attn,
- * kvq_decode_attn_batch and kvq_attn_ex with kernel 0 or 4, n_q * group <=
- * 16); kvq_append_attn runs kvq_append and then that decode; prefill returns
- * UNSUPPORTED for it.
+ * Attention over this codec: kernel 4 (its streaming kernel: decode, verify
+ * and kvq_decode_attn_batch with n_q * group <= 16) and kernel 3 (the
+ * LDS-tiled kernel: kvq_prefill_attn, and decode or verify with more rows);
+ * kernel 0 picks 4 where it applies, else 3.  kvq_append_attn runs
+ * kvq_append and then the attention call.
  */
 int kvq_unit_bytes(const kvq_layout *layout, size_t *bytes);
 int kvq_pool_bytes(const kvq_layout *layout, size_t *bytes);
@@ -170,8 +171,8 @@ int kvq_append(const kvq_layout *layout, void *d_pool,
  * The result does not depend on how the cache is split internally beyond
  * fp32 rounding.  Errors: INVALID_ARG (nulls, n_q < 1, ctx_len < n_q,
  * n_heads % n_kv_heads != 0), UNSUPPORTED (n_heads / n_kv_heads > 16 or
- * n_q * group > 64 for decode; for KVQ_CODEC_INT2 prefill or n_q * group >
- * 16), CAPACITY (ctx_len > n_table * page_size), WORKSPACE, HIP.
+ * n_q * group > 64 for decode; a kernel choice that does not read the
+ * layout's codec), CAPACITY (ctx_len > n_table * page_size), WORKSPACE, HIP.
  */
 
 /* Workspace bytes kvq_decode_attn / kvq_prefill_attn need for this shape. */
@@ -200,9 +201,9 @@ int kvq_prefill_attn(const kvq_layout *layout, const void *d_pool,
  * errors as kvq_decode_attn / kvq_prefill_attn.
  *   kernel: 0 = automatic, 1 = portable VALU kernel (any supported shape),
  *           2 = MFMA streaming kernel (n_q * group <= 64),
- *           3 = MFMA LDS-tiled chunk kernel (these three read KVQ_CODEC_Q8K_Q4V),
- *           4 = MFMA streaming kernel of KVQ_CODEC_INT2 (decode, n_q * group <= 16;
- *               the only choice, and the automatic one, for that codec)
+ *           3 = MFMA LDS-tiled chunk kernel (both codecs),
+ *           4 = MFMA streaming kernel of KVQ_CODEC_INT2 (decode, n_q * group <= 16);
+ *           1 and 2 read KVQ_CODEC_Q8K_Q4V only
  *   chunks_per_split: 32-token chunks per merged partial; 0 = automatic.
  *   kernel_begin_event, kernel_end_event: optional hipEvent_t handles (or
  *           NULL), recorded on `stream` immediately before and after the

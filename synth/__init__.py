@@ -126,6 +126,8 @@ WORKLOADS = {
     "int2decode262k": Workload("int2decode262k", 8, 16, 24, 4, 256, 262143, 1, 1, codec=1),
     # batch16x16k over the 2-bit cache
     "int2batch16x16k": Workload("int2batch16x16k", 9, 16, 24, 4, 256, 16383, 1, 1, n_seqs=16, codec=1),
+    # prefill262k over the 2-bit cache
+    "int2prefill262k": Workload("int2prefill262k", 10, 1, 24, 4, 256, 260096, 2048, 2048, outliers=True, codec=1),
 }
 
 

@@ -166,20 +166,22 @@ def test_int2_codec_layout():
 
 
 def test_int2_attention_plan():
-    """Attention over the INT2 codec: decode and batched decode with up to 16
-    rows per KV head (kernel 0 or 4); prefill, more rows and the other
-    kernels are rejected; kernel 4 needs the INT2 codec."""
+    """Attention over the INT2 codec: kernel 4 for decode with up to 16 rows
+    per KV head (also batched), kernel 3 for prefill and more rows; kernels
+    1 and 2 are rejected, kernel 4 outside its range too, and kernel 4
+    needs the INT2 codec."""
     L = kvq.Layout(2, 256, 64, 100, kvq.KVQ_CODEC_INT2)
     assert kvq.kvq_workspace_bytes(L, 12, 5000, 1) > 0                  # 6 rows
     assert kvq.kvq_workspace_bytes_ex(L, 16, 5000, 2, kernel=4) > 0     # 16 rows
+    assert kvq.kvq_workspace_bytes(L, 12, 5000, 64, True) > 0           # prefill (kernel 3)
+    assert kvq.kvq_workspace_bytes(L, 12, 5000, 3) > 0                  # 18 rows (kernel 3)
 
     def status(fn, *args, **kw):
         with pytest.raises(kvq.KvqError) as e:
             fn(*args, **kw)
         return e.value.status
-    assert status(kvq.kvq_workspace_bytes, L, 12, 5000, 64, True) == kvq.KVQ_ERR_UNSUPPORTED    # prefill
-    assert status(kvq.kvq_workspace_bytes, L, 12, 5000, 3) == kvq.KVQ_ERR_UNSUPPORTED           # 18 rows
-    for kernel in (1, 2, 3):
+    assert status(kvq.kvq_workspace_bytes_ex, L, 12, 5000, 3, kernel=4) == kvq.KVQ_ERR_UNSUPPORTED   # 18 rows
+    for kernel in (1, 2):
         assert status(kvq.kvq_workspace_bytes_ex, L, 12, 5000, 1, kernel=kernel) == kvq.KVQ_ERR_UNSUPPORTED
     assert status(kvq.kvq_workspace_bytes_ex, L, 12, 5000, 1, kernel=5) == kvq.KVQ_ERR_INVALID_ARG
     assert status(kvq.kvq_workspace_bytes_ex, kvq.Layout(2, 256, 64, 100), 12, 5000, 1,

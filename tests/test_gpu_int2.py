@@ -200,3 +200,32 @@ def test_int2_wide_value_ranges():
     # the values, not with the small result: compare in units of the value
     # scale (the tolerance assumes unit-scale values).
     tu.assert_close(out / 1200.0, ref / 1200.0, lse, ref_lse, "INT2 wide ranges (in units of 1,200)")
+
+
+# ---- prefill (and decode with more than 16 rows) over the INT2 cache: the
+# LDS-tiled kernel (kernel 3)
+
+@pytest.mark.parametrize("D,P,cached,n_q,n_kv,G,kernel,cps", [
+    (256, 64, 500, 300, 2, 6, 0, 0),     # a chunk after a cache: several row tiles, ragged
+    (128, 32, 0, 97, 1, 1, 0, 0),        # no cache: causal inside the chunk only
+    (256, 256, 3000, 64, 1, 8, 0, 4),    # many splits, merged
+    (256, 64, 130, 4, 2, 6, 0, 0),       # verify with 24 rows: kernel 3 picked
+    (128, 64, 900, 2, 1, 6, 3, 0),       # kernel 3 asked for a small decode
+])
+def test_int2_prefill_matches_oracle(D, P, cached, n_q, n_kv, G, kernel, cps):
+    ctx = cached + n_q
+    rng, L, pool, pt_dev, cache = _int2_pool(300 + ctx + D, ctx, n_kv, D, P)
+    q = rng.standard_normal((n_q, n_kv * G, D)).astype(np.float32)
+    scale = 1.0 / np.sqrt(D)
+    out, lse = _attend(L, pool, pt_dev, ctx, q, scale, kernel=kernel, cps=cps)
+    ref, ref_lse, _ = oracle.attention(q, cache, scale)
+    tu.assert_close(out, ref, lse, ref_lse, f"INT2 prefill D={D} ctx={ctx} n_q={n_q} G={G} cps={cps}")
+
+
+def test_int2_prefill_outliers():
+    ctx, n_q = 1500, 200
+    rng, L, pool, pt_dev, cache = _int2_pool(41, ctx, 2, 256, 64, outliers=True)
+    q = rng.standard_normal((n_q, 8, 256)).astype(np.float32)
+    out, lse = _attend(L, pool, pt_dev, ctx, q, 0.0625)
+    ref, ref_lse, _ = oracle.attention(q, cache, 0.0625)
+    tu.assert_close(out, ref, lse, ref_lse, "INT2 prefill with outliers")
