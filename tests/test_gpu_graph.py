@@ -6,7 +6,8 @@ them in a graph.  Three layers of kvq_append_attn are captured in one graph;
 the graph is replayed several times with the program's own eager work and a
 synchronization between the replays, and every replay must match the
 oracle, like the eager call before it (the step appends the same rows at the
-same position, so replaying it is idempotent on the pool).
+same position, so replaying it is idempotent on the pool).  The same for the
+INT2 cache (append, its streaming kernel, the merge).
 """
 import math
 
@@ -19,7 +20,8 @@ from tests import kvq_testutil as tu
 pytestmark = pytest.mark.gpu
 
 
-def test_decode_step_graph_replays_match_oracle():
+@pytest.mark.parametrize("codec", [0, 1])
+def test_decode_step_graph_replays_match_oracle(codec):
     import torch
     import attention_quantized_kv_amd as kvq
     rng = np.random.default_rng(81)
@@ -31,12 +33,13 @@ def test_decode_step_graph_replays_match_oracle():
         k = rng.standard_normal((ctx, n_kv, D)).astype(np.float32)
         v = rng.standard_normal((ctx, n_kv, D)).astype(np.float32)
         q = rng.standard_normal((n_new, n_heads, D)).astype(np.float32)
-        L = tu.layout(n_kv, D, P, (ctx + P - 1) // P + 2)
+        L = tu.layout(n_kv, D, P, (ctx + P - 1) // P + 2, codec=codec)
         pool = tu.alloc_pool(L, fill=0xFF)
         pt_dev, _ = tu.page_table_for(ctx, P, L.n_pages, perm_seed=li)
         kd, vd = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
         kvq.kvq_append(L, pool, pt_dev, 0, kd[:pos0].contiguous(), vd[:pos0].contiguous())
-        ref, ref_lse, _ = oracle.attention(q, oracle.QuantCache.from_float(k, v), scale)
+        cache = (oracle.Int2Cache if codec == kvq.KVQ_CODEC_INT2 else oracle.QuantCache).from_float(k, v)
+        ref, ref_lse, _ = oracle.attention(q, cache, scale)
         layers.append(dict(L=L, pool=pool, pt=pt_dev, k=kd[pos0:].contiguous(), v=vd[pos0:].contiguous(),
                            q=torch.from_numpy(q).cuda(), ref=ref, ref_lse=ref_lse,
                            out=torch.full((n_new, n_heads, D), float("nan"), device="cuda"),
