@@ -263,14 +263,25 @@ struct Requests {
 template <int D, int RT, int CODEC>
 __device__ inline void convert_chunk(const uint8_t* slot, uint8_t* stage, int t, int kvalid);
 
+// INT2 operands come out of the fp4 conversion (see convert_chunk_int2) with
+// elements 1 and 2 of every group of 4 swapped: operand element e holds item
+// i2_slot(e) (an involution), for the dims of a K fragment (so q is staged in
+// that order) and the keys of a V fragment (so P is too).
+__host__ __device__ constexpr int i2_slot(int e) { return (e & ~3) | ((e & 1) << 1) | ((e >> 1) & 1); }
+
 // INT2 (the same stage layout; K codes exact, the scale per 128-value block
-// replicated over its four 32-dim steps, zero-points apart, V = z + d c):
-//  K: fragment (tile tt, step s, lane L = 16 g + n) = dims 32 s + 8 g .. +7 of
-//     token 16 tt + n, natural order: word s of lane L's raw K bytes, code e
-//     at bit 16 (e/4) + 8 (s%2) + 2 (e%4) of its dword.
-//  V: fragment (dim tile nt, lane fl = 16 G + n): dim 16 nt + n of keys 4G+i
-//     and 16+4G+i (i < 4); with the pool's interleave the four codes of one
-//     key group are one byte of one raw dword.  hi + lo of z + d c (fp32).
+// replicated over its four 32-dim steps, zero-points apart, V = z + d c).
+// A 2-bit code zero-extended to a nibble is the fp4 (e2m1) value code/2, and
+// gfx950 converts two fp4 values into two fp16 (times a scale) at once: a
+// dword spread into nibbles (x & 0x33333333, (x >> 2) & 0x33333333) gives,
+// byte by byte, codes in the order i2_slot.
+//  K: fragment (tile tt, step s, lane L = 16 g + n) = dims 32 s + 8 g + i2_slot(e)
+//     of token 16 tt + n: word s of lane L's raw K bytes (code e at bit
+//     16 (e/4) + 8 (s%2) + 2 (e%4) of its dword), bytes s%2 and 2 + s%2 of the
+//     nibbles.
+//  V: fragment (dim tile nt, lane fl = 16 G + n): dim 16 nt + n of keys
+//     4G + i2_slot(i) and 16 + 4G + i2_slot(i); the four codes of each key
+//     group are one byte of one raw dword.  hi + lo of z + d c (fp32).
 //  Scales and zero-points: thread t < 32 NB2 takes (token, block).
 template <int D, int RT>
 __device__ inline void convert_chunk_int2(const uint8_t* slot, uint8_t* stage, int t, int kvalid) {
@@ -286,11 +297,21 @@ __device__ inline void convert_chunk_int2(const uint8_t* slot, uint8_t* stage, i
         if (K_OUT % C::THREADS != 0 && item >= K_OUT) break;
         const int tt = item / (C::NB * 64), st = (item / 64) % C::NB, L = item % 64;
         const uint32_t x = *reinterpret_cast<const uint32_t*>(slot + tt * (kTile * D / 4) + L * (D / 16) + (st / 2) * 4);
-        const uint32_t y = x >> (8 * (st & 1));
-        half8 h;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) h[e] = (_Float16)(float)((y >> (16 * (e / 4) + 2 * (e % 4))) & 3u);
-        *reinterpret_cast<half8*>(kf + ((tt * C::NB + st) * 64 + L) * 16) = h;
+        const uint32_t n0 = x & 0x33333333u, n1 = (x >> 2) & 0x33333333u;
+        half2v a, b, c, d;
+        if (st & 1) {                            // uniform: 64 items per wave share st
+            a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(n0, 2.0f, 1);
+            b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(n1, 2.0f, 1);
+            c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(n0, 2.0f, 3);
+            d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(n1, 2.0f, 3);
+        } else {
+            a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(n0, 2.0f, 0);
+            b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(n1, 2.0f, 0);
+            c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(n0, 2.0f, 2);
+            d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(n1, 2.0f, 2);
+        }
+        *reinterpret_cast<half8*>(kf + ((tt * C::NB + st) * 64 + L) * 16) =
+            half8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
     }
 #pragma unroll
     for (int it = 0; it < (C::NT * 64 + C::THREADS - 1) / C::THREADS; ++it) {
@@ -298,20 +319,29 @@ __device__ inline void convert_chunk_int2(const uint8_t* slot, uint8_t* stage, i
         if (C::NT * 64 % C::THREADS != 0 && item >= C::NT * 64) break;
         const int nt = item / 64, fl = item % 64, G = fl / 16, n = fl % 16, b = nt / 8;
         const int sh = 16 * (G % 2) + 8 * (nt % 2);
-        // keys 4G+i (raw lane group G/2) and 16+4G+i (group 2+G/2), word nt
+        // keys 4G.. (raw lane group G/2) in byte 0, 16+4G.. (group 2+G/2) in byte 1
         const uint8_t* vraw = slot + C::I2_V + n * (D / 8) + (nt / 2) * 4;
-        const uint32_t c1 = *reinterpret_cast<const uint32_t*>(vraw + (G / 2) * 16 * (D / 8)) >> sh;
-        const uint32_t c2 = *reinterpret_cast<const uint32_t*>(vraw + (2 + G / 2) * 16 * (D / 8)) >> sh;
+        const uint32_t w = ((*reinterpret_cast<const uint32_t*>(vraw + (G / 2) * 16 * (D / 8)) >> sh) & 0xFFu) |
+                           (((*reinterpret_cast<const uint32_t*>(vraw + (2 + G / 2) * 16 * (D / 8)) >> sh) & 0xFFu) << 8);
+        const uint32_t n0 = w & 0x3333u, n1 = (w >> 2) & 0x3333u;
+        const half2v c01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(n0, 2.0f, 0);
+        const half2v c23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(n1, 2.0f, 0);
+        const half2v c45 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(n0, 2.0f, 1);
+        const half2v c67 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(n1, 2.0f, 1);
+        const half8 code = {c01.x, c01.y, c23.x, c23.y, c45.x, c45.y, c67.x, c67.y};
         const _Float16* vs = reinterpret_cast<const _Float16*>(slot + C::I2_VS) + b * kChunk;
         const _Float16* vz = reinterpret_cast<const _Float16*>(slot + C::I2_VZ) + b * kChunk;
+        const half4 s0 = *reinterpret_cast<const half4*>(vs + 4 * G), s1 = *reinterpret_cast<const half4*>(vs + 16 + 4 * G);
+        const half4 z0 = *reinterpret_cast<const half4*>(vz + 4 * G), z1 = *reinterpret_cast<const half4*>(vz + 16 + 4 * G);
         half8 hi, lo;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int key = i < 4 ? 4 * G + i : 16 + 4 * G + (i - 4);
-            const uint32_t c = ((i < 4 ? c1 : c2) >> (2 * (i % 4))) & 3u;
-            const float v = key < kvalid ? fmaf((float)vs[key], (float)c, (float)vz[key]) : 0.0f;
-            hi[i] = (_Float16)v;
-            lo[i] = (_Float16)(v - (float)hi[i]);
+        for (int e = 0; e < 8; ++e) {
+            const int ki = i2_slot(e % 4);
+            const int key = (e < 4 ? 4 * G : 16 + 4 * G) + ki;
+            const _Float16 sv = e < 4 ? s0[ki] : s1[ki], zv = e < 4 ? z0[ki] : z1[ki];
+            const float v = key < kvalid ? fmaf((float)sv, (float)code[e], (float)zv) : 0.0f;
+            hi[e] = (_Float16)v;
+            lo[e] = (_Float16)(v - (float)hi[e]);
         }
         *reinterpret_cast<half8*>(vf + (nt * 64 + fl) * 16) = hi;
         *reinterpret_cast<half8*>(vf + C::V_FRAG + (nt * 64 + fl) * 16) = lo;
@@ -500,8 +530,9 @@ __device__ inline void chunk_step(Rows<D, RT>& st, const uint8_t* __restrict__ s
                 const float p = __builtin_amdgcn_exp2f(s[rt][tt][i] - mref);
                 lsum += p;
                 const _Float16 h = (_Float16)p;
-                ph[rt][4 * tt + i] = h;
-                pl[rt][4 * tt + i] = (_Float16)(p - (float)h);
+                const int e = 4 * tt + (CODEC == 1 ? i2_slot(i) : i);   // the V fragment's key order
+                ph[rt][e] = h;
+                pl[rt][e] = (_Float16)(p - (float)h);
             }
         st.l[rt] += lsum;
     }
@@ -642,7 +673,8 @@ __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_tiled_kernel(AttnAr
             for (int b = 0; b < C::NB; ++b)
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const float v = src[b * kBlock + i];      // in bounds: rows past the end read row 0
+                    // in bounds: rows past the end read row 0 (INT2: the codes' dim order)
+                    const float v = src[b * kBlock + (CODEC == 1 ? i2_slot(i) : i)];
                     const float x = row_ok[rt] ? v * qscale : 0.0f;
                     qh[rt][b][i] = (_Float16)x;
                     ql[rt][b][i] = (_Float16)(x - (float)qh[rt][b][i]);
