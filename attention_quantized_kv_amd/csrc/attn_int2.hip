@@ -275,6 +275,15 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
     for (int b = 0; b < C::NB2; ++b)
 #pragma unroll
         for (int jj = 0; jj < JJ; ++jj) qs[b][jj] = qsum[logical_row<JJ>(0, 4 * g4 + jj) * C::NB2 + b];
+    // up to 8 rows the q operands stay in registers (one per 32-dim step):
+    // an LDS read before each step's products would put its latency on the
+    // path of every chunk
+    half8 qreg[JJ == 2 ? C::STEPS : 1];
+    if constexpr (JJ == 2) {
+#pragma unroll
+        for (int st = 0; st < C::STEPS; ++st)
+            qreg[st] = *reinterpret_cast<const half8*>(smem + L::Q_OFF + st * L::QSTEP + lane * 16);
+    }
 
     float* plds = reinterpret_cast<float*>(smem + L::PB_OFF + wave * L::PBUF);
     floatx4 o[C::NT];
@@ -305,7 +314,9 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
             for (int st = 0; st < 4; ++st) {
                 const int step = 4 * b + st;
                 const uint8_t* qp = smem + L::Q_OFF + step * L::QSTEP + lane * 16;
-                const half8 qa = *reinterpret_cast<const half8*>(qp);
+                half8 qa;
+                if constexpr (JJ == 2) qa = qreg[step];
+                else qa = *reinterpret_cast<const half8*>(qp);
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt) {
                     const half8 kb = (step & 1) ? i2_word<1, 1>(kcode[tt][step / 2]) : i2_word<0, 1>(kcode[tt][step / 2]);
