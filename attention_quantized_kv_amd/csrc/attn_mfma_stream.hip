@@ -209,9 +209,10 @@ struct WaveState {
 // S = (q_hi + q_lo) K^T for the chunk's two 16-token tiles.  MASK: some key
 // of the chunk lies beyond the last key of some row (causal edge, or
 // positions past ctx_len).  wait(p) runs before slice p's pieces are read,
-// done(p) after they have been read out of LDS.
-template <int D, int R, int JJ, bool MASK, class Wait, class Done>
-__device__ inline void qk_step(floatx4 (&s)[2], const Land& L, const uint8_t* __restrict__ qlds, int lane,
+// done(p) after they have been read out of LDS.  q(i) gives q's operand i
+// (block i / 2, hi for even i, lo for odd).
+template <int D, int R, int JJ, bool MASK, class QSrc, class Wait, class Done>
+__device__ inline void qk_step(floatx4 (&s)[2], const Land& L, QSrc q, int lane,
                                int j0, int first_last, int group, int rows, int rt0, Wait wait, Done done) {
     using C = Cfg<D, R>;
     const int g4 = lane >> 4;
@@ -246,8 +247,8 @@ __device__ inline void qk_step(floatx4 (&s)[2], const Land& L, const uint8_t* __
             const half2v sw = as_h2(ksw[tt][b / 2]);
             ksc[tt] = (b & 1) ? (float)sw.y : (float)sw.x;
         }
-        const half8 qh = *reinterpret_cast<const half8*>(qlds + (2 * b) * 1024 + lane * 16);
-        const half8 ql = *reinterpret_cast<const half8*>(qlds + (2 * b + 1) * 1024 + lane * 16);
+        const half8 qh = q(2 * b);
+        const half8 ql = q(2 * b + 1);
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             floatx4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh, kb[tt], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
@@ -527,6 +528,19 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
         *reinterpret_cast<half8*>(dst + 1024) = lo;
     }
     lds_barrier();                             // q visible to the group; the first chunk stays in flight
+    // up to 8 rows the operands of q stay in registers (64 VGPRs at head_dim
+    // 256): two LDS reads per 32-dim block would add 16 KiB of LDS traffic
+    // per chunk and wave, more than the chunk itself
+    constexpr bool QREG = JJ == 2;
+    half8 qreg[QREG ? 2 * C::NB : 1];
+    if constexpr (QREG) {
+#pragma unroll
+        for (int i = 0; i < 2 * C::NB; ++i) qreg[i] = *reinterpret_cast<const half8*>(qlds + i * 1024 + lane * 16);
+    }
+    auto qop = [&](int i) -> half8 {
+        if constexpr (QREG) return qreg[i];
+        else return *reinterpret_cast<const half8*>(qlds + i * 1024 + lane * 16);
+    };
 
     WaveState<D, R> st;
 #pragma unroll
@@ -600,7 +614,7 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
             refill(2 * C::KL + u);
         };
         floatx4 s[2];
-        qk_step<D, R, JJ, MASK>(s, land, qlds, lane, j0, first_last, mask_group, rows, gi, qk_wait, qk_done);
+        qk_step<D, R, JJ, MASK>(s, land, qop, lane, j0, first_last, mask_group, rows, gi, qk_wait, qk_done);
         lds_fence();                            // K scales read out
         if (more) issue_kscales<D, R>(land, np, lane);
         softmax_step<D, R, JJ>(st, s, plds, lane);
