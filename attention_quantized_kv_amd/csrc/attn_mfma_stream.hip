@@ -248,14 +248,21 @@ __device__ inline void qk_step(floatx4 (&s)[2], const Land& L, QSrc q, int lane,
             ksc[tt] = (b & 1) ? (float)sw.y : (float)sw.x;
         }
         const half8 qh = q(2 * b);
-        const half8 ql = q(2 * b + 1);
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
             floatx4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh, kb[tt], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-            c = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql, kb[tt], c, 0, 0, 0);
+            if constexpr (JJ == 4) c = __builtin_amdgcn_mfma_f32_16x16x32_f16(q(2 * b + 1), kb[tt], c, 0, 0, 0);
             s[tt] += ksc[tt] * c;
         }
         SCHED_FENCE();
+    }
+    // up to 8 rows the lo halves' products sit two rows down: fold them in
+    if constexpr (JJ == 2) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            s[tt][0] += s[tt][2];
+            s[tt][1] += s[tt][3];
+        }
     }
     // causal / tail mask: key j visible to row r iff j <= first_last + r / group
     // (group is huge when every row sees all keys)
@@ -524,21 +531,30 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
             lo[e] = (_Float16)(x - (float)hi[e]);
         }
         uint8_t* dst = smem + WL::Q_OFF + gi * C::Q_BYTES + (2 * b) * 1024 + lane * 16;
-        *reinterpret_cast<half8*>(dst) = hi;
-        *reinterpret_cast<half8*>(dst + 1024) = lo;
+        if constexpr (JJ == 2) {
+            // up to 8 rows one operand holds both halves: the lo half of MFMA
+            // row n goes to row n + 2, a row no query uses (same k group)
+            if ((lane & 2) == 0) {
+                *reinterpret_cast<half8*>(dst) = hi;
+                *reinterpret_cast<half8*>(dst + 32) = lo;
+            }
+        } else {
+            *reinterpret_cast<half8*>(dst) = hi;
+            *reinterpret_cast<half8*>(dst + 1024) = lo;
+        }
     }
     lds_barrier();                             // q visible to the group; the first chunk stays in flight
-    // up to 8 rows the operands of q stay in registers (64 VGPRs at head_dim
-    // 256): two LDS reads per 32-dim block would add 16 KiB of LDS traffic
-    // per chunk and wave, more than the chunk itself
+    // up to 8 rows the operands of q (hi and lo in one per block) stay in
+    // registers, 32 VGPRs at head_dim 256: LDS reads per 32-dim block would
+    // add more LDS traffic per chunk and wave than the chunk itself
     constexpr bool QREG = JJ == 2;
-    half8 qreg[QREG ? 2 * C::NB : 1];
+    half8 qreg[QREG ? C::NB : 1];
     if constexpr (QREG) {
 #pragma unroll
-        for (int i = 0; i < 2 * C::NB; ++i) qreg[i] = *reinterpret_cast<const half8*>(qlds + i * 1024 + lane * 16);
+        for (int i = 0; i < C::NB; ++i) qreg[i] = *reinterpret_cast<const half8*>(qlds + (2 * i) * 1024 + lane * 16);
     }
     auto qop = [&](int i) -> half8 {
-        if constexpr (QREG) return qreg[i];
+        if constexpr (QREG) return qreg[i / 2];
         else return *reinterpret_cast<const half8*>(qlds + i * 1024 + lane * 16);
     };
 
