@@ -1,0 +1,58 @@
+"""Host-side logic of bench.py, checked without a GPU: the single-GPU
+refusal, the algorithmic bytes per token against the library's own pool
+layout, and the rule that counter-based HBM traffic is reported only while
+the kernel's source is the one the counters were taken on."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import attention_quantized_kv_amd as kvq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout.strip() == ""
+
+
+@pytest.mark.parametrize("codec", [0, kvq.KVQ_CODEC_INT2])
+@pytest.mark.parametrize("n_kv,D", [(4, 256), (2, 128), (8, 256)])
+def test_bytes_per_token_match_the_pool_layout(codec, n_kv, D):
+    """bench's algorithmic bytes per token and layer equal the library's pool
+    size per cached token (pages of 256 tokens, every KV head)."""
+    n_pages, P = 10, 256
+    L = kvq.Layout(n_kv, D, P, n_pages, codec)
+    assert kvq.kvq_pool_bytes(L) == n_pages * P * bench.kv_bytes_per_token_layer(n_kv, D, codec)
+
+
+def test_decode_workload_bytes():
+    """Q8_0 K + Q4_0 V at 4 KV heads and head_dim 256: 416 B per KV head and
+    token; 262,144 tokens make the 436,207,616 bytes per layer the decode
+    line reports.  The 2-bit cache takes 144 B per KV head and token."""
+    assert bench.kv_bytes_per_token_layer(4, 256, 0) == 4 * 416
+    assert bench.kv_bytes_per_token_layer(4, 256, 0) * 262144 == 436207616
+    assert bench.kv_bytes_per_token_layer(4, 256, 1) == 4 * 144
+
+
+def test_traffic_only_for_the_profiled_source(monkeypatch):
+    """A committed counter row is reported while the kernel's source digest
+    matches it, and dropped (None) once the source differs."""
+    for workload, kname in (("decode262k", "attn_mfma_stream"), ("int2decode262k", "attn_int2")):
+        rows = [l.split() for l in open(os.path.join(ROOT, "profiles", "hbm_traffic.txt"))
+                if l.startswith(workload + " ")]
+        assert len(rows) == 1
+        if rows[0][2] != bench.source_digest(kname):
+            pytest.skip(f"{kname} changed since its counters were taken")
+        t = bench.measured_traffic(workload, kname)
+        assert t == pytest.approx(float(rows[0][-1]))
+    monkeypatch.setattr(bench, "source_digest", lambda kname: "0" * 64)
+    assert bench.measured_traffic("decode262k", "attn_mfma_stream") is None
+    assert bench.measured_traffic("no_such_workload", "attn_mfma_stream") is None
