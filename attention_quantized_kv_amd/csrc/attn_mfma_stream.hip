@@ -45,6 +45,7 @@
 
 #include "kvq_internal.h"
 #include "kvq_mfma.h"
+#include "kvq_waits.h"
 
 namespace kvq {
 namespace {
@@ -122,33 +123,6 @@ struct WgLds {
     static constexpr int CB_OFF = LIST_OFF + (RG == 1 ? (LIST + 4) * 4 : 0);
     static constexpr int BYTES = CB_OFF + (SMALL_COMBINE ? W * 8 * D * 4 : 0);
     static_assert(BYTES <= 160 * 1024, "LDS budget");
-};
-
-// Wait counts.  Per chunk a wave issues its requests in a fixed order: the
-// QK step consumes code pieces 2p, 2p+1 (slice p, both tiles) and requests
-// the pieces R places further on; then the next chunk's K scales; the PV
-// step consumes piece 2KL+u and requests the one R further on; then the next
-// chunk's V scales.  Piece J of chunk k was requested when piece J-R was
-// consumed, so the number of requests issued after it by the time it is
-// consumed is fixed; s_waitcnt vmcnt(that count) guarantees it has landed
-// (requests complete in order).  The first chunk's requests go out in the
-// same order before the loop, so it uses the same counts; the last chunk
-// (nothing further requested) waits with 0.
-template <int KL, int R>
-struct Waits {
-    static constexpr int NP = 3 * KL, NI = 3 * KL + 2;
-    static constexpr int issue_pos(int j) { return j < 2 * KL ? j : j + 1; }          // slot of "consume j" in a chunk's requests
-    static constexpr int event_pos(int J) { return J < 2 * KL ? 2 * (J / 2) : 2 * KL + 1 + (J - 2 * KL); }
-    static constexpr int after(int J) {
-        const int m = ((J - R) % NP + NP) % NP;
-        return event_pos(J) - issue_pos(m) - 1 + (J < R ? NI : 0);
-    }
-    static constexpr int mn(int a, int b) { return a < b ? a : b; }
-    // QK slice p (and, for p = 0, this chunk's K scales, issued at 2KL of the
-    // chunk before)
-    static constexpr int qk(int p) { return p == 0 ? mn(mn(after(0), after(1)), NI - 2 * KL - 1) : mn(after(2 * p), after(2 * p + 1)); }
-    // PV slice u (and, for u = 0, this chunk's V scales, issued last in the chunk before)
-    static constexpr int pv(int u) { return u == 0 ? mn(after(2 * KL), NI - KL - 1) : after(2 * KL + u); }
 };
 
 // Per-wave LDS of the stream.
@@ -798,7 +772,7 @@ constexpr int stream_waves() { return 8; }
 
 template <int D, int JJ, int RG, class Batch>
 hipError_t launch_dr(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream, const Batch& sb, int n_wg) {
-    constexpr int R = D == 64 ? 3 : D == 128 ? 3 : 4;   // ring slots: a few KiB in flight per wave
+    constexpr int R = stream_ring_slots(D);             // ring slots: a few KiB in flight per wave
     constexpr int W = stream_waves<JJ>();
     using WL = WgLds<D, R, W, RG, JJ>;
     auto kern = attn_mfma_stream_kernel<D, JJ, RG, R, W, Batch>;

@@ -547,6 +547,11 @@ int kvq_hadamard(float* d_x, int64_t n_rows, int32_t dim, void* stream) {
         return fail(KVQ_ERR_INVALID_ARG, "dim %d must be a power of two in [2, 1024]", dim);
     if (n_rows < 0 || n_rows > INT32_MAX)
         return fail(KVQ_ERR_INVALID_ARG, "n_rows %lld outside [0, 2^31 - 1]", (long long)n_rows);
+    // one workgroup of dim/2 threads per row: the grid's work-items must stay
+    // below 2^32
+    if ((uint64_t)n_rows * (uint64_t)(dim / 2) >= (1ull << 32))
+        return fail(KVQ_ERR_INVALID_ARG, "n_rows %lld x dim/2 %d reaches 2^32 work-items; rotate in several calls",
+                    (long long)n_rows, dim / 2);
     if (n_rows == 0) return ok();
     if (d_x == nullptr) return fail(KVQ_ERR_INVALID_ARG, "x is NULL");
     if (((uintptr_t)d_x & 3) != 0) return fail(KVQ_ERR_INVALID_ARG, "x must be 4-byte aligned");
@@ -565,8 +570,10 @@ int kvq_stage_pages(const kvq_layout* host_layout, const void* h_pool, const int
     if (h_pool == nullptr || d_pool == nullptr || h_page_table == nullptr)
         return fail(KVQ_ERR_INVALID_ARG, "pools and page table must be non-NULL");
     if (n_copy < 0) return fail(KVQ_ERR_INVALID_ARG, "n_copy %d < 0", n_copy);
-    if (gh.D != gd.D || gh.P != gd.P || gh.n_kv != gd.n_kv)
-        return fail(KVQ_ERR_INVALID_ARG, "host and device layouts differ (head_dim, page_size or n_kv_heads)");
+    // the copies are sized from the host layout, so every field that sets the
+    // bytes of a page must agree (a different codec changes the unit size)
+    if (gh.D != gd.D || gh.P != gd.P || gh.n_kv != gd.n_kv || gh.codec != gd.codec)
+        return fail(KVQ_ERR_INVALID_ARG, "host and device layouts differ (head_dim, page_size, n_kv_heads or codec)");
     if (dst_first < 0 || (int64_t)dst_first + n_copy > gd.n_pages)
         return fail(KVQ_ERR_INVALID_ARG, "device pages %d..%d outside the pool of %d", dst_first,
                     dst_first + n_copy - 1, gd.n_pages);

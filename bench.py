@@ -79,6 +79,29 @@ def device_normal(shape, seed, device):
     return torch.randn(shape, generator=g, device=device, dtype=torch.float32)
 
 
+def outlier_channels(w, layer, device):
+    """The outlier channels of a workload that has them (1% of the flattened
+    (head, dim) channels of K, V and q, scaled x20 for every token): the same
+    seeded choice the oracle-side generators make (synth.outlier_channels), as
+    device index tensors; (None, None, None) otherwise."""
+    if not w.outliers:
+        return None, None, None
+    import torch
+    import synth
+    pick = lambda t, n: torch.from_numpy(synth.outlier_channels((0, w.wid, layer, t), n)).to(device)
+    return (pick(synth.K, w.n_kv * w.head_dim), pick(synth.V, w.n_kv * w.head_dim),
+            pick(synth.Q, w.n_heads * w.head_dim))
+
+
+def with_outliers(x, channels, factor=20.0):
+    """x [..., H, D] with the given channels of its flattened (H, D) axis
+    scaled by factor, in place (no-op without channels)."""
+    if channels is not None:
+        flat = x.view(x.shape[:-2] + (x.shape[-2] * x.shape[-1],))
+        flat[..., channels] *= factor
+    return x
+
+
 class Layer:
     def __init__(self, w, layer, device, shuffle_pages=False, fill_chunk=16384):
         import torch
@@ -93,14 +116,15 @@ class Layer:
             perm = torch.arange(w.n_pages)
         self.pt = perm.to(torch.int32).to(device)
         base = (w.wid * 1000 + layer) * 1_000_003
+        ch_k, ch_v, ch_q = outlier_channels(w, layer, device)
         for r in range(0, w.cached, fill_chunk):
             n = min(fill_chunk, w.cached - r)
-            k = device_normal((n, w.n_kv, w.head_dim), base + 2 * r + 1, device)
-            v = device_normal((n, w.n_kv, w.head_dim), base + 2 * r + 2, device)
+            k = with_outliers(device_normal((n, w.n_kv, w.head_dim), base + 2 * r + 1, device), ch_k)
+            v = with_outliers(device_normal((n, w.n_kv, w.head_dim), base + 2 * r + 2, device), ch_v)
             kvq.kvq_append(self.L, self.pool, self.pt, r, k, v)
-        self.k_new = device_normal((w.n_new, w.n_kv, w.head_dim), base + 7, device)
-        self.v_new = device_normal((w.n_new, w.n_kv, w.head_dim), base + 8, device)
-        self.q = device_normal((w.n_q, w.n_heads, w.head_dim), base + 9, device)
+        self.k_new = with_outliers(device_normal((w.n_new, w.n_kv, w.head_dim), base + 7, device), ch_k)
+        self.v_new = with_outliers(device_normal((w.n_new, w.n_kv, w.head_dim), base + 8, device), ch_v)
+        self.q = with_outliers(device_normal((w.n_q, w.n_heads, w.head_dim), base + 9, device), ch_q)
         self.out = torch.empty_like(self.q)
         self.lse = torch.empty((w.n_q, w.n_heads), dtype=torch.float32, device=device)
 
@@ -252,7 +276,62 @@ def cpu_baseline(w, min_seconds: float, max_reps: int = 8):
         value = reps * flops / t_total / 1e12
         unit = "TFLOP/s"
     return {"value": value, "unit": unit, "cores": threads, "kind": "oracle",
-            "sample": f"{desc}, {reps} repetition(s), {t_total:.1f} s"}
+            "sample": f"{desc}, {reps} repetition(s), {t_total:.1f} s",
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo (\"unknown\" without it)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def read_ceiling(device, nbytes=436207616, reps=8):
+    """Plain-read bandwidth of this GPU for the decode kernels' access pattern
+    (libkvq_probe.so: whole 1 KiB wave requests, 8 waves per workgroup, one
+    workgroup per CU), best of 4, 8 and 16 pieces in flight per wave, in GB/s;
+    the ceiling a streaming kernel can reach here, next to the nominal 8 TB/s.
+    None when the probe library is missing."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "attention_quantized_kv_amd", "libkvq_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.kvq_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_void_p]
+    lib.kvq_probe_read.restype = ctypes.c_int
+    cus = torch.cuda.get_device_properties(device).multi_processor_count
+    src = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    src.fill_(3)
+    out = torch.empty(cus * 512, dtype=torch.int32, device=device)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    best = {}
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for unroll in (4, 8, 16):
+        call = lambda: lib.kvq_probe_read(ctypes.c_void_p(src.data_ptr()), nbytes, ctypes.c_void_p(out.data_ptr()),
+                                          cus, 8, unroll, stream)
+        for _ in range(2):
+            if call() != 0:
+                raise RuntimeError("kvq_probe_read failed")
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(reps):
+            call()
+        stop.record()
+        torch.cuda.synchronize()
+        best[unroll] = nbytes * reps / (start.elapsed_time(stop) / 1e3) / 1e9
+    del src, out
+    u = max(best, key=best.get)
+    return {"GBps": round(best[u], 1), "pieces_in_flight_per_wave": u,
+            "all": {str(k): round(v, 1) for k, v in best.items()},
+            "probe": f"plain 16 B/lane loads of 1 KiB wave pieces over {nbytes} B, {cus} workgroups x 8 waves"}
 
 
 def bench_stream(args, w, n_layers):
@@ -547,6 +626,12 @@ def main():
 
     rec.update({"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
                 "higher_is_better": True, "scaling": "weak", "vs_baseline": None})
+    if not prefill:
+        ceil = read_ceiling(dev)
+        if ceil is not None:
+            rec["read_ceiling"] = ceil
+            rec["pct_read_ceiling"] = round(100 * value / ceil["GBps"], 2)
+            roof["frac_of_read_ceiling"] = round(achieved / ceil["GBps"], 4)
     rec["roofline"] = roof
     rec.update(extra)
     if args.graph:

@@ -313,8 +313,8 @@ int kvq_decode_attn_batch(const kvq_layout *layout, const void *d_pool,
  *                         the GPU's work; pageable memory also works, with
  *                         copies the runtime may serialize)
  *   h_page_table          int32 [n_copy], HOST memory
- *   dev_layout, d_pool    the device pool; n_kv_heads, head_dim and page_size
- *                         must equal the host pool's
+ *   dev_layout, d_pool    the device pool; n_kv_heads, head_dim, page_size
+ *                         and codec must equal the host pool's
  * The source pages must not change until the copies are done (an event
  * recorded on `stream` after this call tells when).  Errors: INVALID_ARG
  * (nulls, n_copy < 0, layouts that differ, a host page outside the host pool,
@@ -338,7 +338,8 @@ int kvq_stage_pages(const kvq_layout *host_layout, const void *h_pool, const int
  *   dim     a power of two in [2, 1024] (head_dim)
  * fp32 butterflies in a fixed order, then one product by fp32(1/sqrt(dim)).
  * Errors: INVALID_ARG (dim not such a power of two, n_rows < 0 or > 2^31 - 1,
- * NULL or misaligned x), HIP.  n_rows == 0 is a no-op.
+ * n_rows * dim / 2 >= 2^32 (one thread per pair of values: larger inputs go
+ * in several calls), NULL or misaligned x), HIP.  n_rows == 0 is a no-op.
  */
 int kvq_hadamard(float *d_x, int64_t n_rows, int32_t dim, void *stream);
 

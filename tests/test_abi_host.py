@@ -146,6 +146,14 @@ def test_stage_pages_validation():
     assert call(n=-1)[0] == kvq.KVQ_ERR_INVALID_ARG
     assert call(dl=kvq.Layout(4, 128, 256, 8))[0] == kvq.KVQ_ERR_INVALID_ARG     # head_dim differs
     assert call(dl=kvq.Layout(2, 256, 256, 8))[0] == kvq.KVQ_ERR_INVALID_ARG     # KV heads differ
+    # codecs differ: the copy is sized by the host unit (416 B per token and KV
+    # head) and would run past a device pool of INT2 units (144 B); also with
+    # the device pool made large enough in pages
+    for dl in (kvq.Layout(4, 256, 256, 8, kvq.KVQ_CODEC_INT2), kvq.Layout(4, 256, 256, 64, kvq.KVQ_CODEC_INT2)):
+        st, msg = call(dl=dl)
+        assert st == kvq.KVQ_ERR_INVALID_ARG and "codec" in msg
+    st, msg = call(hl=kvq.Layout(4, 256, 256, 16, kvq.KVQ_CODEC_INT2))
+    assert st == kvq.KVQ_ERR_INVALID_ARG and "codec" in msg
     assert call(first=5)[0] == kvq.KVQ_ERR_INVALID_ARG                           # pages 5..8 of 8
     bad = (ctypes.c_int32 * 4)(3, 4, 16, 9)                                      # page 16 of 16
     st, msg = call(t=bad)
@@ -197,6 +205,10 @@ def test_hadamard_arguments():
         assert lib.kvq_hadamard(FAKE, 4, dim, None) == kvq.KVQ_ERR_INVALID_ARG, dim
     assert lib.kvq_hadamard(FAKE, -1, 64, None) == kvq.KVQ_ERR_INVALID_ARG
     assert lib.kvq_hadamard(FAKE, 1 << 31, 64, None) == kvq.KVQ_ERR_INVALID_ARG
+    # one thread per pair of values: n_rows * dim / 2 must stay below 2^32
+    assert lib.kvq_hadamard(FAKE, 1 << 23, 1024, None) == kvq.KVQ_ERR_INVALID_ARG      # exactly 2^32
+    assert "2^32" in kvq.lib().kvq_last_error().decode()
+    assert lib.kvq_hadamard(FAKE, 1 << 30, 8, None) == kvq.KVQ_ERR_INVALID_ARG         # 2^32 again, small dim
     assert lib.kvq_hadamard(None, 4, 64, None) == kvq.KVQ_ERR_INVALID_ARG
     assert lib.kvq_hadamard(ctypes.c_void_p(0x100002), 4, 64, None) == kvq.KVQ_ERR_INVALID_ARG   # misaligned
     assert lib.kvq_hadamard(None, 0, 64, None) == kvq.KVQ_OK                                    # no-op

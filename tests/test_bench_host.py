@@ -56,3 +56,30 @@ def test_traffic_only_for_the_profiled_source(monkeypatch):
     monkeypatch.setattr(bench, "source_digest", lambda kname: "0" * 64)
     assert bench.measured_traffic("decode262k", "attn_mfma_stream") is None
     assert bench.measured_traffic("no_such_workload", "attn_mfma_stream") is None
+
+
+def test_prefill_outliers_are_the_generators_channels():
+    """The timed prefill inputs carry the workload's outlier channels: the
+    same seeded 1% of the flattened (head, dim) channels the oracle-side
+    generators pick, scaled x20, and no other value changed."""
+    import numpy as np
+    import torch
+    import synth
+    w = synth.WORKLOADS["prefill262k"]
+    ck, cv, cq = bench.outlier_channels(w, 0, "cpu")
+    assert np.array_equal(ck.numpy(), synth.outlier_channels((0, w.wid, 0, synth.K), w.n_kv * w.head_dim))
+    assert np.array_equal(cv.numpy(), synth.outlier_channels((0, w.wid, 0, synth.V), w.n_kv * w.head_dim))
+    assert np.array_equal(cq.numpy(), synth.outlier_channels((0, w.wid, 0, synth.Q), w.n_heads * w.head_dim))
+    assert len(ck) == 10 and len(cq) == 61
+    x = torch.randn(5, w.n_kv, w.head_dim)
+    y = bench.with_outliers(x.clone(), ck)
+    xf, yf = x.reshape(5, -1), y.reshape(5, -1)
+    assert torch.equal(yf[:, ck], xf[:, ck] * 20.0)
+    mask = torch.ones(w.n_kv * w.head_dim, dtype=torch.bool)
+    mask[ck] = False
+    assert torch.equal(yf[:, mask], xf[:, mask])
+    assert bench.outlier_channels(synth.WORKLOADS["decode262k"], 0, "cpu") == (None, None, None)
+
+
+def test_cpu_model_is_reported():
+    assert isinstance(bench.cpu_model(), str) and bench.cpu_model() != ""
