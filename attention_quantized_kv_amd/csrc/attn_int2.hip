@@ -496,10 +496,10 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
         const uint8_t* kc = unit + s0 * (D / 4) + lane * 16;
         const uint8_t* vc = unit + g.i2_v_codes_off() + s0 * (D / 4) + lane * 16;
 #pragma unroll
-        for (int i = 0; i < S::CODE_REQS; ++i) dma16(kc + i * 1024, sl + S::K_OFF + i * 1024);
+        for (int i = 0; i < S::CODE_REQS; ++i) dma16<kLoadNT>(kc + i * 1024, sl + S::K_OFF + i * 1024);
 #pragma unroll
-        for (int i = 0; i < S::CODE_REQS; ++i) dma16(vc + i * 1024, sl + S::V_OFF + i * 1024);
-        dma16(unit + pbase + s0 * pmul, sl + S::P_OFF);
+        for (int i = 0; i < S::CODE_REQS; ++i) dma16<kLoadNT>(vc + i * 1024, sl + S::V_OFF + i * 1024);
+        dma16<kLoadNT>(unit + pbase + s0 * pmul, sl + S::P_OFF);
         ++n_req;
     };
 #pragma unroll

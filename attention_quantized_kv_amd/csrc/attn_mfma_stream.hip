@@ -45,6 +45,7 @@
 
 #include "kvq_internal.h"
 #include "kvq_mfma.h"
+#include "kvq_quant.h"
 #include "kvq_waits.h"
 
 namespace kvq {
@@ -150,27 +151,27 @@ __device__ inline ChunkPtr chunk_ptr(const uint8_t* unit, const Geom& g, int slo
 
 // Requests code piece j of a chunk into ring slot j % R.  Full-wave request
 // (see the scale pieces below).
-template <int D, int R>
+template <int D, int R, int POL>
 __device__ inline void issue_piece(const Land& L, const ChunkPtr& cp, int j, int lane) {
     using C = Cfg<D, R>;
     const uint8_t* src;
     if (j < 2 * C::KL) src = cp.k + (j % 2) * kTile * D + (j / 2) * 1024 + lane * 16;
     else src = cp.v + (j - 2 * C::KL) * 1024 + lane * 16;
-    dma16(src, L.ring + (j % R) * 1024);
+    dma16<POL>(src, L.ring + (j % R) * 1024);
 }
 
 // 32 tokens x NB scales = 4*NB pieces of 16 bytes.  Every lane takes part
 // (lanes past 4*NB repeat a piece): a direct-to-LDS load under a
 // lane-dependent branch can get its LDS base merged with a neighbouring one's.
-template <int D, int R>
+template <int D, int R, int POL>
 __device__ inline void issue_kscales(const Land& L, const ChunkPtr& cp, int lane) {
     using C = Cfg<D, R>;
-    dma16(cp.ks + (lane % (4 * C::NB)) * 16, L.ks);
+    dma16<POL>(cp.ks + (lane % (4 * C::NB)) * 16, L.ks);
 }
-template <int D, int R>
+template <int D, int R, int POL>
 __device__ inline void issue_vscales(const Land& L, const ChunkPtr& cp, int lane) {
     using C = Cfg<D, R>;
-    dma16(cp.vs + (lane % (4 * C::NB)) * 16, L.vs);
+    dma16<POL>(cp.vs + (lane % (4 * C::NB)) * 16, L.vs);
 }
 
 template <int D, int R>
@@ -358,9 +359,105 @@ __device__ inline void wait_pv(int p) {
     }
 }
 
-template <int D, int JJ, int RG, int R, int W, class Batch>
+// A row appended by a fused decode step (kvq_append_attn), handled by one
+// wave of one workgroup while the rest of the chip streams the cached keys.
+// New row j (position pos0 + j) of KV head kvh is quantized with the append
+// kernel's block code (the values the pool will hold, bit for bit) and
+// written into the pool; then every query row r of the KV head (query i =
+// r / group) gets the softmax state of this one key as partial part_idx:
+// m = its score, l = 1, acc = its dequantized value when i >= j (causal
+// among the new rows), an empty partial (l = 0) otherwise.  A new row whose
+// page entry lies outside the pool is not written and its partials are NaN.
+// Lane owns dims 64 p + lane (p < D/64): every 32-lane half is one
+// quantization block.  Every pool byte is written by one thread: a V byte
+// holds slots (2k, 2k+1) and is written by the wave of the odd slot's row,
+// or of the even slot's row when the odd slot is not a new row; the other
+// nibble is then the old one, or the partner new row's code, quantized here
+// as well.
+constexpr int kMaxNewRows = 8;
+template <int D>
+__device__ inline void new_row_partials(const AttnArgs& a, const NewRows& nr, int kvh, int group, int rows, int j,
+                                        int part_stride, int part_idx, int lane) {
+    constexpr int NP = D / 64;
+    const Geom& g = a.g;
+    const int pos = nr.pos0 + j, slot = pos % g.P;
+    const bool odd = (pos & 1) != 0;
+    const bool partner_new = odd ? j >= 1 : j + 1 < nr.n_new;   // the other slot of the V byte is a new row
+    const bool own_byte = odd || !partner_new;
+    const size_t src = ((size_t)j * g.n_kv + kvh) * D + lane;
+    const size_t psrc = odd && partner_new ? src - (size_t)g.n_kv * D : src;   // row j - 1
+    float kh[NP], vh[NP], vp[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        kh[p] = nr.k[src + 64 * p];
+        vh[p] = nr.v[src + 64 * p];
+        vp[p] = nr.v[psrc + 64 * p];
+    }
+    const int e = a.page_table[pos / g.P];
+    // the query rows' q (scaled), 8 rows per batch, each batch's loads in
+    // flight together; the first batch is requested before the quantization
+    constexpr int QB = 8;
+    const float qscale = a.scale * kLog2e;
+    float qv[QB][NP];
+    auto load_q = [&](int r0) {
+#pragma unroll
+        for (int b = 0; b < QB; ++b) {
+            const int r = min(r0 + b, rows - 1), qi = r / group, h = kvh * group + r % group;
+#pragma unroll
+            for (int p = 0; p < NP; ++p) qv[b][p] = a.q[((size_t)qi * a.n_heads + h) * D + 64 * p + lane];
+        }
+    };
+    load_q(0);
+    const bool ok = e >= 0 && e < g.n_pages;
+    uint8_t* unit = nr.pool + g.unit_index(ok ? e : 0, kvh) * g.unit_bytes();
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int d = 64 * p + lane;
+        const QCode ck = quant_q8_0(kh[p], lane);
+        const QCode cv = quant_q4_0(vh[p], lane);
+        kh[p] = (float)ck.code * __half2float(__float2half_rn(ck.d));
+        vh[p] = (float)(cv.code - 8) * __half2float(__float2half_rn(cv.d));
+        if (ok) {
+            unit[k_code_pos(g, slot, d)] = (uint8_t)(int8_t)ck.code;
+            if ((lane & (kBlock - 1)) == 0) {
+                reinterpret_cast<uint16_t*>(unit + g.k_scales_off())[slot * g.nb() + d / kBlock] = f16_bits(ck.d);
+                reinterpret_cast<uint16_t*>(unit + g.v_scales_off())[v_scale_idx(g, slot, d / kBlock)] = f16_bits(cv.d);
+            }
+            if (own_byte) {
+                int nib;
+                const int64_t off = v_code_pos(g, slot, d, &nib);
+                const int other = partner_new ? quant_q4_0(vp[p], lane).code : (odd ? unit[off] & 15 : unit[off] >> 4);
+                unit[off] = (uint8_t)(odd ? other | (cv.code << 4) : cv.code | (other << 4));
+            }
+        }
+    }
+    // one partial per query row; rows of queries before j see no new key here
+    for (int r0 = 0; r0 < rows; r0 += QB) {
+        if (r0 > 0) load_q(r0);
+#pragma unroll
+        for (int b = 0; b < QB; ++b) {
+            const int r = r0 + b;
+            if (r >= rows) break;                          // uniform
+            const int qi = r / group, h = kvh * group + r % group;
+            const size_t ps = ((size_t)qi * a.n_heads + h) * part_stride + part_idx;
+            const bool sees = qi >= j;
+            float dot = 0.0f;
+#pragma unroll
+            for (int p = 0; p < NP; ++p) dot = fmaf(qv[b][p] * qscale, kh[p], dot);
+            const float sc = wave_sum(dot, lane);
+            if (lane == 0) {
+                a.ws_m[ps] = !sees ? -INFINITY : ok ? sc : NAN;
+                a.ws_l[ps] = !sees ? 0.0f : ok ? 1.0f : NAN;
+            }
+#pragma unroll
+            for (int p = 0; p < NP; ++p) a.ws_acc[ps * D + 64 * p + lane] = sees ? vh[p] : 0.0f;
+        }
+    }
+}
+
+template <int D, int JJ, int RG, int R, int W, class Batch, bool NEWR>
 __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, int cps, int n_splits, int group,
-                                                                  int rows, Batch sb) {
+                                                                  int rows, Batch sb, NewRows nr, int part_stride) {
     using C = Cfg<D, R>;
     using WT = Waits<C::KL, R>;
     using WL = WgLds<D, R, W, RG, JJ>;
@@ -368,6 +465,9 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
     // deal its chunks among themselves.  Every group streams the same
     // chunks, so a chunk read by a second group mostly comes from L2.
     constexpr int WPG = W / RG;
+    // the cache is read once: non-temporal loads, except where several row
+    // groups read each chunk and the later ones hit in L2
+    constexpr int POL = RG == 1 ? kLoadNT : kLoadPlain;
     extern __shared__ __align__(16) uint8_t smem[];
     const Geom& g = a.g;
     const int lane = threadIdx.x & 63;
@@ -379,6 +479,7 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
         const int b = seq_of(sb.wg0, sb.n, wg);
         wg -= sb.wg0[b];
         n_splits = sb.n_splits[b];
+        part_stride = n_splits;                 // the sequence's own partials per row
         a.ctx = sb.ctx[b];
         a.page_table += (size_t)b * sb.n_table;
         a.q += (size_t)b * a.n_q * a.n_heads * D;
@@ -483,12 +584,12 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
             const ChunkPtr cp = chunk_ptr<D>(u_cur, g, slot_cur);
 #pragma unroll
             for (int J = 0; J < 2 * C::KL; ++J)
-                if (J + R >= C::NP) issue_piece<D, R>(land, cp, J + R - C::NP, lane);
-            issue_kscales<D, R>(land, cp, lane);
+                if (J + R >= C::NP) issue_piece<D, R, POL>(land, cp, J + R - C::NP, lane);
+            issue_kscales<D, R, POL>(land, cp, lane);
 #pragma unroll
             for (int J = 2 * C::KL; J < C::NP; ++J)
-                if (J + R >= C::NP) issue_piece<D, R>(land, cp, J + R - C::NP, lane);
-            issue_vscales<D, R>(land, cp, lane);
+                if (J + R >= C::NP) issue_piece<D, R, POL>(land, cp, J + R - C::NP, lane);
+            issue_vscales<D, R, POL>(land, cp, lane);
         }
     }
 
@@ -531,6 +632,15 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
         if constexpr (QREG) return qreg[i / 2];
         else return *reinterpret_cast<const half8*>(qlds + i * 1024 + lane * 16);
     };
+    // fused decode step: appended row j is handled by the last wave of split
+    // n_splits - 1 - j of each KV head -- the last splits hold the fewest
+    // chunks -- before its loop (its first chunk's requests stay in flight;
+    // in list mode the other waves take its share)
+    if constexpr (NEWR) {
+        if (wave == W - 1)
+            for (int j = n_splits - 1 - split; j < nr.n_new; j += n_splits)
+                new_row_partials<D>(a, nr, kvh, group, rows, j, part_stride, n_splits + j, lane);
+    }
 
     WaveState<D, R> st;
 #pragma unroll
@@ -583,8 +693,8 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
         // consuming piece J requests piece J + R: of this chunk, or of the next
         auto refill = [&](int J) {
             const int jn = J + R;
-            if (jn < C::NP) issue_piece<D, R>(land, cp, jn, lane);
-            else if (more) issue_piece<D, R>(land, np, jn - C::NP, lane);
+            if (jn < C::NP) issue_piece<D, R, POL>(land, cp, jn, lane);
+            else if (more) issue_piece<D, R, POL>(land, np, jn - C::NP, lane);
         };
         auto qk_wait = [&](int p) {
             if (!more) vm_wait<0>();
@@ -606,11 +716,11 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
         floatx4 s[2];
         qk_step<D, R, JJ, MASK>(s, land, qop, lane, j0, first_last, mask_group, rows, gi, qk_wait, qk_done);
         lds_fence();                            // K scales read out
-        if (more) issue_kscales<D, R>(land, np, lane);
+        if (more) issue_kscales<D, R, POL>(land, np, lane);
         softmax_step<D, R, JJ>(st, s, plds, lane);
         pv_step<D, R, MASK>(st, land, plds, lane, pv_wait, pv_done);
         lds_fence();                            // V scales read out
-        if (more) issue_vscales<D, R>(land, np, lane);
+        if (more) issue_vscales<D, R, POL>(land, np, lane);
         if (has_next && !ok_next) bad = true;
         u_cur = u_next;
         slot_cur = slot_next;
@@ -676,7 +786,7 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
                 const floatx4 o = *reinterpret_cast<const floatx4*>(cb + w * SLOTW + slot * D + dim);
                 acc += f * o;
             }
-            const size_t ps = ((size_t)(row / group) * a.n_heads + kvh * group + row % group) * n_splits + split;
+            const size_t ps = ((size_t)(row / group) * a.n_heads + kvh * group + row % group) * part_stride + split;
             *reinterpret_cast<floatx4*>(a.ws_acc + ps * D + dim) = acc;
             if (dim == 0) {
                 a.ws_m[ps] = mm;
@@ -754,7 +864,7 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
         const int row = logical_row<JJ>(gi, 4 * g4 + jj);
         if (row < 0 || row >= rows) continue;
         const int qi = row / group, h = kvh * group + row % group;
-        const size_t ps = ((size_t)qi * a.n_heads + h) * n_splits + split;
+        const size_t ps = ((size_t)qi * a.n_heads + h) * part_stride + split;
         if (n16 == 0) {
             a.ws_m[ps] = M[jj];
             a.ws_l[ps] = Ltot[jj];
@@ -770,38 +880,41 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
 template <int JJ>
 constexpr int stream_waves() { return 8; }
 
-template <int D, int JJ, int RG, class Batch>
-hipError_t launch_dr(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream, const Batch& sb, int n_wg) {
+template <int D, int JJ, int RG, bool NEWR, class Batch>
+hipError_t launch_dr(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream, const Batch& sb, int n_wg,
+                     const NewRows& nr, int part_stride) {
     constexpr int R = stream_ring_slots(D);             // ring slots: a few KiB in flight per wave
     constexpr int W = stream_waves<JJ>();
     using WL = WgLds<D, R, W, RG, JJ>;
-    auto kern = attn_mfma_stream_kernel<D, JJ, RG, R, W, Batch>;
+    auto kern = attn_mfma_stream_kernel<D, JJ, RG, R, W, Batch, NEWR>;
     if (WL::BYTES > 64 * 1024) {
-        hipError_t e = allow_lds<attn_mfma_stream_kernel<D, JJ, RG, R, W, Batch>>(WL::BYTES);
+        hipError_t e = allow_lds<attn_mfma_stream_kernel<D, JJ, RG, R, W, Batch, NEWR>>(WL::BYTES);
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kern, dim3(n_wg), dim3(W * 64), WL::BYTES, stream, a, pl.chunks_per_split, pl.n_splits,
-                       pl.group, pl.rows, sb);
+                       pl.group, pl.rows, sb, nr, part_stride);
     return hipGetLastError();
 }
 
 // Up to 8 rows two per lane group (JJ = 2), up to 16 rows one per MFMA row,
 // more rows in 2 or 4 row groups of 16.
-template <int D, class Batch>
-hipError_t launch_d(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream, const Batch& sb, int n_wg) {
-    if (pl.rows <= 8) return launch_dr<D, 2, 1>(a, pl, stream, sb, n_wg);
-    if (pl.rows <= 16) return launch_dr<D, 4, 1>(a, pl, stream, sb, n_wg);
-    if (pl.rows <= 32) return launch_dr<D, 4, 2>(a, pl, stream, sb, n_wg);
-    if (pl.rows <= 64) return launch_dr<D, 4, 4>(a, pl, stream, sb, n_wg);
+template <int D, bool NEWR, class Batch>
+hipError_t launch_d(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream, const Batch& sb, int n_wg,
+                    const NewRows& nr, int part_stride) {
+    if (pl.rows <= 8) return launch_dr<D, 2, 1, NEWR>(a, pl, stream, sb, n_wg, nr, part_stride);
+    if (pl.rows <= 16) return launch_dr<D, 4, 1, NEWR>(a, pl, stream, sb, n_wg, nr, part_stride);
+    if (pl.rows <= 32) return launch_dr<D, 4, 2, NEWR>(a, pl, stream, sb, n_wg, nr, part_stride);
+    if (pl.rows <= 64) return launch_dr<D, 4, 4, NEWR>(a, pl, stream, sb, n_wg, nr, part_stride);
     return hipErrorInvalidValue;
 }
 
-template <class Batch>
-hipError_t launch_any(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream, const Batch& sb, int n_wg) {
+template <bool NEWR, class Batch>
+hipError_t launch_any(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream, const Batch& sb, int n_wg,
+                      const NewRows& nr, int part_stride) {
     switch (a.g.D) {
-        case 64: return launch_d<64>(a, pl, stream, sb, n_wg);
-        case 128: return launch_d<128>(a, pl, stream, sb, n_wg);
-        case 256: return launch_d<256>(a, pl, stream, sb, n_wg);
+        case 64: return launch_d<64, NEWR>(a, pl, stream, sb, n_wg, nr, part_stride);
+        case 128: return launch_d<128, NEWR>(a, pl, stream, sb, n_wg, nr, part_stride);
+        case 256: return launch_d<256, NEWR>(a, pl, stream, sb, n_wg, nr, part_stride);
         default: return hipErrorInvalidValue;
     }
 }
@@ -814,8 +927,15 @@ int mfma_stream_waves(int rows) {
 }
 
 hipError_t launch_attn_mfma_stream(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream, const SeqBatch* batch) {
-    if (batch != nullptr && batch->n > 0) return launch_any(a, pl, stream, *batch, batch->wg0[batch->n]);
-    return launch_any(a, pl, stream, NoBatch{}, pl.n_splits * a.g.n_kv);
+    const NewRows none{nullptr, nullptr, nullptr, 0, 0};
+    if (batch != nullptr && batch->n > 0)
+        return launch_any<false>(a, pl, stream, *batch, batch->wg0[batch->n], none, pl.n_splits);
+    return launch_any<false>(a, pl, stream, NoBatch{}, pl.n_splits * a.g.n_kv, none, pl.n_splits);
+}
+
+hipError_t launch_attn_mfma_stream_new(const AttnArgs& a, const AttnPlan& pl, const NewRows& nr, hipStream_t stream) {
+    if (nr.n_new < 1 || nr.n_new > kMaxNewRows || pl.n_splits < 1) return hipErrorInvalidValue;
+    return launch_any<true>(a, pl, stream, NoBatch{}, pl.n_splits * a.g.n_kv, nr, pl.n_splits + nr.n_new);
 }
 
 }  // namespace kvq

@@ -226,6 +226,24 @@ bool append_attn_fused(const kvq_layout* L, int32_t n_heads, int32_t n_new, cons
     return L->codec == KVQ_CODEC_Q8K_Q4V && (kernel == 0 || kernel == 2) && n_new * (n_heads / L->n_kv_heads) <= 64;
 }
 
+// Where a fused step's new rows are quantized and scored.  With one row
+// group the split kernel does it: one wave per new row, whose share of the
+// cached chunks the other waves of its workgroup take over from the LDS list.
+// With several row groups (the verify batch's fixed chunk order) that wave
+// would hold up its workgroup's end, so the merge kernel does it instead.
+bool new_rows_in_split(const kvq::AttnPlan& pl) { return pl.n_splits > 0 && kvq::mfma_stream_row_groups(pl.rows) == 1; }
+
+// Partials per row of a fused step: the splits over the cached keys, and one
+// per new row when the split kernel handles them.
+int fused_parts(const kvq::AttnPlan& pl, int n_new) { return pl.n_splits + (new_rows_in_split(pl) ? n_new : 0); }
+
+size_t fused_ws_bytes(const kvq::AttnPlan& pl, int n_new, int n_heads, int D) {
+    if (pl.n_splits <= 0) return 0;
+    kvq::AttnPlan pw = pl;
+    pw.n_splits = fused_parts(pl, n_new);
+    return kvq::ws_bytes_for(pw, n_new, n_heads, D);
+}
+
 // Plan of the cached part (fused) or of the whole attention (otherwise).
 int append_attn_plan(const kvq_layout* L, int32_t n_heads, int32_t pos0, int32_t n_new, const kvq_attn_opts* opts,
                      bool fused, kvq::AttnPlan* pl) {
@@ -398,7 +416,8 @@ int kvq_append_attn_workspace_bytes(const kvq_layout* layout, int32_t n_heads, i
     kvq::AttnPlan pl;
     st = append_attn_plan(layout, n_heads, pos0, n_new, opts, fused, &pl);
     if (st) return st;
-    *bytes = pl.n_splits > 0 ? kvq::ws_bytes_for(pl, n_new, n_heads, layout->head_dim) : 0;
+    *bytes = fused ? fused_ws_bytes(pl, n_new, n_heads, layout->head_dim)
+                   : pl.n_splits > 0 ? kvq::ws_bytes_for(pl, n_new, n_heads, layout->head_dim) : 0;
     return ok();
 }
 
@@ -425,7 +444,7 @@ int kvq_append_attn(const kvq_layout* layout, void* d_pool, const int32_t* d_pag
     kvq::AttnPlan pl;
     st = append_attn_plan(layout, n_heads, pos0, n_new, opts, true, &pl);
     if (st) return st;
-    const size_t need = pl.n_splits > 0 ? kvq::ws_bytes_for(pl, n_new, n_heads, layout->head_dim) : 0;
+    const size_t need = fused_ws_bytes(pl, n_new, n_heads, layout->head_dim);
     if (need > 0 && (d_ws == nullptr || ws_bytes < need))
         return fail(KVQ_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given%s", need, ws_bytes,
                     d_ws == nullptr ? " (NULL)" : "");
@@ -443,8 +462,9 @@ int kvq_append_attn(const kvq_layout* layout, void* d_pool, const int32_t* d_pag
     a.out = d_out;
     a.lse = d_lse;
     a.causal = 0;
+    const int parts = fused_parts(pl, n_new);
     const size_t rows = (size_t)n_new * n_heads;
-    const size_t ml = (rows * pl.n_splits * sizeof(float) + 255) / 256 * 256;
+    const size_t ml = (rows * parts * sizeof(float) + 255) / 256 * 256;
     uint8_t* ws = static_cast<uint8_t*>(d_ws);
     a.ws_m = reinterpret_cast<float*>(ws);
     a.ws_l = reinterpret_cast<float*>(ws + ml);
@@ -455,10 +475,22 @@ int kvq_append_attn(const kvq_layout* layout, void* d_pool, const int32_t* d_pag
     hipError_t e = hipSuccess;
     if (opts != nullptr && opts->kernel_begin_event != nullptr)
         e = hipEventRecord(static_cast<hipEvent_t>(opts->kernel_begin_event), s);
-    if (e == hipSuccess && pl.n_splits > 0) e = kvq::launch_attn_mfma_stream(a, pl, s);
+    // The split pass over the cached keys either also appends the new rows
+    // and leaves their partials (the merge then only folds), or leaves them
+    // to the merge kernel, which appends and scores them itself (also when
+    // there are no cached keys, pos0 = 0).
+    const bool in_split = new_rows_in_split(pl);
+    if (e == hipSuccess && in_split) e = kvq::launch_attn_mfma_stream_new(a, pl, nr, s);
+    else if (e == hipSuccess && pl.n_splits > 0) e = kvq::launch_attn_mfma_stream(a, pl, s);
     if (e == hipSuccess && opts != nullptr && opts->kernel_end_event != nullptr)
         e = hipEventRecord(static_cast<hipEvent_t>(opts->kernel_end_event), s);
-    if (e == hipSuccess) e = kvq::launch_merge_new(a, nr, pl.n_splits, s);
+    if (e == hipSuccess && in_split) {
+        kvq::AttnPlan pm = pl;
+        pm.n_splits = parts;
+        e = kvq::launch_merge(a, pm, s);
+    } else if (e == hipSuccess) {
+        e = kvq::launch_merge_new(a, nr, pl.n_splits, s);
+    }
     if (e != hipSuccess) return fail(KVQ_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return ok();
 }

@@ -190,6 +190,11 @@ hipError_t launch_merge(const AttnArgs& a, const AttnPlan& pl, hipStream_t strea
 // Merge of n_splits partials (0: none) with the new rows' keys, and the
 // rows' quantized write into the pool.
 hipError_t launch_merge_new(const AttnArgs& a, const NewRows& nr, int n_splits, hipStream_t stream);
+// The streaming MFMA kernel of a fused decode step (pl.n_splits >= 1 over the
+// cached keys): it also quantizes the nr.n_new appended rows into the pool
+// and leaves new row j's softmax state as partial n_splits + j of every row
+// (n_splits + n_new partials per row, folded by launch_merge with that count).
+hipError_t launch_attn_mfma_stream_new(const AttnArgs& a, const AttnPlan& pl, const NewRows& nr, hipStream_t stream);
 // Streaming MFMA kernel: row groups per workgroup, and waves sharing one row
 // group (each partial folds that many waves' chunks), for a given row count.
 int mfma_stream_row_groups(int rows);

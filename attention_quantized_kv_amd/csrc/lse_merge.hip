@@ -13,12 +13,11 @@
 // entry outside the pool) propagates to the output.
 //
 // The merge runs after the split kernel, on the same stream, so its duration
-// adds straight to every decode step: it is built for latency.  One wavefront
+// adds straight to every decode step: it is built for latency.  A workgroup
 // per (query row, 64-dim slice) -- D/64 times more workgroups than rows, so
-// the work spreads over the chip -- loads everything it needs in one memory
-// round trip (a batch of 64 splits' accumulators for its 64 dims, one split
-// per lane for (m, l), the new rows), folds the (m, l) of the batch across
-// lanes and broadcasts each split's weight with readlane.
+// the partials' bytes spread over the chip -- issues every load it needs at
+// once (a few 16-byte loads per thread), so the merge costs one memory round
+// trip plus a few hundred instructions.
 #include <type_traits>
 
 #include "kvq_quant.h"
@@ -31,32 +30,42 @@ constexpr int kMaxNew = 8;      // rows appended by one fused call (the decode /
 constexpr int kSlice = 64;      // output dims per workgroup (one per lane)
 constexpr float kLog2eM = 1.4426950408889634f;
 
-__device__ inline float readlane_f(float x, int l) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
-}
-
-// Workgroup = one wavefront: query row `row` (all rows are n_q * n_heads, in
-// (query, head) order; a batched launch stacks its sequences), output dims
-// 64 z .. 64 z + 63 (lane = dim).
+// Workgroup = 4 wavefronts for query row `row` (all rows are n_q * n_heads,
+// in (query, head) order; a batched launch stacks its sequences) and output
+// dims 64 z .. 64 z + 63.  Partials: per round of 64 splits, thread (wave w,
+// lane = 16 si + dq) reads 16 bytes (dims 4 dq .. 4 dq + 3 of the slice) of
+// splits 16 p + 4 w + si, p < 4: four 16-byte loads, no branches (addresses
+// past the last split are clamped and weighted 0).  Every wave folds the
+// round's (m, l) itself (lane = split), so M, L and the weights are the same
+// in all of them; a thread takes its splits' weights with a lane shuffle,
+// the 4 split groups of a wave are summed with permlane swaps, and the 4
+// waves through 1 KiB of LDS; wave 0 then owns dim 64 z + lane.
 //
 // NEW (the second half of the fused append + attention call): row (i, h) --
 // query i at position pos0 + i -- has the split partials over the cached
 // keys 0..pos0-1 and sees the new rows 0..i as well (causal among the new
-// rows).  Each workgroup quantizes the visible new K rows of its KV head over
-// all D dims and the V rows over its own dims, with the append kernel's block
-// code (so the values are the ones the pool will hold, bit for bit), scores
-// the dequantized keys, and folds them in as one more partial after the
-// splits.  The workgroups of (i, first head of the group) write new row i of
-// that KV head into the pool, each its own dims: K codes and both scales by
-// plain stores, the V nibble (which shares a byte with its pair slot) by an
-// atomic and-or on the containing dword.
+// rows).  Thread t quantizes dim t of the visible new K rows of its KV head
+// (all D dims over the workgroup) and wave 0 dim 64 z + lane of the V rows,
+// with the append kernel's block code (so the values are the ones the pool
+// will hold, bit for bit); the scores of the dequantized keys are summed over
+// the waves with the partials, and the new keys are folded in as one more
+// partial after the splits.  The workgroups of (i, first head of the group)
+// write new row i of that KV head into the pool, each its own 64 dims, with
+// plain stores: K codes and both scales.  Two slots (2k, 2k+1) share every V
+// byte, so the byte is written once, by the workgroup of the later new row
+// of the pair, which sees both rows (the other nibble is either new row i-1
+// or a slot no new row touches, kept as it was).  No byte of the pool is
+// written by two workgroups, so no atomics are needed and no L2 of another
+// XCD can hold a stale copy of a byte being changed.
 template <int D, bool NEW, class Batch>
-__global__ __launch_bounds__(64) void merge_rows_kernel(AttnArgs a, NewRows nr, int n_splits, int group, Batch sb) {
+__global__ __launch_bounds__(256) void merge_rows_kernel(AttnArgs a, NewRows nr, int n_splits, int group, Batch sb) {
     constexpr int NS = D / kSlice;          // slices per row
+    __shared__ float4 red4[4][16];          // per wave: the 64 dims' sums of its splits
+    __shared__ float dots[kMaxNew][4];      // per wave: its part of each new key's score
     const Geom& g = a.g;
-    const int lane = threadIdx.x;
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int si = lane >> 4, dq = lane & 15;
     const int row = blockIdx.x / NS, z = blockIdx.x % NS;
-    const int d = kSlice * z + lane;
     size_t p0 = (size_t)row * n_splits;     // this row's first partial
     if constexpr (!std::is_same_v<Batch, NoBatch>) {
         const int rps = a.n_q * a.n_heads;
@@ -66,32 +75,39 @@ __global__ __launch_bounds__(64) void merge_rows_kernel(AttnArgs a, NewRows nr, 
     }
     const float* m = a.ws_m + p0;
     const float* l = a.ws_l + p0;
-    const float* acc = a.ws_acc + p0 * D + d;
+    const float* acc = a.ws_acc + p0 * D + kSlice * z + 4 * dq;
 
-    // ---- every load up front: the first batch of partials and, for NEW, q,
-    // the visible new K rows (all dims) and V rows (this slice), their page
-    // entries
-    const int nb0 = min(kBatch, n_splits);
-    float x[kBatch];
+    // ---- every load up front: the first round of partials and, for NEW, q,
+    // the visible new K rows (dim t) and V rows (wave 0: dim 64 z + lane), and
+    // their page entries
+    auto load_round = [&](int s0, float4 (&x)[4], float& mk, float& lk) {
+        const int last = n_splits - 1;
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) x[k] = k < nb0 ? acc[(size_t)k * D] : 0.0f;
-    float mk = lane < nb0 ? m[lane] : -INFINITY;
-    float lk = lane < nb0 ? l[lane] : 0.0f;
+        for (int p = 0; p < 4; ++p) {
+            const int s = min(s0 + 16 * p + 4 * wv + si, last);
+            x[p] = *reinterpret_cast<const float4*>(acc + (size_t)s * D);
+        }
+        const int s = min(s0 + lane, last);
+        mk = m[s];
+        lk = l[s];
+    };
+    float4 x[4];
+    float mk = -INFINITY, lk = 0.0f;
+    if (n_splits > 0) load_round(0, x, mk, lk);
 
     const int qi = row / a.n_heads, h = row % a.n_heads, kvh = h / group;
     const int n_vis = NEW ? qi + 1 : 0;     // new rows visible to query qi (uniform)
-    float qx[NS], kx[NEW ? kMaxNew : 1][NS], vx[NEW ? kMaxNew : 1];
+    const bool kdim = t < D;                // threads that quantize a K dim
+    float qx = 0.0f, kx[NEW ? kMaxNew : 1], vx[NEW ? kMaxNew : 1];
     int phys = -1;
     bool bad_page = false;
     if constexpr (NEW) {
-#pragma unroll
-        for (int s = 0; s < NS; ++s) qx[s] = a.q[(size_t)row * D + kSlice * s + lane] * (a.scale * kLog2eM);
+        if (kdim) qx = a.q[(size_t)row * D + t] * (a.scale * kLog2eM);
 #pragma unroll
         for (int j = 0; j < kMaxNew; ++j) {
             const size_t src = ((size_t)j * g.n_kv + kvh) * D;
-#pragma unroll
-            for (int s = 0; s < NS; ++s) kx[j][s] = j < n_vis ? nr.k[src + kSlice * s + lane] : 0.0f;
-            vx[j] = j < n_vis ? nr.v[src + d] : 0.0f;
+            kx[j] = j < n_vis && kdim ? nr.k[src + t] : 0.0f;
+            vx[j] = j < n_vis && wv == 0 ? nr.v[src + kSlice * z + lane] : 0.0f;
         }
         // a visible new row whose page entry lies outside the pool makes the
         // row's result NaN (as a cached key on such a page does); a row whose
@@ -105,72 +121,106 @@ __global__ __launch_bounds__(64) void merge_rows_kernel(AttnArgs a, NewRows nr, 
         }
     }
 
-    // ---- fold the split partials, 64 per round
-    float M = -INFINITY, L = 0.0f, o = 0.0f;
-    for (int s0 = 0; s0 < n_splits; s0 += kBatch) {
-        const int nb = min(kBatch, n_splits - s0);
-        if (s0 > 0) {
+    // ---- the new keys: quantize, score (this thread's dim), write this
+    // slice's dims of the row's own new key into the pool
+    float vhat[NEW ? kMaxNew : 1];
+    int vc_self = 0, vc_prev = 0;           // V codes (this lane's dim) of new rows qi and qi - 1
+    const bool writer = NEW && h % group == 0 && phys >= 0 && phys < g.n_pages;
+    uint8_t* unit = NEW ? nr.pool + g.unit_index(writer ? phys : 0, kvh) * g.unit_bytes() : nullptr;
+    const int slot = NEW ? (nr.pos0 + qi) % g.P : 0;
+    if constexpr (NEW) {
 #pragma unroll
-            for (int k = 0; k < kBatch; ++k) x[k] = k < nb ? acc[(size_t)(s0 + k) * D] : 0.0f;
-            mk = lane < nb ? m[s0 + lane] : -INFINITY;
-            lk = lane < nb ? l[s0 + lane] : 0.0f;
+        for (int j = 0; j < kMaxNew; ++j) {
+            if (j >= n_vis) break;                         // uniform
+            if (kdim) {                                    // uniform per wave
+                const QCode ck = quant_q8_0(kx[j], lane);
+                const float kd = __half2float(__float2half_rn(ck.d));
+                const float part = wave_sum(qx * ((float)ck.code * kd), lane);
+                if (lane == 0) dots[j][wv] = part;
+                if (writer && j == qi && wv == z) {
+                    unit[k_code_pos(g, slot, t)] = (uint8_t)(int8_t)ck.code;
+                    if ((lane & (kBlock - 1)) == 0)
+                        reinterpret_cast<uint16_t*>(unit + g.k_scales_off())[slot * g.nb() + t / kBlock] = f16_bits(ck.d);
+                }
+            }
+            if (wv == 0) {
+                const QCode cv = quant_q4_0(vx[j], lane);
+                vhat[j] = (float)(cv.code - 8) * __half2float(__float2half_rn(cv.d));
+                if (j == qi) vc_self = cv.code;
+                if (j == qi - 1) vc_prev = cv.code;
+                if (writer && j == qi && (lane & (kBlock - 1)) == 0)
+                    reinterpret_cast<uint16_t*>(unit + g.v_scales_off())[v_scale_idx(g, slot, (kSlice * z + lane) / kBlock)] =
+                        f16_bits(cv.d);
+            }
         }
+        // the V byte of the pair holding slot (pos0 + qi): written here when
+        // qi is the pair's odd slot, or its even slot with no new row after it
+        if (writer && wv == 0) {
+            const bool odd = ((nr.pos0 + qi) & 1) != 0;
+            if (odd || qi == nr.n_new - 1) {
+                int nib;
+                const int64_t off = v_code_pos(g, slot, kSlice * z + lane, &nib);
+                const int old = unit[off];
+                const int lo = odd ? (qi >= 1 ? vc_prev : (old & 15)) : vc_self;
+                const int hi = odd ? vc_self : (old >> 4);
+                unit[off] = (uint8_t)(lo | (hi << 4));
+            }
+        }
+    }
+
+    // ---- fold the split partials, 64 per round
+    float M = -INFINITY, L = 0.0f;
+    float4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int s0 = 0; s0 < n_splits; s0 += kBatch) {
+        if (s0 > 0) load_round(s0, x, mk, lk);
+        const bool in = s0 + lane < n_splits;
         // splits with no visible key (l = 0) do not count; a NaN partial
         // (page outside the pool) propagates through its weight
-        const float bm = wave_max(lk != 0.0f ? mk : -INFINITY, lane);
+        const bool live = in && lk != 0.0f;
+        const float bm = wave_max(live ? mk : -INFINITY, lane);
         const float Mn = fmaxf(M, bm);
-        const float wk = lk != 0.0f ? exp2f(mk - Mn) : 0.0f;
+        const float wk = live ? exp2f(mk - Mn) : 0.0f;
         const float sl = wave_sum(wk * lk, lane);
         const float al = M == -INFINITY ? 0.0f : exp2f(M - Mn);
         L = L * al + sl;
         M = Mn;
-        float sum = o * al;
+        o *= al;
 #pragma unroll
-        for (int k = 0; k < kBatch; ++k) sum = fmaf(readlane_f(wk, k), x[k], sum);
-        o = sum;
+        for (int p = 0; p < 4; ++p) {
+            const float w = __shfl(wk, 16 * p + 4 * wv + si);
+            o += w * x[p];
+        }
     }
-
+    // sum the 4 split groups of the wave (lanes dq, dq + 16, dq + 32, dq + 48)
+    o.x += xor16_f(o.x, lane);
+    o.y += xor16_f(o.y, lane);
+    o.z += xor16_f(o.z, lane);
+    o.w += xor16_f(o.w, lane);
+    o.x += xor32_f(o.x, lane);
+    o.y += xor32_f(o.y, lane);
+    o.z += xor32_f(o.z, lane);
+    o.w += xor32_f(o.w, lane);
+    if (lane < 16) red4[wv][lane] = o;
+    __syncthreads();
+    if (wv != 0) return;
+    // wave 0: dim 64 z + lane
+    const float* r = reinterpret_cast<const float*>(red4);
+    const float od = r[lane] + r[64 + lane] + r[128 + lane] + r[192 + lane];
+    const size_t oi = (size_t)row * D + kSlice * z + lane;
     if constexpr (!NEW) {
-        a.out[(size_t)row * D + d] = o / L;
+        a.out[oi] = od / L;
         if (a.lse != nullptr && z == 0 && lane == 0) a.lse[row] = (M + log2f(L)) * 0.69314718055994531f;
-        return;
     } else {
-        // ---- the new rows: quantize, score, fold in after the splits; this
-        // row's own new row goes to the pool
-        const bool writer = h % group == 0 && phys >= 0 && phys < g.n_pages;
-        uint8_t* unit = nr.pool + g.unit_index(writer ? phys : 0, kvh) * g.unit_bytes();
-        const int slot = (nr.pos0 + qi) % g.P;
-        float sj[kMaxNew], vhat[kMaxNew];
+        float sj[kMaxNew];
         float m_new = -INFINITY;
 #pragma unroll
         for (int j = 0; j < kMaxNew; ++j) {
-            if (j >= n_vis) break;                         // uniform
-            float dot = 0.0f;
+            if (j >= n_vis) break;
+            float sum = 0.0f;
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                const QCode ck = quant_q8_0(kx[j][s], lane);
-                const float kd = __half2float(__float2half_rn(ck.d));
-                dot = fmaf(qx[s], (float)ck.code * kd, dot);
-                if (s == z && writer && j == qi) {
-                    unit[k_code_pos(g, slot, d)] = (uint8_t)(int8_t)ck.code;
-                    if ((lane & (kBlock - 1)) == 0)
-                        reinterpret_cast<uint16_t*>(unit + g.k_scales_off())[slot * g.nb() + d / kBlock] = f16_bits(ck.d);
-                }
-            }
-            sj[j] = wave_sum(dot, lane);
-            m_new = fmaxf(m_new, sj[j]);
-            const QCode cv = quant_q4_0(vx[j], lane);
-            vhat[j] = (float)(cv.code - 8) * __half2float(__float2half_rn(cv.d));
-            if (writer && j == qi) {
-                int nib;
-                const int64_t off = v_code_pos(g, slot, d, &nib);
-                unsigned int* dw = reinterpret_cast<unsigned int*>(unit + (off & ~(int64_t)3));
-                const int shift = (int)(off & 3) * 8 + nib * 4;
-                atomicAnd(dw, ~(0xFu << shift));
-                atomicOr(dw, (unsigned int)cv.code << shift);
-                if ((lane & (kBlock - 1)) == 0)
-                    reinterpret_cast<uint16_t*>(unit + g.v_scales_off())[v_scale_idx(g, slot, d / kBlock)] = f16_bits(cv.d);
-            }
+            for (int w = 0; w < D / 64; ++w) sum += dots[j][w];
+            sj[j] = sum;
+            m_new = fmaxf(m_new, sum);
         }
         float l_new = 0.0f, acc_new = 0.0f;
 #pragma unroll
@@ -184,7 +234,7 @@ __global__ __launch_bounds__(64) void merge_rows_kernel(AttnArgs a, NewRows nr, 
         const float a_old = M == -INFINITY ? 0.0f : exp2f(M - Mt);
         const float a_new = exp2f(m_new - Mt);
         const float Lt = L * a_old + l_new * a_new;
-        a.out[(size_t)row * D + d] = bad_page ? NAN : (o * a_old + acc_new * a_new) / Lt;
+        a.out[oi] = bad_page ? NAN : (od * a_old + acc_new * a_new) / Lt;
         if (a.lse != nullptr && z == 0 && lane == 0)
             a.lse[row] = bad_page ? NAN : (Mt + log2f(Lt)) * 0.69314718055994531f;
     }
@@ -196,15 +246,15 @@ hipError_t launch_rows(const AttnArgs& a, const NewRows& nr, int n_splits, int n
     const int group = a.n_heads / a.g.n_kv;
     switch (a.g.D) {
         case 64:
-            hipLaunchKernelGGL((merge_rows_kernel<64, NEW, Batch>), dim3(n_rows), dim3(64), 0, stream, a, nr, n_splits,
+            hipLaunchKernelGGL((merge_rows_kernel<64, NEW, Batch>), dim3(n_rows), dim3(256), 0, stream, a, nr, n_splits,
                                group, sb);
             break;
         case 128:
-            hipLaunchKernelGGL((merge_rows_kernel<128, NEW, Batch>), dim3(n_rows * 2), dim3(64), 0, stream, a, nr,
+            hipLaunchKernelGGL((merge_rows_kernel<128, NEW, Batch>), dim3(n_rows * 2), dim3(256), 0, stream, a, nr,
                                n_splits, group, sb);
             break;
         case 256:
-            hipLaunchKernelGGL((merge_rows_kernel<256, NEW, Batch>), dim3(n_rows * 4), dim3(64), 0, stream, a, nr,
+            hipLaunchKernelGGL((merge_rows_kernel<256, NEW, Batch>), dim3(n_rows * 4), dim3(256), 0, stream, a, nr,
                                n_splits, group, sb);
             break;
         default: return hipErrorInvalidValue;

@@ -295,7 +295,8 @@ def cpu_model() -> str:
 def read_ceiling(device, nbytes=436207616, reps=8):
     """Plain-read bandwidth of this GPU for the decode kernels' access pattern
     (libkvq_probe.so: whole 1 KiB wave requests, 8 waves per workgroup, one
-    workgroup per CU), best of 4, 8 and 16 pieces in flight per wave, in GB/s;
+    workgroup per CU), best of 4 and 8 pieces in flight per wave, with and
+    without the non-temporal hint, in GB/s;
     the ceiling a streaming kernel can reach here, next to the nominal 8 TB/s.
     None when the probe library is missing."""
     import ctypes
@@ -305,7 +306,7 @@ def read_ceiling(device, nbytes=436207616, reps=8):
         return None
     lib = ctypes.CDLL(path)
     lib.kvq_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
-                                   ctypes.c_int, ctypes.c_void_p]
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.kvq_probe_read.restype = ctypes.c_int
     cus = torch.cuda.get_device_properties(device).multi_processor_count
     src = torch.empty(nbytes, dtype=torch.uint8, device=device)
@@ -314,9 +315,9 @@ def read_ceiling(device, nbytes=436207616, reps=8):
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     best = {}
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for unroll in (4, 8, 16):
+    for unroll, nt in ((4, 0), (8, 0), (4, 1), (8, 1)):
         call = lambda: lib.kvq_probe_read(ctypes.c_void_p(src.data_ptr()), nbytes, ctypes.c_void_p(out.data_ptr()),
-                                          cus, 8, unroll, stream)
+                                          cus, 8, unroll, nt, stream)
         for _ in range(2):
             if call() != 0:
                 raise RuntimeError("kvq_probe_read failed")
@@ -326,12 +327,13 @@ def read_ceiling(device, nbytes=436207616, reps=8):
             call()
         stop.record()
         torch.cuda.synchronize()
-        best[unroll] = nbytes * reps / (start.elapsed_time(stop) / 1e3) / 1e9
+        best[(unroll, nt)] = nbytes * reps / (start.elapsed_time(stop) / 1e3) / 1e9
     del src, out
     u = max(best, key=best.get)
-    return {"GBps": round(best[u], 1), "pieces_in_flight_per_wave": u,
-            "all": {str(k): round(v, 1) for k, v in best.items()},
-            "probe": f"plain 16 B/lane loads of 1 KiB wave pieces over {nbytes} B, {cus} workgroups x 8 waves"}
+    return {"GBps": round(best[u], 1), "pieces_in_flight_per_wave": u[0], "nontemporal": bool(u[1]),
+            "all": {f"{k[0]}{'nt' if k[1] else ''}": round(v, 1) for k, v in best.items()},
+            "probe": f"16 B/lane loads of 1 KiB wave pieces over {nbytes} B, {cus} workgroups x 8 waves, "
+                     "plain or non-temporal"}
 
 
 def bench_stream(args, w, n_layers):

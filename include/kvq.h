@@ -243,8 +243,8 @@ int kvq_attn_ex(const kvq_layout *layout, const void *d_pool,
  *   d_q, d_out, d_lse      as for attention with n_q = n_new
  *   d_ws   workspace of at least kvq_append_attn_workspace_bytes() bytes
  *          (NULL if that is 0); opts as for kvq_attn_ex, may be NULL.
- * The rows' V nibbles are written with atomic and/or on their pool dwords;
- * the same ordering rules as kvq_append apply.  Errors: as kvq_append and
+ * Every pool byte the call changes is written by one thread (the two slots
+ * of a V byte together); the same ordering rules as kvq_append apply.  Errors: as kvq_append and
  * kvq_attn_ex (INVALID_ARG also for n_new outside [1, KVQ_MAX_NQ_DECODE]).
  */
 int kvq_append_attn_workspace_bytes(const kvq_layout *layout, int32_t n_heads, int32_t pos0,

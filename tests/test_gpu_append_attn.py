@@ -79,6 +79,8 @@ CASES = [
     (7, 256, 1, 4, 32, 61, 7),        # new rows across a chunk and a page edge
     (8, 64, 3, 5, 96, 190, 3),        # page size not a power of two
     (9, 256, 4, 6, 256, 0, 4),        # verify with no cached keys
+    (10, 256, 4, 6, 256, 131072, 4),  # the verify workload's positions (two pairs of new rows)
+    (12, 128, 3, 2, 64, 33, 8),       # odd pos0, 8 rows: three pairs of new rows, the last row alone
 ]
 
 
