@@ -29,7 +29,7 @@ KERNEL_AUTO, KERNEL_VALU, KERNEL_MFMA_STREAM, KERNEL_MFMA_TILED = 0, 1, 2, 3
 EXPORTS = (
     "kvq_unit_bytes", "kvq_pool_bytes", "kvq_append", "kvq_workspace_bytes",
     "kvq_decode_attn", "kvq_prefill_attn", "kvq_workspace_bytes_ex", "kvq_attn_ex",
-    "kvq_append_attn_workspace_bytes", "kvq_append_attn",
+    "kvq_append_attn_workspace_bytes", "kvq_append_attn", "kvq_noalloc_scratch_bytes", "kvq_append_attn_noalloc",
     "kvq_decode_attn_batch_workspace_bytes", "kvq_decode_attn_batch", "kvq_stage_pages", "kvq_hadamard",
     "kvq_status_str", "kvq_last_error", "kvq_version",
 )
@@ -89,6 +89,8 @@ def lib() -> ctypes.CDLL:
         "kvq_attn_ex": [LP, P, P, i32, i32, i32, i32, P, ctypes.c_float, P, P, P, sz, OP, P],
         "kvq_append_attn_workspace_bytes": [LP, i32, i32, i32, OP, SZP],
         "kvq_append_attn": [LP, P, P, i32, i32, i32, P, P, i32, P, ctypes.c_float, P, P, P, sz, OP, P],
+        "kvq_noalloc_scratch_bytes": [],
+        "kvq_append_attn_noalloc": [LP, P, P, i32, i32, i32, P, P, i32, P, ctypes.c_float, P, P, OP, P],
         "kvq_decode_attn_batch_workspace_bytes": [LP, i32, P, i32, i32, SZP],
         "kvq_decode_attn_batch": [LP, P, P, i32, i32, P, i32, i32, P, ctypes.c_float, P, P, P, sz, OP, P],
         "kvq_stage_pages": [LP, P, P, i32, LP, P, i32, P],
@@ -101,6 +103,7 @@ def lib() -> ctypes.CDLL:
         f = getattr(L, name)
         f.argtypes = args
         f.restype = ctypes.c_int
+    L.kvq_noalloc_scratch_bytes.restype = ctypes.c_size_t
     L.kvq_status_str.restype = ctypes.c_char_p
     L.kvq_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -287,6 +290,33 @@ def kvq_append_attn(layout: Layout, pool, page_table, pos0: int, k, v, q, scale:
     _check(lib().kvq_append_attn(ctypes.byref(layout), _ptr(pool), _ptr(page_table), nt, int(pos0), n_q,
                                  _ptr(k), _ptr(v), n_heads, _ptr(q), float(scale), _ptr(out), _ptr(lse),
                                  _ptr(ws), ws_bytes, ctypes.byref(opts), _stream(stream)), "kvq_append_attn")
+
+
+def kvq_noalloc_scratch_bytes() -> int:
+    """Bytes of the static device scratch kvq_append_attn_noalloc uses."""
+    return int(lib().kvq_noalloc_scratch_bytes())
+
+
+def kvq_append_attn_noalloc(layout: Layout, pool, page_table, pos0: int, k, v, q, scale: float, out, lse=None,
+                            kernel: int = 0, chunks_per_split: int = 0, stream=None, n_table=None, events=None):
+    """kvq_append_attn with the library's static device scratch instead of a
+    workspace (no device allocation by the call)."""
+    import torch
+    _need(k, "k", torch.float32)
+    _need(v, "v", torch.float32)
+    n_q, n_heads, _ = _attn_args(pool, page_table, q, out, lse, None)
+    if k.shape[0] != n_q or v.shape[0] != n_q:
+        raise ValueError("k, v and q must hold the same number of rows")
+    nt = _n_table(page_table) if n_table is None else n_table
+    opts = AttnOpts(kernel, chunks_per_split)
+    if events is not None:
+        if not events[0] or not events[1]:
+            raise ValueError("events must be two created hipEvent_t handles")
+        opts.kernel_begin_event = events[0]
+        opts.kernel_end_event = events[1]
+    _check(lib().kvq_append_attn_noalloc(ctypes.byref(layout), _ptr(pool), _ptr(page_table), nt, int(pos0), n_q,
+                                         _ptr(k), _ptr(v), n_heads, _ptr(q), float(scale), _ptr(out), _ptr(lse),
+                                         ctypes.byref(opts), _stream(stream)), "kvq_append_attn_noalloc")
 
 
 def _ctx_array(ctx_lens):

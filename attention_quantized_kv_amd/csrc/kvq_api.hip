@@ -5,6 +5,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "../../include/kvq.h"
 #include "kvq_internal.h"
@@ -421,10 +422,14 @@ int kvq_append_attn_workspace_bytes(const kvq_layout* layout, int32_t n_heads, i
     return ok();
 }
 
-int kvq_append_attn(const kvq_layout* layout, void* d_pool, const int32_t* d_page_table, int32_t n_table,
-                    int32_t pos0, int32_t n_new, const float* d_k, const float* d_v, int32_t n_heads,
-                    const float* d_q, float scale, float* d_out, float* d_lse, void* d_ws, size_t ws_bytes,
-                    const kvq_attn_opts* opts, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int append_attn_impl(const kvq_layout* layout, void* d_pool, const int32_t* d_page_table, int32_t n_table,
+                     int32_t pos0, int32_t n_new, const float* d_k, const float* d_v, int32_t n_heads,
+                     const float* d_q, float scale, float* d_out, float* d_lse, void* d_ws, size_t ws_bytes,
+                     const kvq_attn_opts* opts, void* stream) {
     kvq::Geom g;
     int st = check_layout(layout, &g);
     if (st) return st;
@@ -493,6 +498,64 @@ int kvq_append_attn(const kvq_layout* layout, void* d_pool, const int32_t* d_pag
     }
     if (e != hipSuccess) return fail(KVQ_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return ok();
+}
+
+// Scratch of kvq_append_attn_noalloc: the split partials live here instead
+// of in a caller's workspace.  Host code never names the array itself (its
+// host-side name is not a device address): it takes the device address once
+// per device with hipGetSymbolAddress and passes that to the kernels.
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+int scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(KVQ_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(KVQ_ERR_UNSUPPORTED, "device %d beyond the %d the scratch table covers", dev, kMaxDevices);
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(KVQ_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+        g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+    *out = p;
+    return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvq_append_attn(const kvq_layout* layout, void* d_pool, const int32_t* d_page_table, int32_t n_table,
+                    int32_t pos0, int32_t n_new, const float* d_k, const float* d_v, int32_t n_heads,
+                    const float* d_q, float scale, float* d_out, float* d_lse, void* d_ws, size_t ws_bytes,
+                    const kvq_attn_opts* opts, void* stream) {
+    return append_attn_impl(layout, d_pool, d_page_table, n_table, pos0, n_new, d_k, d_v, n_heads, d_q, scale, d_out,
+                            d_lse, d_ws, ws_bytes, opts, stream);
+}
+
+size_t kvq_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int kvq_append_attn_noalloc(const kvq_layout* layout, void* d_pool, const int32_t* d_page_table, int32_t n_table,
+                            int32_t pos0, int32_t n_new, const float* d_k, const float* d_v, int32_t n_heads,
+                            const float* d_q, float scale, float* d_out, float* d_lse, const kvq_attn_opts* opts,
+                            void* stream) {
+    size_t need = 0;
+    int st = kvq_append_attn_workspace_bytes(layout, n_heads, pos0, n_new, opts, &need);
+    if (st) return st;
+    if (need > kScratchBytes)
+        return fail(KVQ_ERR_WORKSPACE,
+                    "this step needs %zu bytes of scratch; the static scratch holds %zu (use kvq_append_attn with a "
+                    "workspace, or fewer query rows or a shorter context)",
+                    need, kScratchBytes);
+    void* ws = nullptr;
+    st = scratch_address(&ws);
+    if (st) return st;
+    return append_attn_impl(layout, d_pool, d_page_table, n_table, pos0, n_new, d_k, d_v, n_heads, d_q, scale, d_out,
+                            d_lse, ws, kScratchBytes, opts, stream);
 }
 
 int kvq_attn_ex(const kvq_layout* layout, const void* d_pool, const int32_t* d_page_table, int32_t n_table,

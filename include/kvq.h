@@ -259,6 +259,29 @@ int kvq_append_attn(const kvq_layout *layout, void *d_pool,
                     void *d_ws, size_t ws_bytes, const kvq_attn_opts *opts, void *stream);
 
 /*
+ * kvq_append_attn_noalloc -- kvq_append_attn without a workspace, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  The split partials live in
+ * a static device array of kvq_noalloc_scratch_bytes() bytes (8 MiB) that the
+ * library holds on every GPU it runs on until the process ends; the call
+ * itself allocates nothing.  Arguments, results and errors are those of
+ * kvq_append_attn with d_ws / ws_bytes left out, plus WORKSPACE when the step
+ * needs more scratch than the array holds (kvq_append_attn_workspace_bytes()
+ * tells; e.g. 24 heads over 4 KV heads at head_dim 256 fit up to n_new = 4).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (several host threads, or several streams) race and give wrong
+ * results.  Nothing in the array needs to start at any value.
+ */
+size_t kvq_noalloc_scratch_bytes(void);
+
+int kvq_append_attn_noalloc(const kvq_layout *layout, void *d_pool,
+                            const int32_t *d_page_table, int32_t n_table,
+                            int32_t pos0, int32_t n_new,
+                            const float *d_k, const float *d_v,
+                            int32_t n_heads, const float *d_q, float scale,
+                            float *d_out, float *d_lse, const kvq_attn_opts *opts, void *stream);
+
+/*
  * Batched decode: n_seqs independent sequences in one call, each with its own
  * context length and page-table row, all in one page pool (sequences normally
  * own disjoint pages).  For every sequence b it computes exactly what

@@ -225,3 +225,23 @@ def test_binding_raises():
     with pytest.raises(kvq.KvqError) as e:
         kvq.kvq_pool_bytes(kvq.Layout(4, 100, 256, 1))
     assert e.value.status == kvq.KVQ_ERR_UNSUPPORTED
+
+
+def test_noalloc_rejects_steps_beyond_its_scratch():
+    """kvq_append_attn_noalloc checks on the host that the step's partials fit
+    its static scratch and refuses, before any GPU call, when they do not."""
+    lib = kvq.lib()
+    cap = kvq.kvq_noalloc_scratch_bytes()
+    assert cap == 8 << 20
+    L = kvq.Layout(4, 256, 256, 2048)
+    # 8 queries x 64 heads: 512 rows of 64 splits of 1 KiB partials, over 8 MiB
+    assert kvq.kvq_append_attn_workspace_bytes(L, 64, 262000, 8) > cap
+    st = lib.kvq_append_attn_noalloc(ctypes.byref(L), FAKE, FAKE, 2048, 262000, 8, FAKE, FAKE, 64, FAKE,
+                                     ctypes.c_float(0.0625), FAKE, None, None, None)
+    assert st == kvq.KVQ_ERR_WORKSPACE
+    assert "static scratch" in lib.kvq_last_error().decode()
+    # bad arguments are refused as by kvq_append_attn, before the size check
+    assert lib.kvq_append_attn_noalloc(ctypes.byref(L), FAKE, FAKE, 2048, 100, 0, FAKE, FAKE, 24, FAKE,
+                                       ctypes.c_float(0.0625), FAKE, None, None, None) == kvq.KVQ_ERR_INVALID_ARG
+    # the decode workload's step fits
+    assert kvq.kvq_append_attn_workspace_bytes(L, 24, 262143, 1) <= cap
