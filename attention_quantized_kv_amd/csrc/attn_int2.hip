@@ -356,7 +356,7 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
         bool grow = false;
 #pragma unroll
         for (int jj = 0; jj < JJ; ++jj) {
-            mnew[jj] = row16_max(fmaxf(s[0][jj], s[1][jj]));
+            mnew[jj] = row16_max(max2(s[0][jj], s[1][jj]));
             grow |= mnew[jj] > m[jj] + kTau;
         }
         if (__builtin_amdgcn_ballot_w64(grow) != 0) {

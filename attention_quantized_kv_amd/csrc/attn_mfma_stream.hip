@@ -82,7 +82,7 @@ __device__ inline half8 v_codes_to_half(uint32_t x, uint32_t magic) {
     return h * mul + add;
 }
 
-template <int D, int R>
+template <int D, int R, int RT = 1>
 struct Cfg {
     static constexpr int NB = D / kBlock;       // quant blocks per row
     static constexpr int KL = D / 64;           // 64-dim slices (1 KiB pieces per K tile / V chunk)
@@ -93,35 +93,36 @@ struct Cfg {
     static constexpr int RING = R * 1024;
     static constexpr int LAND_KS = 1024;        // 32 x NB fp16, padded to one full-wave request
     static constexpr int LAND_VS = 1024;        // NB x 32 fp16, padded likewise
-    static constexpr int PBUF = 16 * kPStride * 4;
-    static constexpr int WAVE_BYTES = RING + LAND_KS + LAND_VS + PBUF;
-    static constexpr int Q_BYTES = NB * 2 * 1024;   // one row group's q, fp16 hi/lo, MFMA A layout
+    static constexpr int PBUF = 16 * kPStride * 4;  // one row tile's P
+    static constexpr int WAVE_BYTES = RING + LAND_KS + LAND_VS + RT * PBUF;
+    static constexpr int Q_BYTES = NB * 2 * 1024;   // one row tile's q, fp16 hi/lo, MFMA A layout
 };
 
-// Workgroup LDS: W per-wave areas (reused by the final combine) | q of each
-// of the RG row groups | (m, l) per wave and row.  The combine first folds the
-// waves past the largest power of two P2 <= WPG into the first ones, then
-// halves P2 down to one wave; SLOTS partial sums per group are in flight.
-template <int D, int R, int W, int RG, int JJ>
+// Workgroup LDS: W per-wave areas | q of each of the RG row groups (both
+// reused by the final combine) | (m, l) per wave, row tile and row | the
+// chunk list (one row group) | the small combine's rows (up to 8 rows).
+template <int D, int R, int W, int RG, int JJ, int RT = 1>
 struct WgLds {
-    using C = Cfg<D, R>;
+    using C = Cfg<D, R, RT>;
     static constexpr int WPG = W / RG;
-    static constexpr int P2 = WPG >= 8 ? 8 : WPG >= 4 ? 4 : WPG >= 2 ? 2 : 1;
-    static_assert(WPG < 16, "power-of-two fold");
-    static constexpr int SLOTS = (P2 / 2 > WPG - P2 ? P2 / 2 : WPG - P2) > 0 ? (P2 / 2 > WPG - P2 ? P2 / 2 : WPG - P2) : 1;
-    static constexpr int COMB_BYTES = RG * SLOTS * 16 * D * 4;
-    static constexpr int MAIN_BYTES = W * C::WAVE_BYTES > COMB_BYTES ? W * C::WAVE_BYTES : COMB_BYTES;
-    static constexpr int Q_OFF = MAIN_BYTES;
-    static constexpr int ML_OFF = Q_OFF + RG * C::Q_BYTES;
-    // one row group: the workgroup's chunk list (page entries) and the index
-    // of the next chunk to hand out
-    static constexpr int LIST = 256;
-    static constexpr int LIST_OFF = ML_OFF + W * 16 * 2 * 4;
     // up to 8 rows (JJ = 2): the waves' rows for the one-barrier combine, in
     // a region of their own so that a wave can store them while others still
     // stream
-    static constexpr bool SMALL_COMBINE = JJ == 2 && RG == 1;
-    static constexpr int CB_OFF = LIST_OFF + (RG == 1 ? (LIST + 4) * 4 : 0);
+    static constexpr bool SMALL_COMBINE = JJ == 2 && RG == 1 && RT == 1;
+    // otherwise every wave's sums of one row tile, [W][NT][64] float4, over
+    // the rings and q (dead by then)
+    static constexpr int COMB_BYTES = SMALL_COMBINE ? 0 : W * C::NT * 64 * 16;
+    static constexpr int Q_ALL = RG * RT * C::Q_BYTES;
+    static constexpr int MAIN_BYTES = W * C::WAVE_BYTES > COMB_BYTES - Q_ALL ? W * C::WAVE_BYTES : COMB_BYTES - Q_ALL;
+    static constexpr int Q_OFF = MAIN_BYTES;
+    static constexpr int ML_OFF = Q_OFF + Q_ALL;
+    // one row group: the workgroup's chunk list (page entries) and the index
+    // of the next chunk to hand out
+    static constexpr int LIST = 256;
+    static constexpr int LIST_OFF = ML_OFF + W * RT * 16 * 2 * 4;
+    // the partial index of every row of every tile (-1: no row there)
+    static constexpr int PS_OFF = LIST_OFF + (RG == 1 ? (LIST + 4) * 4 : 0);
+    static constexpr int CB_OFF = PS_OFF + RG * RT * 16 * 4;
     static constexpr int BYTES = CB_OFF + (SMALL_COMBINE ? W * 8 * D * 4 : 0);
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
@@ -175,10 +176,14 @@ __device__ inline void issue_vscales(const Land& L, const ChunkPtr& cp, int lane
 }
 
 template <int D, int R>
-struct WaveState {
-    floatx4 o[Cfg<D, R>::NT];   // unnormalized output, MFMA C layout
+struct TileState {
+    floatx4 o[Cfg<D, R>::NT];   // unnormalized output of the tile, MFMA C layout
     float m[4];                 // reference max of each of the lane's 4 rows
     float l[4];                 // this lane's share of the row sums
+};
+template <int D, int R, int RT = 1>
+struct WaveState {
+    TileState<D, R> t[RT];      // one per row tile
 };
 
 // S = (q_hi + q_lo) K^T for the chunk's two 16-token tiles.  MASK: some key
@@ -186,8 +191,8 @@ struct WaveState {
 // positions past ctx_len).  wait(p) runs before slice p's pieces are read,
 // done(p) after they have been read out of LDS.  q(i) gives q's operand i
 // (block i / 2, hi for even i, lo for odd).
-template <int D, int R, int JJ, bool MASK, class QSrc, class Wait, class Done>
-__device__ inline void qk_step(floatx4 (&s)[2], const Land& L, QSrc q, int lane,
+template <int D, int R, int JJ, int RT, bool MASK, class QSrc, class Wait, class Done>
+__device__ inline void qk_step(floatx4 (&s)[RT][2], const Land& L, QSrc q, int lane,
                                int j0, int first_last, int group, int rows, int rt0, Wait wait, Done done) {
     using C = Cfg<D, R>;
     const int g4 = lane >> 4;
@@ -202,8 +207,27 @@ __device__ inline void qk_step(floatx4 (&s)[2], const Land& L, QSrc q, int lane,
         for (int w = 0; w < C::NB / 2; ++w) ksw[tt][w] = src[w];
     }
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) s[tt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) s[rt][tt] = floatx4{0.f, 0.f, 0.f, 0.f};
     u32x4 kr[2];
+    // The products are scaled by the K scales and added to s in the block
+    // that made them (several row tiles: the other tiles' MFMAs cover the
+    // latency) or one block later (one tile), and pinned there: left alone,
+    // the compiler sinks every scaling to the end and keeps all the blocks'
+    // raw products live, 64 VGPRs per row tile at head_dim 256.
+    constexpr bool LAG = RT == 1;
+    floatx4 cp[RT][2];
+    float kscp[2];
+    auto fold = [&]() {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                s[rt][tt] += kscp[tt] * cp[rt][tt];
+                asm volatile("" :: "v"(s[rt][tt]));
+            }
+    };
 #pragma unroll
     for (int b = 0; b < C::NB; ++b) {
         if ((b & 1) == 0) {
@@ -222,40 +246,63 @@ __device__ inline void qk_step(floatx4 (&s)[2], const Land& L, QSrc q, int lane,
             const half2v sw = as_h2(ksw[tt][b / 2]);
             ksc[tt] = (b & 1) ? (float)sw.y : (float)sw.x;
         }
-        const half8 qh = q(2 * b);
+        // the converted codes serve every row tile of the wave
+        floatx4 c[RT][2];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const half8 qh = q(rt, 2 * b);
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+                c[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh, kb[tt], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        }
+        if constexpr (JJ == 4) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const half8 ql = q(rt, 2 * b + 1);
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+                    c[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql, kb[tt], c[rt][tt], 0, 0, 0);
+            }
+        }
+        if (LAG && b > 0) fold();
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-            floatx4 c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh, kb[tt], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-            if constexpr (JJ == 4) c = __builtin_amdgcn_mfma_f32_16x16x32_f16(q(2 * b + 1), kb[tt], c, 0, 0, 0);
-            s[tt] += ksc[tt] * c;
+            kscp[tt] = ksc[tt];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) cp[rt][tt] = c[rt][tt];
         }
+        if (!LAG) fold();
         SCHED_FENCE();
     }
+    if (LAG) fold();
     // up to 8 rows the lo halves' products sit two rows down: fold them in
     if constexpr (JJ == 2) {
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-            s[tt][0] += s[tt][2];
-            s[tt][1] += s[tt][3];
+            s[0][tt][0] += s[0][tt][2];
+            s[0][tt][1] += s[0][tt][3];
         }
     }
     // causal / tail mask: key j visible to row r iff j <= first_last + r / group
     // (group is huge when every row sees all keys)
     if (MASK) {
 #pragma unroll
-        for (int jj = 0; jj < JJ; ++jj) {
-            const int row = logical_row<JJ>(rt0, 4 * g4 + jj);
-            const int last = row >= 0 && row < rows ? first_last + row / group : -1;
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-                if (j0 + tt * kTile + n16 > last) s[tt][jj] = -INFINITY;
-        }
+            for (int jj = 0; jj < JJ; ++jj) {
+                const int row = logical_row<JJ>(rt0 + rt, 4 * g4 + jj);
+                const int last = row >= 0 && row < rows ? first_last + row / group : -1;
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+                    if (j0 + tt * kTile + n16 > last) s[rt][tt][jj] = -INFINITY;
+            }
     }
 }
 
-// Online softmax over the chunk's scores; writes P to the wave's LDS buffer.
+// Online softmax over the chunk's scores of row tile rt; writes P to the
+// tile's LDS buffer.
 template <int D, int R, int JJ>
-__device__ inline void softmax_step(WaveState<D, R>& st, floatx4 (&s)[2], float* __restrict__ plds, int lane) {
+__device__ inline void softmax_step(TileState<D, R>& st, floatx4 (&s)[2], float* __restrict__ plds, int lane) {
     using C = Cfg<D, R>;
     const int g4 = lane >> 4;
     const int n16 = lane & 15;
@@ -263,7 +310,7 @@ __device__ inline void softmax_step(WaveState<D, R>& st, floatx4 (&s)[2], float*
     bool grow = false;
 #pragma unroll
     for (int jj = 0; jj < JJ; ++jj) {
-        mnew[jj] = row16_max(fmaxf(s[0][jj], s[1][jj]));
+        mnew[jj] = row16_max(max2(s[0][jj], s[1][jj]));
         grow |= mnew[jj] > st.m[jj] + kTau;
     }
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
@@ -295,19 +342,20 @@ __device__ inline void softmax_step(WaveState<D, R>& st, floatx4 (&s)[2], float*
 
 // O += (P * vscale) Vcodes for the chunk.  wait(u) / done(u) around the
 // read of V slice u.
-template <int D, int R, bool MASK, class Wait, class Done>
-__device__ inline void pv_step(WaveState<D, R>& st, const Land& L, const float* __restrict__ plds, int lane,
+template <int D, int R, int RT, bool MASK, class Wait, class Done>
+__device__ inline void pv_step(WaveState<D, R, RT>& st, const Land& L, const float* __restrict__ plds, int lane,
                                Wait wait, Done done) {
-    using C = Cfg<D, R>;
+    using C = Cfg<D, R, RT>;
     const int g4 = lane >> 4;
     const int n16 = lane & 15;
     uint32_t magic = 0x64006400u;
     asm volatile("" : "+v"(magic));          // keep the constant in a VGPR
-    float pf[8];
-    {
-        const float* prow = plds + n16 * kPStride + 8 * g4;
+    float pf[RT][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pf[i] = prow[i];
+    for (int rt = 0; rt < RT; ++rt) {
+        const float* prow = plds + rt * (C::PBUF / 4) + n16 * kPStride + 8 * g4;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pf[rt][i] = prow[i];
     }
     u32x4 vr;
 #pragma unroll
@@ -321,23 +369,28 @@ __device__ inline void pv_step(WaveState<D, R>& st, const Land& L, const float* 
         // V scales of the lane's 8 tokens (8*g4 .. 8*g4+7) for block b
         const half8 sc = *reinterpret_cast<const half8*>(L.vs + (b * kChunk + 8 * g4) * 2);
         // P' = p * vscale: one fused fp32 multiply rounded once to fp16
-        half8 a;
+        half8 a[RT];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            float x0 = fmaf(pf[k], (float)sc[k], 0.0f);
-            float x1 = fmaf(pf[k + 4], (float)sc[k + 4], 0.0f);
-            if (MASK) {             // masked keys may hold unwritten scales
-                x0 = pf[k] == 0.0f ? 0.0f : x0;
-                x1 = pf[k + 4] == 0.0f ? 0.0f : x1;
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                float x0 = fmaf(pf[rt][k], (float)sc[k], 0.0f);
+                float x1 = fmaf(pf[rt][k + 4], (float)sc[k + 4], 0.0f);
+                if (MASK) {             // masked keys may hold unwritten scales
+                    x0 = pf[rt][k] == 0.0f ? 0.0f : x0;
+                    x1 = pf[rt][k + 4] == 0.0f ? 0.0f : x1;
+                }
+                a[rt][2 * k] = (_Float16)x0;
+                a[rt][2 * k + 1] = (_Float16)x1;
             }
-            a[2 * k] = (_Float16)x0;
-            a[2 * k + 1] = (_Float16)x1;
-        }
+        // the converted V codes serve every row tile of the wave
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int nt = 2 * b + h;
             const half8 bv = v_codes_to_half(vr[nt % 4], magic);
-            st.o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bv, st.o[nt], 0, 0, 0);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                st.t[rt].o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[rt], bv, st.t[rt].o[nt], 0, 0, 0);
         }
         SCHED_FENCE();
     }
@@ -455,15 +508,17 @@ __device__ inline void new_row_partials(const AttnArgs& a, const NewRows& nr, in
     }
 }
 
-template <int D, int JJ, int RG, int R, int W, class Batch, bool NEWR>
+template <int D, int JJ, int RG, int R, int W, int RT, class Batch, bool NEWR>
 __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, int cps, int n_splits, int group,
                                                                   int rows, Batch sb, NewRows nr, int part_stride) {
-    using C = Cfg<D, R>;
+    using C = Cfg<D, R, RT>;
     using WT = Waits<C::KL, R>;
-    using WL = WgLds<D, R, W, RG, JJ>;
-    // RG row groups of 16 rows; the WPG waves of group gi share its rows and
-    // deal its chunks among themselves.  Every group streams the same
-    // chunks, so a chunk read by a second group mostly comes from L2.
+    using WL = WgLds<D, R, W, RG, JJ, RT>;
+    // RG row groups of 16 RT rows; the WPG waves of group gi share its rows
+    // and deal its chunks among themselves.  Every group streams the same
+    // chunks, so a chunk read by a second group mostly comes from L2.  A wave
+    // holds RT row tiles of 16 rows: it converts every code of its chunks
+    // once and feeds the result to the MFMAs of all its tiles.
     constexpr int WPG = W / RG;
     // the cache is read once: non-temporal loads, except where several row
     // groups read each chunk and the later ones hit in L2
@@ -499,7 +554,7 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
     uint8_t* wbase = smem + wave * C::WAVE_BYTES;
     const Land land = {wbase, wbase + C::RING, wbase + C::RING + C::LAND_KS};
     float* plds = reinterpret_cast<float*>(wbase + C::RING + C::LAND_KS + C::LAND_VS);
-    float* mls = reinterpret_cast<float*>(smem + WL::ML_OFF);        // [wave][16][2]
+    float* mls = reinterpret_cast<float*>(smem + WL::ML_OFF);        // [wave][RT][16][2]
 
     // ---- this wave's chunks: wave g of a row group takes the group's chunks
     // g, g + N, g + 2N, ... (N waves per group and KV head), so all waves
@@ -547,19 +602,37 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
     // group's waves take the blocks round-robin.  The loads go out before the
     // page-table gather, so both arrive in one round trip.
     const float qscale = a.scale * kLog2e;
-    const uint8_t* qlds = smem + WL::Q_OFF + gi * C::Q_BYTES;
+    const uint8_t* qlds = smem + WL::Q_OFF + gi * RT * C::Q_BYTES;   // tile rt at + rt * Q_BYTES
     constexpr int QB = (C::NB + WPG - 1) / WPG;      // blocks per wave
-    float qv[QB][8];
-    const int q_row = logical_row<JJ>(gi, lane & 15);
-    const bool q_ok = q_row >= 0 && q_row < rows;
-    {
-        const int qi = q_ok ? q_row / group : 0, h = kvh * group + (q_ok ? q_row % group : 0);
+    float qv[RT][QB][8];
+    bool q_ok[RT];
+    if constexpr (RT == 1) {
+        // (straight-line for one tile: the loop form below, even of one
+        // trip, made the register allocator spill the decode kernel)
+        const int q_row = logical_row<JJ>(gi, lane & 15);
+        q_ok[0] = q_row >= 0 && q_row < rows;
+        const bool ok = q_ok[0];
+        const int qi = ok ? q_row / group : 0, h = kvh * group + (ok ? q_row % group : 0);
         const float* src = a.q + ((size_t)qi * a.n_heads + h) * D + 8 * (lane >> 4);
 #pragma unroll
         for (int i = 0; i < QB; ++i) {
             const int b = wig + i * WPG < C::NB ? wig + i * WPG : 0;   // waves with no block left reload block 0
 #pragma unroll
-            for (int e = 0; e < 8; ++e) qv[i][e] = src[b * kBlock + e];   // rows past the end read row 0
+            for (int e = 0; e < 8; ++e) qv[0][i][e] = src[b * kBlock + e];   // rows past the end read row 0
+        }
+    } else {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int q_row = logical_row<JJ>(gi * RT + rt, lane & 15);
+            q_ok[rt] = q_row >= 0 && q_row < rows;
+            const int qi = q_ok[rt] ? q_row / group : 0, h = kvh * group + (q_ok[rt] ? q_row % group : 0);
+            const float* src = a.q + ((size_t)qi * a.n_heads + h) * D + 8 * (lane >> 4);
+#pragma unroll
+            for (int i = 0; i < QB; ++i) {
+                const int b = wig + i * WPG < C::NB ? wig + i * WPG : 0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qv[rt][i][e] = src[b * kBlock + e];
+            }
         }
     }
 
@@ -595,17 +668,19 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
 
     // q into LDS (hi + lo fp16 halves; rows past the end are zero)
 #pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
     for (int i = 0; i < QB; ++i) {
         const int b = wig + i * WPG;
         if (b >= C::NB) break;
         half8 hi, lo;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float x = q_ok ? qv[i][e] * qscale : 0.0f;
+            const float x = q_ok[rt] ? qv[rt][i][e] * qscale : 0.0f;
             hi[e] = (_Float16)x;
             lo[e] = (_Float16)(x - (float)hi[e]);
         }
-        uint8_t* dst = smem + WL::Q_OFF + gi * C::Q_BYTES + (2 * b) * 1024 + lane * 16;
+        uint8_t* dst = smem + WL::Q_OFF + (gi * RT + rt) * C::Q_BYTES + (2 * b) * 1024 + lane * 16;
         if constexpr (JJ == 2) {
             // up to 8 rows one operand holds both halves: the lo half of MFMA
             // row n goes to row n + 2, a row no query uses (same k group)
@@ -628,9 +703,9 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
 #pragma unroll
         for (int i = 0; i < C::NB; ++i) qreg[i] = *reinterpret_cast<const half8*>(qlds + (2 * i) * 1024 + lane * 16);
     }
-    auto qop = [&](int i) -> half8 {
-        if constexpr (QREG) return qreg[i / 2];
-        else return *reinterpret_cast<const half8*>(qlds + i * 1024 + lane * 16);
+    auto qop = [&](int rt, int i) -> half8 {
+        if constexpr (QREG) return qreg[i / 2];       // (one row tile)
+        else return *reinterpret_cast<const half8*>(qlds + rt * C::Q_BYTES + i * 1024 + lane * 16);
     };
     // fused decode step: appended row j is handled by the last wave of split
     // n_splits - 1 - j of each KV head -- the last splits hold the fewest
@@ -642,11 +717,14 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
                 new_row_partials<D>(a, nr, kvh, group, rows, j, part_stride, n_splits + j, lane);
     }
 
-    WaveState<D, R> st;
+    WaveState<D, R, RT> st;
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) { st.m[jj] = -INFINITY; st.l[jj] = 0.0f; }
+    for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
-    for (int nt = 0; nt < C::NT; ++nt) st.o[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int jj = 0; jj < 4; ++jj) { st.t[rt].m[jj] = -INFINITY; st.t[rt].l[jj] = 0.0f; }
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt) st.t[rt].o[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
 
     // ---- stream.  A page-table entry outside the pool stops the wave
     // (nothing is loaded from it) and turns its partial into NaN.
@@ -713,12 +791,13 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
             lds_fence();
             refill(2 * C::KL + u);
         };
-        floatx4 s[2];
-        qk_step<D, R, JJ, MASK>(s, land, qop, lane, j0, first_last, mask_group, rows, gi, qk_wait, qk_done);
+        floatx4 s[RT][2];
+        qk_step<D, R, JJ, RT, MASK>(s, land, qop, lane, j0, first_last, mask_group, rows, gi * RT, qk_wait, qk_done);
         lds_fence();                            // K scales read out
         if (more) issue_kscales<D, R, POL>(land, np, lane);
-        softmax_step<D, R, JJ>(st, s, plds, lane);
-        pv_step<D, R, MASK>(st, land, plds, lane, pv_wait, pv_done);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) softmax_step<D, R, JJ>(st.t[rt], s[rt], plds + rt * (C::PBUF / 4), lane);
+        pv_step<D, R, RT, MASK>(st, land, plds, lane, pv_wait, pv_done);
         lds_fence();                            // V scales read out
         if (more) issue_vscales<D, R, POL>(land, np, lane);
         if (has_next && !ok_next) bad = true;
@@ -737,10 +816,12 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
     // ---- finish the row sums, combine the group's waves in a fixed order
     const int g4 = lane >> 4, n16 = lane & 15;
 #pragma unroll
-    for (int jj = 0; jj < JJ; ++jj) {
-        st.l[jj] = row16_sum(st.l[jj]) * 16.0f;        // weights carried 2^-kTau
-        if (bad) { st.m[jj] = NAN; st.l[jj] = NAN; }
-    }
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int jj = 0; jj < JJ; ++jj) {
+            st.t[rt].l[jj] = row16_sum(st.t[rt].l[jj]) * 16.0f;        // weights carried 2^-kTau
+            if (bad) { st.t[rt].m[jj] = NAN; st.t[rt].l[jj] = NAN; }
+        }
     if constexpr (WL::SMALL_COMBINE) {
         // At most 8 rows: every wave stores its unscaled rows ([wave][row
         // slot][dim], row slot = 4 jj + g4) and their (m, l) ([row slot][wave]);
@@ -752,13 +833,13 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
 #pragma unroll
         for (int nt = 0; nt < C::NT; ++nt)
 #pragma unroll
-            for (int jj = 0; jj < JJ; ++jj) cb[wave * SLOTW + (4 * jj + g4) * D + 16 * nt + n16] = st.o[nt][jj];
+            for (int jj = 0; jj < JJ; ++jj) cb[wave * SLOTW + (4 * jj + g4) * D + 16 * nt + n16] = st.t[0].o[nt][jj];
         if (n16 == 0) {
 #pragma unroll
             for (int jj = 0; jj < JJ; ++jj) {
                 float* d = mls + ((4 * jj + g4) * W + wave) * 2;
-                d[0] = st.m[jj];
-                d[1] = st.l[jj];
+                d[0] = st.t[0].m[jj];
+                d[1] = st.t[0].l[jj];
             }
         }
         __syncthreads();
@@ -795,82 +876,85 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
         }
         return;
     }
+    // 16-row tiles: every wave's (m, l) per row of each tile; then per tile
+    // each wave scales its sums to the group's maximum and stores them
+    // ([wave][nt][lane] float4: the MFMA layout, conflict-free), and after a
+    // barrier all threads of the workgroup sum the group's waves in wave
+    // order and write the partial.  The buffer covers the rings and q, which
+    // are dead once every wave has left its loop (the first barrier).
 #pragma unroll
-    for (int jj = 0; jj < JJ; ++jj) {
-        if (n16 == 0) {
-            const int row = 4 * g4 + jj;
-            mls[(wave * 16 + row) * 2 + 0] = st.m[jj];
-            mls[(wave * 16 + row) * 2 + 1] = st.l[jj];
-        }
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int jj = 0; jj < JJ; ++jj)
+            if (n16 == 0) {
+                float* d = mls + ((wave * RT + rt) * 16 + 4 * g4 + jj) * 2;
+                d[0] = st.t[rt].m[jj];
+                d[1] = st.t[rt].l[jj];
+            }
+    int* const pst = reinterpret_cast<int*>(smem + WL::PS_OFF);      // [RG * RT tiles][16 rows]
+    if (threadIdx.x < RG * RT * 16) {
+        const int lrow = logical_row<JJ>(threadIdx.x / 16, threadIdx.x % 16);
+        pst[threadIdx.x] = lrow >= 0 && lrow < rows
+                               ? ((lrow / group) * a.n_heads + kvh * group + lrow % group) * part_stride + split
+                               : -1;
     }
-    __syncthreads();                       // every wave is done with its landing zone
-    float M[4], Ltot[4];
+    __syncthreads();
+    floatx4* const cb = reinterpret_cast<floatx4*>(smem);          // [W][NT][64]
 #pragma unroll
-    for (int jj = 0; jj < JJ; ++jj) {
-        const int row = 4 * g4 + jj;
-        float mm = -INFINITY;
+    for (int rt = 0; rt < RT; ++rt) {
+        if (rt > 0) __syncthreads();                // the tile before has been read out
+        {
+            // lane L looks after row L % 16 of the tile and waves L / 16,
+            // L / 16 + 4, ... of the group: the group's maximum and weight
+            // sum of the row, and this wave's factor for it
+            const int r = lane & 15;
+            const float* mrow = mls + ((gi * WPG * RT + rt) * 16 + r) * 2;     // + wave-in-group * RT * 32
+            float mm = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < WPG; ++j) mm = fmaxf(mm, mls[((gi * WPG + j) * 16 + row) * 2]);
-        float lt = 0.0f;
+            for (int j = g4; j < WPG; j += 4) mm = fmaxf(mm, mrow[j * RT * 32]);
+            mm = fmaxf(mm, xor16_f(mm, lane));
+            mm = fmaxf(mm, xor32_f(mm, lane));
+            float lt = 0.0f;
 #pragma unroll
-        for (int j = 0; j < WPG; ++j) {
-            const int w = gi * WPG + j;
-            const float mw = mls[(w * 16 + row) * 2], lw = mls[(w * 16 + row) * 2 + 1];
-            lt += lw == 0.0f ? 0.0f : lw * exp2f(mw - mm);
-        }
-        M[jj] = mm;
-        Ltot[jj] = lt;
-        const float f = st.l[jj] == 0.0f ? 0.0f : exp2f(st.m[jj] - mm);
+            for (int j = g4; j < WPG; j += 4) {
+                const float mw = mrow[j * RT * 32], lw = mrow[j * RT * 32 + 1];
+                // NaN (a bad page) propagates; a wave without keys adds nothing
+                lt += lw == 0.0f ? 0.0f : lw * fast_exp2(mw - mm);
+            }
+            lt += xor16_f(lt, lane);
+            lt += xor32_f(lt, lane);
+            const float ms = mrow[wig * RT * 32], ls = mrow[wig * RT * 32 + 1];
+            const float fr = ls == 0.0f ? 0.0f : fast_exp2(ms - mm);
+            // lane (g4, n16) holds rows 4 g4 + jj: their factors sit in lanes 4 g4 + jj
 #pragma unroll
-        for (int nt = 0; nt < C::NT; ++nt) st.o[nt][jj] *= f;
-    }
-    float* ob = reinterpret_cast<float*>(smem);          // [RG * SLOTS][16][D]
-    auto put = [&](int slot) {
+            for (int jj = 0; jj < JJ; ++jj) {
+                const float f = __shfl(fr, 4 * g4 + jj);
 #pragma unroll
-        for (int nt = 0; nt < C::NT; ++nt)
-#pragma unroll
-            for (int jj = 0; jj < JJ; ++jj)
-                ob[((size_t)slot * 16 + 4 * g4 + jj) * D + 16 * nt + n16] = st.o[nt][jj];
-    };
-    auto add = [&](int slot) {
-#pragma unroll
-        for (int nt = 0; nt < C::NT; ++nt)
-#pragma unroll
-            for (int jj = 0; jj < JJ; ++jj)
-                st.o[nt][jj] += ob[((size_t)slot * 16 + 4 * g4 + jj) * D + 16 * nt + n16];
-    };
-    // inside each row group: waves [P2, WPG) first hand their sums to waves
-    // [0, WPG - P2), then waves [h, 2h) to waves [0, h) for h = P2/2 .. 1;
-    // group gi uses buffer slots gi*SLOTS .. (gi+1)*SLOTS - 1
-    constexpr int P2 = WL::P2;
-    if constexpr (WPG > P2) {
-        if (wig >= P2) put(gi * WL::SLOTS + wig - P2);
-        __syncthreads();
-        if (wig < WPG - P2) add(gi * WL::SLOTS + wig);
-        __syncthreads();
-    }
-#pragma unroll
-    for (int h = P2 / 2; h >= 1; h /= 2) {
-        if (wig >= h && wig < 2 * h) put(gi * WL::SLOTS + wig - h);
-        __syncthreads();
-        if (wig < h) add(gi * WL::SLOTS + wig);
-        __syncthreads();
-    }
-    if (wig != 0) return;
-
-    // ---- write the partial of each row this row group serves
-#pragma unroll
-    for (int jj = 0; jj < JJ; ++jj) {
-        const int row = logical_row<JJ>(gi, 4 * g4 + jj);
-        if (row < 0 || row >= rows) continue;
-        const int qi = row / group, h = kvh * group + row % group;
-        const size_t ps = ((size_t)qi * a.n_heads + h) * part_stride + split;
-        if (n16 == 0) {
-            a.ws_m[ps] = M[jj];
-            a.ws_l[ps] = Ltot[jj];
+                for (int nt = 0; nt < C::NT; ++nt) st.t[rt].o[nt][jj] *= f;
+            }
+            // (m, l) of the partial: the group's first wave
+            const int ps = pst[(gi * RT + rt) * 16 + r];
+            if (wig == 0 && lane < 16 && ps >= 0) {
+                a.ws_m[ps] = mm;
+                a.ws_l[ps] = lt;
+            }
         }
 #pragma unroll
-        for (int nt = 0; nt < C::NT; ++nt) a.ws_acc[ps * D + 16 * nt + n16] = st.o[nt][jj];
+        for (int nt = 0; nt < C::NT; ++nt) cb[(wave * C::NT + nt) * 64 + lane] = st.t[rt].o[nt];
+        __syncthreads();
+        // element e = (group, nt, lane of the MFMA layout): rows 4 (lane / 16)
+        // + jj of the group's tile rt, column 16 nt + lane % 16
+        for (int e = threadIdx.x; e < RG * C::NT * 64; e += W * 64) {
+            const int eg = e / (C::NT * 64), ent = (e / 64) % C::NT, el = e % 64;
+            floatx4 acc = cb[((eg * WPG) * C::NT + ent) * 64 + el];
+#pragma unroll
+            for (int j = 1; j < WPG; ++j) acc += cb[((eg * WPG + j) * C::NT + ent) * 64 + el];
+#pragma unroll
+            for (int jj = 0; jj < JJ; ++jj) {
+                const int ps = pst[(eg * RT + rt) * 16 + 4 * (el >> 4) + jj];
+                if (ps >= 0) a.ws_acc[(size_t)ps * D + 16 * ent + (el & 15)] = acc[jj];
+            }
+        }
     }
 }
 
@@ -880,15 +964,15 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
 template <int JJ>
 constexpr int stream_waves() { return 8; }
 
-template <int D, int JJ, int RG, bool NEWR, class Batch>
+template <int D, int JJ, int RG, int RT, bool NEWR, class Batch>
 hipError_t launch_dr(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream, const Batch& sb, int n_wg,
                      const NewRows& nr, int part_stride) {
-    constexpr int R = stream_ring_slots(D);             // ring slots: a few KiB in flight per wave
+    constexpr int R = stream_ring_slots(D, RT == 2 && RG == 1);   // ring slots: a few KiB in flight per wave
     constexpr int W = stream_waves<JJ>();
-    using WL = WgLds<D, R, W, RG, JJ>;
-    auto kern = attn_mfma_stream_kernel<D, JJ, RG, R, W, Batch, NEWR>;
+    using WL = WgLds<D, R, W, RG, JJ, RT>;
+    auto kern = attn_mfma_stream_kernel<D, JJ, RG, R, W, RT, Batch, NEWR>;
     if (WL::BYTES > 64 * 1024) {
-        hipError_t e = allow_lds<attn_mfma_stream_kernel<D, JJ, RG, R, W, Batch, NEWR>>(WL::BYTES);
+        hipError_t e = allow_lds<attn_mfma_stream_kernel<D, JJ, RG, R, W, RT, Batch, NEWR>>(WL::BYTES);
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kern, dim3(n_wg), dim3(W * 64), WL::BYTES, stream, a, pl.chunks_per_split, pl.n_splits,
@@ -897,14 +981,15 @@ hipError_t launch_dr(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream, 
 }
 
 // Up to 8 rows two per lane group (JJ = 2), up to 16 rows one per MFMA row,
-// more rows in 2 or 4 row groups of 16.
+// up to 32 rows two row tiles per wave (every code converted once for both),
+// more rows in 2 row groups of two tiles.
 template <int D, bool NEWR, class Batch>
 hipError_t launch_d(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream, const Batch& sb, int n_wg,
                     const NewRows& nr, int part_stride) {
-    if (pl.rows <= 8) return launch_dr<D, 2, 1, NEWR>(a, pl, stream, sb, n_wg, nr, part_stride);
-    if (pl.rows <= 16) return launch_dr<D, 4, 1, NEWR>(a, pl, stream, sb, n_wg, nr, part_stride);
-    if (pl.rows <= 32) return launch_dr<D, 4, 2, NEWR>(a, pl, stream, sb, n_wg, nr, part_stride);
-    if (pl.rows <= 64) return launch_dr<D, 4, 4, NEWR>(a, pl, stream, sb, n_wg, nr, part_stride);
+    if (pl.rows <= 8) return launch_dr<D, 2, 1, 1, NEWR>(a, pl, stream, sb, n_wg, nr, part_stride);
+    if (pl.rows <= 16) return launch_dr<D, 4, 1, 1, NEWR>(a, pl, stream, sb, n_wg, nr, part_stride);
+    if (pl.rows <= 32) return launch_dr<D, 4, 1, 2, NEWR>(a, pl, stream, sb, n_wg, nr, part_stride);
+    if (pl.rows <= 64) return launch_dr<D, 4, 2, 2, NEWR>(a, pl, stream, sb, n_wg, nr, part_stride);
     return hipErrorInvalidValue;
 }
 
@@ -921,7 +1006,7 @@ hipError_t launch_any(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream,
 
 }  // namespace
 
-int mfma_stream_row_groups(int rows) { return rows <= 16 ? 1 : rows <= 32 ? 2 : 4; }
+int mfma_stream_row_groups(int rows) { return rows <= 32 ? 1 : 2; }
 int mfma_stream_waves(int rows) {
     return (rows <= 8 ? stream_waves<2>() : stream_waves<4>()) / mfma_stream_row_groups(rows);
 }

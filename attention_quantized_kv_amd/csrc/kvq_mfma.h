@@ -58,6 +58,15 @@ KVQ_MAX_DPP(ror4)
 KVQ_MAX_DPP(swap2)
 KVQ_MAX_DPP(swap1)
 
+// max(a, b) as one v_max_f32: fmaxf adds a NaN-quieting max per operand
+// whenever the compiler cannot prove the operands canonical (values that
+// reach the softmax from another basic block, here)
+__device__ inline float max2(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 // Reductions over the 16 lanes of a DPP row (rotate by 8, by 4, then swap
 // pairs inside quads): every lane ends with the row's result.
 __device__ inline float row16_max(float x) {

@@ -7,8 +7,12 @@
 namespace kvq {
 
 // Ring slots of the streaming kernel per head_dim: a few KiB in flight per
-// wave (the slots must divide the 3 * D / 64 code pieces of a chunk).
-constexpr int stream_ring_slots(int D) { return D == 256 ? 4 : 3; }
+// wave (the slots must divide the 3 * D / 64 code pieces of a chunk).  DEEP:
+// a wave with two row tiles spends about twice as long on each piece, so it
+// asks for its pieces further ahead (where the LDS holds one row group's q).
+constexpr int stream_ring_slots(int D, bool deep = false) {
+    return D == 256 ? (deep ? 6 : 4) : D == 128 ? (deep ? 6 : 3) : 3;
+}
 
 // Wait counts.  Per chunk a wave issues its requests in a fixed order: the
 // QK step consumes code pieces 2p, 2p+1 (slice p, both tiles) and requests

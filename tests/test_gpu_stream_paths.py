@@ -1,12 +1,12 @@
 """GPU: the streaming MFMA kernel's fixed-order chunk path against the oracle.
 
 The kernel hands a workgroup's chunks to its waves in two ways.  With one row
-group (at most 16 query rows per KV head) and at most 256 chunks per
-workgroup, the chunks form a list in LDS that waves pop as they go.  With
-several row groups (17-64 rows: verify batches), or more than 256 chunks per
-workgroup, every wave walks a fixed round-robin order instead and picks its
-page-table entries out of a register that holds the next 64 of them,
-reloading it every 64 chunks.  These cases force that path with one split
+group (at most 32 query rows per KV head: a wave holds one 16-row tile, or
+two for 17-32 rows) and at most 256 chunks per workgroup, the chunks form a
+list in LDS that waves pop as they go.  With two row groups (33-64 rows), or
+more than 256 chunks per workgroup, every wave walks a fixed round-robin
+order instead and picks its page-table entries out of a register that holds
+the next 64 of them, reloading it every 64 chunks.  These cases force that path with one split
 (chunks_per_split large), so each wave walks more than 128 chunks and the
 entries are reloaded at least twice, and check every output element against
 the fp64 oracle (|o - ref| <= 2e-3 + 1e-3 |ref|, lse within 1e-4 + 1e-5
@@ -34,12 +34,13 @@ def _case(seed, ctx, n_kv, D, perm=True):
 
 
 @pytest.mark.parametrize("n_q,G,ctx", [
-    (4, 6, 17000),     # 24 rows: two row groups of four waves, ~133 chunks per wave
-    (3, 8, 17000),     # 24 rows, the other grouping of heads
-    (8, 8, 9000),      # 64 rows: four row groups of two waves, ~141 chunks per wave
-    (2, 16, 12345),    # 32 rows, ragged tail page
+    (4, 6, 34000),     # 24 rows: one row group, two tiles per wave, ~133 chunks per wave
+    (3, 8, 34000),     # 24 rows, the other grouping of heads
+    (8, 8, 17000),     # 64 rows: two row groups of four waves, ~133 chunks per wave
+    (2, 16, 34567),    # 32 rows, ragged tail page
+    (5, 8, 17000),     # 40 rows: the second group's second tile holds no row
 ])
-def test_row_groups_walk_more_than_128_chunks(n_q, G, ctx):
+def test_verify_rows_walk_more_than_64_chunks(n_q, G, ctx):
     n_kv, D = 2, 256
     c, rng = _case(1000 * n_q + G, ctx, n_kv, D)
     q = rng.standard_normal((n_q, n_kv * G, D)).astype(np.float32)
@@ -67,7 +68,7 @@ def test_one_row_group_with_more_than_256_chunks(D, G, ctx):
 
 
 @pytest.mark.parametrize("n_q,G,ctx,bad_page", [
-    (4, 6, 17000, 40),     # row groups: wave k of group 0 reaches page 40 at its chunk ~80
+    (4, 6, 34000, 80),     # two tiles per wave: page 80 at a wave's chunk ~80
     (1, 6, 40000, 120),    # one row group, fixed order: page 120 at a wave's chunk ~120
 ])
 def test_bad_page_after_the_first_64_entries(n_q, G, ctx, bad_page):
@@ -90,7 +91,7 @@ def test_bad_page_after_the_first_64_entries(n_q, G, ctx, bad_page):
     tu.assert_close(out, ref, lse, ref_lse, "restored table")
 
 
-def test_row_groups_with_several_splits_match_one_split():
+def test_verify_batch_with_several_splits_matches_one_split():
     """The same verify batch with the automatic plan (several splits, merged)
     and with one split: both match the oracle."""
     n_kv, D, n_q, G, ctx = 2, 256, 4, 6, 17000

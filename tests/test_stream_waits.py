@@ -2,7 +2,7 @@
 the CPU against a simulation of its request stream.
 
 Each wave of attn_mfma_stream.hip streams its chunks through a ring of R
-one-KiB slots with direct-to-LDS loads and, before it reads a piece out of
+one-KiB slots (R depends on head_dim, and is larger for waves with two row tiles) with direct-to-LDS loads and, before it reads a piece out of
 LDS, waits until at most N of its vector-memory requests are outstanding
 (requests complete in issue order).  N comes from the constexpr table
 Waits<KL, R> in csrc/kvq_waits.h.  A count that is too high would let a wave
@@ -26,20 +26,22 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "attention_quantized_kv_amd", "csrc", "kvq_waits.h")
 HEAD_DIMS = (64, 128, 256)
+DEEP = (0, 1)               # the deeper ring of waves with two row tiles
+CASES = [(D, deep) for D in HEAD_DIMS for deep in DEEP]
 
 
 def _table(tmp_path):
     src = tmp_path / "waits.cpp"
     src.write_text(f'#include "{HEADER}"\n#include <cstdio>\n' + r'''
-template <int D> void dump() {
-    constexpr int KL = D / 64, R = kvq::stream_ring_slots(D);
+template <int D, int DEEP> void dump() {
+    constexpr int KL = D / 64, R = kvq::stream_ring_slots(D, DEEP != 0);
     using W = kvq::Waits<KL, R>;
-    std::printf("%d %d", D, R);
+    std::printf("%d %d %d", D, DEEP, R);
     for (int p = 0; p < KL; ++p) std::printf(" %d", W::qk(p));
     for (int u = 0; u < KL; ++u) std::printf(" %d", W::pv(u));
     std::printf("\n");
 }
-int main() { dump<64>(); dump<128>(); dump<256>(); }
+int main() { dump<64, 0>(); dump<64, 1>(); dump<128, 0>(); dump<128, 1>(); dump<256, 0>(); dump<256, 1>(); }
 ''')
     exe = str(tmp_path / "waits")
     subprocess.run(["g++", "-std=c++17", "-O0", "-o", exe, str(src)], check=True, capture_output=True)
@@ -47,8 +49,8 @@ int main() { dump<64>(); dump<128>(); dump<256>(); }
     for line in subprocess.run([exe], check=True, capture_output=True, text=True).stdout.split("\n"):
         if line.strip():
             f = [int(x) for x in line.split()]
-            D, R, KL = f[0], f[1], f[0] // 64
-            out[D] = (R, f[2:2 + KL], f[2 + KL:2 + 2 * KL])
+            D, deep, R, KL = f[0], f[1], f[2], f[0] // 64
+            out[(D, deep)] = (R, f[3:3 + KL], f[3 + KL:3 + 2 * KL])
     return out
 
 
@@ -105,14 +107,14 @@ def simulate(KL, R, qk, pv, n_chunks):
 @pytest.mark.skipif(shutil.which("g++") is None, reason="g++ not found")
 def test_wait_counts_never_exceed_the_requests_issued_since(tmp_path):
     table = _table(tmp_path)
-    assert sorted(table) == list(HEAD_DIMS)
-    for D in HEAD_DIMS:
-        R, qk, pv = table[D]
+    assert sorted(table) == CASES
+    for D, deep in CASES:
+        R, qk, pv = table[(D, deep)]
         KL = D // 64
         assert (3 * KL) % R == 0 and R <= 3 * KL
         for n_chunks in range(1, 70):
             for what, count, margin in simulate(KL, R, qk, pv, n_chunks):
-                assert 0 <= count <= margin, f"D={D} R={R} {n_chunks} chunks, {what}: waits for {count} " \
+                assert 0 <= count <= margin, f"D={D} deep={deep} R={R} {n_chunks} chunks, {what}: waits for {count} " \
                                              f"but only {margin} requests follow the needed one"
 
 
@@ -122,11 +124,11 @@ def test_wait_counts_are_tight_in_the_steady_state(tmp_path):
     requests issued since the needed one (a smaller count would only cost
     time, not correctness)."""
     table = _table(tmp_path)
-    for D in HEAD_DIMS:
-        R, qk, pv = table[D]
+    for D, deep in CASES:
+        R, qk, pv = table[(D, deep)]
         for what, count, margin in simulate(D // 64, R, qk, pv, 8):
             if not what.startswith("chunk 7"):
-                assert count == margin, f"D={D}: {what} waits for {count}, {margin} follow"
+                assert count == margin, f"D={D} deep={deep}: {what} waits for {count}, {margin} follow"
 
 
 def test_simulation_catches_a_count_one_too_high():
