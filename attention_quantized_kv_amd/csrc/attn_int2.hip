@@ -352,12 +352,15 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
             }
         }
         // online softmax (lazy rescaling by kTau; weights 2^(s - m - kTau) <= 1)
-        float mnew[4];
+        // The row maxima only when some score of the wave passes its row's
+        // reference by more than kTau: a row's maximum does iff one of its
+        // scores does, so the test needs no cross-lane step.
+        float smax[4];
         bool grow = false;
 #pragma unroll
         for (int jj = 0; jj < JJ; ++jj) {
-            mnew[jj] = row16_max(max2(s[0][jj], s[1][jj]));
-            grow |= mnew[jj] > m[jj] + kTau;
+            smax[jj] = max2(s[0][jj], s[1][jj]);
+            grow |= smax[jj] > m[jj] + kTau;
         }
         if (__builtin_amdgcn_ballot_w64(grow) != 0) {
             // rows whose maximum did not move get alpha = 1: one straight pass
@@ -365,10 +368,11 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
             floatx4 alpha = {1.0f, 1.0f, 1.0f, 1.0f};
 #pragma unroll
             for (int jj = 0; jj < JJ; ++jj) {
-                const bool up = mnew[jj] > m[jj];
-                alpha[jj] = up ? fast_exp2(m[jj] - mnew[jj]) : 1.0f;
+                const float mnew = row16_max(smax[jj]);
+                const bool up = mnew > m[jj];
+                alpha[jj] = up ? fast_exp2(m[jj] - mnew) : 1.0f;
                 l[jj] *= alpha[jj];
-                m[jj] = up ? mnew[jj] : m[jj];
+                m[jj] = up ? mnew : m[jj];
             }
             if constexpr (JJ == 2) {             // the lo rows follow their rows
                 alpha[2] = alpha[0];

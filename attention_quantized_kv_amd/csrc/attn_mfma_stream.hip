@@ -306,12 +306,15 @@ __device__ inline void softmax_step(TileState<D, R>& st, floatx4 (&s)[2], float*
     using C = Cfg<D, R>;
     const int g4 = lane >> 4;
     const int n16 = lane & 15;
-    float mnew[4];
+    // The row maxima only when some score of the wave passes its row's
+    // reference by more than kTau: a row's maximum does iff one of its
+    // scores does, so the test needs no cross-lane step.
+    float smax[4];
     bool grow = false;
 #pragma unroll
     for (int jj = 0; jj < JJ; ++jj) {
-        mnew[jj] = row16_max(max2(s[0][jj], s[1][jj]));
-        grow |= mnew[jj] > st.m[jj] + kTau;
+        smax[jj] = max2(s[0][jj], s[1][jj]);
+        grow |= smax[jj] > st.m[jj] + kTau;
     }
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
         // rows whose maximum did not move get alpha = 1: one straight pass
@@ -319,10 +322,11 @@ __device__ inline void softmax_step(TileState<D, R>& st, floatx4 (&s)[2], float*
         floatx4 alpha = {1.0f, 1.0f, 1.0f, 1.0f};
 #pragma unroll
         for (int jj = 0; jj < JJ; ++jj) {
-            const bool up = mnew[jj] > st.m[jj];
-            alpha[jj] = up ? fast_exp2(st.m[jj] - mnew[jj]) : 1.0f;
+            const float mnew = row16_max(smax[jj]);
+            const bool up = mnew > st.m[jj];
+            alpha[jj] = up ? fast_exp2(st.m[jj] - mnew) : 1.0f;
             st.l[jj] *= alpha[jj];
-            st.m[jj] = up ? mnew[jj] : st.m[jj];
+            st.m[jj] = up ? mnew : st.m[jj];
         }
 #pragma unroll
         for (int nt = 0; nt < C::NT; ++nt) st.o[nt] *= alpha;

@@ -42,11 +42,13 @@ __device__ inline float dpp(float x) {
 // max(x, x of the lane that DPP control CTRL names), one v_max_f32_dpp (the
 // builtin route adds a move and a NaN-quieting max per step).  s_nop 1 covers
 // the two wait states a DPP read needs after the VALU write of its source.
+// Volatile: the compiler would otherwise hoist the reductions out of the
+// rarely taken branch that needs them.
 #define KVQ_MAX_DPP(CTRL)                                                                  \
     __device__ inline float max_dpp_##CTRL(float x) {                                     \
         float r;                                                                          \
-        asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 " KVQ_DPP_##CTRL " row_mask:0xf bank_mask:0xf" \
-            : "=v"(r) : "v"(x));                                                          \
+        asm volatile("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 " KVQ_DPP_##CTRL                 \
+                     " row_mask:0xf bank_mask:0xf" : "=v"(r) : "v"(x));                   \
         return r;                                                                         \
     }
 #define KVQ_DPP_ror8 "row_ror:8"
