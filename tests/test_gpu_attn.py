@@ -100,6 +100,8 @@ def test_tiny_workload(kernel):
 @pytest.mark.parametrize("D,G,ctx,n_q", [
     (64, 1, 1, 1), (64, 2, 255, 1), (128, 6, 256, 1), (256, 6, 257, 1), (256, 6, 1000, 4),
     (64, 8, 300, 8), (128, 2, 513, 3), (256, 1, 2049, 2), (64, 16, 97, 4),
+    (128, 6, 700, 3),       # 18 rows: a second row tile with 2 rows
+    (64, 11, 800, 3),       # 33 rows: a second row group with one row
 ])
 def test_decode_shapes(kernel, D, G, ctx, n_q):
     c, rng = _rand_case(D * 1000 + G * 10 + n_q, ctx, 2, D, P=64 if ctx < 600 else 256)

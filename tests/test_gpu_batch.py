@@ -3,9 +3,11 @@
 Several sequences share one page pool, each with its own page-table row
 (disjoint, shuffled pages) and context length; every sequence's output and
 lse must match the oracle run on that sequence alone.  Cases: ragged lengths
-from 8 to 20,000 keys (a single key in the largest batch), n_q = 1..8 (all
-four row layouts of the streaming kernel), the largest batch (64 sequences), and a page-table entry
-outside the pool in one sequence (that sequence NaN, the others exact).
+from 8 to 20,000 keys (a single key in the largest batch), n_q = 1..8 over
+every row layout of the streaming kernel (up to 8 rows, one 16-row tile, two
+tiles per wave -- full at 32 rows, half at 24 -- and two row groups at 48
+rows), the largest batch (64 sequences), and a page-table entry outside the
+pool in one sequence (that sequence NaN, the others exact).
 The same over the INT2 cache (its streaming kernel, up to 16 rows).
 """
 import math
@@ -67,7 +69,7 @@ def ragged():
     return Batch(91, [8, 97, 3000, 257, 20000, 64, 9], n_kv=2, D=128, P=64)
 
 
-@pytest.mark.parametrize("G,n_q", [(4, 1), (4, 2), (4, 4), (4, 8), (1, 1)])
+@pytest.mark.parametrize("G,n_q", [(4, 1), (4, 2), (4, 4), (4, 8), (6, 4), (8, 6), (1, 1)])
 def test_batch_matches_oracle_per_sequence(ragged, G, n_q):
     q, scale, out, lse = ragged.run(G, n_q)
     for b, c in enumerate(ragged.ctx_lens):
