@@ -99,31 +99,34 @@ struct Cfg {
 };
 
 // Workgroup LDS: W per-wave areas | q of each of the RG row groups (both
-// reused by the final combine) | (m, l) per wave, row tile and row | the
-// chunk list (one row group) | the small combine's rows (up to 8 rows).
+// reused by the final combine; up to 8 rows q's area grows to hold the small
+// combine's rows) | (m, l) per wave, row tile and row | the chunk list (one
+// row group) | the partial index of every row.
 template <int D, int R, int W, int RG, int JJ, int RT = 1>
 struct WgLds {
     using C = Cfg<D, R, RT>;
     static constexpr int WPG = W / RG;
     // up to 8 rows (JJ = 2): the waves' rows for the one-barrier combine, in
     // a region of their own so that a wave can store them while others still
-    // stream
+    // stream -- q's region, which is dead once every wave holds q in
+    // registers (a barrier after those reads)
     static constexpr bool SMALL_COMBINE = JJ == 2 && RG == 1 && RT == 1;
+    static constexpr int CB_BYTES = SMALL_COMBINE ? W * 8 * D * 4 : 0;
     // otherwise every wave's sums of one row tile, [W][NT][64] float4, over
     // the rings and q (dead by then)
     static constexpr int COMB_BYTES = SMALL_COMBINE ? 0 : W * C::NT * 64 * 16;
     static constexpr int Q_ALL = RG * RT * C::Q_BYTES;
     static constexpr int MAIN_BYTES = W * C::WAVE_BYTES > COMB_BYTES - Q_ALL ? W * C::WAVE_BYTES : COMB_BYTES - Q_ALL;
     static constexpr int Q_OFF = MAIN_BYTES;
-    static constexpr int ML_OFF = Q_OFF + Q_ALL;
+    static constexpr int CB_OFF = Q_OFF;
+    static constexpr int ML_OFF = Q_OFF + (CB_BYTES > Q_ALL ? CB_BYTES : Q_ALL);
     // one row group: the workgroup's chunk list (page entries) and the index
     // of the next chunk to hand out
     static constexpr int LIST = 256;
     static constexpr int LIST_OFF = ML_OFF + W * RT * 16 * 2 * 4;
     // the partial index of every row of every tile (-1: no row there)
     static constexpr int PS_OFF = LIST_OFF + (RG == 1 ? (LIST + 4) * 4 : 0);
-    static constexpr int CB_OFF = PS_OFF + RG * RT * 16 * 4;
-    static constexpr int BYTES = CB_OFF + (SMALL_COMBINE ? W * 8 * D * 4 : 0);
+    static constexpr int BYTES = PS_OFF + RG * RT * 16 * 4;
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -706,6 +709,8 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
     if constexpr (QREG) {
 #pragma unroll
         for (int i = 0; i < C::NB; ++i) qreg[i] = *reinterpret_cast<const half8*>(qlds + (2 * i) * 1024 + lane * 16);
+        static_assert(!QREG || WL::SMALL_COMBINE, "the small combine reuses q's LDS");
+        lds_barrier();                         // every wave holds q: its LDS is free for the small combine
     }
     auto qop = [&](int rt, int i) -> half8 {
         if constexpr (QREG) return qreg[i / 2];       // (one row tile)
@@ -971,7 +976,7 @@ constexpr int stream_waves() { return 8; }
 template <int D, int JJ, int RG, int RT, bool NEWR, class Batch>
 hipError_t launch_dr(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream, const Batch& sb, int n_wg,
                      const NewRows& nr, int part_stride) {
-    constexpr int R = stream_ring_slots(D, RT == 2 && RG == 1);   // ring slots: a few KiB in flight per wave
+    constexpr int R = stream_ring_slots(D, JJ == 2 || (RT == 2 && RG == 1));   // ring slots: a few KiB in flight per wave
     constexpr int W = stream_waves<JJ>();
     using WL = WgLds<D, R, W, RG, JJ, RT>;
     auto kern = attn_mfma_stream_kernel<D, JJ, RG, R, W, RT, Batch, NEWR>;

@@ -8,8 +8,9 @@ namespace kvq {
 
 // Ring slots of the streaming kernel per head_dim: a few KiB in flight per
 // wave (the slots must divide the 3 * D / 64 code pieces of a chunk).  DEEP:
-// a wave with two row tiles spends about twice as long on each piece, so it
-// asks for its pieces further ahead (where the LDS holds one row group's q).
+// waves with up to 8 rows (more of their requests land while they compute)
+// and waves with two row tiles (about twice as long on each piece) ask for
+// their pieces further ahead, where the LDS has room.
 constexpr int stream_ring_slots(int D, bool deep = false) {
     return D == 256 ? (deep ? 6 : 4) : D == 128 ? (deep ? 6 : 3) : 3;
 }
