@@ -189,6 +189,18 @@ struct WaveState {
     TileState<D, R> t[RT];      // one per row tile
 };
 
+// Row layout of tile rt of a wave with RT tiles.  JJ = 3 (17-24 rows): the
+// last tile holds at most 8 rows in the JJ = 2 layout -- one MFMA per block
+// for q's hi and lo halves, half the softmax -- and the others JJ = 4.
+template <int JJ, int RT>
+__device__ constexpr int tile_jj(int rt) { return JJ == 3 ? (rt == RT - 1 ? 2 : 4) : JJ; }
+// The query row at MFMA row prow of tile t (the group's tile index), which is
+// tile rt of its wave, or -1.
+template <int JJ, int RT>
+__device__ inline int tile_row(int t, int rt, int prow) {
+    return tile_jj<JJ, RT>(rt) == 4 ? logical_row<4>(t, prow) : logical_row<2>(t, prow);
+}
+
 // S = (q_hi + q_lo) K^T for the chunk's two 16-token tiles.  MASK: some key
 // of the chunk lies beyond the last key of some row (causal edge, or
 // positions past ctx_len).  wait(p) runs before slice p's pieces are read,
@@ -258,9 +270,10 @@ __device__ inline void qk_step(floatx4 (&s)[RT][2], const Land& L, QSrc q, int l
             for (int tt = 0; tt < 2; ++tt)
                 c[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh, kb[tt], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
         }
-        if constexpr (JJ == 4) {
+        if constexpr (JJ != 2) {
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
+                if (tile_jj<JJ, RT>(rt) != 4) continue;      // (hi and lo in one operand)
                 const half8 ql = q(rt, 2 * b + 1);
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt)
@@ -278,12 +291,15 @@ __device__ inline void qk_step(floatx4 (&s)[RT][2], const Land& L, QSrc q, int l
         SCHED_FENCE();
     }
     if (LAG) fold();
-    // up to 8 rows the lo halves' products sit two rows down: fold them in
-    if constexpr (JJ == 2) {
+    // in a tile of up to 8 rows the lo halves' products sit two rows down:
+    // fold them in
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        if (tile_jj<JJ, RT>(rt) != 2) continue;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
-            s[0][tt][0] += s[0][tt][2];
-            s[0][tt][1] += s[0][tt][3];
+            s[rt][tt][0] += s[rt][tt][2];
+            s[rt][tt][1] += s[rt][tt][3];
         }
     }
     // causal / tail mask: key j visible to row r iff j <= first_last + r / group
@@ -292,8 +308,8 @@ __device__ inline void qk_step(floatx4 (&s)[RT][2], const Land& L, QSrc q, int l
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int jj = 0; jj < JJ; ++jj) {
-                const int row = logical_row<JJ>(rt0 + rt, 4 * g4 + jj);
+            for (int jj = 0; jj < tile_jj<JJ, RT>(rt); ++jj) {
+                const int row = tile_row<JJ, RT>(rt0 + rt, rt, 4 * g4 + jj);
                 const int last = row >= 0 && row < rows ? first_last + row / group : -1;
 #pragma unroll
                 for (int tt = 0; tt < 2; ++tt)
@@ -630,7 +646,7 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
     } else {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            const int q_row = logical_row<JJ>(gi * RT + rt, lane & 15);
+            const int q_row = tile_row<JJ, RT>(gi * RT + rt, rt, lane & 15);
             q_ok[rt] = q_row >= 0 && q_row < rows;
             const int qi = q_ok[rt] ? q_row / group : 0, h = kvh * group + (q_ok[rt] ? q_row % group : 0);
             const float* src = a.q + ((size_t)qi * a.n_heads + h) * D + 8 * (lane >> 4);
@@ -688,7 +704,7 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
             lo[e] = (_Float16)(x - (float)hi[e]);
         }
         uint8_t* dst = smem + WL::Q_OFF + (gi * RT + rt) * C::Q_BYTES + (2 * b) * 1024 + lane * 16;
-        if constexpr (JJ == 2) {
+        if (tile_jj<JJ, RT>(rt) == 2) {
             // up to 8 rows one operand holds both halves: the lo half of MFMA
             // row n goes to row n + 2, a row no query uses (same k group)
             if ((lane & 2) == 0) {
@@ -805,7 +821,10 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
         lds_fence();                            // K scales read out
         if (more) issue_kscales<D, R, POL>(land, np, lane);
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) softmax_step<D, R, JJ>(st.t[rt], s[rt], plds + rt * (C::PBUF / 4), lane);
+        for (int rt = 0; rt < RT; ++rt) {
+            if (tile_jj<JJ, RT>(rt) == 2) softmax_step<D, R, 2>(st.t[rt], s[rt], plds + rt * (C::PBUF / 4), lane);
+            else softmax_step<D, R, 4>(st.t[rt], s[rt], plds + rt * (C::PBUF / 4), lane);
+        }
         pv_step<D, R, RT, MASK>(st, land, plds, lane, pv_wait, pv_done);
         lds_fence();                            // V scales read out
         if (more) issue_vscales<D, R, POL>(land, np, lane);
@@ -827,7 +846,7 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int jj = 0; jj < JJ; ++jj) {
+        for (int jj = 0; jj < tile_jj<JJ, RT>(rt); ++jj) {
             st.t[rt].l[jj] = row16_sum(st.t[rt].l[jj]) * 16.0f;        // weights carried 2^-kTau
             if (bad) { st.t[rt].m[jj] = NAN; st.t[rt].l[jj] = NAN; }
         }
@@ -894,7 +913,7 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int jj = 0; jj < JJ; ++jj)
+        for (int jj = 0; jj < tile_jj<JJ, RT>(rt); ++jj)
             if (n16 == 0) {
                 float* d = mls + ((wave * RT + rt) * 16 + 4 * g4 + jj) * 2;
                 d[0] = st.t[rt].m[jj];
@@ -902,7 +921,7 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
             }
     int* const pst = reinterpret_cast<int*>(smem + WL::PS_OFF);      // [RG * RT tiles][16 rows]
     if (threadIdx.x < RG * RT * 16) {
-        const int lrow = logical_row<JJ>(threadIdx.x / 16, threadIdx.x % 16);
+        const int lrow = tile_row<JJ, RT>(threadIdx.x / 16, (threadIdx.x / 16) % RT, threadIdx.x % 16);
         pst[threadIdx.x] = lrow >= 0 && lrow < rows
                                ? ((lrow / group) * a.n_heads + kvh * group + lrow % group) * part_stride + split
                                : -1;
@@ -936,7 +955,7 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
             const float fr = ls == 0.0f ? 0.0f : fast_exp2(ms - mm);
             // lane (g4, n16) holds rows 4 g4 + jj: their factors sit in lanes 4 g4 + jj
 #pragma unroll
-            for (int jj = 0; jj < JJ; ++jj) {
+            for (int jj = 0; jj < tile_jj<JJ, RT>(rt); ++jj) {
                 const float f = __shfl(fr, 4 * g4 + jj);
 #pragma unroll
                 for (int nt = 0; nt < C::NT; ++nt) st.t[rt].o[nt][jj] *= f;
@@ -959,7 +978,7 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
 #pragma unroll
             for (int j = 1; j < WPG; ++j) acc += cb[((eg * WPG + j) * C::NT + ent) * 64 + el];
 #pragma unroll
-            for (int jj = 0; jj < JJ; ++jj) {
+            for (int jj = 0; jj < 4; ++jj) {                  // (rows a tile does not hold have ps = -1)
                 const int ps = pst[(eg * RT + rt) * 16 + 4 * (el >> 4) + jj];
                 if (ps >= 0) a.ws_acc[(size_t)ps * D + 16 * ent + (el & 15)] = acc[jj];
             }
@@ -990,13 +1009,15 @@ hipError_t launch_dr(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream, 
 }
 
 // Up to 8 rows two per lane group (JJ = 2), up to 16 rows one per MFMA row,
-// up to 32 rows two row tiles per wave (every code converted once for both),
-// more rows in 2 row groups of two tiles.
+// up to 32 rows two row tiles per wave (every code converted once for both;
+// up to 24 the second tile in the 8-row layout, JJ = 3), more rows in 2 row
+// groups of two tiles.
 template <int D, bool NEWR, class Batch>
 hipError_t launch_d(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream, const Batch& sb, int n_wg,
                     const NewRows& nr, int part_stride) {
     if (pl.rows <= 8) return launch_dr<D, 2, 1, 1, NEWR>(a, pl, stream, sb, n_wg, nr, part_stride);
     if (pl.rows <= 16) return launch_dr<D, 4, 1, 1, NEWR>(a, pl, stream, sb, n_wg, nr, part_stride);
+    if (pl.rows <= 24) return launch_dr<D, 3, 1, 2, NEWR>(a, pl, stream, sb, n_wg, nr, part_stride);
     if (pl.rows <= 32) return launch_dr<D, 4, 1, 2, NEWR>(a, pl, stream, sb, n_wg, nr, part_stride);
     if (pl.rows <= 64) return launch_dr<D, 4, 2, 2, NEWR>(a, pl, stream, sb, n_wg, nr, part_stride);
     return hipErrorInvalidValue;

@@ -23,15 +23,16 @@ constexpr float kLog2e = 1.4426950408889634f;
 // at the end.
 constexpr float kTau = 4.0f;
 
-// MFMA row placement.  Row tile rt holds MFMA rows 0..15; lane group g4 of the
-// S / O layouts owns rows 4*g4 .. 4*g4+3.  With at most 8 query rows (JJ = 2)
-// the rows go to MFMA rows {0,1, 4,5, 8,9, 12,13}, so each lane holds 2 real
-// rows and the softmax work per lane halves; otherwise (JJ = 4) row i sits at
-// MFMA row i.  Returns the query row at MFMA row prow of tile rt, or -1.
+// MFMA row placement.  Row tile rt holds query rows 16 rt .. 16 rt + 15 in
+// MFMA rows 0..15; lane group g4 of the S / O layouts owns rows 4*g4 ..
+// 4*g4+3.  A tile with at most 8 query rows (JJ = 2) puts them in MFMA rows
+// {0,1, 4,5, 8,9, 12,13}, so each lane holds 2 real rows and the softmax work
+// per lane halves; otherwise (JJ = 4) row i sits at MFMA row i.  Returns the
+// query row at MFMA row prow of tile rt, or -1.
 template <int JJ>
 __device__ inline int logical_row(int rt, int prow) {
     if (JJ == 4) return 16 * rt + prow;
-    return (prow & 3) < 2 ? 8 * rt + 2 * (prow >> 2) + (prow & 3) : -1;
+    return (prow & 3) < 2 ? 16 * rt + 2 * (prow >> 2) + (prow & 3) : -1;
 }
 
 template <int CTRL>
