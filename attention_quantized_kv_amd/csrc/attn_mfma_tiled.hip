@@ -21,7 +21,9 @@
 //    chunk before reads the other): K codes exactly to fp16 (int8 -> fp16 is
 //    exact, the scale stays apart), V to (c - 8) * scale as an exact fp16
 //    hi + lo pair, laid out as the MFMA operand fragments the waves read with
-//    one 16-byte LDS load;
+//    one 16-byte LDS load.  A wave with rows runs its share of this between
+//    its PV products of the chunk before (its raw inputs read one product
+//    group ahead), so that the VALU work partly hides under the matrix core;
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_f16, one K = 32 step per quant block:
 //    the block's scale multiplies the fp32 result per key (fma_mix), and q is
 //    split into fp16 hi + lo parts (two MFMAs), so every score is the exact
@@ -260,10 +262,29 @@ struct Requests {
 //  K scales: thread t < 4*NB spreads 8 of them to [tile][block][16 keys].
 // kvalid: tokens of the chunk that exist (< ctx); V of the others is zeroed so
 // that a masked key (weight 0) cannot meet an unwritten, non-finite scale.
+// The work is cut into parts, one pass of the threads over K items (it < KI),
+// V items (KI <= it < KI + VI) or the scales (the last part), so that a wave
+// can run the parts of the next chunk between the products of this one.
 template <int D, int RT, int CODEC>
-__device__ inline void convert_chunk(const uint8_t* slot, uint8_t* stage, int t, int kvalid);
+struct Parts {
+    using C = TCfg<D, RT, CODEC>;
+    static constexpr int K_N = CODEC == 1 ? 2 * C::NB * 64 : C::K_ITEMS;
+    static constexpr int V_N = C::NT * 64;
+    static constexpr int KI = (K_N + C::THREADS - 1) / C::THREADS;
+    static constexpr int VI = (V_N + C::THREADS - 1) / C::THREADS;
+    static constexpr int N = KI + VI + 1;
+};
 
-// INT2 operands come out of the fp4 conversion (see convert_chunk_int2) with
+// Raw inputs of one part (read from the ring slot), kept in registers between
+// the LDS reads and the arithmetic that consumes them.
+struct PartRaw {
+    uint32_t w[10];
+};
+
+template <int D, int RT, int CODEC, bool FULL = false>
+__device__ inline void convert_part(int part, const uint8_t* slot, uint8_t* stage, int t, int kvalid);
+
+// INT2 operands come out of the fp4 conversion (see part_store_int2) with
 // elements 1 and 2 of every group of 4 swapped: operand element e holds item
 // i2_slot(e) (an involution), for the dims of a K fragment (so q is staged in
 // that order) and the keys of a V fragment (so P is too).
@@ -284,19 +305,47 @@ __host__ __device__ constexpr int i2_slot(int e) { return (e & ~3) | ((e & 1) <<
 //     group are one byte of one raw dword.  hi + lo of z + d c (fp32).
 //  Scales and zero-points: thread t < 32 NB2 takes (token, block).
 template <int D, int RT>
-__device__ inline void convert_chunk_int2(const uint8_t* slot, uint8_t* stage, int t, int kvalid) {
+__device__ inline void part_load_int2(int part, const uint8_t* slot, int t, PartRaw& r) {
     using C = TCfg<D, RT, 1>;
+    using PP = Parts<D, RT, 1>;
+    if (part < PP::KI) {
+        const int item = part * C::THREADS + t;
+        if (PP::K_N % C::THREADS != 0 && item >= PP::K_N) return;
+        const int tt = item / (C::NB * 64), st = (item / 64) % C::NB, L = item % 64;
+        r.w[0] = *reinterpret_cast<const uint32_t*>(slot + tt * (kTile * D / 4) + L * (D / 16) + (st / 2) * 4);
+    } else if (part < PP::KI + PP::VI) {
+        const int item = (part - PP::KI) * C::THREADS + t;
+        if (PP::V_N % C::THREADS != 0 && item >= PP::V_N) return;
+        const int nt = item / 64, fl = item % 64, G = fl / 16, n = fl % 16, b = nt / 8;
+        // keys 4G.. (raw lane group G/2), 16+4G.. (group 2+G/2)
+        const uint8_t* vraw = slot + C::I2_V + n * (D / 8) + (nt / 2) * 4;
+        r.w[0] = *reinterpret_cast<const uint32_t*>(vraw + (G / 2) * 16 * (D / 8));
+        r.w[1] = *reinterpret_cast<const uint32_t*>(vraw + (2 + G / 2) * 16 * (D / 8));
+        const uint8_t* vs = slot + C::I2_VS + b * kChunk * 2;
+        const uint8_t* vz = slot + C::I2_VZ + b * kChunk * 2;
+        const u32x2 s0 = *reinterpret_cast<const u32x2*>(vs + 8 * G), s1 = *reinterpret_cast<const u32x2*>(vs + 32 + 8 * G);
+        const u32x2 z0 = *reinterpret_cast<const u32x2*>(vz + 8 * G), z1 = *reinterpret_cast<const u32x2*>(vz + 32 + 8 * G);
+        r.w[2] = s0.x; r.w[3] = s0.y; r.w[4] = s1.x; r.w[5] = s1.y;
+        r.w[6] = z0.x; r.w[7] = z0.y; r.w[8] = z1.x; r.w[9] = z1.y;
+    } else if (t < kChunk * C::NB2) {
+        const int tok = t / C::NB2, b = t % C::NB2;
+        r.w[0] = *reinterpret_cast<const uint32_t*>(slot + C::I2_P + (tok * C::NB2 + b) * 4);
+    }
+}
+
+template <int D, int RT, bool FULL>
+__device__ inline void part_store_int2(int part, const PartRaw& r, uint8_t* stage, int t, int kvalid) {
+    using C = TCfg<D, RT, 1>;
+    using PP = Parts<D, RT, 1>;
     uint8_t* kf = stage;
     _Float16* ksl = reinterpret_cast<_Float16*>(stage + C::K_FRAG);
     _Float16* kzl = reinterpret_cast<_Float16*>(stage + C::K_FRAG + C::KS);
     uint8_t* vf = stage + C::K_FRAG + C::KS + C::KZ;
-    constexpr int K_OUT = 2 * C::NB * 64;       // K fragments per chunk
-#pragma unroll
-    for (int it = 0; it < (K_OUT + C::THREADS - 1) / C::THREADS; ++it) {
-        const int item = it * C::THREADS + t;
-        if (K_OUT % C::THREADS != 0 && item >= K_OUT) break;
+    if (part < PP::KI) {
+        const int item = part * C::THREADS + t;
+        if (PP::K_N % C::THREADS != 0 && item >= PP::K_N) return;
         const int tt = item / (C::NB * 64), st = (item / 64) % C::NB, L = item % 64;
-        const uint32_t x = *reinterpret_cast<const uint32_t*>(slot + tt * (kTile * D / 4) + L * (D / 16) + (st / 2) * 4);
+        const uint32_t x = r.w[0];
         const uint32_t n0 = x & 0x33333333u, n1 = (x >> 2) & 0x33333333u;
         half2v a, b, c, d;
         if (st & 1) {                            // uniform: 64 items per wave share st
@@ -312,43 +361,36 @@ __device__ inline void convert_chunk_int2(const uint8_t* slot, uint8_t* stage, i
         }
         *reinterpret_cast<half8*>(kf + ((tt * C::NB + st) * 64 + L) * 16) =
             half8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
-    }
-#pragma unroll
-    for (int it = 0; it < (C::NT * 64 + C::THREADS - 1) / C::THREADS; ++it) {
-        const int item = it * C::THREADS + t;
-        if (C::NT * 64 % C::THREADS != 0 && item >= C::NT * 64) break;
-        const int nt = item / 64, fl = item % 64, G = fl / 16, n = fl % 16, b = nt / 8;
+    } else if (part < PP::KI + PP::VI) {
+        const int item = (part - PP::KI) * C::THREADS + t;
+        if (PP::V_N % C::THREADS != 0 && item >= PP::V_N) return;
+        const int nt = item / 64, fl = item % 64, G = fl / 16;
         const int sh = 16 * (G % 2) + 8 * (nt % 2);
-        // keys 4G.. (raw lane group G/2) in byte 0, 16+4G.. (group 2+G/2) in byte 1
-        const uint8_t* vraw = slot + C::I2_V + n * (D / 8) + (nt / 2) * 4;
-        const uint32_t w = ((*reinterpret_cast<const uint32_t*>(vraw + (G / 2) * 16 * (D / 8)) >> sh) & 0xFFu) |
-                           (((*reinterpret_cast<const uint32_t*>(vraw + (2 + G / 2) * 16 * (D / 8)) >> sh) & 0xFFu) << 8);
+        // keys 4G.. in byte 0, 16+4G.. in byte 1
+        const uint32_t w = ((r.w[0] >> sh) & 0xFFu) | (((r.w[1] >> sh) & 0xFFu) << 8);
         const uint32_t n0 = w & 0x3333u, n1 = (w >> 2) & 0x3333u;
         const half2v c01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(n0, 2.0f, 0);
         const half2v c23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(n1, 2.0f, 0);
         const half2v c45 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(n0, 2.0f, 1);
         const half2v c67 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(n1, 2.0f, 1);
         const half8 code = {c01.x, c01.y, c23.x, c23.y, c45.x, c45.y, c67.x, c67.y};
-        const _Float16* vs = reinterpret_cast<const _Float16*>(slot + C::I2_VS) + b * kChunk;
-        const _Float16* vz = reinterpret_cast<const _Float16*>(slot + C::I2_VZ) + b * kChunk;
-        const half4 s0 = *reinterpret_cast<const half4*>(vs + 4 * G), s1 = *reinterpret_cast<const half4*>(vs + 16 + 4 * G);
-        const half4 z0 = *reinterpret_cast<const half4*>(vz + 4 * G), z1 = *reinterpret_cast<const half4*>(vz + 16 + 4 * G);
+        const half4 s0 = __builtin_bit_cast(half4, u32x2{r.w[2], r.w[3]}), s1 = __builtin_bit_cast(half4, u32x2{r.w[4], r.w[5]});
+        const half4 z0 = __builtin_bit_cast(half4, u32x2{r.w[6], r.w[7]}), z1 = __builtin_bit_cast(half4, u32x2{r.w[8], r.w[9]});
         half8 hi, lo;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int ki = i2_slot(e % 4);
             const int key = (e < 4 ? 4 * G : 16 + 4 * G) + ki;
             const _Float16 sv = e < 4 ? s0[ki] : s1[ki], zv = e < 4 ? z0[ki] : z1[ki];
-            const float v = key < kvalid ? fmaf((float)sv, (float)code[e], (float)zv) : 0.0f;
+            const float v = FULL || key < kvalid ? fmaf((float)sv, (float)code[e], (float)zv) : 0.0f;
             hi[e] = (_Float16)v;
             lo[e] = (_Float16)(v - (float)hi[e]);
         }
         *reinterpret_cast<half8*>(vf + (nt * 64 + fl) * 16) = hi;
         *reinterpret_cast<half8*>(vf + C::V_FRAG + (nt * 64 + fl) * 16) = lo;
-    }
-    if (t < kChunk * C::NB2) {
+    } else if (t < kChunk * C::NB2) {
         const int tok = t / C::NB2, b = t % C::NB2;
-        const half2v dz = as_h2(*reinterpret_cast<const uint32_t*>(slot + C::I2_P + (tok * C::NB2 + b) * 4));
+        const half2v dz = as_h2(r.w[0]);
         const int tt = tok / kTile, key = tok % kTile;
 #pragma unroll
         for (int st = 4 * b; st < 4 * b + 4; ++st) ksl[(tt * C::NB + st) * kTile + key] = dz.x;
@@ -357,47 +399,69 @@ __device__ inline void convert_chunk_int2(const uint8_t* slot, uint8_t* stage, i
 }
 
 template <int D, int RT, int CODEC>
-__device__ inline void convert_chunk(const uint8_t* slot, uint8_t* stage, int t, int kvalid) {
+__device__ inline void part_load(int part, const uint8_t* slot, int t, PartRaw& r) {
     if constexpr (CODEC == 1) {
-        convert_chunk_int2<D, RT>(slot, stage, t, kvalid);
+        part_load_int2<D, RT>(part, slot, t, r);
         return;
     }
     using C = TCfg<D, RT, CODEC>;
-    uint8_t* kf = stage;
-    _Float16* ksl = reinterpret_cast<_Float16*>(stage + C::K_FRAG);
-    uint8_t* vf = stage + C::K_FRAG + C::KS;
-#pragma unroll
-    for (int it = 0; it < (C::K_ITEMS + C::THREADS - 1) / C::THREADS; ++it) {
-        const int item = it * C::THREADS + t;
-        if (C::K_ITEMS % C::THREADS != 0 && item >= C::K_ITEMS) break;
+    using PP = Parts<D, RT, CODEC>;
+    if (part < PP::KI) {
+        const int item = part * C::THREADS + t;
+        if (C::K_ITEMS % C::THREADS != 0 && item >= C::K_ITEMS) return;
         const int tt = item / (64 * C::KL), pc = (item / 64) % C::KL, L = item % 64;
         const u32x4 k = *reinterpret_cast<const u32x4*>(slot + (tt * C::KL + pc) * 1024 + L * 16);
-        *reinterpret_cast<half8*>(kf + ((tt * C::NB + 2 * pc) * 64 + L) * 16) = k_codes_to_half(k.x, k.y);
-        *reinterpret_cast<half8*>(kf + ((tt * C::NB + 2 * pc + 1) * 64 + L) * 16) = k_codes_to_half(k.z, k.w);
-    }
-    uint32_t magic = 0x64006400u;
-    asm volatile("" : "+v"(magic));
-#pragma unroll
-    for (int it = 0; it < (C::NT * 64 + C::THREADS - 1) / C::THREADS; ++it) {
-        const int item = it * C::THREADS + t;
-        if (C::NT * 64 % C::THREADS != 0 && item >= C::NT * 64) break;
+        r.w[0] = k.x; r.w[1] = k.y; r.w[2] = k.z; r.w[3] = k.w;
+    } else if (part < PP::KI + PP::VI) {
+        const int item = (part - PP::KI) * C::THREADS + t;
+        if (PP::V_N % C::THREADS != 0 && item >= PP::V_N) return;
         const int nt = item / 64, fl = item % 64, G = fl / 16, n = fl % 16;
         const int u = nt / 4, w = nt % 4, b = nt / 2;
         const uint8_t* vraw = slot + C::OFF_V + u * 1024 + n * 16 + w * 4;
-        const uint32_t x1 = *reinterpret_cast<const uint32_t*>(vraw + (G / 2) * 256);         // tokens 8(G/2)..
-        const uint32_t x2 = *reinterpret_cast<const uint32_t*>(vraw + (2 + G / 2) * 256);     // tokens 16+8(G/2)..
+        r.w[0] = *reinterpret_cast<const uint32_t*>(vraw + (G / 2) * 256);         // tokens 8(G/2)..
+        r.w[1] = *reinterpret_cast<const uint32_t*>(vraw + (2 + G / 2) * 256);     // tokens 16+8(G/2)..
         const u32x2 s1 = *reinterpret_cast<const u32x2*>(slot + C::OFF_VS + (b * kChunk + 4 * G) * 2);
         const u32x2 s2 = *reinterpret_cast<const u32x2*>(slot + C::OFF_VS + (b * kChunk + 16 + 4 * G) * 2);
+        r.w[2] = s1.x; r.w[3] = s1.y; r.w[4] = s2.x; r.w[5] = s2.y;
+    } else if (t < C::KS_ITEMS) {
+        const u32x4 h = *reinterpret_cast<const u32x4*>(slot + C::OFF_KS + t * 16);
+        r.w[0] = h.x; r.w[1] = h.y; r.w[2] = h.z; r.w[3] = h.w;
+    }
+}
+
+template <int D, int RT, int CODEC, bool FULL>
+__device__ inline void part_store(int part, const PartRaw& r, uint8_t* stage, int t, int kvalid) {
+    if constexpr (CODEC == 1) {
+        part_store_int2<D, RT, FULL>(part, r, stage, t, kvalid);
+        return;
+    }
+    using C = TCfg<D, RT, CODEC>;
+    using PP = Parts<D, RT, CODEC>;
+    uint8_t* kf = stage;
+    _Float16* ksl = reinterpret_cast<_Float16*>(stage + C::K_FRAG);
+    uint8_t* vf = stage + C::K_FRAG + C::KS;
+    if (part < PP::KI) {
+        const int item = part * C::THREADS + t;
+        if (C::K_ITEMS % C::THREADS != 0 && item >= C::K_ITEMS) return;
+        const int tt = item / (64 * C::KL), pc = (item / 64) % C::KL, L = item % 64;
+        *reinterpret_cast<half8*>(kf + ((tt * C::NB + 2 * pc) * 64 + L) * 16) = k_codes_to_half(r.w[0], r.w[1]);
+        *reinterpret_cast<half8*>(kf + ((tt * C::NB + 2 * pc + 1) * 64 + L) * 16) = k_codes_to_half(r.w[2], r.w[3]);
+    } else if (part < PP::KI + PP::VI) {
+        const int item = (part - PP::KI) * C::THREADS + t;
+        if (PP::V_N % C::THREADS != 0 && item >= PP::V_N) return;
+        uint32_t magic = 0x64006400u;
+        asm volatile("" : "+v"(magic));
+        const int nt = item / 64, fl = item % 64, G = fl / 16;
         const int sh = 16 * (G % 2);
-        const uint32_t y1 = x1 >> sh, y2 = x2 >> sh;    // keys 4G..4G+3 / 16+4G.. in the low 16 bits
+        const uint32_t y1 = r.w[0] >> sh, y2 = r.w[1] >> sh;    // keys 4G..4G+3 / 16+4G.. in the low 16 bits
         half2v h0, h1, h2, h3, l0, l1, l2, l3;
-        v_pair<0>(y1, as_h2(s1.x), magic, h0, l0);
-        v_pair<1>(y1, as_h2(s1.y), magic, h1, l1);
-        v_pair<0>(y2, as_h2(s2.x), magic, h2, l2);
-        v_pair<1>(y2, as_h2(s2.y), magic, h3, l3);
+        v_pair<0>(y1, as_h2(r.w[2]), magic, h0, l0);
+        v_pair<1>(y1, as_h2(r.w[3]), magic, h1, l1);
+        v_pair<0>(y2, as_h2(r.w[4]), magic, h2, l2);
+        v_pair<1>(y2, as_h2(r.w[5]), magic, h3, l3);
         half8 hi = {h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
         half8 lo = {l0[0], l0[1], l1[0], l1[1], l2[0], l2[1], l3[0], l3[1]};
-        if (kvalid < kChunk) {
+        if (!FULL && kvalid < kChunk) {
             const _Float16 z = (_Float16)0.0f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -407,15 +471,27 @@ __device__ inline void convert_chunk(const uint8_t* slot, uint8_t* stage, int t,
         }
         *reinterpret_cast<half8*>(vf + (nt * 64 + fl) * 16) = hi;
         *reinterpret_cast<half8*>(vf + C::V_FRAG + (nt * 64 + fl) * 16) = lo;
-    }
-    if (t < C::KS_ITEMS) {
-        const half8 h = *reinterpret_cast<const half8*>(slot + C::OFF_KS + t * 16);
+    } else if (t < C::KS_ITEMS) {
+        const half8 h = __builtin_bit_cast(half8, u32x4{r.w[0], r.w[1], r.w[2], r.w[3]});
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int e = 8 * t + i, j = e / C::NB, bb = e % C::NB;
             ksl[((j / kTile) * C::NB + bb) * kTile + j % kTile] = h[i];
         }
     }
+}
+
+template <int D, int RT, int CODEC, bool FULL>
+__device__ inline void convert_part(int part, const uint8_t* slot, uint8_t* stage, int t, int kvalid) {
+    PartRaw r;
+    part_load<D, RT, CODEC>(part, slot, t, r);
+    part_store<D, RT, CODEC, FULL>(part, r, stage, t, kvalid);
+}
+
+template <int D, int RT, int CODEC>
+__device__ inline void convert_chunk(const uint8_t* slot, uint8_t* stage, int t, int kvalid) {
+#pragma unroll
+    for (int part = 0; part < Parts<D, RT, CODEC>::N; ++part) convert_part<D, RT, CODEC>(part, slot, stage, t, kvalid);
 }
 
 template <int D, int RT>
@@ -425,14 +501,33 @@ struct Rows {
     float l[RT];                      // this lane's share of the row sum
 };
 
+// Orders the instructions of one scheduling region that holds NM matrix
+// products and conversion work: two products, then one product per four VALU
+// instructions (VALU work issues while independent products run on the
+// matrix core), then the rest and the LDS writes.
+template <int NM>
+__device__ inline void interleave_products() {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);      // MFMA
+#pragma unroll
+    for (int i = 2; i < NM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+    }
+    __builtin_amdgcn_sched_group_barrier(0x002, 256, 0);
+    __builtin_amdgcn_sched_group_barrier(0x200, 32, 0);     // LDS writes
+}
+
 // One chunk: S^T = K Q^T, online softmax, O^T += V^T P^T for the wave's RT
 // row tiles.  MASK: some key of the chunk lies beyond some row's last key.
-template <int D, int RT, int CODEC, bool MASK>
+// FUSE: the wave also converts the next raw chunk (cslot, whole) into the
+// other stage (cstage), its parts spread over the PV products.
+template <int D, int RT, int CODEC, bool MASK, bool FUSE>
 __device__ inline void chunk_step(Rows<D, RT>& st, const uint8_t* __restrict__ stage,
                                   const half8 (&qh)[RT][D / kBlock], const half8 (&ql)[RT][D / kBlock],
                                   const float (&qsum)[RT][D / kBlock2 > 0 ? D / kBlock2 : 1], int lane, int j0,
-                                  const int (&last)[RT]) {
+                                  const int (&last)[RT], const uint8_t* cslot, uint8_t* cstage, int t) {
     using C = TCfg<D, RT, CODEC>;
+    using PP = Parts<D, RT, CODEC>;
     const uint8_t* kf = stage;
     const _Float16* ksl = reinterpret_cast<const _Float16*>(stage + C::K_FRAG);
     const _Float16* kzl = reinterpret_cast<const _Float16*>(stage + C::K_FRAG + C::KS);
@@ -540,6 +635,62 @@ __device__ inline void chunk_step(Rows<D, RT>& st, const uint8_t* __restrict__ s
     // output tiles at a time so that dependent products are 4 RT apart; each
     // V fragment serves all RT row tiles
     constexpr int NG = 4;
+    constexpr int NGR = C::NT / NG;                 // groups of output tiles
+    constexpr int NP = PP::KI + PP::VI;             // conversion parts under the products
+    if constexpr (FUSE) {
+        // Registers for one group of fragments only: each is reloaded with
+        // the next group's as soon as its last product has been issued.
+        half8 vh[NG], vl[NG];
+#pragma unroll
+        for (int i = 0; i < NG; ++i) {
+            vh[i] = *reinterpret_cast<const half8*>(vf + (i * 64 + lane) * 16);
+            vl[i] = *reinterpret_cast<const half8*>(vf + C::V_FRAG + (i * 64 + lane) * 16);
+        }
+        // the parts of group g are read in group g - 1's region (group 0's
+        // own parts, if any, in its region)
+        PartRaw raw[NP];
+#pragma unroll
+        for (int part = 0; part < 1 * NP / NGR; ++part) part_load<D, RT, CODEC>(part, cslot, t, raw[part]);
+#pragma unroll
+        for (int n0 = 0; n0 < C::NT; n0 += NG) {
+            const int g = n0 / NG;
+#pragma unroll
+            for (int part = g * NP / NGR; part < (g + 1) * NP / NGR; ++part)
+                part_store<D, RT, CODEC, true>(part, raw[part], cstage, t, kChunk);
+#pragma unroll
+            for (int part = (g + 1) * NP / NGR; part < (g + 2) * NP / NGR && part < NP; ++part)
+                part_load<D, RT, CODEC>(part, cslot, t, raw[part]);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int i = 0; i < NG; ++i)
+                    st.o[rt][n0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh[i], ph[rt], st.o[rt][n0 + i], 0, 0, 0);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int i = 0; i < NG; ++i)
+                    st.o[rt][n0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh[i], pl[rt], st.o[rt][n0 + i], 0, 0, 0);
+            if (n0 + NG < C::NT) {
+#pragma unroll
+                for (int i = 0; i < NG; ++i)
+                    vh[i] = *reinterpret_cast<const half8*>(vf + ((n0 + NG + i) * 64 + lane) * 16);
+            }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int i = 0; i < NG; ++i)
+                    st.o[rt][n0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vl[i], ph[rt], st.o[rt][n0 + i], 0, 0, 0);
+            if (n0 + NG < C::NT) {
+#pragma unroll
+                for (int i = 0; i < NG; ++i)
+                    vl[i] = *reinterpret_cast<const half8*>(vf + C::V_FRAG + ((n0 + NG + i) * 64 + lane) * 16);
+            }
+            interleave_products<3 * NG * RT>();
+            SCHED_FENCE();
+        }
+        convert_part<D, RT, CODEC, true>(PP::N - 1, cslot, cstage, t, kChunk);
+        return;
+    }
     half8 vh[NG], vl[NG], vhn[NG], vln[NG];
     auto load_group = [&](int n0, half8 (&h)[NG], half8 (&l)[NG]) {
 #pragma unroll
@@ -706,26 +857,44 @@ __global__ __launch_bounds__(kThreadsFor<RT>) void attn_mfma_tiled_kernel(AttnAr
         convert(c_begin);
         lds_barrier();
     }
-    // Per chunk c: convert c + 1 (landed before the last barrier) into the
-    // other stage, request c + kRing into the slot c just left, run the math
-    // on c, wait for this wave's requests of c + 2, barrier.
-    auto step = [&](int c, auto masked) {
-        if (c + 1 < c_end) convert(c + 1);
+    // Per chunk c: request c + kRing into the slot chunk c was converted
+    // from, run the math on c, convert c + 1 (landed before the last barrier)
+    // into the other stage, wait for this wave's requests of c + 2, barrier.
+    // FUSE: the conversion runs under the products of c (a wave with rows,
+    // a next chunk in the range that is whole); otherwise before the math.
+    auto step = [&](int c, auto masked, auto fuse) {
+        constexpr bool MASKED = decltype(masked)::value;
         const bool more = c + kRing < c_end;
         if (more) issue_next();
         SCHED_FENCE();
-        if (wave_active)
-            chunk_step<D, RT, CODEC, decltype(masked)::value>(st, smem + (c & 1) * C::STAGE, qh, ql, qsum, lane,
-                                                              c * kChunk, last);
+        if constexpr (decltype(fuse)::value) {
+            chunk_step<D, RT, CODEC, MASKED, true>(st, smem + (c & 1) * C::STAGE, qh, ql, qsum, lane, c * kChunk,
+                                                   last, ring + ((c + 1) & (kRing - 1)) * C::SLOT,
+                                                   smem + ((c + 1) & 1) * C::STAGE, t);
+        } else {
+            if (c + 1 < c_end) convert(c + 1);
+            SCHED_FENCE();
+            if (wave_active)
+                chunk_step<D, RT, CODEC, MASKED, false>(st, smem + (c & 1) * C::STAGE, qh, ql, qsum, lane,
+                                                        c * kChunk, last, nullptr, nullptr, t);
+        }
         SCHED_FENCE();
         if (more) vm_wait<(kRing - 2) * C::ND>(); else vm_wait<0>();
         lds_barrier();
     };
-    // chunks ending at or before min_last need no mask: run them in a loop of
-    // their own, then the masked tail
+    // Chunks ending at or before min_last need no mask; chunks before c_fuse
+    // have a whole next chunk in the range.  Each kind runs in a loop of its
+    // own, in chunk order (the fused and plain steps in one loop would need
+    // more registers than a wave has).
     const int c_mask = max(c_begin, min(c_end, (min_last + 1) / kChunk));
-    for (int c = c_begin; c < c_mask; ++c) step(c, std::false_type{});
-    for (int c = c_mask; c < c_end; ++c) step(c, std::true_type{});
+    const int c_fuse = wave_active ? min(c_end, a.ctx / kChunk) - 1 : c_begin;
+    const std::false_type no{};
+    const std::true_type yes{};
+    int c = c_begin;
+    for (const int e = max(c_begin, min(c_mask, c_fuse)); c < e; ++c) step(c, no, yes);
+    for (; c < c_mask; ++c) step(c, no, no);
+    for (const int e = max(c_mask, c_fuse); c < e; ++c) step(c, yes, yes);
+    for (; c < c_end; ++c) step(c, yes, no);
 
     const int grp = lane >> 4;
 #pragma unroll
