@@ -177,18 +177,23 @@ def test_large_magnitudes(kernel):
     tu.assert_close(out, ref, lse, ref_lse, "large")
 
 
-def test_prefill_chunk(kernel):
-    c, rng = _rand_case(41, 1200, 2, 128, P=64)
-    q = rng.standard_normal((200, 12, 128)).astype(np.float32)
+@pytest.mark.parametrize("D,ctx,n_q,G,P", [
+    (128, 1200, 200, 6, 64),    # ragged last chunk, 10 row tiles
+    (256, 2500, 64, 6, 256),    # head_dim 256: three row tiles, ragged last chunk
+    (64, 700, 100, 4, 32),
+])
+def test_prefill_chunk(kernel, D, ctx, n_q, G, P):
+    c, rng = _rand_case(41 + D, ctx, 2, D, P=P)
+    q = rng.standard_normal((n_q, 2 * G, D)).astype(np.float32)
     if kernel == KERNELS["mfma_stream"]:
         import attention_quantized_kv_amd as kvq
-        with pytest.raises(kvq.KvqError) as e:      # 1200 rows per KV head > 64
-            c.run(q, 1 / math.sqrt(128), kernel=kernel, prefill=True)
+        with pytest.raises(kvq.KvqError) as e:      # more than 64 rows per KV head
+            c.run(q, 1 / math.sqrt(D), kernel=kernel, prefill=True)
         assert e.value.status == kvq.KVQ_ERR_UNSUPPORTED
         return
-    out, lse = c.run(q, 1 / math.sqrt(128), kernel=kernel, prefill=True)
-    ref, ref_lse = c.ref(q, 1 / math.sqrt(128))
-    tu.assert_close(out, ref, lse, ref_lse, "prefill")
+    out, lse = c.run(q, 1 / math.sqrt(D), kernel=kernel, prefill=True)
+    ref, ref_lse = c.ref(q, 1 / math.sqrt(D))
+    tu.assert_close(out, ref, lse, ref_lse, f"prefill D={D} ctx={ctx} n_q={n_q}")
 
 
 def test_invalid_page_entry_gives_nan_not_fault(kernel):
