@@ -471,7 +471,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the library has no multi-GPU path; "
               "the single-GPU value is the measurement.", file=sys.stderr)
         sys.exit(2)
 

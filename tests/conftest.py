@@ -13,7 +13,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests are skipped only where torch sees no GPU at all; on a GPU machine a
+    # GPU tests are skipped only where torch sees no GPU at all; on a machine with a GPU a
     # missing or broken library fails the tests loudly instead.
     try:
         import torch
