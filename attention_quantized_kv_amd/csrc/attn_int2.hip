@@ -37,6 +37,7 @@
 
 #include "kvq_internal.h"
 #include "kvq_mfma.h"
+#include "kvq_quant.h"
 
 namespace kvq {
 namespace {
@@ -170,6 +171,244 @@ __device__ inline half8 i2_word(uint32_t x) {
 // The code (of a word) in operand element s.
 __host__ __device__ constexpr int code_slot(int s) { return (s & 4) | ((s & 1) << 1) | ((s >> 1) & 1); }
 
+// ---- Rows appended by a fused decode step (kvq_append_attn over the INT2
+// cache).  The workgroup of the last split of each KV head takes every new
+// row, after its waves have streamed their chunks: the 8 tokens of a group
+// share each V code dword, so a single workgroup writes each such dword once,
+// with no atomics.  Its inputs (the new rows' first blocks, the query rows,
+// the page entries, the old V code dwords of the new rows' 8-token groups)
+// are requested when the kernel starts and arrive with the first round trip.
+// At the end the eight waves share the work:
+//  1. wave w quantizes 128-value blocks w, w + 8, ... of the new rows (K and
+//     V) with the append kernel's arithmetic -- two values per lane, the
+//     block minimum and maximum over the wave -- so codes, scales and
+//     zero-points are those kvq_append writes, bit for bit; it writes the
+//     block's (scale, zero) into the pool and leaves codes and dequantized
+//     values in LDS;
+//  2. wave r < rows scores query row r against each new key and leaves the
+//     key's softmax state as partial n_splits + j of the row: m = the score,
+//     l = 1, acc = the dequantized V row (an empty partial, l = 0, for rows
+//     of earlier queries, which do not see it; NaN when the row's page entry
+//     lies outside the pool); wave W - 1 packs the new rows' K code dwords
+//     and wave W - 2 rewrites the groups' V code dwords (the other tokens'
+//     codes as they were).
+// The cached chunks this launch streams end before the new positions, so
+// the bytes written here are never read by it, except the other tokens'
+// codes of a shared V dword, which are written back unchanged.
+constexpr int kI2NewRows = 8;                   // rows one fused call appends (and query rows, JJ = 2)
+template <int D>
+struct I2NewIn {
+    static constexpr int NV = D / 64;           // a lane holds dims NV lane .. NV lane + NV - 1 of a row
+    static constexpr int GW = D / 128;          // V code dwords of an 8-token group per lane
+    float x[2];                                 // this wave's first block: dims 128 b + 2 lane, + 1
+    float q[NV];                                // query row `wave` (row rows - 1 past the last)
+    int e[2];                                   // page entries of the first and last new 8-token group
+    uint32_t old[2][GW];                        // those groups' V code dwords (wave W - 2)
+};
+// LDS of the end phase: codes [2][8][D] bytes (K, V), dequantized values
+// [2][8][D] floats
+template <int D>
+struct I2NewLds {
+    static constexpr int CODES = 0;
+    static constexpr int XHAT = 2 * kI2NewRows * D;
+    static constexpr int BYTES = XHAT + 2 * kI2NewRows * D * 4;
+};
+
+template <int NV>
+__device__ inline void load_row(const float* src, float (&x)[NV]) {
+    if constexpr (NV == 4) {
+        const floatx4 t = *reinterpret_cast<const floatx4*>(src);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = t[i];
+    } else {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) x[i] = src[i];
+    }
+}
+
+// Block `it` of the new rows: row j, tensor t (0 K, 1 V), block b.
+template <int D>
+__device__ inline const float* new_block_src(const NewRows& nr, int n_kv, int kvh, int it, int lane, int& j, int& t,
+                                             int& b) {
+    constexpr int NB2 = D / kBlock2;
+    j = it / (2 * NB2);
+    t = (it / NB2) % 2;
+    b = it % NB2;
+    return (t == 0 ? nr.k : nr.v) + ((size_t)j * n_kv + kvh) * D + kBlock2 * b + 2 * lane;
+}
+
+// Requests the inputs that need no page entry (the first round trip).
+template <int D, int W>
+__device__ inline void new_rows_load(const AttnArgs& a, const NewRows& nr, int kvh, int group, int rows, int wave,
+                                     int lane, I2NewIn<D>& in) {
+    constexpr int NV = I2NewIn<D>::NV;
+    const Geom& g = a.g;
+    if (wave < nr.n_new * 2 * (D / kBlock2)) {
+        int j, t, b;
+        const float* src = new_block_src<D>(nr, g.n_kv, kvh, wave, lane, j, t, b);
+        in.x[0] = src[0];
+        in.x[1] = src[1];
+    }
+    const int r = min(wave, rows - 1), qi = r / group, h = kvh * group + r % group;
+    load_row<NV>(a.q + ((size_t)qi * a.n_heads + h) * D + NV * lane, in.q);
+    const int g0 = nr.pos0 >> 3, g1 = (nr.pos0 + nr.n_new - 1) >> 3;
+    in.e[0] = a.page_table[(8 * g0) / g.P];
+    in.e[1] = a.page_table[(8 * g1) / g.P];
+}
+
+// Requests the old V code dwords of the new rows' groups (after the page
+// entries have arrived).  Dword u of a group, u = lane + 64 i: dims
+// 32 (u / 16) + u % 16 and 32 (u / 16) + 16 + u % 16 of its 8 tokens.
+template <int D>
+__device__ inline void new_rows_load_old(const AttnArgs& a, const NewRows& nr, int kvh, int lane, I2NewIn<D>& in) {
+    const Geom& g = a.g;
+    const int g0 = nr.pos0 >> 3, g1 = (nr.pos0 + nr.n_new - 1) >> 3;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int grp = t == 0 ? g0 : g1;
+        const bool ok = in.e[t] >= 0 && in.e[t] < g.n_pages && (t == 0 || g1 != g0);
+        const uint8_t* unit = a.pool + g.unit_index(ok ? in.e[t] : 0, kvh) * g.unit_bytes();
+#pragma unroll
+        for (int i = 0; i < I2NewIn<D>::GW; ++i) {
+            const int u = lane + 64 * i;
+            int bit;
+            const int64_t off = i2_v_dword(g, (8 * grp) % g.P, 32 * (u / 16) + u % 16, &bit);
+            in.old[t][i] = ok ? *reinterpret_cast<const uint32_t*>(unit + off) : 0u;
+        }
+    }
+}
+
+// The end phase of the new rows (every wave of the workgroup; starts and
+// ends at a workgroup barrier).  lds: I2NewLds<D>::BYTES of scratch no longer
+// read by the stream.
+template <int D, int W>
+__device__ inline void new_rows_finish(const AttnArgs& a, const NewRows& nr, int kvh, int group, int rows,
+                                       int n_splits, int part_stride, int wave, int lane, const I2NewIn<D>& in,
+                                       uint8_t* lds) {
+#pragma clang fp contract(off)
+    constexpr int NV = I2NewIn<D>::NV;
+    constexpr int NB2 = D / kBlock2;
+    using NL = I2NewLds<D>;
+    const Geom& g = a.g;
+    const int g0 = nr.pos0 >> 3, g1 = (nr.pos0 + nr.n_new - 1) >> 3;
+    auto entry = [&](int j) { return ((nr.pos0 + j) >> 3) == g0 ? in.e[0] : in.e[1]; };
+    auto valid = [&](int e) { return e >= 0 && e < g.n_pages; };
+    uint8_t* codes = lds + NL::CODES;                                // [t][j][D]
+    float* xhat = reinterpret_cast<float*>(lds + NL::XHAT);          // [t][j][D]
+    __syncthreads();                           // every wave has streamed its chunks: the scratch is free
+
+    // 1. the blocks: quantize, (scale, zero) into the pool, codes and values to LDS
+    const int n_items = nr.n_new * 2 * NB2;
+    for (int it = wave; it < n_items; it += W) {
+        int j, t, b;
+        const float* src = new_block_src<D>(nr, g.n_kv, kvh, it, lane, j, t, b);
+        const float x0 = it == wave ? in.x[0] : src[0];
+        const float x1 = it == wave ? in.x[1] : src[1];
+        const float mn = -wave_max(-fminf(x0, x1), lane);   // exact: negation and max
+        const float mx = wave_max(fmaxf(x0, x1), lane);
+        const Int2Par pr = int2_params(mn, mx);
+        const int c0 = int2_code(x0, mn, pr.id), c1 = int2_code(x1, mn, pr.id);
+        const uint16_t hs = f16_bits(pr.d), hz = f16_bits(mn);
+        const float d = __half2float(__ushort_as_half(hs)), z = __half2float(__ushort_as_half(hz));
+        const int dim = kBlock2 * b + 2 * lane;
+        *reinterpret_cast<uint16_t*>(codes + (t * kI2NewRows + j) * D + dim) = (uint16_t)(c0 | (c1 << 8));
+        // d c is exact: one rounding, as z + d c
+        *reinterpret_cast<float2*>(xhat + (t * kI2NewRows + j) * D + dim) =
+            float2{fmaf(d, (float)c0, z), fmaf(d, (float)c1, z)};
+        const int e = entry(j), slot = (nr.pos0 + j) % g.P;
+        if (lane == 0 && valid(e)) {
+            uint8_t* unit = nr.pool + g.unit_index(e, kvh) * g.unit_bytes();
+            if (t == 0) {
+                uint16_t* kp = reinterpret_cast<uint16_t*>(unit + g.i2_k_params_off()) + ((size_t)slot * NB2 + b) * 2;
+                kp[0] = hs;
+                kp[1] = hz;
+            } else {
+                const size_t vi = ((size_t)(slot / kChunk) * NB2 + b) * kChunk + slot % kChunk;
+                reinterpret_cast<uint16_t*>(unit + g.i2_v_scales_off())[vi] = hs;
+                reinterpret_cast<uint16_t*>(unit + g.i2_v_zeros_off())[vi] = hz;
+            }
+        }
+    }
+    __syncthreads();                           // codes and values visible to every wave
+
+    // 2a. wave r: query row r's partial for every new key
+    const float qscale = a.scale * kLog2e;
+    if (wave < rows) {
+        const int qi = wave / group, h = kvh * group + wave % group;
+        for (int j = 0; j < nr.n_new; ++j) {
+            float kh[NV], vh[NV];
+            load_row<NV>(xhat + j * D + NV * lane, kh);
+            load_row<NV>(xhat + (kI2NewRows + j) * D + NV * lane, vh);
+            float dot = 0.0f;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) dot = fmaf(in.q[i] * qscale, kh[i], dot);
+            const float sc = wave_sum(dot, lane);
+            const bool sees = qi >= j, ok = valid(entry(j));
+            const size_t ps = ((size_t)qi * a.n_heads + h) * part_stride + n_splits + j;
+            if (lane == 0) {
+                a.ws_m[ps] = !sees ? -INFINITY : ok ? sc : NAN;
+                a.ws_l[ps] = !sees ? 0.0f : ok ? 1.0f : NAN;
+            }
+            float* dst = a.ws_acc + ps * D + NV * lane;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) dst[i] = sees ? vh[i] : 0.0f;
+        }
+    }
+    // 2b. wave W - 1: the K code dwords (each token's own); lane l packs dword
+    // w = l % (D/16) of row j: dims 32 (2 k + h) + 8 grp + e, h < 2, e < 8,
+    // for grp = w / (D/64), k = w % (D/64)
+    if (wave == W - 1) {
+        constexpr int PER = D / 16;            // dwords per row
+        for (int j = lane / PER; j < nr.n_new; j += 64 / PER) {
+            const int e = entry(j);
+            if (!valid(e)) continue;
+            const int w = lane % PER, grp = w / (D / 64), k = w % (D / 64);
+            uint32_t word = 0;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t* src = reinterpret_cast<const uint32_t*>(codes + j * D + 32 * (2 * k + h) + 8 * grp);
+                const uint32_t c0 = src[0], c1 = src[1];   // dims e = 0..3 and 4..7, one code per byte
+#pragma unroll
+                for (int ee = 0; ee < 4; ++ee) {
+                    word |= ((c0 >> (8 * ee)) & 3u) << i2_bit(h, ee);
+                    word |= ((c1 >> (8 * ee)) & 3u) << i2_bit(h, ee + 4);
+                }
+            }
+            uint8_t* unit = nr.pool + g.unit_index(e, kvh) * g.unit_bytes();
+            int bit;
+            *reinterpret_cast<uint32_t*>(unit + i2_k_dword(g, (nr.pos0 + j) % g.P, 32 * (2 * k) + 8 * grp, &bit)) =
+                word;
+        }
+    }
+    // 2c. wave W - 2: the V code dwords of the new rows' groups, the new rows'
+    // two codes in each, the other tokens' codes as they were
+    if (wave == W - 2) {
+        const uint8_t* vcodes = codes + kI2NewRows * D;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int grp = t == 0 ? g0 : g1;
+            const bool ok = valid(in.e[t]) && (t == 0 || g1 != g0);
+            if (!ok) continue;
+            uint8_t* unit = nr.pool + g.unit_index(in.e[t], kvh) * g.unit_bytes();
+            const int j_lo = max(8 * grp, nr.pos0) - nr.pos0;
+            const int j_hi = min(8 * grp + 8, nr.pos0 + nr.n_new) - nr.pos0;
+#pragma unroll
+            for (int i = 0; i < I2NewIn<D>::GW; ++i) {
+                const int u = lane + 64 * i, n = u % 16, wi = u / 16;
+                uint32_t keep = in.old[t][i], put = 0;
+                for (int j = j_lo; j < j_hi; ++j) {
+                    const int ee = (nr.pos0 + j) & 7;
+                    const uint8_t* src = vcodes + j * D + 32 * wi + n;
+                    put |= ((uint32_t)src[0] << i2_bit(0, ee)) | ((uint32_t)src[16] << i2_bit(1, ee));
+                    keep &= ~((3u << i2_bit(0, ee)) | (3u << i2_bit(1, ee)));
+                }
+                int bit;
+                *reinterpret_cast<uint32_t*>(unit + i2_v_dword(g, (8 * grp) % g.P, 32 * wi + n, &bit)) = keep | put;
+            }
+        }
+    }
+}
+
 template <int D, int JJ, int W, int NSLOT>
 struct I2Lds {
     using C = I2Cfg<D>;
@@ -192,8 +431,9 @@ struct I2Lds {
     static_assert(BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <int D, int JJ, int W, int NSLOT, class Batch>
-__global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_splits, int group, int rows, Batch sb) {
+template <int D, int JJ, int W, int NSLOT, class Batch, bool NEWR>
+__global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_splits, int group, int rows, Batch sb,
+                                                           NewRows nr, int part_stride) {
     using C = I2Cfg<D>;
     using S = I2Slot<D>;
     using L = I2Lds<D, JJ, W, NSLOT>;
@@ -209,6 +449,7 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
         const int b = seq_of(sb.wg0, sb.n, wg);
         wg -= sb.wg0[b];
         n_splits = sb.n_splits[b];
+        part_stride = n_splits;
         a.ctx = sb.ctx[b];
         a.page_table += (size_t)b * sb.n_table;
         a.q += (size_t)b * a.n_q * a.n_heads * D;
@@ -227,6 +468,14 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
         const int ck = c0 + (kb + lane) * stride;
         return ck < c1 ? a.page_table[(ck * kChunk) / g.P] : -1;
     };
+    // fused decode step: this wave appends the new rows (after its chunks);
+    // their inputs are requested now
+    static_assert(!NEWR || (JJ == 2 && W == 8), "new rows with the up-to-8-rows layout, one wave per row");
+    const bool helper = NEWR && split == n_splits - 1;   // uniform over the workgroup
+    I2NewIn<D> nin;
+    if constexpr (NEWR) {
+        if (helper) new_rows_load<D, W>(a, nr, kvh, group, rows, wave, lane, nin);
+    }
     int ents = load_ents(0);
 
     // ---- q: A operands and per-block sums in LDS.  Thread (r, b, i) takes
@@ -242,10 +491,17 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
         if (b < C::NB2 && r < NROW) {           // uniform per 16 lanes
             const bool ok = r < rows;
             const int qi = ok ? r / group : 0, h = kvh * group + (ok ? r % group : 0);
+            // rows past the end read row 0 (a valid address), so the loads
+            // are unconditional: all in flight at once, no wait per element
             const float* src = a.q + ((size_t)qi * a.n_heads + h) * D + kBlock2 * b + 8 * i;
+            const floatx4 x0 = *reinterpret_cast<const floatx4*>(src);
+            const floatx4 x1 = *reinterpret_cast<const floatx4*>(src + 4);
             float x[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = ok ? src[e] * qscale : 0.0f;
+            for (int e = 0; e < 4; ++e) {
+                x[e] = ok ? x0[e] * qscale : 0.0f;
+                x[e + 4] = ok ? x1[e] * qscale : 0.0f;
+            }
             half8 hi, lo;
             float sum = 0.0f;
 #pragma unroll
@@ -506,6 +762,10 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
         dma16<kLoadNT>(unit + pbase + s0 * pmul, sl + S::P_OFF);
         ++n_req;
     };
+    if constexpr (NEWR) {
+        // older than every chunk request, so the chunk waits count as before
+        if (helper && wave == W - 2) new_rows_load_old<D>(a, nr, kvh, lane, nin);
+    }
 #pragma unroll
     for (int i = 0; i + 1 < NSLOT; ++i) request();
 
@@ -523,6 +783,13 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
     while (ci < n_mine && ci < stop) step(std::true_type{});
     bad = ci < n_mine;
     vm_wait<0>();          // nothing in flight into LDS past this point
+    if constexpr (NEWR) {
+        static_assert(!NEWR || L::CB_BYTES + I2NewLds<D>::BYTES <= L::LOOP_BYTES, "end-phase scratch");
+        // (scratch past the combine's buffer: rings, q and P buffers, dead by now)
+        if (helper)
+            new_rows_finish<D, W>(a, nr, kvh, group, rows, n_splits, part_stride, wave, lane, nin,
+                                  smem + L::CB_BYTES);
+    }
 
     // ---- finish: row sums, the zero-point term into o, then the W waves'
     // partials combined in wave order into one per workgroup
@@ -594,7 +861,7 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
             lt += lw[w] * f;
             acc += f * *reinterpret_cast<const floatx4*>(cb + w * SLOTW + slot * D + dim);
         }
-        const size_t ps = ((size_t)(row / group) * a.n_heads + kvh * group + row % group) * n_splits + split;
+        const size_t ps = ((size_t)(row / group) * a.n_heads + kvh * group + row % group) * part_stride + split;
         *reinterpret_cast<floatx4*>(a.ws_acc + ps * D + dim) = acc;
         if (dim == 0) {
             a.ws_m[ps] = mm;
@@ -606,31 +873,36 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
 constexpr int kInt2Waves = 8;   // two per SIMD, one workgroup per CU
 constexpr int kInt2Slots = 3;   // chunks in a wave's ring: two in flight while one is computed
 
-template <int D, int JJ, class Batch>
-hipError_t launch_dj(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream, const Batch& sb, int n_wg) {
+template <int D, int JJ, bool NEWR, class Batch>
+hipError_t launch_dj(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream, const Batch& sb, int n_wg,
+                     const NewRows& nr, int part_stride) {
     constexpr int W = kInt2Waves, NS = kInt2Slots;
     using L = I2Lds<D, JJ, W, NS>;
     if (L::BYTES > 64 * 1024) {
-        hipError_t e = allow_lds<attn_int2_kernel<D, JJ, W, NS, Batch>>(L::BYTES);
+        hipError_t e = allow_lds<attn_int2_kernel<D, JJ, W, NS, Batch, NEWR>>(L::BYTES);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((attn_int2_kernel<D, JJ, W, NS, Batch>), dim3(n_wg), dim3(W * 64), L::BYTES, stream, a,
-                       pl.n_splits, pl.group, pl.rows, sb);
+    hipLaunchKernelGGL((attn_int2_kernel<D, JJ, W, NS, Batch, NEWR>), dim3(n_wg), dim3(W * 64), L::BYTES, stream,
+                       a, pl.n_splits, pl.group, pl.rows, sb, nr, part_stride);
     return hipGetLastError();
 }
 
-template <int D, class Batch>
-hipError_t launch_d(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream, const Batch& sb, int n_wg) {
-    if (pl.rows <= 8) return launch_dj<D, 2>(a, pl, stream, sb, n_wg);
-    if (pl.rows <= 16) return launch_dj<D, 4>(a, pl, stream, sb, n_wg);
+template <int D, bool NEWR, class Batch>
+hipError_t launch_d(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream, const Batch& sb, int n_wg,
+                    const NewRows& nr, int part_stride) {
+    if (pl.rows <= 8) return launch_dj<D, 2, NEWR>(a, pl, stream, sb, n_wg, nr, part_stride);
+    if constexpr (!NEWR) {
+        if (pl.rows <= 16) return launch_dj<D, 4, false>(a, pl, stream, sb, n_wg, nr, part_stride);
+    }
     return hipErrorInvalidValue;
 }
 
-template <class Batch>
-hipError_t launch_any(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream, const Batch& sb, int n_wg) {
+template <bool NEWR, class Batch>
+hipError_t launch_any(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream, const Batch& sb, int n_wg,
+                      const NewRows& nr, int part_stride) {
     switch (a.g.D) {
-        case 128: return launch_d<128>(a, pl, stream, sb, n_wg);
-        case 256: return launch_d<256>(a, pl, stream, sb, n_wg);
+        case 128: return launch_d<128, NEWR>(a, pl, stream, sb, n_wg, nr, part_stride);
+        case 256: return launch_d<256, NEWR>(a, pl, stream, sb, n_wg, nr, part_stride);
         default: return hipErrorInvalidValue;
     }
 }
@@ -638,10 +910,18 @@ hipError_t launch_any(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream,
 }  // namespace
 
 int int2_waves() { return kInt2Waves; }
+int int2_max_new_rows() { return kI2NewRows; }
 
 hipError_t launch_attn_int2(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream, const SeqBatch* batch) {
-    if (batch != nullptr && batch->n > 0) return launch_any(a, pl, stream, *batch, batch->wg0[batch->n]);
-    return launch_any(a, pl, stream, NoBatch{}, pl.n_splits * a.g.n_kv);
+    const NewRows none{nullptr, nullptr, nullptr, 0, 0};
+    if (batch != nullptr && batch->n > 0)
+        return launch_any<false>(a, pl, stream, *batch, batch->wg0[batch->n], none, 0);
+    return launch_any<false>(a, pl, stream, NoBatch{}, pl.n_splits * a.g.n_kv, none, pl.n_splits);
+}
+
+hipError_t launch_attn_int2_new(const AttnArgs& a, const AttnPlan& pl, const NewRows& nr, hipStream_t stream) {
+    if (nr.n_new < 1 || nr.n_new > kI2NewRows || pl.rows > kI2NewRows || pl.n_splits < 1) return hipErrorInvalidValue;
+    return launch_any<true>(a, pl, stream, NoBatch{}, pl.n_splits * a.g.n_kv, nr, pl.n_splits + nr.n_new);
 }
 
 }  // namespace kvq

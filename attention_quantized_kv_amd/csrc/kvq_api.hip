@@ -222,9 +222,16 @@ int attn_impl(const kvq_layout* L, const void* d_pool, const int32_t* d_page_tab
 // Fused append + attention.  The streaming kernel can take the cached keys
 // alone (every new row sees all of them) and the merge kernel adds the new
 // rows; other kernel choices run kvq_append and then the attention call.
-bool append_attn_fused(const kvq_layout* L, int32_t n_heads, int32_t n_new, const kvq_attn_opts* opts) {
+// Over the INT2 cache the INT2 streaming kernel appends and scores the new
+// rows itself, up to 8 query rows per KV head and with cached keys before
+// them; other INT2 steps run kvq_append and then the attention call.
+bool append_attn_fused(const kvq_layout* L, int32_t n_heads, int32_t pos0, int32_t n_new, const kvq_attn_opts* opts) {
     const int kernel = opts ? opts->kernel : 0;
-    return L->codec == KVQ_CODEC_Q8K_Q4V && (kernel == 0 || kernel == 2) && n_new * (n_heads / L->n_kv_heads) <= 64;
+    const int rows = n_new * (n_heads / L->n_kv_heads);
+    if (L->codec == KVQ_CODEC_INT2)
+        return (kernel == 0 || kernel == 4) && pos0 > 0 && rows <= kvq::int2_max_new_rows() &&
+               n_new <= kvq::int2_max_new_rows();
+    return L->codec == KVQ_CODEC_Q8K_Q4V && (kernel == 0 || kernel == 2) && rows <= 64;
 }
 
 // Where a fused step's new rows are quantized and scored.  With one row
@@ -232,7 +239,12 @@ bool append_attn_fused(const kvq_layout* L, int32_t n_heads, int32_t n_new, cons
 // cached chunks the other waves of its workgroup take over from the LDS list.
 // With several row groups (the verify batch's fixed chunk order) that wave
 // would hold up its workgroup's end, so the merge kernel does it instead.
-bool new_rows_in_split(const kvq::AttnPlan& pl) { return pl.n_splits > 0 && kvq::mfma_stream_row_groups(pl.rows) == 1; }
+// The INT2 streaming kernel always does it (one wave per KV head, after its
+// chunks).
+bool new_rows_in_split(const kvq::AttnPlan& pl) {
+    if (pl.kernel == 4) return pl.n_splits > 0;
+    return pl.n_splits > 0 && kvq::mfma_stream_row_groups(pl.rows) == 1;
+}
 
 // Partials per row of a fused step: the splits over the cached keys, and one
 // per new row when the split kernel handles them.
@@ -250,7 +262,7 @@ int append_attn_plan(const kvq_layout* L, int32_t n_heads, int32_t pos0, int32_t
                      bool fused, kvq::AttnPlan* pl) {
     if (!fused) return make_plan(L, n_heads, pos0 + n_new, n_new, false, opts, pl);
     kvq_attn_opts o = opts ? *opts : kvq_attn_opts{0, 0, nullptr, nullptr};
-    o.kernel = 2;
+    o.kernel = L->codec == KVQ_CODEC_INT2 ? 4 : 2;
     if (pos0 > 0) return make_plan(L, n_heads, pos0, n_new, false, &o, pl);
     int st = make_plan(L, n_heads, kvq::kChunk, n_new, false, &o, pl);   // checks only: no cached keys
     pl->n_splits = 0;
@@ -413,7 +425,7 @@ int kvq_append_attn_workspace_bytes(const kvq_layout* layout, int32_t n_heads, i
     if (bytes == nullptr) return fail(KVQ_ERR_INVALID_ARG, "bytes is NULL");
     st = check_append_attn(layout, INT32_MAX / layout->page_size, pos0, n_new, n_heads);
     if (st) return st;
-    const bool fused = append_attn_fused(layout, n_heads, n_new, opts);
+    const bool fused = append_attn_fused(layout, n_heads, pos0, n_new, opts);
     kvq::AttnPlan pl;
     st = append_attn_plan(layout, n_heads, pos0, n_new, opts, fused, &pl);
     if (st) return st;
@@ -439,7 +451,7 @@ int append_attn_impl(const kvq_layout* layout, void* d_pool, const int32_t* d_pa
     st = check_append_attn(layout, n_table, pos0, n_new, n_heads);
     if (st) return st;
     if (((uintptr_t)d_pool & 255) != 0) return fail(KVQ_ERR_INVALID_ARG, "pool must be 256-byte aligned");
-    const bool fused = append_attn_fused(layout, n_heads, n_new, opts);
+    const bool fused = append_attn_fused(layout, n_heads, pos0, n_new, opts);
     if (!fused) {
         st = kvq_append(layout, d_pool, d_page_table, n_table, pos0, n_new, d_k, d_v, stream);
         if (st) return st;
@@ -485,7 +497,8 @@ int append_attn_impl(const kvq_layout* layout, void* d_pool, const int32_t* d_pa
     // to the merge kernel, which appends and scores them itself (also when
     // there are no cached keys, pos0 = 0).
     const bool in_split = new_rows_in_split(pl);
-    if (e == hipSuccess && in_split) e = kvq::launch_attn_mfma_stream_new(a, pl, nr, s);
+    if (e == hipSuccess && in_split)
+        e = pl.kernel == 4 ? kvq::launch_attn_int2_new(a, pl, nr, s) : kvq::launch_attn_mfma_stream_new(a, pl, nr, s);
     else if (e == hipSuccess && pl.n_splits > 0) e = kvq::launch_attn_mfma_stream(a, pl, s);
     if (e == hipSuccess && opts != nullptr && opts->kernel_end_event != nullptr)
         e = hipEventRecord(static_cast<hipEvent_t>(opts->kernel_end_event), s);

@@ -156,4 +156,24 @@ __device__ inline QCode quant_q4_0(float x, int lane_in_wave) {
     return {min(15, __float2int_rz(t)), d};
 }
 
+// INT2 (128-value blocks, value = zero + scale * code): from the block's
+// minimum mn and maximum mx, d = (mx - mn) / 3 and its reciprocal id (0 when
+// d = 0), and the code of x, min(3, trunc((x - mn) * id + 0.5)) -- the
+// nearest of the four levels, ties upward.  The minimum and maximum are exact
+// whatever the reduction order, so every kernel that quantizes a block gets
+// the same codes and fp16 (scale, zero) = (fp16(d), fp16(mn)).
+struct Int2Par {
+    float d;
+    float id;
+};
+__device__ inline Int2Par int2_params(float mn, float mx) {
+#pragma clang fp contract(off)
+    const float d = __fdiv_rn(mx - mn, 3.0f);
+    return {d, d != 0.0f ? __fdiv_rn(1.0f, d) : 0.0f};
+}
+__device__ inline int int2_code(float x, float mn, float id) {
+#pragma clang fp contract(off)
+    return min(3, (int)(mul_rounded(x - mn, id) + 0.5f));
+}
+
 }  // namespace kvq

@@ -102,11 +102,10 @@ __global__ __launch_bounds__(512) void append_int2_kernel(Geom g, uint8_t* __res
             const float x0 = x[src], x1 = x[src + 1];
             const float mn = -wave_max(-fminf(x0, x1), lane);  // exact: negation and max
             const float mx = wave_max(fmaxf(x0, x1), lane);
-            const float d = __fdiv_rn(mx - mn, 3.0f);
-            const float id = d != 0.0f ? __fdiv_rn(1.0f, d) : 0.0f;
-            codes[e][2 * lane] = (uint8_t)min(3, (int)(mul_rounded(x0 - mn, id) + 0.5f));
-            codes[e][2 * lane + 1] = (uint8_t)min(3, (int)(mul_rounded(x1 - mn, id) + 0.5f));
-            hs = f16_bits(d);
+            const Int2Par pr = int2_params(mn, mx);
+            codes[e][2 * lane] = (uint8_t)int2_code(x0, mn, pr.id);
+            codes[e][2 * lane + 1] = (uint8_t)int2_code(x1, mn, pr.id);
+            hs = f16_bits(pr.d);
             hz = f16_bits(mn);
         };
         uint16_t hs, hz;

@@ -514,8 +514,8 @@ def main():
     else:
         layers = [Layer(w, i, dev, shuffle_pages=args.shuffle_pages) for i in range(n_layers)]
     Layer.cps = args.cps
-    # (the INT2 codec has no fused append + attention: append, then attend)
-    fused = not prefill and not args.unfused and not batched and w.codec == 0
+    # decode and verify run the fused step kvq_append_attn (over both codecs)
+    fused = not prefill and not args.unfused and not batched
     if batched:
         ws_n = kvq.kvq_decode_attn_batch_workspace_bytes(layers[0].L, layers[0].ctx_lens, w.n_heads, w.n_q)
     elif fused:

@@ -233,12 +233,15 @@ int kvq_attn_ex(const kvq_layout *layout, const void *d_pool,
  * kvq_attn_ex(ctx_len = pos0 + n_new, n_q = n_new), in two launches instead
  * of three ("Qwen 27B (IQ4_XS, Q8/Q4 KV) on a 16GB RX 9070 XT at 262k
  * context, via adaptive KV streaming": quantize on append, paged decode
- * attention, online log-sum-exp across pages).  With the streaming kernel
- * (opts->kernel 0 or 2, n_new * group <= 64) the split pass reads the pos0
- * cached keys only, and the merge pass quantizes the new rows (the same codes
- * and scales kvq_append writes), scores them, folds them into the softmax and
- * writes them into the pool.  Other kernel choices run kvq_append and the
- * attention one after the other.
+ * attention, online log-sum-exp across pages).  Over the Q8_0/Q4_0 cache
+ * with the streaming kernel (opts->kernel 0 or 2, n_new * group <= 64), and
+ * over the INT2 cache with its streaming kernel (opts->kernel 0 or 4,
+ * n_new * group <= 8, pos0 >= 1), the split pass reads the pos0 cached keys
+ * only; the new rows are quantized (the same codes and scales kvq_append
+ * writes), written into the pool and scored by the split pass (or, over
+ * Q8_0/Q4_0 with more than 32 query rows or no cached keys, by the merge
+ * pass), and the merge pass folds them into the softmax.  Other choices run
+ * kvq_append and the attention one after the other.
  *   pos0, n_new, d_k, d_v  as for kvq_append (1 <= n_new <= KVQ_MAX_NQ_DECODE)
  *   d_q, d_out, d_lse      as for attention with n_q = n_new
  *   d_ws   workspace of at least kvq_append_attn_workspace_bytes() bytes

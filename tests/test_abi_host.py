@@ -245,3 +245,38 @@ def test_noalloc_rejects_steps_beyond_its_scratch():
                                        ctypes.c_float(0.0625), FAKE, None, None, None) == kvq.KVQ_ERR_INVALID_ARG
     # the decode workload's step fits
     assert kvq.kvq_append_attn_workspace_bytes(L, 24, 262143, 1) <= cap
+
+
+def _ws_expected(rows, parts, D):
+    """Workspace of `parts` partials per row: acc [rows][parts][D] floats,
+    then m and l [rows][parts] floats, each rounded up to 256 bytes."""
+    ml = (rows * parts * 4 + 255) // 256 * 256
+    return rows * parts * D * 4 + 2 * ml
+
+
+def test_int2_fused_step_plan():
+    """kvq_append_attn over the INT2 codec: with cached keys and at most 8
+    query rows per KV head the step is fused (the split kernel's partials
+    over the cached keys plus one partial per new row); without cached keys,
+    or with more rows, it is kvq_append followed by the attention call, whose
+    workspace it then asks for."""
+    D, n_kv, n_heads = 256, 4, 24
+    L = kvq.Layout(n_kv, D, 256, 1100, kvq.KVQ_CODEC_INT2)
+    pos0 = 262143
+    # the attention plan over the cached keys alone gives the split count
+    attn = kvq.kvq_workspace_bytes_ex(L, n_heads, pos0, 1, kernel=4)
+    rows = 1 * n_heads
+    splits = [s for s in range(1, 4097) if _ws_expected(rows, s, D) == attn]
+    assert len(splits) == 1
+    fused = kvq.kvq_append_attn_workspace_bytes(L, n_heads, pos0, 1)
+    assert fused == _ws_expected(rows, splits[0] + 1, D)
+    # no cached keys: kvq_append, then attention over the one new key
+    assert kvq.kvq_append_attn_workspace_bytes(L, n_heads, 0, 1) == kvq.kvq_workspace_bytes_ex(L, n_heads, 1, 1)
+    # 12 rows per KV head (two queries, group 6): not fused
+    assert kvq.kvq_append_attn_workspace_bytes(L, n_heads, 5000, 2) == kvq.kvq_workspace_bytes_ex(L, n_heads, 5002, 2)
+    # 8 rows (four queries, group 2) with kernel 4 asked for: fused
+    L2 = kvq.Layout(2, 128, 32, 300, kvq.KVQ_CODEC_INT2)
+    a2 = kvq.kvq_workspace_bytes_ex(L2, 4, 901, 4, kernel=4)
+    s2 = [s for s in range(1, 4097) if _ws_expected(16, s, 128) == a2]
+    assert len(s2) == 1
+    assert kvq.kvq_append_attn_workspace_bytes(L2, 4, 901, 4, kernel=4) == _ws_expected(16, s2[0] + 4, 128)
