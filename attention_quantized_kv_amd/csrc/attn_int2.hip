@@ -185,7 +185,7 @@ __host__ __device__ constexpr int code_slot(int s) { return (s & 4) | ((s & 1) <
 //     zero-points are those kvq_append writes, bit for bit; it writes the
 //     block's (scale, zero) into the pool and leaves codes and dequantized
 //     values in LDS;
-//  2. wave r < rows scores query row r against each new key and leaves the
+//  2. wave r scores query rows r and r + 8 (< rows) against each new key and leaves the
 //     key's softmax state as partial n_splits + j of the row: m = the score,
 //     l = 1, acc = the dequantized V row (an empty partial, l = 0, for rows
 //     of earlier queries, which do not see it; NaN when the row's page entry
@@ -195,13 +195,13 @@ __host__ __device__ constexpr int code_slot(int s) { return (s & 4) | ((s & 1) <
 // The cached chunks this launch streams end before the new positions, so
 // the bytes written here are never read by it, except the other tokens'
 // codes of a shared V dword, which are written back unchanged.
-constexpr int kI2NewRows = 8;                   // rows one fused call appends (and query rows, JJ = 2)
-template <int D>
+constexpr int kI2NewRows = 8;                   // rows one fused call appends
+template <int D, int QW>
 struct I2NewIn {
     static constexpr int NV = D / 64;           // a lane holds dims NV lane .. NV lane + NV - 1 of a row
     static constexpr int GW = D / 128;          // V code dwords of an 8-token group per lane
     float x[2];                                 // this wave's first block: dims 128 b + 2 lane, + 1
-    float q[NV];                                // query row `wave` (row rows - 1 past the last)
+    float q[QW][NV];                            // query rows `wave` (and `wave` + 8, QW = 2); row rows - 1 past the last
     int e[2];                                   // page entries of the first and last new 8-token group
     uint32_t old[2][GW];                        // those groups' V code dwords (wave W - 2)
 };
@@ -238,10 +238,10 @@ __device__ inline const float* new_block_src(const NewRows& nr, int n_kv, int kv
 }
 
 // Requests the inputs that need no page entry (the first round trip).
-template <int D, int W>
+template <int D, int W, int QW>
 __device__ inline void new_rows_load(const AttnArgs& a, const NewRows& nr, int kvh, int group, int rows, int wave,
-                                     int lane, I2NewIn<D>& in) {
-    constexpr int NV = I2NewIn<D>::NV;
+                                     int lane, I2NewIn<D, QW>& in) {
+    constexpr int NV = I2NewIn<D, QW>::NV;
     const Geom& g = a.g;
     if (wave < nr.n_new * 2 * (D / kBlock2)) {
         int j, t, b;
@@ -249,8 +249,11 @@ __device__ inline void new_rows_load(const AttnArgs& a, const NewRows& nr, int k
         in.x[0] = src[0];
         in.x[1] = src[1];
     }
-    const int r = min(wave, rows - 1), qi = r / group, h = kvh * group + r % group;
-    load_row<NV>(a.q + ((size_t)qi * a.n_heads + h) * D + NV * lane, in.q);
+#pragma unroll
+    for (int i = 0; i < QW; ++i) {
+        const int r = min(wave + 8 * i, rows - 1), qi = r / group, h = kvh * group + r % group;
+        load_row<NV>(a.q + ((size_t)qi * a.n_heads + h) * D + NV * lane, in.q[i]);
+    }
     const int g0 = nr.pos0 >> 3, g1 = (nr.pos0 + nr.n_new - 1) >> 3;
     in.e[0] = a.page_table[(8 * g0) / g.P];
     in.e[1] = a.page_table[(8 * g1) / g.P];
@@ -259,8 +262,9 @@ __device__ inline void new_rows_load(const AttnArgs& a, const NewRows& nr, int k
 // Requests the old V code dwords of the new rows' groups (after the page
 // entries have arrived).  Dword u of a group, u = lane + 64 i: dims
 // 32 (u / 16) + u % 16 and 32 (u / 16) + 16 + u % 16 of its 8 tokens.
-template <int D>
-__device__ inline void new_rows_load_old(const AttnArgs& a, const NewRows& nr, int kvh, int lane, I2NewIn<D>& in) {
+template <int D, int QW>
+__device__ inline void new_rows_load_old(const AttnArgs& a, const NewRows& nr, int kvh, int lane,
+                                         I2NewIn<D, QW>& in) {
     const Geom& g = a.g;
     const int g0 = nr.pos0 >> 3, g1 = (nr.pos0 + nr.n_new - 1) >> 3;
 #pragma unroll
@@ -269,7 +273,7 @@ __device__ inline void new_rows_load_old(const AttnArgs& a, const NewRows& nr, i
         const bool ok = in.e[t] >= 0 && in.e[t] < g.n_pages && (t == 0 || g1 != g0);
         const uint8_t* unit = a.pool + g.unit_index(ok ? in.e[t] : 0, kvh) * g.unit_bytes();
 #pragma unroll
-        for (int i = 0; i < I2NewIn<D>::GW; ++i) {
+        for (int i = 0; i < I2NewIn<D, QW>::GW; ++i) {
             const int u = lane + 64 * i;
             int bit;
             const int64_t off = i2_v_dword(g, (8 * grp) % g.P, 32 * (u / 16) + u % 16, &bit);
@@ -281,12 +285,12 @@ __device__ inline void new_rows_load_old(const AttnArgs& a, const NewRows& nr, i
 // The end phase of the new rows (every wave of the workgroup; starts and
 // ends at a workgroup barrier).  lds: I2NewLds<D>::BYTES of scratch no longer
 // read by the stream.
-template <int D, int W>
+template <int D, int W, int QW>
 __device__ inline void new_rows_finish(const AttnArgs& a, const NewRows& nr, int kvh, int group, int rows,
-                                       int n_splits, int part_stride, int wave, int lane, const I2NewIn<D>& in,
+                                       int n_splits, int part_stride, int wave, int lane, const I2NewIn<D, QW>& in,
                                        uint8_t* lds) {
 #pragma clang fp contract(off)
-    constexpr int NV = I2NewIn<D>::NV;
+    constexpr int NV = I2NewIn<D, QW>::NV;
     constexpr int NB2 = D / kBlock2;
     using NL = I2NewLds<D>;
     const Geom& g = a.g;
@@ -331,17 +335,20 @@ __device__ inline void new_rows_finish(const AttnArgs& a, const NewRows& nr, int
     }
     __syncthreads();                           // codes and values visible to every wave
 
-    // 2a. wave r: query row r's partial for every new key
+    // 2a. wave w: query rows w and w + 8, each row's partial for every new key
     const float qscale = a.scale * kLog2e;
-    if (wave < rows) {
-        const int qi = wave / group, h = kvh * group + wave % group;
+#pragma unroll
+    for (int i = 0; i < QW; ++i) {
+        const int r = wave + 8 * i;
+        if (r >= rows) break;                  // uniform
+        const int qi = r / group, h = kvh * group + r % group;
         for (int j = 0; j < nr.n_new; ++j) {
             float kh[NV], vh[NV];
             load_row<NV>(xhat + j * D + NV * lane, kh);
             load_row<NV>(xhat + (kI2NewRows + j) * D + NV * lane, vh);
             float dot = 0.0f;
 #pragma unroll
-            for (int i = 0; i < NV; ++i) dot = fmaf(in.q[i] * qscale, kh[i], dot);
+            for (int e = 0; e < NV; ++e) dot = fmaf(in.q[i][e] * qscale, kh[e], dot);
             const float sc = wave_sum(dot, lane);
             const bool sees = qi >= j, ok = valid(entry(j));
             const size_t ps = ((size_t)qi * a.n_heads + h) * part_stride + n_splits + j;
@@ -351,7 +358,7 @@ __device__ inline void new_rows_finish(const AttnArgs& a, const NewRows& nr, int
             }
             float* dst = a.ws_acc + ps * D + NV * lane;
 #pragma unroll
-            for (int i = 0; i < NV; ++i) dst[i] = sees ? vh[i] : 0.0f;
+            for (int e = 0; e < NV; ++e) dst[e] = sees ? vh[e] : 0.0f;
         }
     }
     // 2b. wave W - 1: the K code dwords (each token's own); lane l packs dword
@@ -393,7 +400,7 @@ __device__ inline void new_rows_finish(const AttnArgs& a, const NewRows& nr, int
             const int j_lo = max(8 * grp, nr.pos0) - nr.pos0;
             const int j_hi = min(8 * grp + 8, nr.pos0 + nr.n_new) - nr.pos0;
 #pragma unroll
-            for (int i = 0; i < I2NewIn<D>::GW; ++i) {
+            for (int i = 0; i < I2NewIn<D, QW>::GW; ++i) {
                 const int u = lane + 64 * i, n = u % 16, wi = u / 16;
                 uint32_t keep = in.old[t][i], put = 0;
                 for (int j = j_lo; j < j_hi; ++j) {
@@ -470,11 +477,12 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
     };
     // fused decode step: this wave appends the new rows (after its chunks);
     // their inputs are requested now
-    static_assert(!NEWR || (JJ == 2 && W == 8), "new rows with the up-to-8-rows layout, one wave per row");
+    static_assert(!NEWR || W == 8, "new rows: eight waves, each with query rows w and w + 8");
     const bool helper = NEWR && split == n_splits - 1;   // uniform over the workgroup
-    I2NewIn<D> nin;
+    constexpr int QW = JJ == 4 ? 2 : 1;        // query rows per wave: up to 8 or up to 16 in all
+    I2NewIn<D, QW> nin;
     if constexpr (NEWR) {
-        if (helper) new_rows_load<D, W>(a, nr, kvh, group, rows, wave, lane, nin);
+        if (helper) new_rows_load<D, W, QW>(a, nr, kvh, group, rows, wave, lane, nin);
     }
     int ents = load_ents(0);
 
@@ -764,7 +772,7 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
     };
     if constexpr (NEWR) {
         // older than every chunk request, so the chunk waits count as before
-        if (helper && wave == W - 2) new_rows_load_old<D>(a, nr, kvh, lane, nin);
+        if (helper && wave == W - 2) new_rows_load_old<D, QW>(a, nr, kvh, lane, nin);
     }
 #pragma unroll
     for (int i = 0; i + 1 < NSLOT; ++i) request();
@@ -787,7 +795,7 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
         static_assert(!NEWR || L::CB_BYTES + I2NewLds<D>::BYTES <= L::LOOP_BYTES, "end-phase scratch");
         // (scratch past the combine's buffer: rings, q and P buffers, dead by now)
         if (helper)
-            new_rows_finish<D, W>(a, nr, kvh, group, rows, n_splits, part_stride, wave, lane, nin,
+            new_rows_finish<D, W, QW>(a, nr, kvh, group, rows, n_splits, part_stride, wave, lane, nin,
                                   smem + L::CB_BYTES);
     }
 
@@ -891,9 +899,7 @@ template <int D, bool NEWR, class Batch>
 hipError_t launch_d(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream, const Batch& sb, int n_wg,
                     const NewRows& nr, int part_stride) {
     if (pl.rows <= 8) return launch_dj<D, 2, NEWR>(a, pl, stream, sb, n_wg, nr, part_stride);
-    if constexpr (!NEWR) {
-        if (pl.rows <= 16) return launch_dj<D, 4, false>(a, pl, stream, sb, n_wg, nr, part_stride);
-    }
+    if (pl.rows <= 16) return launch_dj<D, 4, NEWR>(a, pl, stream, sb, n_wg, nr, part_stride);
     return hipErrorInvalidValue;
 }
 
@@ -920,7 +926,7 @@ hipError_t launch_attn_int2(const AttnArgs& a, const AttnPlan& pl, hipStream_t s
 }
 
 hipError_t launch_attn_int2_new(const AttnArgs& a, const AttnPlan& pl, const NewRows& nr, hipStream_t stream) {
-    if (nr.n_new < 1 || nr.n_new > kI2NewRows || pl.rows > kI2NewRows || pl.n_splits < 1) return hipErrorInvalidValue;
+    if (nr.n_new < 1 || nr.n_new > kI2NewRows || pl.rows > 16 || pl.n_splits < 1) return hipErrorInvalidValue;
     return launch_any<true>(a, pl, stream, NoBatch{}, pl.n_splits * a.g.n_kv, nr, pl.n_splits + nr.n_new);
 }
 

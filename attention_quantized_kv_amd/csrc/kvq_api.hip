@@ -223,14 +223,14 @@ int attn_impl(const kvq_layout* L, const void* d_pool, const int32_t* d_page_tab
 // alone (every new row sees all of them) and the merge kernel adds the new
 // rows; other kernel choices run kvq_append and then the attention call.
 // Over the INT2 cache the INT2 streaming kernel appends and scores the new
-// rows itself, up to 8 query rows per KV head and with cached keys before
-// them; other INT2 steps run kvq_append and then the attention call.
+// rows itself, up to 16 query rows per KV head (its range) and with cached
+// keys before them; other INT2 steps run kvq_append and then the attention
+// call.
 bool append_attn_fused(const kvq_layout* L, int32_t n_heads, int32_t pos0, int32_t n_new, const kvq_attn_opts* opts) {
     const int kernel = opts ? opts->kernel : 0;
     const int rows = n_new * (n_heads / L->n_kv_heads);
     if (L->codec == KVQ_CODEC_INT2)
-        return (kernel == 0 || kernel == 4) && pos0 > 0 && rows <= kvq::int2_max_new_rows() &&
-               n_new <= kvq::int2_max_new_rows();
+        return (kernel == 0 || kernel == 4) && pos0 > 0 && rows <= 16 && n_new <= kvq::int2_max_new_rows();
     return L->codec == KVQ_CODEC_Q8K_Q4V && (kernel == 0 || kernel == 2) && rows <= 64;
 }
 

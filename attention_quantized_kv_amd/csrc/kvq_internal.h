@@ -206,7 +206,7 @@ hipError_t launch_hadamard(float* x, int64_t n_rows, int dim, hipStream_t stream
 hipError_t launch_attn_int2(const AttnArgs& a, const AttnPlan& pl, hipStream_t stream,
                             const SeqBatch* batch = nullptr);
 int int2_waves();
-// The INT2 streaming kernel of a fused decode step (rows <= 8, pl.n_splits
+// The INT2 streaming kernel of a fused decode step (rows <= 16, pl.n_splits
 // >= 1 over the cached keys, 1 <= nr.n_new <= int2_max_new_rows()): it also
 // quantizes the appended rows into the pool and leaves new row j's softmax
 // state as partial n_splits + j of every row, like

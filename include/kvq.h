@@ -236,7 +236,7 @@ int kvq_attn_ex(const kvq_layout *layout, const void *d_pool,
  * attention, online log-sum-exp across pages).  Over the Q8_0/Q4_0 cache
  * with the streaming kernel (opts->kernel 0 or 2, n_new * group <= 64), and
  * over the INT2 cache with its streaming kernel (opts->kernel 0 or 4,
- * n_new * group <= 8, pos0 >= 1), the split pass reads the pos0 cached keys
+ * n_new * group <= 16, pos0 >= 1), the split pass reads the pos0 cached keys
  * only; the new rows are quantized (the same codes and scales kvq_append
  * writes), written into the pool and scored by the split pass (or, over
  * Q8_0/Q4_0 with more than 32 query rows or no cached keys, by the merge

@@ -255,7 +255,7 @@ def _ws_expected(rows, parts, D):
 
 
 def test_int2_fused_step_plan():
-    """kvq_append_attn over the INT2 codec: with cached keys and at most 8
+    """kvq_append_attn over the INT2 codec: with cached keys and at most 16
     query rows per KV head the step is fused (the split kernel's partials
     over the cached keys plus one partial per new row); without cached keys,
     or with more rows, it is kvq_append followed by the attention call, whose
@@ -272,8 +272,14 @@ def test_int2_fused_step_plan():
     assert fused == _ws_expected(rows, splits[0] + 1, D)
     # no cached keys: kvq_append, then attention over the one new key
     assert kvq.kvq_append_attn_workspace_bytes(L, n_heads, 0, 1) == kvq.kvq_workspace_bytes_ex(L, n_heads, 1, 1)
-    # 12 rows per KV head (two queries, group 6): not fused
-    assert kvq.kvq_append_attn_workspace_bytes(L, n_heads, 5000, 2) == kvq.kvq_workspace_bytes_ex(L, n_heads, 5002, 2)
+    # 18 rows per KV head (three queries, group 6: past the INT2 streaming
+    # kernel's 16): not fused
+    assert kvq.kvq_append_attn_workspace_bytes(L, n_heads, 5000, 3) == kvq.kvq_workspace_bytes_ex(L, n_heads, 5003, 3)
+    # 12 rows (two queries, group 6): fused
+    a12 = kvq.kvq_workspace_bytes_ex(L, n_heads, 5000, 2, kernel=4)
+    s12 = [s for s in range(1, 4097) if _ws_expected(2 * n_heads, s, D) == a12]
+    assert len(s12) == 1
+    assert kvq.kvq_append_attn_workspace_bytes(L, n_heads, 5000, 2) == _ws_expected(2 * n_heads, s12[0] + 2, D)
     # 8 rows (four queries, group 2) with kernel 4 asked for: fused
     L2 = kvq.Layout(2, 128, 32, 300, kvq.KVQ_CODEC_INT2)
     a2 = kvq.kvq_workspace_bytes_ex(L2, 4, 901, 4, kernel=4)

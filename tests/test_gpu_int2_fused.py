@@ -1,5 +1,5 @@
 """GPU: the fused decode step over the INT2 cache (kvq_append_attn with up to
-8 query rows per KV head and cached keys before the new rows), where the INT2
+16 query rows per KV head and cached keys before the new rows), where the INT2
 streaming kernel also quantizes the new rows into the pool and scores them.
 
 For every case the pool after the fused step must equal, byte for byte, the
@@ -9,7 +9,8 @@ dwords), and the output must match the oracle's fp64 attention over the
 whole cache (cached keys plus the new rows, causal among the new rows).
 Cases: one decode row over four KV heads, several new rows spanning two
 8-token groups, a new-row run across a page boundary, head_dim 128 and 256,
-a single cached key, eight new rows with group 1, a split count forced low
+a single cached key, eight new rows with group 1, 12 and 16 query rows (two
+per wave in the end phase), a split count forced low
 (many chunks per wave), and a bad page entry for the new rows (NaN, nothing
 written).
 """
@@ -64,6 +65,9 @@ def _step(L, pool, pt_dev, pos0, k_new, v_new, q, scale, cps=0):
     (4, 128, 32, 1, 8, 2, 1, 0),           # a single cached key, eight new rows
     (5, 256, 32, 20000, 1, 2, 8, 40),      # group 8; few splits, many chunks per wave
     (6, 128, 64, 4093, 2, 1, 4, 0),        # ragged last chunk, causal pair
+    (9, 256, 64, 5000, 2, 2, 6, 0),        # 12 rows: the 16-row layout, two query rows per wave
+    (10, 128, 32, 1234, 4, 1, 4, 0),       # 16 rows, four causal new rows in one group
+    (11, 256, 256, 30000, 2, 4, 8, 0),     # 16 rows over four KV heads
 ])
 def test_int2_fused_step_matches_append_and_oracle(seed, D, P, pos0, n_new, n_kv, G, cps):
     import torch
