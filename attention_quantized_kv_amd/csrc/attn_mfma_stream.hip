@@ -659,11 +659,13 @@ __global__ __launch_bounds__(W * 64) void attn_mfma_stream_kernel(AttnArgs a, in
         }
     }
 
+    // the wave's own entries go out before the list gather, whose stores
+    // into LDS wait for their loads: all of them arrive in one round trip
+    int ents = load_ents(0);
     if (dyn) {
         for (int p = threadIdx.x; p < n_list; p += W * 64) lst[p] = a.page_table[(list_chunk(p) * kChunk) / g.P];
         if (threadIdx.x == 0) lctr[0] = W;
     }
-    int ents = load_ents(0);
     asm volatile("" : "+v"(ents));             // wait for it (and q) here, before any chunk request
     // first slot of the current chunk in its page; it advances by dslot (mod P)
     // from one chunk of the wave to the next
