@@ -770,6 +770,10 @@ __global__ __launch_bounds__(W * 64) void attn_int2_kernel(AttnArgs a, int n_spl
         dma16<kLoadNT>(unit + pbase + s0 * pmul, sl + S::P_OFF);
         ++n_req;
     };
+    // the page entries are in by now, but their waits sat in the q staging's
+    // branch: use them here, so that no wait before the first chunk request
+    // (the first readlane) also waits for loads issued after this point
+    asm volatile("" : "+v"(ents));
     if constexpr (NEWR) {
         // older than every chunk request, so the chunk waits count as before
         if (helper && wave == W - 2) new_rows_load_old<D, QW>(a, nr, kvh, lane, nin);
