@@ -185,16 +185,17 @@ __host__ __device__ constexpr int code_slot(int s) { return (s & 4) | ((s & 1) <
 //     zero-points are those kvq_append writes, bit for bit; it writes the
 //     block's (scale, zero) into the pool and leaves codes and dequantized
 //     values in LDS;
-//  2. wave r scores query rows r and r + 8 (< rows) against each new key and leaves the
-//     key's softmax state as partial n_splits + j of the row: m = the score,
-//     l = 1, acc = the dequantized V row (an empty partial, l = 0, for rows
-//     of earlier queries, which do not see it; NaN when the row's page entry
-//     lies outside the pool); wave W - 1 packs the new rows' K code dwords
-//     and wave W - 2 rewrites the groups' V code dwords (the other tokens'
-//     codes as they were).
-// The cached chunks this launch streams end before the new positions, so
-// the bytes written here are never read by it, except the other tokens'
-// codes of a shared V dword, which are written back unchanged.
+//  2. wave r scores query rows r and r + 8 (those below rows) against each
+//     new key and leaves the key's softmax state as partial n_splits + j of
+//     the row: m = the score, l = 1, acc = the dequantized V row (an empty
+//     partial, l = 0, for rows of earlier queries, which do not see it; NaN
+//     when the row's page entry lies outside the pool); wave W - 1 packs the
+//     new rows' K code dwords and wave W - 2 rewrites the groups' V code
+//     dwords (the other tokens' codes as they were).
+// This launch reads the bytes written here only within the last cached
+// chunk, when the new positions share it: there they are masked keys, whose
+// values do not count (weights 0, scores -inf, zero-points replaced by 0),
+// and the other tokens' codes of a shared V dword are written back unchanged.
 constexpr int kI2NewRows = 8;                   // rows one fused call appends
 template <int D, int QW>
 struct I2NewIn {
