@@ -8,10 +8,11 @@ Inputs come from the seeded host generators (synth), so the oracle sees the
 same fp32 values.  Checked against the oracle:
   * K/V codes and scales of sampled pages (first, middle, the appended tail),
     bit for bit;
-  * for the 2-bit cache (int2decode262k, int2prefill262k: K and V INT2,
-    decoded with the header's layout) codes, scales and zero-points of
-    sampled pages, bit for bit, and the outputs of every query row (decode)
-    or of the sampled rows (prefill);
+  * for the 2-bit cache (int2decode262k, also through the fused step, and
+    int2prefill262k: K and V INT2, decoded with the header's layout) codes,
+    scales and zero-points of sampled pages (the appended tail among them),
+    bit for bit, and the outputs of every query row (decode) or of the
+    sampled rows (prefill);
   * attention outputs and lse of every query row for the decode and verify
     workloads, and of sampled rows (first and last queries of the chunk, the
     page edges 255/256, seeded random ones; heads of every KV group) for the
@@ -103,10 +104,11 @@ def test_full_size(name, fused):
     tu.assert_close(got, ref, got_lse, ref_lse, f"{name}{' fused' if fused else ''} ({len(rows)} rows)")
 
 
-@pytest.mark.parametrize("name", ["int2decode262k", "int2prefill262k"])
-def test_full_size_int2(name):
+@pytest.mark.parametrize("name,fused", [("int2decode262k", False), ("int2prefill262k", False),
+                                        ("int2decode262k", True)])
+def test_full_size_int2(name, fused):
     w = synth.WORKLOADS[name]
-    k, v, q, L, pool, pt, out, lse = _run(w)
+    k, v, q, L, pool, pt, out, lse = _run(w, fused)
     cache = oracle.Int2Cache.from_float(k, v)
     del k, v
     pool_np = pool.cpu().numpy()
@@ -121,4 +123,4 @@ def test_full_size_int2(name):
     ref, ref_lse = oracle.attention(q, cache, w.scale, rows=rows)
     got = np.stack([out[i, h] for i, h in rows])
     got_lse = np.array([lse[i, h] for i, h in rows])
-    tu.assert_close(got, ref, got_lse, ref_lse, f"{name} ({len(rows)} rows)")
+    tu.assert_close(got, ref, got_lse, ref_lse, f"{name}{' fused' if fused else ''} ({len(rows)} rows)")
