@@ -410,14 +410,17 @@ def bench_stream(args, w, n_layers):
     for e in evs:
         hip_ev.destroy(e[0])
         hip_ev.destroy(e[1])
-    # the link's rate for one plain pinned copy of a layer, for reference
+    # the link's rate for plain pinned copies of the same host buffers, as
+    # many as the timed steps make (every layer's, in order, once per step),
+    # for reference
     torch.cuda.synchronize()
     start.record()
-    for _ in range(4):
-        bufs[0].copy_(hosts[0], non_blocking=True)
+    for _ in range(args.steps):
+        for h in hosts:
+            bufs[0].copy_(h, non_blocking=True)
     stop.record()
     torch.cuda.synchronize()
-    copy_gbs = 4 * nbytes / (start.elapsed_time(stop) / 1e3) / 1e9
+    copy_gbs = args.steps * len(hosts) * nbytes / (start.elapsed_time(stop) / 1e3) / 1e9
     bytes_layer = w.ctx * kv_bytes_per_token_layer(w.n_kv, w.head_dim, w.codec)
     us_per_layer = 1000.0 * total_ms / args.steps / n_layers
     value = bytes_layer / (us_per_layer / 1e6) / 1e9
