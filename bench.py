@@ -459,7 +459,8 @@ def main():
                              "stream262k", "int2decode262k", "int2batch16x16k", "int2prefill262k"])
     ap.add_argument("--layers", type=int, default=None, help="layers in the stack (default: the workload's)")
     ap.add_argument("--kernel", type=int, default=0, help="0 auto, 1 VALU, 2 MFMA streaming, 3 MFMA tiled")
-    ap.add_argument("--cps", type=int, default=0, help="32-token chunks per split (0: the library's choice)")
+    ap.add_argument("--cps", type=int, default=0, help="chunks_per_split of kvq_attn_opts: 32-token chunks per wave of a split for the "
+                    "streaming kernels, per split for the others (0: the library's choice)")
     ap.add_argument("--unfused", action="store_true",
                     help="decode / verify: kvq_append, then the attention call (three kernels per layer)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)

@@ -204,7 +204,10 @@ int kvq_prefill_attn(const kvq_layout *layout, const void *d_pool,
  *           3 = MFMA LDS-tiled chunk kernel (both codecs),
  *           4 = MFMA streaming kernel of KVQ_CODEC_INT2 (decode, n_q * group <= 16);
  *           1 and 2 read KVQ_CODEC_Q8K_Q4V only
- *   chunks_per_split: 32-token chunks per merged partial; 0 = automatic.
+ *   chunks_per_split: 0 = automatic.  Kernels 1 and 3: 32-token chunks per
+ *           merged partial.  Kernels 2 and 4: 32-token chunks per wave of a
+ *           split; a merged partial covers the split's waves (the 8 waves of
+ *           a workgroup, or the 4 of a row group above 32 rows) times this.
  *   kernel_begin_event, kernel_end_event: optional hipEvent_t handles (or
  *           NULL), recorded on `stream` immediately before and after the
  *           attention kernel itself (not the split merge), so a caller can time
