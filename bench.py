@@ -200,14 +200,29 @@ def kernel_name(w, kernel: int) -> str:
     return {1: "attn_valu", 2: "attn_mfma_stream", 3: "attn_mfma_tiled"}[kernel]
 
 
-def source_digest(kname: str):
-    """sha256 over the kernel's .hip file and the two headers every kernel
-    includes (kvq_internal.h, kvq_mfma.h), in that order; None if missing."""
-    import hashlib
+def kernel_source_files(kname: str):
+    """The kernel's .hip file and every local header it includes, directly or
+    through another one (`#include "..."` lines), in first-include order."""
+    import re
     csrc = os.path.join(ROOT, "attention_quantized_kv_amd", "csrc")
+    files, todo = [], [os.path.join(csrc, KERNEL_SOURCES[kname])]
+    while todo:
+        path = os.path.normpath(todo.pop(0))
+        if path in files:
+            continue
+        files.append(path)
+        if os.path.exists(path):
+            for m in re.finditer(r'^\s*#\s*include\s+"([^"]+)"', open(path).read(), re.M):
+                todo.append(os.path.join(os.path.dirname(path), m.group(1)))
+    return files
+
+
+def source_digest(kname: str):
+    """sha256 over the kernel's source files (kernel_source_files, in that
+    order); None if one is missing."""
+    import hashlib
     h = hashlib.sha256()
-    for name in (KERNEL_SOURCES[kname], "kvq_internal.h", "kvq_mfma.h"):
-        path = os.path.join(csrc, name)
+    for path in kernel_source_files(kname):
         if not os.path.exists(path):
             return None
         h.update(open(path, "rb").read())

@@ -83,3 +83,28 @@ def test_prefill_outliers_are_the_generators_channels():
 
 def test_cpu_model_is_reported():
     assert isinstance(bench.cpu_model(), str) and bench.cpu_model() != ""
+
+
+def test_source_digest_covers_the_included_headers(tmp_path, monkeypatch):
+    """The digest that gates the committed traffic covers the kernel file and
+    every local header it includes, directly or through another: an edit to
+    kvq_quant.h (included by the streaming and 2-bit kernels, not the tiled
+    one) changes exactly the digests of the kernels that include it."""
+    import shutil
+    src = os.path.join(ROOT, "attention_quantized_kv_amd", "csrc")
+    dst = tmp_path / "attention_quantized_kv_amd" / "csrc"
+    shutil.copytree(src, dst, ignore=shutil.ignore_patterns("*.o"))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    names = {k: [os.path.basename(f) for f in bench.kernel_source_files(k)]
+             for k in ("attn_mfma_stream", "attn_int2", "attn_mfma_tiled")}
+    assert names["attn_mfma_stream"][0] == "attn_mfma_stream.hip"
+    assert {"kvq_internal.h", "kvq_mfma.h", "kvq_quant.h", "kvq_waits.h"} <= set(names["attn_mfma_stream"])
+    assert {"kvq_internal.h", "kvq_mfma.h", "kvq_quant.h"} <= set(names["attn_int2"])
+    assert "kvq_quant.h" not in names["attn_mfma_tiled"]
+    before = {k: bench.source_digest(k) for k in names}
+    with open(dst / "kvq_quant.h", "a") as f:
+        f.write("\n// edited\n")
+    after = {k: bench.source_digest(k) for k in names}
+    assert after["attn_mfma_stream"] != before["attn_mfma_stream"]
+    assert after["attn_int2"] != before["attn_int2"]
+    assert after["attn_mfma_tiled"] == before["attn_mfma_tiled"]
